@@ -1,0 +1,311 @@
+"""Plain fp64 CPU oracle for the ZGCM-1 hybrid attention path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this module.  The product path (the
+HIP library and its Python binding) never imports, calls or falls back to it,
+and this module imports nothing from the product package.
+
+Sources, cited by page title and section:
+
+* [RB] "ZGCM-1:面向数学与智能体搜索的全开源高效基础模型"
+  (paper.rainbus.top/paper/2609.13356): section 前置知识 › 滑动窗口注意力(SWA)与
+  混合注意力 (every token attends to its 128 neighbouring tokens; 27 gated SWA
+  layers + 5 global layers at layers 6/12/18/24/30); section 核心方法 (GQA
+  32 query / 8 KV heads, partial RoPE ratio 0.33, hidden 4096); the
+  structured-data table, row "256K 上下文推理 KV 缓存" (5.0 GiB vs 32.0 GiB, 6.4x).
+* [SB] "7B 打 235B？中关村学院把'小模型怎么活'这道题答成了一份全开源配方"
+  (shibing624.github.io ai-paper-analysis): section 🏗️ 架构 (QK RMSNorm, GQA,
+  RoPE ratio 0.33, 128-token gated SWA, sigmoid gate on the local output,
+  KV 128 KiB -> 20 KiB per token); section 📊 数据与课程 (RoPE base 10M at 256K).
+
+The pages give the method in prose only; the formula of the gate was lost when
+the page was extracted.  Where the pages are silent this module takes the
+plainest reading and says so in each function's docstring.
+
+Everything is computed in float64 from the exact (bf16-representable) input
+values.  Row blocking below is for memory only and changes no arithmetic.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_to_f64",
+    "rms_norm",
+    "rope_angles",
+    "apply_partial_rope",
+    "visible",
+    "attention_fwd",
+    "decode_group",
+    "attention_decode",
+    "kv_cache_bytes_per_token",
+    "kv_cache_bytes",
+    "layer_schedule",
+    "inband_pairs",
+]
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Widen raw bf16 bit patterns (uint16) to float64 exactly."""
+    u = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return u.view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Step 1: QK-RMSNorm  ([SB] 🏗️ 架构: "QK 用 RMSNorm 归一化")
+# ---------------------------------------------------------------------------
+def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm over the last axis (one attention head of D values).
+
+    Reading: per-head statistics over the D = 128 dims, one weight vector of
+    length D shared by all heads, multiplicative weight, epsilon added to the
+    mean square:  x_hat = x / sqrt(mean(x^2) + eps) * gamma.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * np.asarray(gamma, dtype=np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Step 2: partial RoPE  ([RB] 核心方法 / [SB] 🏗️ 架构: rotary ratio 0.33)
+# ---------------------------------------------------------------------------
+def rope_angles(positions: np.ndarray, rope_dim: int, theta: float) -> np.ndarray:
+    """Rotation angles phi[p, j] = p * theta^(-2j/R) for j < R/2 (float64).
+
+    Reading: the frequency exponent is taken over the R rotary dims, not over
+    the whole head.
+    """
+    half = rope_dim // 2
+    j = np.arange(half, dtype=np.float64)
+    omega = np.power(float(theta), -2.0 * j / float(rope_dim))
+    return np.asarray(positions, dtype=np.float64)[:, None] * omega[None, :]
+
+
+def apply_partial_rope(x: np.ndarray, positions: np.ndarray, rope_dim: int,
+                       theta: float) -> np.ndarray:
+    """Rotate the first ``rope_dim`` dims of every head; the rest pass through.
+
+    ``x`` has shape [S, H, D] and ``positions`` shape [S].  Reading: the
+    rotary dims are the first R = floor(0.33 * D) dims, paired rotate-half
+    style as (j, j + R/2):
+        y_j       = x_j cos(phi_j) - x_{j+R/2} sin(phi_j)
+        y_{j+R/2} = x_{j+R/2} cos(phi_j) + x_j sin(phi_j)
+    """
+    x = np.asarray(x, dtype=np.float64)
+    y = x.copy()
+    if rope_dim == 0:
+        return y
+    half = rope_dim // 2
+    phi = rope_angles(positions, rope_dim, theta)  # [S, half]
+    c = np.cos(phi)[:, None, :]
+    s = np.sin(phi)[:, None, :]
+    x1 = x[..., :half]
+    x2 = x[..., half:rope_dim]
+    y[..., :half] = x1 * c - x2 * s
+    y[..., half:rope_dim] = x2 * c + x1 * s
+    return y
+
+
+# ---------------------------------------------------------------------------
+# Steps 3-7: banded / global causal GQA attention with the sigmoid gate
+# ---------------------------------------------------------------------------
+def visible(i: np.ndarray, j: np.ndarray, window: int) -> np.ndarray:
+    """Key j is visible to query i iff j <= i and (window == 0 or i - j < window).
+
+    Reading of [RB] 前置知识 ("与相邻 128 个 token"): the band holds 128 keys
+    including the query itself; window == 0 means global causal attention.
+    """
+    ok = j <= i
+    if window > 0:
+        ok &= (i - j) < window
+    return ok
+
+
+def _sigmoid(g: np.ndarray) -> np.ndarray:
+    # 1 / (1 + e^-g): exact 1 at +inf and exact 0 at -inf.
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-g))
+
+
+def attention_fwd(q, k, v, gate, q_norm_w, k_norm_w, *, window: int,
+                  rope_dim: int, rope_theta: float, rms_eps: float,
+                  softmax_scale: float = 0.0, pos_offset: int = 0,
+                  rows=None, chunk: int = 1024):
+    """Prefill / training forward of one attention layer, in float64.
+
+    Shapes: q [B,S,Hq,D], k and v [B,S,Hkv,D], gate [B,S,Hq,D] or None,
+    norm weights [D].  Returns (out [B,R,Hq,D], lse [B,Hq,R]) where R is S, or
+    len(rows) when ``rows`` (sorted query indices) selects a sample.
+
+    Per query head h the key/value head is h // (Hq // Hkv) (reading: GQA
+    with contiguous groups).  Scores are tau * q'_i . k'_j with
+    tau = softmax_scale or 1/sqrt(D) (reading), softmax over visible keys,
+    out_i = sum_j P_ij v_j, then on a gated layer out_i *= sigmoid(G_i)
+    elementwise (reading of the gate whose formula the page lost: the local
+    attention output is multiplied by a sigmoid gate of the output's shape).
+    LSE is the natural-log log-sum-exp of the scaled scores.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    assert Hq % Hkv == 0
+    grp = Hq // Hkv
+    tau = softmax_scale if softmax_scale > 0 else 1.0 / math.sqrt(D)
+    rows = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    nr = len(rows)
+    out = np.zeros((B, nr, Hq, D), dtype=np.float64)
+    lse = np.zeros((B, Hq, nr), dtype=np.float64)
+    pos = pos_offset + np.arange(S, dtype=np.int64)
+    for b in range(B):
+        # Keys needed: everything up to the last requested row.
+        kmax = int(rows.max()) + 1 if nr else 0
+        kn = rms_norm(k[b, :kmax], k_norm_w, rms_eps)
+        kn = apply_partial_rope(kn, pos[:kmax], rope_dim, rope_theta)
+        vb = v[b, :kmax]
+        for c0 in range(0, nr, chunk):
+            ridx = rows[c0:c0 + chunk]
+            qn = rms_norm(q[b, ridx], q_norm_w, rms_eps)
+            qn = apply_partial_rope(qn, pos[ridx], rope_dim, rope_theta)
+            lo = 0 if window == 0 else max(0, int(ridx.min()) - window + 1)
+            hi = int(ridx.max()) + 1
+            jj = np.arange(lo, hi)
+            mask = visible(ridx[:, None], jj[None, :], window)  # [r, keys]
+            for g in range(Hkv):
+                kg = kn[lo:hi, g, :]                  # [keys, D]
+                vg = vb[lo:hi, g, :]
+                for hh in range(grp):
+                    h = g * grp + hh
+                    s = tau * (qn[:, h, :] @ kg.T)    # [r, keys]
+                    s = np.where(mask, s, -np.inf)
+                    m = np.max(s, axis=1, keepdims=True)
+                    e = np.exp(s - m)
+                    den = np.sum(e, axis=1, keepdims=True)
+                    o = (e @ vg) / den
+                    if gate is not None:
+                        o = o * _sigmoid(np.asarray(gate[b, ridx, h, :], dtype=np.float64))
+                    out[b, c0:c0 + len(ridx), h, :] = o
+                    lse[b, h, c0:c0 + len(ridx)] = (m + np.log(den))[:, 0]
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# Step 8: decode = the last row of the forward over the cached keys
+# ---------------------------------------------------------------------------
+def decode_group(q_group, k_new, v_new, k_cache, v_cache, seq_len: int, *,
+                 ring: bool, window: int, gate_group, q_norm_w, k_norm_w,
+                 rope_dim: int, rope_theta: float, rms_eps: float,
+                 softmax_scale: float = 0.0, pos_offset: int = 0):
+    """One decode step for the query heads of ONE KV head of ONE sequence.
+
+    q_group [G,D] raw new-token queries; k_new, v_new [D] raw new key/value
+    or None when the new token is already in the cache; k_cache, v_cache
+    [cap,D] cache contents before the append, K stored post-norm/RoPE.
+    The new token sits at position p = pos_offset + seq_len - 1 and in cache
+    slot seq_len-1 (linear cache) or (seq_len-1) % cap (ring).  Visible keys
+    are the positions max(0, L-W)..L-1 (W = cap for a ring, W = window > 0
+    for a banded linear cache, all of 0..L-1 for a global one).
+
+    Returns (out [G,D], lse [G], k_appended [D] or None).  Reading: the
+    cache holds K' (normalised and rotated at its own position) and decode is
+    exactly row L-1 of ``attention_fwd`` over the same keys.
+    """
+    q_group = np.asarray(q_group, dtype=np.float64)
+    G, D = q_group.shape
+    cap = k_cache.shape[0]
+    L = int(seq_len)
+    p = pos_offset + L - 1
+    tau = softmax_scale if softmax_scale > 0 else 1.0 / math.sqrt(D)
+    W = cap if ring else window
+    first = max(0, L - W) if W > 0 else 0
+    positions = np.arange(first, L)
+    slots = positions % cap if ring else positions
+    kk = np.asarray(k_cache, dtype=np.float64)[slots].copy()
+    vv = np.asarray(v_cache, dtype=np.float64)[slots].copy()
+    k_app = None
+    if k_new is not None:
+        kn = rms_norm(np.asarray(k_new, dtype=np.float64)[None, None, :], k_norm_w, rms_eps)
+        kn = apply_partial_rope(kn, np.array([p]), rope_dim, rope_theta)[0, 0]
+        k_app = kn
+        kk[-1] = kn
+        vv[-1] = np.asarray(v_new, dtype=np.float64)
+    qn = rms_norm(q_group[None], q_norm_w, rms_eps)
+    qn = apply_partial_rope(qn, np.array([p]), rope_dim, rope_theta)[0]  # [G,D]
+    s = tau * (qn @ kk.T)                       # [G, keys]
+    m = np.max(s, axis=1, keepdims=True)
+    e = np.exp(s - m)
+    den = np.sum(e, axis=1, keepdims=True)
+    o = (e @ vv) / den
+    if gate_group is not None:
+        o = o * _sigmoid(np.asarray(gate_group, dtype=np.float64))
+    return o, (m + np.log(den))[:, 0], k_app
+
+
+def attention_decode(q, k_new, v_new, k_cache, v_cache, seq_lens, *, ring: bool,
+                     window: int, gate, q_norm_w, k_norm_w, rope_dim: int,
+                     rope_theta: float, rms_eps: float, softmax_scale: float = 0.0,
+                     pos_offset: int = 0):
+    """Batched decode: q [B,Hq,D]; k_new, v_new [B,Hkv,D] or None;
+    caches [B,Hkv,cap,D]; seq_lens [B]; gate [B,Hq,D] or None.
+
+    Returns (out [B,Hq,D], lse [B,Hq], cache_k_after [B,Hkv,cap,D]) where the
+    last is the K cache with the appended rows written in.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    grp = Hq // Hkv
+    out = np.zeros((B, Hq, D))
+    lse = np.zeros((B, Hq))
+    k_after = np.array(k_cache, dtype=np.float64, copy=True)
+    for b in range(B):
+        L = int(seq_lens[b])
+        for g in range(Hkv):
+            hs = slice(g * grp, (g + 1) * grp)
+            o, ls, ka = decode_group(
+                q[b, hs], None if k_new is None else k_new[b, g],
+                None if v_new is None else v_new[b, g], k_cache[b, g], v_cache[b, g], L,
+                ring=ring, window=window, gate_group=None if gate is None else gate[b, hs],
+                q_norm_w=q_norm_w, k_norm_w=k_norm_w, rope_dim=rope_dim,
+                rope_theta=rope_theta, rms_eps=rms_eps, softmax_scale=softmax_scale,
+                pos_offset=pos_offset)
+            out[b, hs] = o
+            lse[b, hs] = ls
+            if ka is not None:
+                slot = (L - 1) % cap if ring else L - 1
+                k_after[b, g, slot] = ka
+    return out, lse, k_after
+
+
+# ---------------------------------------------------------------------------
+# KV-cache arithmetic and the layer schedule
+# ([RB] structured-data table row "256K 上下文推理 KV 缓存"; [SB] 🏗️ 架构)
+# ---------------------------------------------------------------------------
+def kv_cache_bytes_per_token(n_layers: int, n_kv_heads: int, head_dim: int,
+                             bytes_per_elem: int) -> int:
+    """Bytes of K and V cached per token over ``n_layers`` attention layers."""
+    return n_layers * n_kv_heads * head_dim * 2 * bytes_per_elem
+
+
+def kv_cache_bytes(n_layers: int, n_kv_heads: int, head_dim: int,
+                   bytes_per_elem: int, n_tokens: int, batch: int = 1) -> int:
+    """Cache bytes for ``batch`` sequences of ``n_tokens`` tokens."""
+    return kv_cache_bytes_per_token(n_layers, n_kv_heads, head_dim, bytes_per_elem) \
+        * n_tokens * batch
+
+
+def layer_schedule(n_layers: int = 32, period: int = 6) -> list:
+    """Layer kinds, 1-based: every ``period``-th layer is global, the rest
+    are gated sliding-window ([RB] 前置知识: global layers 6/12/18/24/30)."""
+    return ["global" if (l % period) == 0 else "swa" for l in range(1, n_layers + 1)]
+
+
+def inband_pairs(S: int, window: int) -> int:
+    """Number of visible (query, key) pairs of one head over S rows."""
+    if window == 0 or window >= S:
+        return S * (S + 1) // 2
+    return window * (window + 1) // 2 + (S - window) * window

@@ -1,0 +1,376 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each test ties one part of the oracle to a closed form, an invariant, a
+brute-force restatement in scalar Python, a library routine on a special
+case, or the numbers printed on the source pages (tests/golden/*.json).
+Chosen so that a dropped term, a wrong sign or index, or a transposed operand
+anywhere in the oracle fails at least one of them.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+from global_attention_zg_amd import inputs
+from oracle import zg_oracle as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+D = 128
+
+
+def _draw(key, shape):
+    n = int(np.prod(shape))
+    bits = inputs.normal_bf16_bits(key, n)
+    return orc.bf16_bits_to_f64(bits).reshape(shape)
+
+
+def _case(S=40, Hq=4, Hkv=1, B=1, seed=0, gated=True):
+    q = _draw((900, seed, inputs.T_Q), (B, S, Hq, D))
+    k = _draw((900, seed, inputs.T_K), (B, S, Hkv, D))
+    v = _draw((900, seed, inputs.T_V), (B, S, Hkv, D))
+    g = _draw((900, seed, inputs.T_GATE), (B, S, Hq, D)) if gated else None
+    gq = inputs.norm_weight((900, seed, inputs.T_GQ), D).astype(np.float64)
+    gk = inputs.norm_weight((900, seed, inputs.T_GK), D).astype(np.float64)
+    return q, k, v, g, gq, gk
+
+
+KW = dict(rope_dim=42, rope_theta=10000.0, rms_eps=1e-6)
+
+
+# ----------------------------------------------------------------------------
+# band / window
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("W", [37, 40, 41, 1000])
+def test_window_at_least_S_equals_global(W):
+    q, k, v, g, gq, gk = _case(S=37)
+    o_w, l_w = orc.attention_fwd(q, k, v, None, gq, gk, window=W, **KW)
+    o_g, l_g = orc.attention_fwd(q, k, v, None, gq, gk, window=0, **KW)
+    np.testing.assert_allclose(o_w, o_g, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l_w, l_g, rtol=0, atol=1e-13)
+
+
+def test_window_one_is_gated_value():
+    """W = 1: each query sees only itself, so O = sigmoid(G) * V_g exactly."""
+    q, k, v, g, gq, gk = _case(S=33, Hq=4, Hkv=2)
+    o, lse = orc.attention_fwd(q, k, v, g, gq, gk, window=1, **KW)
+    vg = np.repeat(v, 2, axis=2)
+    np.testing.assert_allclose(o, scipy.special.expit(g) * vg, rtol=1e-15, atol=1e-15)
+
+
+@pytest.mark.parametrize("W", [0, 1, 5, 16])
+def test_uniform_scores_give_band_average(W):
+    """q = 0 makes every visible score 0: O_i = mean of V over band(i) and
+    LSE_i = ln(#visible keys)."""
+    S = 29
+    q, k, v, g, gq, gk = _case(S=S, Hq=2, Hkv=1)
+    q[:] = 0.0
+    o, lse = orc.attention_fwd(q, k, v, None, gq, gk, window=W, **KW)
+    cs = np.concatenate([np.zeros((1, D)), np.cumsum(v[0, :, 0, :], axis=0)])
+    for i in range(S):
+        lo = 0 if W == 0 else max(0, i - W + 1)
+        n = i + 1 - lo
+        ref = (cs[i + 1] - cs[lo]) / n
+        for h in range(2):
+            np.testing.assert_allclose(o[0, i, h], ref, rtol=0, atol=1e-13)
+            assert abs(lse[0, h, i] - math.log(n)) < 1e-13
+
+
+def test_probability_rows_sum_to_one():
+    """With V == 1 every output is the row sum of P: exactly 1 (fp64)."""
+    q, k, v, g, gq, gk = _case(S=50, Hq=4, Hkv=1)
+    v[:] = 1.0
+    for W in (0, 7, 128):
+        o, _ = orc.attention_fwd(q, k, v, None, gq, gk, window=W, **KW)
+        np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# gate
+# ----------------------------------------------------------------------------
+def test_gate_limits():
+    q, k, v, g, gq, gk = _case(S=20)
+    o_u, _ = orc.attention_fwd(q, k, v, None, gq, gk, window=8, **KW)
+    o_p, _ = orc.attention_fwd(q, k, v, np.full_like(g, np.inf), gq, gk, window=8, **KW)
+    o_n, _ = orc.attention_fwd(q, k, v, np.full_like(g, -np.inf), gq, gk, window=8, **KW)
+    o_0, _ = orc.attention_fwd(q, k, v, np.zeros_like(g), gq, gk, window=8, **KW)
+    assert np.array_equal(o_p, o_u)           # sigmoid(+inf) == 1 exactly
+    assert np.array_equal(o_n, np.zeros_like(o_u))
+    np.testing.assert_allclose(o_0, 0.5 * o_u, rtol=0, atol=0)
+
+
+def test_gate_is_elementwise_sigmoid():
+    q, k, v, g, gq, gk = _case(S=20)
+    o_u, _ = orc.attention_fwd(q, k, v, None, gq, gk, window=8, **KW)
+    o_g, _ = orc.attention_fwd(q, k, v, g, gq, gk, window=8, **KW)
+    np.testing.assert_allclose(o_g, o_u * scipy.special.expit(g), rtol=1e-14, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# RMSNorm
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("eps", [0.0, 1e-6, 0.5])
+def test_rmsnorm_closed_form(eps):
+    x = _draw((901, 0, 0), (64, D)) * np.linspace(0.01, 3.0, 64)[:, None]
+    gamma = inputs.norm_weight((901, 0, 1), D).astype(np.float64)
+    y = orc.rms_norm(x, gamma, eps)
+    ms = np.mean(x * x, axis=1)
+    np.testing.assert_allclose(np.sum((y / gamma) ** 2, axis=1), D * ms / (ms + eps), rtol=1e-13)
+    # direction of each row is unchanged (y / gamma is a positive multiple of x)
+    r = (y / gamma) / x
+    np.testing.assert_allclose(r, r[:, :1] * np.ones_like(r), rtol=1e-13)
+
+
+def test_scale_invariance_without_eps():
+    q, k, v, g, gq, gk = _case(S=24)
+    kw = dict(KW, rms_eps=0.0)
+    o1, l1 = orc.attention_fwd(q, k, v, g, gq, gk, window=8, **kw)
+    o2, l2 = orc.attention_fwd(3.7 * q, 0.25 * k, v, g, gq, gk, window=8, **kw)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# partial RoPE
+# ----------------------------------------------------------------------------
+def test_rope_norm_preserving_and_passthrough():
+    x = _draw((902, 0, 0), (50, 3, D))
+    pos = np.arange(50) * 977 + 5
+    y = orc.apply_partial_rope(x, pos, 42, 10000.0)
+    np.testing.assert_allclose(np.linalg.norm(y[..., :42], axis=-1),
+                               np.linalg.norm(x[..., :42], axis=-1), rtol=1e-13)
+    assert np.array_equal(y[..., 42:], x[..., 42:])
+    assert np.array_equal(orc.apply_partial_rope(x, pos, 0, 10000.0), x)
+
+
+def test_rope_one_hot_rotation_convention():
+    """Reading of the pairing/frequency convention (the pages fix only the
+    ratio): e_j at position p goes to cos(p w_j) e_j + sin(p w_j) e_{j+21},
+    w_j = 1e4^(-2j/42); e_{j+21} goes to -sin e_j + cos e_{j+21}."""
+    R, half = 42, 21
+    for p in (1, 7, 262144):
+        for j in (0, 5, 20):
+            w = 10000.0 ** (-2.0 * j / R)
+            c, s = math.cos(p * w), math.sin(p * w)
+            e = np.zeros((1, 1, D)); e[0, 0, j] = 1.0
+            y = orc.apply_partial_rope(e, np.array([p]), R, 10000.0)[0, 0]
+            ref = np.zeros(D); ref[j] = c; ref[j + half] = s
+            np.testing.assert_allclose(y, ref, rtol=0, atol=1e-12)
+            e = np.zeros((1, 1, D)); e[0, 0, j + half] = 1.0
+            y = orc.apply_partial_rope(e, np.array([p]), R, 10000.0)[0, 0]
+            ref = np.zeros(D); ref[j] = -s; ref[j + half] = c
+            np.testing.assert_allclose(y, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("W", [0, 6])
+def test_relative_position_invariance(W):
+    """Shifting every position by the same offset leaves attention unchanged."""
+    q, k, v, g, gq, gk = _case(S=30, Hq=4, Hkv=2)
+    o0, l0 = orc.attention_fwd(q, k, v, g, gq, gk, window=W, **KW)
+    o1, l1 = orc.attention_fwd(q, k, v, g, gq, gk, window=W, pos_offset=100003, **KW)
+    np.testing.assert_allclose(o0, o1, rtol=0, atol=1e-10)
+    np.testing.assert_allclose(l0, l1, rtol=0, atol=1e-10)
+
+
+def test_rope_changes_result_when_enabled():
+    q, k, v, g, gq, gk = _case(S=30)
+    o0, _ = orc.attention_fwd(q, k, v, None, gq, gk, window=0, **dict(KW, rope_dim=0))
+    o1, _ = orc.attention_fwd(q, k, v, None, gq, gk, window=0, **KW)
+    assert np.max(np.abs(o0 - o1)) > 1e-3
+
+
+# ----------------------------------------------------------------------------
+# GQA
+# ----------------------------------------------------------------------------
+def test_gqa_equals_repeated_mha():
+    q, k, v, g, gq, gk = _case(S=26, Hq=8, Hkv=2)
+    o1, l1 = orc.attention_fwd(q, k, v, g, gq, gk, window=5, **KW)
+    k4, v4 = np.repeat(k, 4, axis=2), np.repeat(v, 4, axis=2)
+    o2, l2 = orc.attention_fwd(q, k4, v4, g, gq, gk, window=5, **KW)
+    assert np.array_equal(o1, o2) or np.max(np.abs(o1 - o2)) < 1e-14
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# brute force in scalar Python (math.fsum), and a library special case
+# ----------------------------------------------------------------------------
+def _brute(q, k, v, g, gq, gk, W, R, theta, eps, pos_offset=0):
+    S, Hq, _ = q.shape
+    Hkv = k.shape[1]
+    grp = Hq // Hkv
+    tau = 1.0 / math.sqrt(D)
+
+    def norm(x, gam):
+        ms = math.fsum(t * t for t in x) / D
+        r = 1.0 / math.sqrt(ms + eps)
+        return [x[d] * r * gam[d] for d in range(D)]
+
+    def rot(x, p):
+        y = list(x)
+        half = R // 2
+        for j in range(half):
+            a = p * theta ** (-2.0 * j / R)
+            y[j] = x[j] * math.cos(a) - x[j + half] * math.sin(a)
+            y[j + half] = x[j + half] * math.cos(a) + x[j] * math.sin(a)
+        return y
+
+    kn = [[rot(norm(list(k[j, gg]), gk), pos_offset + j) for gg in range(Hkv)] for j in range(S)]
+    out = np.zeros((S, Hq, D))
+    lse = np.zeros((Hq, S))
+    for i in range(S):
+        for h in range(Hq):
+            gg = h // grp
+            qi = rot(norm(list(q[i, h]), gq), pos_offset + i)
+            keys = [j for j in range(S) if j <= i and (W == 0 or i - j < W)]
+            sc = [tau * math.fsum(qi[d] * kn[j][gg][d] for d in range(D)) for j in keys]
+            m = max(sc)
+            ex = [math.exp(s - m) for s in sc]
+            den = math.fsum(ex)
+            for d in range(D):
+                val = math.fsum(ex[t] * v[keys[t], gg, d] for t in range(len(keys))) / den
+                if g is not None:
+                    val *= 1.0 / (1.0 + math.exp(-g[i, h, d]))
+                out[i, h, d] = val
+            lse[h, i] = m + math.log(den)
+    return out, lse
+
+
+@pytest.mark.parametrize("W,S", [(1, 9), (3, 12), (128, 16), (0, 11)])
+def test_brute_force_tiny(W, S):
+    q, k, v, g, gq, gk = _case(S=S, Hq=4, Hkv=1, seed=W)
+    o, lse = orc.attention_fwd(q, k, v, g, gq, gk, window=W, pos_offset=3, **KW)
+    ob, lb = _brute(q[0], k[0], v[0], g[0], gq, gk, W, 42, 10000.0, 1e-6, pos_offset=3)
+    np.testing.assert_allclose(o[0], ob, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[0], lb, rtol=0, atol=1e-12)
+
+
+def test_torch_sdpa_special_case():
+    """R = 0, gamma = 1, no gate: equals torch's fp64 SDPA with a band mask on
+    rms-normalised q and k (torch.nn.functional.rms_norm)."""
+    torch = pytest.importorskip("torch")
+    F = torch.nn.functional
+    S, Hq, Hkv, W = 45, 8, 2, 9
+    q, k, v, g, gq, gk = _case(S=S, Hq=Hq, Hkv=Hkv, B=2)
+    ones = np.ones(D)
+    o, _ = orc.attention_fwd(q, k, v, None, ones, ones, window=W, rope_dim=0,
+                             rope_theta=10000.0, rms_eps=1e-6)
+    tq = F.rms_norm(torch.from_numpy(q), (D,), eps=1e-6).transpose(1, 2)
+    tk = F.rms_norm(torch.from_numpy(k), (D,), eps=1e-6).transpose(1, 2)
+    tv = torch.from_numpy(v).transpose(1, 2)
+    i = torch.arange(S)[:, None]
+    j = torch.arange(S)[None, :]
+    mask = (j <= i) & (i - j < W)
+    ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, enable_gqa=True)
+    np.testing.assert_allclose(o, ref.transpose(1, 2).numpy(), rtol=0, atol=1e-13)
+
+
+def test_sampled_rows_match_full():
+    q, k, v, g, gq, gk = _case(S=70, Hq=4, Hkv=1)
+    rows = np.array([0, 1, 31, 32, 69])
+    for W in (0, 16):
+        o, l = orc.attention_fwd(q, k, v, g, gq, gk, window=W, **KW)
+        os_, ls = orc.attention_fwd(q, k, v, g, gq, gk, window=W, rows=rows, **KW)
+        np.testing.assert_allclose(os_, o[:, rows], rtol=0, atol=1e-14)
+        np.testing.assert_allclose(ls, l[:, :, rows], rtol=0, atol=1e-14)
+
+
+def test_chunking_changes_nothing():
+    q, k, v, g, gq, gk = _case(S=70, Hq=4, Hkv=1)
+    o1, l1 = orc.attention_fwd(q, k, v, g, gq, gk, window=9, **KW)
+    o2, l2 = orc.attention_fwd(q, k, v, g, gq, gk, window=9, chunk=7, **KW)
+    np.testing.assert_allclose(o1, o2, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, rtol=0, atol=1e-14)
+
+
+# ----------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------
+def _prefilled_cache(k, v, gk, cap, ring, S):
+    """Cache holding K' (normalised + rotated) of positions 0..S-2."""
+    kn = orc.rms_norm(k[0], gk, 1e-6)
+    kn = orc.apply_partial_rope(kn, np.arange(S), 42, 10000.0)
+    Hkv = k.shape[2]
+    kc = np.full((Hkv, cap, D), 7.0)   # junk in unused slots
+    vc = np.full((Hkv, cap, D), -3.0)
+    for p in range(S - 1):
+        slot = p % cap if ring else p
+        kc[:, slot] = kn[p]
+        vc[:, slot] = v[0, p]
+    return kc, vc, kn
+
+
+@pytest.mark.parametrize("ring,W,S,cap", [(False, 0, 37, 48), (True, 8, 37, 8),
+                                          (True, 8, 5, 8), (False, 6, 21, 32)])
+def test_decode_is_last_row_of_prefill(ring, W, S, cap):
+    q, k, v, g, gq, gk = _case(S=S, Hq=4, Hkv=2)
+    o, l = orc.attention_fwd(q, k, v, g, gq, gk, window=W, **KW)
+    kc, vc, kn = _prefilled_cache(k, v, gk, cap, ring, S)
+    for gg in range(2):
+        hs = slice(2 * gg, 2 * gg + 2)
+        od, ld, ka = orc.decode_group(q[0, S - 1, hs], k[0, S - 1, gg], v[0, S - 1, gg],
+                                      kc[gg], vc[gg], S, ring=ring, window=W,
+                                      gate_group=g[0, S - 1, hs], q_norm_w=gq, k_norm_w=gk, **KW)
+        np.testing.assert_allclose(od, o[0, S - 1, hs], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(ld, l[0, hs, S - 1], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(ka, kn[S - 1, gg], rtol=0, atol=1e-15)
+        # new token already in the cache gives the same answer
+        kc2, vc2 = kc[gg].copy(), vc[gg].copy()
+        slot = (S - 1) % cap if ring else S - 1
+        kc2[slot], vc2[slot] = ka, v[0, S - 1, gg]
+        od2, _, _ = orc.decode_group(q[0, S - 1, hs], None, None, kc2, vc2, S, ring=ring,
+                                     window=W, gate_group=g[0, S - 1, hs], q_norm_w=gq,
+                                     k_norm_w=gk, **KW)
+        np.testing.assert_allclose(od2, od, rtol=0, atol=0)
+
+
+def test_batched_decode_wrapper():
+    S, cap = 19, 24
+    q, k, v, g, gq, gk = _case(S=S, Hq=4, Hkv=2)
+    kc, vc, kn = _prefilled_cache(k, v, gk, cap, False, S)
+    out, lse, kafter = orc.attention_decode(
+        q[:, S - 1], k[:, S - 1], v[:, S - 1], kc[None], vc[None], [S], ring=False,
+        window=0, gate=g[:, S - 1], q_norm_w=gq, k_norm_w=gk, **KW)
+    o, l = orc.attention_fwd(q, k, v, g, gq, gk, window=0, **KW)
+    np.testing.assert_allclose(out[0], o[0, S - 1], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(kafter[0, :, S - 1], kn[S - 1], rtol=0, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# the pages' own numbers
+# ----------------------------------------------------------------------------
+def test_kv_cache_arithmetic_matches_pages():
+    with open(os.path.join(GOLDEN, "kv_cache_pages.json")) as f:
+        gd = json.load(f)
+    full_tok = orc.kv_cache_bytes_per_token(gd["n_layers"], gd["n_kv_heads"], gd["head_dim"],
+                                            gd["bytes_per_elem"])
+    hyb_tok = orc.kv_cache_bytes_per_token(gd["n_global_layers"], gd["n_kv_heads"],
+                                           gd["head_dim"], gd["bytes_per_elem"])
+    assert full_tok == gd["per_token_full_KiB"] * 1024
+    assert hyb_tok == gd["per_token_hybrid_KiB"] * 1024
+    full = orc.kv_cache_bytes(gd["n_layers"], gd["n_kv_heads"], gd["head_dim"],
+                              gd["bytes_per_elem"], gd["context_tokens"], gd["batch"])
+    hyb = orc.kv_cache_bytes(gd["n_global_layers"], gd["n_kv_heads"], gd["head_dim"],
+                             gd["bytes_per_elem"], gd["context_tokens"], gd["batch"])
+    assert round(full / 2**30, 1) == gd["full_GiB"]
+    assert round(hyb / 2**30, 1) == gd["hybrid_GiB"]
+    assert round(full / hyb, 1) == gd["reduction"]
+
+
+def test_layer_schedule_matches_pages():
+    with open(os.path.join(GOLDEN, "layer_schedule_pages.json")) as f:
+        gd = json.load(f)
+    sched = orc.layer_schedule(gd["n_layers"])
+    glob = [i + 1 for i, t in enumerate(sched) if t == "global"]
+    assert glob == gd["global_layers_1based"]
+    assert sched.count("swa") == gd["n_swa_layers"]
+
+
+def test_inband_pair_count_matches_enumeration():
+    for S, W in ((1, 128), (100, 128), (300, 128), (300, 0), (64, 1)):
+        i = np.arange(S)[:, None]
+        j = np.arange(S)[None, :]
+        assert orc.inband_pairs(S, W) == int(orc.visible(i, j, W).sum())
