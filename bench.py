@@ -1,0 +1,326 @@
+#!/usr/bin/env python3
+"""Benchmark of the ZGCM-1 hybrid attention path on one MI355X.
+
+One step = one forward pass of a 256K-token 5:1 block: five gated
+sliding-window (W = 128) layers and one global causal layer, batch 1, GQA
+32/8, head dim 128, each layer on its own seeded bf16 N(0,1) inputs (QK-RMSNorm
+and partial RoPE on 42 dims run inside the library).  The printed JSON line
+reports the block's attention TFLOP/s (in-band pairs only, 512 flop per pair
+per query head) and tokens/s, the roofline of the dominant kernel (the global
+layer's flash kernel, MFMA-bound), the other workloads as components (gated
+SWA B4xS4096, global S16384, one decode step against a 256K cache) and the
+fp64 CPU oracle timed on a bounded sample of the same block.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+FLOP_PER_PAIR = 4 * 128     # QK^T and PV, 2 flop per MAC, head dim 128
+D = 128
+KW = dict(rope_dim=42, rope_theta=10000.0, rms_eps=1e-6)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flash_fwd_global_256k_traffic.json")
+FLASH_SRC = os.path.join(ROOT, "global_attention_zg_amd", "csrc", "flash_fwd.hip")
+
+
+def inband_pairs(S, W):
+    if W == 0 or W >= S:
+        return S * (S + 1) // 2
+    return W * (W + 1) // 2 + (S - W) * W
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def dev_tensor(torch, key, shape):
+    from global_attention_zg_amd import inputs
+    n = int(np.prod(shape))
+    out = torch.empty(shape, dtype=torch.bfloat16, device="cuda")
+    flat = out.view(-1)
+    step = 1 << 26
+    for s0 in range(0, n, step):
+        s1 = min(n, s0 + step)
+        bits = inputs.normal_bf16_bits(key, n, s0, s1)
+        flat[s0:s1].copy_(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16))
+    return out
+
+
+def norm_w(torch, key):
+    from global_attention_zg_amd import inputs
+    return torch.from_numpy(inputs.norm_weight(key, D)).cuda()
+
+
+class Layer:
+    """Device-resident inputs, outputs and workspace of one forward layer."""
+
+    def __init__(self, torch, bd, tag, layer, B, S, Hq, Hkv, window, gated):
+        from global_attention_zg_amd import inputs
+        self.window = window
+        self.q = dev_tensor(torch, (tag, layer, inputs.T_Q), (B, S, Hq, D))
+        self.k = dev_tensor(torch, (tag, layer, inputs.T_K), (B, S, Hkv, D))
+        self.v = dev_tensor(torch, (tag, layer, inputs.T_V), (B, S, Hkv, D))
+        self.g = dev_tensor(torch, (tag, layer, inputs.T_GATE), (B, S, Hq, D)) if gated else None
+        self.gq = norm_w(torch, (tag, layer, inputs.T_GQ))
+        self.gk = norm_w(torch, (tag, layer, inputs.T_GK))
+        self.out = torch.empty_like(self.q)
+        p = bd.make_params(B, S, Hq, Hkv, D, window)
+        self.ws = torch.empty(bd.zg_attn_fwd_workspace_size(p), dtype=torch.uint8, device="cuda")
+        self.bd = bd
+        self.flops = B * Hq * inband_pairs(S, window) * FLOP_PER_PAIR
+        self.alg_bytes = (self.q.numel() + self.k.numel() + self.v.numel() + self.out.numel()
+                          + (self.g.numel() if gated else 0)) * 2
+
+    def __call__(self):
+        self.bd.zg_attn_fwd(self.q, self.k, self.v, self.g, self.gq, self.gk, window=self.window,
+                            out=self.out, workspace=self.ws, **KW)
+
+
+def time_events(torch, fn, iters):
+    """Average duration of fn() on the current stream, by HIP events."""
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for a, b in evs:
+        a.record(st)
+        fn()
+        b.record(st)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
+
+
+def flash_source_hash():
+    with open(FLASH_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per launch of the global-layer flash kernel from the committed
+    rocprofv3 counter summary, or None if it is missing or stale."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("flash_fwd_sha256_16") != flash_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline():
+    """The fp64 oracle timed on a bounded sample of the block: the first 4096
+    query rows of one gated SWA layer and the first 8192 rows of the global
+    layer (all 32 query heads), with the same seeded inputs."""
+    from global_attention_zg_amd import inputs
+    from oracle import zg_oracle as orc
+
+    S_full = 262144
+
+    def f64(key, shape):
+        # prefix of the full [1, S_full, H, D] tensor, same seeded elements
+        total = S_full * int(np.prod(shape[2:]))
+        n = int(np.prod(shape))
+        return orc.bf16_bits_to_f64(inputs.normal_bf16_bits(key, total, 0, n)).reshape(shape)
+
+    flops = 0
+    t_total = 0.0
+    for layer, window, rows, gated in ((0, 128, 4096, True), (5, 0, 8192, False)):
+        # the first `rows` positions of the layer's tensors are a prefix of the
+        # full [1, S, H, D] tensors in the flat element order
+        q = f64((4, layer, inputs.T_Q), (1, rows, 32, D))
+        k = f64((4, layer, inputs.T_K), (1, rows, 8, D))
+        v = f64((4, layer, inputs.T_V), (1, rows, 8, D))
+        g = f64((4, layer, inputs.T_GATE), (1, rows, 32, D)) if gated else None
+        gq = inputs.norm_weight((4, layer, inputs.T_GQ), D).astype(np.float64)
+        gk = inputs.norm_weight((4, layer, inputs.T_GK), D).astype(np.float64)
+        t0 = time.perf_counter()
+        orc.attention_fwd(q, k, v, g, gq, gk, window=window, **KW)
+        t_total += time.perf_counter() - t0
+        flops += 32 * inband_pairs(rows, window) * FLOP_PER_PAIR
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    return dict(value=round(flops / t_total / 1e12, 6), unit="TFLOP/s", cores=int(threads),
+                kind="oracle",
+                sample="first 4096 query rows of one gated SWA layer + first 8192 rows of the "
+                       "global layer of the 256K block, all 32 query heads, fp64 numpy; "
+                       f"{flops / 1e9:.1f} GFLOP in {t_total:.1f} s",
+                seconds=round(t_total, 2))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from global_attention_zg_amd import binding as bd
+    torch.cuda.set_device(0)
+
+    # ---- the 256K 5:1 block: five gated SWA layers + one global layer
+    S, B, Hq, Hkv = 262144, 1, 32, 8
+    log("generating the 256K block inputs (6 layers)")
+    layers = [Layer(torch, bd, 4, l, B, S, Hq, Hkv, 128, True) for l in range(5)]
+    layers.append(Layer(torch, bd, 4, 5, B, S, Hq, Hkv, 0, False))
+    glob = layers[-1]
+    block_flops = sum(l.flops for l in layers)
+
+    def step(ev=None):
+        for l in layers[:5]:
+            l()
+        if ev is not None:
+            ev[0].record()
+        glob()
+        if ev is not None:
+            ev[1].record()
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    gevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(gevs[i])
+    torch.cuda.synchronize()
+    t_step = (time.perf_counter() - t0) / args.steps
+    t_glob = float(np.mean([a.elapsed_time(b) for a, b in gevs])) * 1e-3
+    log(f"step {t_step * 1e3:.2f} ms, global layer {t_glob * 1e3:.2f} ms")
+    swa_t = time_events(torch, layers[0], 5)
+    achieved = glob.flops / t_glob / 1e12
+    traffic = read_traffic()
+
+    result = {
+        "metric": "attention TFLOP/s & tokens/s per MI355X, gated SWA-128 + global, 4K-256K",
+        "value": round(block_flops / t_step / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t_step * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded bf16 N(0,1) q/k/v/gate per layer, RMSNorm weights 1+0.1N(0,1)",
+        "config": {"workload": "zgcm1_5to1_block_prefill_256k", "global_batch": B, "seq_len": S,
+                   "layers": "5 gated SWA (W=128) + 1 global causal", "q_heads": Hq,
+                   "kv_heads": Hkv, "head_dim": D, "rope_dim": 42, "parallelism": "none"},
+        "tokens_per_s": round(B * S / t_step, 1),
+        "roofline": {"bound": "mfma", "kernel": "flash_fwd_kernel (global causal, S=262144)",
+                     "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "block_breakdown_ms": {"swa_layer": round(swa_t * 1e3, 3),
+                               "global_layer": round(t_glob * 1e3, 3)},
+    }
+    del layers, glob
+    torch.cuda.empty_cache()
+
+    if not args.no_components:
+        comps = {}
+        log("component: gated SWA B4 S4096")
+        l2 = Layer(torch, bd, 2, 0, 4, 4096, 32, 8, 128, True)
+        for _ in range(3):
+            l2()
+        t = time_events(torch, l2, 20)
+        comps["swa_4k_b4"] = {"ms": round(t * 1e3, 4), "tflops": round(l2.flops / t / 1e12, 2),
+                              "tokens_per_s": round(4 * 4096 / t, 1),
+                              "hbm_gbs_alg": round(l2.alg_bytes / t / 1e9, 1),
+                              "frac_hbm": round(l2.alg_bytes / t / 1e9 / PEAK_HBM_GBS, 4)}
+        del l2
+        log("component: global S16384")
+        l3 = Layer(torch, bd, 3, 0, 1, 16384, 32, 8, 0, False)
+        for _ in range(2):
+            l3()
+        t = time_events(torch, l3, 10)
+        comps["global_16k"] = {"ms": round(t * 1e3, 4), "tflops": round(l3.flops / t / 1e12, 2),
+                               "tokens_per_s": round(16384 / t, 1),
+                               "frac_mfma": round(l3.flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del l3
+        torch.cuda.empty_cache()
+        comps.update(decode_components(torch, bd))
+        result["components"] = comps
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle, bounded sample)")
+        result["cpu_baseline"] = cpu_baseline()
+    result["host"] = {"cpu": platform.processor() or platform.machine(),
+                      "affinity_cores": len(os.sched_getaffinity(0))}
+    print(json.dumps(result), flush=True)
+
+
+def decode_components(torch, bd):
+    """One decode step of the block's two layer kinds at 256K: B16, one new
+    token at position 262144 against the global layer's 262145-key cache and
+    the SWA layer's 128-slot ring."""
+    from global_attention_zg_amd import inputs
+    B, Hq, Hkv, L = 16, 32, 8, 262145
+    out = {}
+    for kind, layer, cap, ring, window, gated in (("decode_global_256k", 0, L, False, 0, False),
+                                                  ("decode_swa_ring", 1, 128, True, 128, True)):
+        log(f"component: {kind}")
+        kc = dev_tensor(torch, (5, layer, inputs.T_KCACHE), (B, Hkv, cap, D))
+        vc = dev_tensor(torch, (5, layer, inputs.T_VCACHE), (B, Hkv, cap, D))
+        q = dev_tensor(torch, (5, layer, inputs.T_Q), (B, Hq, D))
+        kn = dev_tensor(torch, (5, layer, inputs.T_KNEW), (B, Hkv, D))
+        vn = dev_tensor(torch, (5, layer, inputs.T_VNEW), (B, Hkv, D))
+        g = dev_tensor(torch, (5, layer, inputs.T_GATE), (B, Hq, D)) if gated else None
+        gq = norm_w(torch, (5, layer, inputs.T_GQ))
+        gk = norm_w(torch, (5, layer, inputs.T_GK))
+        sl = torch.full((B,), L, dtype=torch.int32, device="cuda")
+        o = torch.empty_like(q)
+        p = bd.make_params(B, 0, Hq, Hkv, D, window)
+        ws = torch.empty(bd.zg_attn_decode_workspace_size(p, cap, 0), dtype=torch.uint8,
+                         device="cuda")
+
+        def fn():
+            bd.zg_attn_decode(q, kn, vn, kc, vc, sl, ring=ring, window=window, gate=g,
+                              q_norm_w=gq, k_norm_w=gk, out=o, workspace=ws, **KW)
+
+        for _ in range(2):
+            fn()
+        t = time_events(torch, fn, 10)
+        keys = min(L, cap)
+        alg = B * Hkv * keys * D * 2 * 2 + (q.numel() * 2 + o.numel()) * 2
+        flops = B * Hq * keys * FLOP_PER_PAIR
+        out[kind] = {"ms": round(t * 1e3, 4), "tokens_per_s": round(B / t, 1),
+                     "hbm_gbs_alg": round(alg / t / 1e9, 1),
+                     "frac_hbm": round(alg / t / 1e9 / PEAK_HBM_GBS, 4),
+                     "tflops": round(flops / t / 1e12, 3),
+                     "splits": bd.zg_attn_decode_num_splits(p, cap)}
+        del kc, vc
+        torch.cuda.empty_cache()
+    return out
+
+
+if __name__ == "__main__":
+    main()

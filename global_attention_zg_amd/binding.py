@@ -1,0 +1,161 @@
+"""Thin ctypes binding over libzgattn.so (C ABI in include/zg_attn.h).
+
+Argument marshalling only: tensors are passed as device pointers and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  torch is used for device memory (outputs, workspace) and streams.
+Importing this module loads the library and raises if it is missing: there is
+no other implementation to fall back to.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libzgattn.so")
+
+ZG_OK = 0
+ZG_ERR_INVALID = -1
+ZG_ERR_UNSUPPORTED = -2
+ZG_ERR_WORKSPACE = -3
+ZG_ERR_HIP = -4
+
+
+class ZgAttnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"zg_attn status {status}: {msg}")
+        self.status = status
+
+
+class Params(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int),
+        ("seqlen", ctypes.c_int),
+        ("n_q_heads", ctypes.c_int),
+        ("n_kv_heads", ctypes.c_int),
+        ("head_dim", ctypes.c_int),
+        ("window", ctypes.c_int),
+        ("rope_dim", ctypes.c_int),
+        ("rope_theta", ctypes.c_float),
+        ("rms_eps", ctypes.c_float),
+        ("softmax_scale", ctypes.c_float),
+        ("pos_offset", ctypes.c_longlong),
+    ]
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built; run global_attention_zg_amd.build")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.POINTER(Params)
+    vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.zg_attn_fwd_workspace_size.argtypes = [P]
+    lib.zg_attn_fwd_workspace_size.restype = sz
+    lib.zg_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.zg_attn_fwd.restype = i
+    lib.zg_attn_decode_num_splits.argtypes = [P, i]
+    lib.zg_attn_decode_num_splits.restype = i
+    lib.zg_attn_decode_workspace_size.argtypes = [P, i, i]
+    lib.zg_attn_decode_workspace_size.restype = sz
+    lib.zg_attn_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, i, i, vp, vp, vp, vp, i, vp, sz, vp]
+    lib.zg_attn_decode.restype = i
+    lib.zg_attn_strerror.argtypes = [i]
+    lib.zg_attn_strerror.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+EXPORTED = ("zg_attn_fwd_workspace_size", "zg_attn_fwd", "zg_attn_decode_num_splits",
+            "zg_attn_decode_workspace_size", "zg_attn_decode", "zg_attn_strerror")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def zg_attn_strerror(status: int) -> str:
+    return _lib.zg_attn_strerror(status).decode()
+
+
+def _check(status: int):
+    if status != ZG_OK:
+        raise ZgAttnError(status, zg_attn_strerror(status))
+
+
+def make_params(batch, seqlen, n_q_heads, n_kv_heads, head_dim=128, window=0, rope_dim=42,
+                rope_theta=10000.0, rms_eps=1e-6, softmax_scale=0.0, pos_offset=0) -> Params:
+    return Params(batch, seqlen, n_q_heads, n_kv_heads, head_dim, window, rope_dim,
+                  rope_theta, rms_eps, softmax_scale, pos_offset)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def zg_attn_fwd_workspace_size(p: Params) -> int:
+    return int(_lib.zg_attn_fwd_workspace_size(ctypes.byref(p)))
+
+
+def zg_attn_fwd(q, k, v, gate, q_norm_w, k_norm_w, *, window, rope_dim=42, rope_theta=10000.0,
+                rms_eps=1e-6, softmax_scale=0.0, pos_offset=0, out=None, lse=None,
+                want_lse=False, k_out=None, workspace=None, stream=None):
+    """q [B,S,Hq,128], k/v [B,S,Hkv,128], gate [B,S,Hq,128] or None (bf16, CUDA);
+    norm weights fp32 [128].  Returns (out, lse or None)."""
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    p = make_params(B, S, Hq, Hkv, D, window, rope_dim, rope_theta, rms_eps, softmax_scale,
+                    pos_offset)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    ws_bytes = 0
+    if k_out is None:
+        ws_bytes = zg_attn_fwd_workspace_size(p)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.zg_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(q_norm_w),
+                          _ptr(k_norm_w), _ptr(out), _ptr(lse), _ptr(k_out),
+                          _ptr(workspace) if k_out is None else None, ws_bytes, _stream(stream))
+    _check(st)
+    return out, lse
+
+
+def zg_attn_decode_num_splits(p: Params, cache_cap: int) -> int:
+    return int(_lib.zg_attn_decode_num_splits(ctypes.byref(p), cache_cap))
+
+
+def zg_attn_decode_workspace_size(p: Params, cache_cap: int, num_splits: int = 0) -> int:
+    return int(_lib.zg_attn_decode_workspace_size(ctypes.byref(p), cache_cap, num_splits))
+
+
+def zg_attn_decode(q, k_new, v_new, k_cache, v_cache, seq_lens, *, ring, window, gate, q_norm_w,
+                   k_norm_w, rope_dim=42, rope_theta=10000.0, rms_eps=1e-6, softmax_scale=0.0,
+                   pos_offset=0, num_splits=0, out=None, workspace=None, stream=None):
+    """q [B,Hq,128]; k_new/v_new [B,Hkv,128] or None; caches [B,Hkv,cap,128]
+    (updated in place); seq_lens int32 [B] on the device.  Returns out."""
+    B, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    p = make_params(B, 0, Hq, Hkv, D, window, rope_dim, rope_theta, rms_eps, softmax_scale,
+                    pos_offset)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        nbytes = zg_attn_decode_workspace_size(p, cap, num_splits)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.zg_attn_decode(ctypes.byref(p), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache),
+                             _ptr(v_cache), _ptr(seq_lens), cap, int(ring), _ptr(gate),
+                             _ptr(q_norm_w), _ptr(k_norm_w), _ptr(out), num_splits,
+                             _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st)
+    return out

@@ -1,0 +1,204 @@
+// C ABI of libzgattn (declared in include/zg_attn.h): argument validation,
+// workspace sizing and kernel launches on the caller's stream.
+//
+// Nothing here allocates device memory or synchronises; every error is
+// reported before the first launch.
+
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/zg_attn.h"
+#include "zg_launch.h"
+
+namespace {
+
+using zg::kD;
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// Shape / numeric checks common to both entry points.
+int check_params(const zg_attn_params* p) {
+  if (!p) return ZG_ERR_INVALID;
+  if (p->batch < 0 || p->seqlen < 0 || p->n_q_heads < 1 || p->n_kv_heads < 1 || p->window < 0)
+    return ZG_ERR_INVALID;
+  if (p->n_q_heads % p->n_kv_heads != 0) return ZG_ERR_INVALID;
+  const int grp = p->n_q_heads / p->n_kv_heads;
+  if (grp != 1 && grp != 2 && grp != 4 && grp != 8) return ZG_ERR_UNSUPPORTED;
+  if (p->head_dim <= 0) return ZG_ERR_INVALID;
+  if (p->head_dim != kD) return ZG_ERR_UNSUPPORTED;
+  if (p->rope_dim < 0 || (p->rope_dim & 1) || p->rope_dim > p->head_dim) return ZG_ERR_INVALID;
+  if (p->rope_dim > p->head_dim / 2) return ZG_ERR_UNSUPPORTED;
+  if (p->rope_dim > 0 && !(isfinite(p->rope_theta) && p->rope_theta > 0.f)) return ZG_ERR_INVALID;
+  if (!(isfinite(p->rms_eps) && p->rms_eps >= 0.f)) return ZG_ERR_INVALID;
+  if (!(isfinite(p->softmax_scale) && p->softmax_scale >= 0.f)) return ZG_ERR_INVALID;
+  return ZG_OK;
+}
+
+zg::RopeTable make_rope_table(const zg_attn_params* p) {
+  zg::RopeTable t{};
+  const int half = p->rope_dim / 2;
+  for (int i = 0; i < half; ++i)
+    t.rev[i] = pow((double)p->rope_theta, -2.0 * i / (double)p->rope_dim) / (2.0 * M_PI);
+  return t;
+}
+
+float scale_log2(const zg_attn_params* p) {
+  const double s = p->softmax_scale > 0.f ? (double)p->softmax_scale : 1.0 / sqrt((double)kD);
+  return (float)(s * 1.4426950408889634);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? ZG_OK : ZG_ERR_HIP; }
+
+size_t kprime_bytes(const zg_attn_params* p) {
+  return (size_t)p->batch * (size_t)p->seqlen * (size_t)p->n_kv_heads * kD * 2;
+}
+
+int auto_splits(const zg_attn_params* p, int cache_cap) {
+  const long long pairs = (long long)p->batch * p->n_kv_heads;
+  if (pairs <= 0) return 1;
+  long long s = (1024 + pairs - 1) / pairs;       // ~4 workgroups per CU
+  const long long by_len = (cache_cap + 255) / 256;  // >= 256 keys per split
+  if (s > by_len) s = by_len;
+  if (s < 1) s = 1;
+  if (s > 64) s = 64;
+  return (int)s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* zg_attn_strerror(int status) {
+  switch (status) {
+    case ZG_OK: return "ok";
+    case ZG_ERR_INVALID: return "invalid argument (null pointer, bad shape or misaligned pointer)";
+    case ZG_ERR_UNSUPPORTED: return "unsupported configuration";
+    case ZG_ERR_WORKSPACE: return "workspace missing or too small";
+    case ZG_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t zg_attn_fwd_workspace_size(const zg_attn_params* p) {
+  if (check_params(p) != ZG_OK) return 0;
+  return kprime_bytes(p);
+}
+
+int zg_attn_fwd(const zg_attn_params* p, const void* q, const void* k, const void* v,
+                const void* gate, const float* q_norm_w, const float* k_norm_w, void* out,
+                float* lse, void* k_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_params(p);
+  if (st != ZG_OK) return st;
+  if ((long long)p->seqlen * p->n_q_heads > 0x7fffffffLL) return ZG_ERR_UNSUPPORTED;
+  if (p->batch == 0 || p->seqlen == 0) return ZG_OK;
+  if (!q || !k || !v || !q_norm_w || !k_norm_w || !out) return ZG_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_norm_w) ||
+      !aligned16(k_norm_w) || !aligned16(out) || (gate && !aligned16(gate)) ||
+      (k_out && !aligned16(k_out)) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return ZG_ERR_INVALID;
+  void* kp = k_out;
+  if (!kp) {
+    if (!workspace || workspace_bytes < kprime_bytes(p)) return ZG_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ZG_ERR_INVALID;
+    kp = workspace;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const zg::RopeTable tab = make_rope_table(p);
+  const long long krows = (long long)p->batch * p->seqlen * p->n_kv_heads;
+  hipError_t e = zg::launch_k_prologue(static_cast<const uint16_t*>(k), k_norm_w,
+                                       static_cast<uint16_t*>(kp), krows, p->seqlen,
+                                       p->n_kv_heads, p->pos_offset, p->rope_dim / 2,
+                                       p->rms_eps, tab, s);
+  if (e != hipSuccess) return ZG_ERR_HIP;
+  zg::FlashParams fp{};
+  fp.q = static_cast<const uint16_t*>(q);
+  fp.kp = static_cast<const uint16_t*>(kp);
+  fp.v = static_cast<const uint16_t*>(v);
+  fp.gate = static_cast<const uint16_t*>(gate);
+  fp.q_norm_w = q_norm_w;
+  fp.out = static_cast<uint16_t*>(out);
+  fp.lse = lse;
+  fp.B = p->batch;
+  fp.S = p->seqlen;
+  fp.Hq = p->n_q_heads;
+  fp.Hkv = p->n_kv_heads;
+  fp.window = p->window;
+  fp.rope_half = p->rope_dim / 2;
+  fp.scale_log2 = scale_log2(p);
+  fp.eps = p->rms_eps;
+  fp.pos_offset = p->pos_offset;
+  fp.tab = tab;
+  return hip_status(zg::launch_flash_fwd(fp, s));
+}
+
+int zg_attn_decode_num_splits(const zg_attn_params* p, int cache_cap) {
+  if (check_params(p) != ZG_OK || cache_cap < 1) return 0;
+  return auto_splits(p, cache_cap);
+}
+
+size_t zg_attn_decode_workspace_size(const zg_attn_params* p, int cache_cap, int num_splits) {
+  if (check_params(p) != ZG_OK || cache_cap < 1 || num_splits < 0 || num_splits > 256) return 0;
+  const int ns = num_splits ? num_splits : auto_splits(p, cache_cap);
+  return (size_t)p->batch * p->n_q_heads * ns * (kD + 2) * sizeof(float);
+}
+
+int zg_attn_decode(const zg_attn_params* p, const void* q, const void* k_new, const void* v_new,
+                   void* k_cache, void* v_cache, const int* seq_lens, int cache_cap, int ring,
+                   const void* gate, const float* q_norm_w, const float* k_norm_w, void* out,
+                   int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_params(p);
+  if (st != ZG_OK) return st;
+  if (cache_cap < 1 || num_splits < 0 || num_splits > 256 || (ring != 0 && ring != 1))
+    return ZG_ERR_INVALID;
+  if (ring && p->window != cache_cap) return ZG_ERR_INVALID;
+  if ((k_new == nullptr) != (v_new == nullptr)) return ZG_ERR_INVALID;
+  if (p->batch == 0) return ZG_OK;
+  if (!q || !k_cache || !v_cache || !seq_lens || !q_norm_w || !k_norm_w || !out)
+    return ZG_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q_norm_w) ||
+      !aligned16(k_norm_w) || !aligned16(out) || (gate && !aligned16(gate)) ||
+      (k_new && (!aligned16(k_new) || !aligned16(v_new))) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return ZG_ERR_INVALID;
+  const int ns = num_splits ? num_splits : auto_splits(p, cache_cap);
+  const size_t need = (size_t)p->batch * p->n_q_heads * ns * (kD + 2) * sizeof(float);
+  if (!workspace || workspace_bytes < need) return ZG_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ZG_ERR_INVALID;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const zg::RopeTable tab = make_rope_table(p);
+  if (k_new) {
+    hipError_t e = zg::launch_decode_append(
+        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), seq_lens, k_norm_w,
+        p->batch, p->n_kv_heads, cache_cap, ring, p->pos_offset, p->rope_dim / 2, p->rms_eps,
+        tab, s);
+    if (e != hipSuccess) return ZG_ERR_HIP;
+  }
+  zg::DecodeParams dp{};
+  dp.q = static_cast<const uint16_t*>(q);
+  dp.k_cache = static_cast<const uint16_t*>(k_cache);
+  dp.v_cache = static_cast<const uint16_t*>(v_cache);
+  dp.seq_lens = seq_lens;
+  dp.q_norm_w = q_norm_w;
+  dp.gate = static_cast<const uint16_t*>(gate);
+  dp.out = static_cast<uint16_t*>(out);
+  float* ws = static_cast<float*>(workspace);
+  dp.part_o = ws;
+  dp.part_ml = ws + (size_t)p->batch * p->n_q_heads * ns * kD;
+  dp.B = p->batch;
+  dp.Hq = p->n_q_heads;
+  dp.Hkv = p->n_kv_heads;
+  dp.cap = cache_cap;
+  dp.ring = ring;
+  dp.window = p->window;
+  dp.nsplit = ns;
+  dp.rope_half = p->rope_dim / 2;
+  dp.scale_log2 = scale_log2(p);
+  dp.eps = p->rms_eps;
+  dp.pos_offset = p->pos_offset;
+  dp.tab = tab;
+  return hip_status(zg::launch_decode(dp, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,282 @@
+// Split-KV decode attention and its log-sum-exp merge.
+//
+// Page "ZGCM-1:面向数学与智能体搜索的全开源高效基础模型" (paper.rainbus.top),
+// section 前置知识 › 滑动窗口注意力(SWA)与混合注意力: the sliding-window
+// layers keep a constant-size KV cache (here a ring of `window` slots); the
+// global layers keep every position.  Structured-data table, row
+// "256K 上下文推理 KV 缓存": at 256K tokens the cache of the 5 global layers is
+// what decode must stream.  Page "7B 打 235B？…全开源配方", section 🏗️ 架构:
+// the sliding-window output is multiplied by a sigmoid gate.
+//
+// One new query token per sequence.  A 256-thread workgroup takes one
+// (batch, kv head, split) and the query heads of that kv head (the GQA group,
+// up to 8, padded to the 16 columns of v_mfma_f32_16x16x32_bf16).  Its four
+// waves stream disjoint 32-key slices of the split's key range straight from
+// HBM (16-byte loads): S^T = K' Q'^T on MFMA, online softmax in fp32, then
+// O^T += V^T P^T with the V slice transposed through a wave-private LDS tile.
+// Each workgroup writes an unnormalised partial (max, sum, acc[128]) per query
+// head; the merge kernel combines the splits and applies the gate.
+
+#include "zg_common.h"
+#include "zg_launch.h"
+
+namespace zg {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kKeysPerWave = 32;
+constexpr int kKeysPerIter = kKeysPerWave * kWaves;
+constexpr int kVtwStride = kKeysPerWave + 8;  // bf16 per V^T row of a wave tile (80 B)
+constexpr int kQsStride = kD + 8;             // bf16 per Q' operand row (272 B)
+constexpr int kMaxGroup = 8;
+constexpr float kRescaleThreshold = 8.0f;
+
+// LDS carve-up (bytes)
+constexpr int kVtBytes = kWaves * kD * kVtwStride * 2;        // 40960, reused for the reduction
+constexpr int kQsBytes = 16 * kQsStride * 2;                  // 4352
+constexpr int kQnBytes = kMaxGroup * kD * 4;                  // 4096
+constexpr int kRedOBytes = kWaves * kMaxGroup * kD * 4;       // 16384 (inside the Vt area)
+static_assert(kRedOBytes <= kVtBytes, "reduction area must fit in the V^T area");
+
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kVtBytes + kQsBytes + kQnBytes];
+  __shared__ float red_m[kWaves][16];
+  __shared__ float red_l[kWaves][16];
+  uint16_t* vt_all = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* qs = reinterpret_cast<uint16_t*>(smem + kVtBytes);
+  float* qn = reinterpret_cast<float*>(smem + kVtBytes + kQsBytes);
+  float* red_o = reinterpret_cast<float*>(smem);  // after the key loop
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int col = lane & 15;  // MFMA column: query head within the group
+  const int kg = lane >> 4;   // 0..3
+  const int grp = p.Hq / p.Hkv;
+
+  const int split = blockIdx.x % p.nsplit;
+  const int bg = blockIdx.x / p.nsplit;
+  const int g = bg % p.Hkv;
+  const int b = bg / p.Hkv;
+
+  int L = p.seq_lens[b];
+  L = L < 1 ? 1 : L;
+  if (!p.ring && L > p.cap) L = p.cap;
+  const int W = p.ring ? p.cap : p.window;
+  const int lo = p.ring ? 0 : (W > 0 ? max(0, L - W) : 0);
+  const int hi = p.ring ? min(L, p.cap) : L;
+  const int n = hi - lo;
+  const int chunk = (((n + p.nsplit - 1) / p.nsplit) + 63) & ~63;
+  const int start = min(hi, lo + split * chunk);
+  const int end = min(hi, start + chunk);
+
+  // ---- query prologue for the group's heads (RMSNorm, partial RoPE)
+  const long long pos = p.pos_offset + L - 1;
+  for (int c = wv; c < grp; c += kWaves) {
+    const uint16_t* src = p.q + ((long long)b * p.Hq + g * grp + c) * kD;
+    float x0 = __uint_as_float((uint32_t)src[lane] << 16);
+    float x1 = __uint_as_float((uint32_t)src[64 + lane] << 16);
+    float ss = x0 * x0 + x1 * x1;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    const float r = 1.0f / sqrtf(ss * (1.0f / kD) + p.eps);
+    qn[c * kD + lane] = x0 * r * p.q_norm_w[lane];
+    qn[c * kD + 64 + lane] = x1 * r * p.q_norm_w[64 + lane];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 16 * kD; idx += kThreads) {
+    const int c = idx / kD, d = idx % kD;
+    float v = 0.f;
+    if (c < grp) {
+      v = qn[c * kD + d];
+      if (d < 2 * p.rope_half) {
+        const int t = d < p.rope_half ? d : d - p.rope_half;
+        float cs, sn;
+        rope_cos_sin(p.tab, t, pos, cs, sn);
+        v = d < p.rope_half ? v * cs - qn[c * kD + d + p.rope_half] * sn
+                            : v * cs + qn[c * kD + d - p.rope_half] * sn;
+      }
+    }
+    qs[c * kQsStride + d] = __builtin_bit_cast(uint16_t, (__bf16)v);
+  }
+  __syncthreads();
+  bf16x8 qf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    qf[kk] = *reinterpret_cast<const bf16x8*>(qs + col * kQsStride + 32 * kk + 8 * kg);
+
+  // ---- stream the split's keys
+  const long long slab = ((long long)b * p.Hkv + g) * p.cap * kD;
+  const uint16_t* kb = p.k_cache + slab;
+  const uint16_t* vb = p.v_cache + slab;
+  uint16_t* vt = vt_all + wv * kD * kVtwStride;
+  f32x4 o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int nit = end > start ? (end - start + kKeysPerIter - 1) / kKeysPerIter : 0;
+  const int mr = lane & 15;
+  const int krel = 8 * (mr >> 2) + (mr & 3);  // + 4*blk: key of MFMA row mr
+  const float rescale_raw = kRescaleThreshold / p.scale_log2;
+
+  for (int it = 0; it < nit; ++it) {
+    const int base = start + it * kKeysPerIter + wv * kKeysPerWave;
+    bf16x8 kf[2][4];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int key = base + krel + 4 * blk;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        u32x4 u = key < end ? ld16(kb + (long long)key * kD + 32 * kk + 8 * kg)
+                            : u32x4{0, 0, 0, 0};
+        kf[blk][kk] = __builtin_bit_cast(bf16x8, u);
+      }
+    }
+    u32x4 vr[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int key = base + 8 * kg + j;
+      vr[j] = key < end ? ld16(vb + (long long)key * kD + 8 * col) : u32x4{0, 0, 0, 0};
+    }
+
+    f32x4 s[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      s[blk] = f32x4{};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[blk][kk], qf[kk], s[blk], 0, 0, 0);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = base + 8 * kg + 4 * blk + e;
+        const float v = key < end ? s[blk][e] : -INFINITY;
+        s[blk][e] = v;
+        mx = fmaxf(mx, v);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run + rescale_raw)) {
+      const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2((m_run - m_new) * p.scale_log2);
+#pragma unroll
+      for (int db = 0; db < 8; ++db) o[db] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float neg_mc = m_run == -INFINITY ? 0.0f : -m_run * p.scale_log2;
+    float pv[8];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        pv[4 * blk + e] = fast_exp2(__builtin_fmaf(s[blk][e], p.scale_log2, neg_mc));
+        l_run += pv[4 * blk + e];
+      }
+    }
+    const bf16x8 pf = pack_bf16x8(pv);
+
+    // V slice (keys 8kg..8kg+7, dims 8col..8col+7 per lane) -> V^T tile
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int wd = i >> 1;
+      u32x4 t;
+#pragma unroll
+      for (int q2 = 0; q2 < 4; ++q2) {
+        const uint32_t a = vr[2 * q2][wd], c = vr[2 * q2 + 1][wd];
+        t[q2] = (i & 1) ? ((a >> 16) | (c & 0xffff0000u)) : ((a & 0xffffu) | (c << 16));
+      }
+      st16(vt + (8 * col + i) * kVtwStride + 8 * kg, t);
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(vt + (16 * db + mr) * kVtwStride + 8 * kg);
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, o[db], 0, 0, 0);
+    }
+  }
+
+  // ---- combine the four waves, write this split's partial
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  __syncthreads();  // V^T tiles are dead; reuse them for red_o
+  if (kg == 0) {
+    red_m[wv][col] = m_run == -INFINITY ? -INFINITY : m_run * p.scale_log2;
+    red_l[wv][col] = l_run;
+  }
+  if (col < grp) {
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        red_o[(wv * kMaxGroup + col) * kD + 16 * db + 4 * kg + e] = o[db][e];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < grp * kD; idx += kThreads) {
+    const int c = idx / kD, d = idx % kD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) M = fmaxf(M, red_m[w2][c]);
+    float acc = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kWaves; ++w2) {
+      const float mw = red_m[w2][c];
+      const float f = mw == -INFINITY ? 0.f : fast_exp2(mw - M);
+      acc += f * red_o[(w2 * kMaxGroup + c) * kD + d];
+      lsum += f * red_l[w2][c];
+    }
+    const long long pi = ((long long)b * p.Hq + g * grp + c) * p.nsplit + split;
+    p.part_o[pi * kD + d] = acc;
+    if (d == 0) {
+      p.part_ml[2 * pi] = M;
+      p.part_ml[2 * pi + 1] = lsum;
+    }
+  }
+}
+
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
+  const int bh = blockIdx.x;  // b * Hq + h
+  const int lane = threadIdx.x;
+  const float* ml = p.part_ml + (long long)bh * p.nsplit * 2;
+  const float* po = p.part_o + (long long)bh * p.nsplit * kD;
+  float M = -INFINITY;
+  for (int s = 0; s < p.nsplit; ++s) M = fmaxf(M, ml[2 * s]);
+  float a0 = 0.f, a1 = 0.f, lsum = 0.f;
+  for (int s = 0; s < p.nsplit; ++s) {
+    const float ms = ml[2 * s];
+    const float f = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
+    lsum += f * ml[2 * s + 1];
+    a0 += f * po[(long long)s * kD + lane];
+    a1 += f * po[(long long)s * kD + 64 + lane];
+  }
+  const float inv = 1.0f / lsum;
+  float o0 = a0 * inv, o1 = a1 * inv;
+  if (p.gate) {
+    const uint16_t* gs = p.gate + (long long)bh * kD;
+    o0 *= sigmoidf_(__uint_as_float((uint32_t)gs[lane] << 16));
+    o1 *= sigmoidf_(__uint_as_float((uint32_t)gs[64 + lane] << 16));
+  }
+  uint16_t* dst = p.out + (long long)bh * kD;
+  dst[lane] = __builtin_bit_cast(uint16_t, (__bf16)o0);
+  dst[64 + lane] = __builtin_bit_cast(uint16_t, (__bf16)o1);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  if (p.B == 0) return hipSuccess;
+  const long long blocks = (long long)p.B * p.Hkv * p.nsplit;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(p.B * p.Hq), dim3(64), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace zg

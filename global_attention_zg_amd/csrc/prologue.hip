@@ -1,0 +1,153 @@
+// QK-RMSNorm + partial RoPE of the keys.
+//
+// Page "7B 打 235B？中关村学院把'小模型怎么活'这道题答成了一份全开源配方"
+// (shibing624.github.io), section 🏗️ 架构: Q and K are normalised with
+// RMSNorm and rotated with RoPE on a 0.33 fraction of the head dim.  Here, per
+// key row of D = 128 values: x_hat = x / sqrt(mean(x^2) + eps) * w, then the
+// first R dims are rotated pairwise (t, t + R/2) by pos * theta^(-2t/R); the
+// remaining dims pass through.  The queries get the same treatment inside the
+// attention kernels, fused into their Q-tile loads.
+//
+// Layout: 16 lanes per row, 8 bf16 (16 bytes) per lane, 16 rows per
+// 256-thread block.  The row's normalised values go through LDS so that each
+// lane can read the partner dim of its rotary pairs.
+
+#include "zg_common.h"
+#include "zg_launch.h"
+
+namespace zg {
+
+namespace {
+
+constexpr int kRowsPerBlock = 16;
+
+// Normalise + rotate one row held as 8 values per lane (lane c16 = 0..15 of
+// the row owns dims 8*c16 .. 8*c16+7).  `xs` is the row's LDS scratch.
+__device__ __forceinline__ void norm_rope_row(float* x, int c16, const float* w, float eps,
+                                              int rope_half, const RopeTable& tab,
+                                              long long pos, float* xs) {
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
+  // reduce over the 16 lanes of this row
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 16);
+  const float r = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+  const u32x4 w0 = ld16(w + 8 * c16);
+  const u32x4 w1 = ld16(w + 8 * c16 + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] *= r * __uint_as_float(w0[i]);
+    x[4 + i] *= r * __uint_as_float(w1[i]);
+  }
+  if (rope_half == 0) return;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xs[8 * c16 + i] = x[i];
+  __syncthreads();
+  const int R = 2 * rope_half;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int d = 8 * c16 + i;
+    if (d < R) {
+      const int t = d < rope_half ? d : d - rope_half;
+      float c, s;
+      rope_cos_sin(tab, t, pos, c, s);
+      if (d < rope_half)
+        x[i] = x[i] * c - xs[d + rope_half] * s;
+      else
+        x[i] = x[i] * c + xs[d - rope_half] * s;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_prologue_kernel(const uint16_t* __restrict__ k,
+                                                         const float* __restrict__ w,
+                                                         uint16_t* __restrict__ kout,
+                                                         long long rows, int S, int Hkv,
+                                                         long long pos_offset, int rope_half,
+                                                         float eps, RopeTable tab) {
+  __shared__ float xs[kRowsPerBlock][kD];
+  const int lrow = threadIdx.x / 16;
+  const int c16 = threadIdx.x % 16;
+  const long long row = (long long)blockIdx.x * kRowsPerBlock + lrow;
+  const bool ok = row < rows;
+  float x[8];
+  if (ok) {
+    unpack_bf16x8(ld16(k + row * kD + 8 * c16), x);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = 0.f;
+  }
+  const long long s = (row / Hkv) % S;
+  norm_rope_row(x, c16, w, eps, rope_half, tab, pos_offset + s, xs[lrow]);
+  if (ok) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    st16(kout + row * kD + 8 * c16, o);
+  }
+}
+
+// Decode: normalise + rotate the new key of each (b, kv head) at position
+// pos_offset + len - 1 and write it, with the new value, into its cache slot.
+__global__ __launch_bounds__(256) void decode_append_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+    uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
+    const int* __restrict__ seq_lens, const float* __restrict__ w, int rows, int Hkv,
+    int cap, int ring, long long pos_offset, int rope_half, float eps, RopeTable tab) {
+  __shared__ float xs[kRowsPerBlock][kD];
+  const int lrow = threadIdx.x / 16;
+  const int c16 = threadIdx.x % 16;
+  const int row = blockIdx.x * kRowsPerBlock + lrow;  // b * Hkv + g
+  const bool ok = row < rows;
+  const int b = ok ? row / Hkv : 0;
+  int L = ok ? seq_lens[b] : 1;
+  L = L < 1 ? 1 : L;
+  if (!ring && L > cap) L = cap;
+  const int slot = ring ? (L - 1) % cap : L - 1;
+  float x[8];
+  u32x4 vv = {0, 0, 0, 0};
+  if (ok) {
+    unpack_bf16x8(ld16(k_new + (long long)row * kD + 8 * c16), x);
+    vv = ld16(v_new + (long long)row * kD + 8 * c16);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = 0.f;
+  }
+  norm_rope_row(x, c16, w, eps, rope_half, tab, pos_offset + L - 1, xs[lrow]);
+  if (ok) {
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    const long long dst = ((long long)row * cap + slot) * kD + 8 * c16;
+    st16(k_cache + dst, o);
+    st16(v_cache + dst, vv);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_k_prologue(const uint16_t* k, const float* w, uint16_t* kout, long long rows,
+                             int S, int Hkv, long long pos_offset, int rope_half, float eps,
+                             const RopeTable& tab, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const long long blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  hipLaunchKernelGGL(k_prologue_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k, w,
+                     kout, rows, S, Hkv, pos_offset, rope_half, eps, tab);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache,
+                                uint16_t* v_cache, const int* seq_lens, const float* w, int B,
+                                int Hkv, int cap, int ring, long long pos_offset, int rope_half,
+                                float eps, const RopeTable& tab, hipStream_t stream) {
+  const int rows = B * Hkv;
+  if (rows == 0) return hipSuccess;
+  const int blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  hipLaunchKernelGGL(decode_append_kernel, dim3(blocks), dim3(256), 0, stream, k_new, v_new,
+                     k_cache, v_cache, seq_lens, w, rows, Hkv, cap, ring, pos_offset, rope_half,
+                     eps, tab);
+  return hipGetLastError();
+}
+
+}  // namespace zg

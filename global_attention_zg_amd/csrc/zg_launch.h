@@ -1,0 +1,57 @@
+// Host-side launchers of the libzgattn kernels (internal; the public C ABI
+// is include/zg_attn.h).  Every launcher enqueues on `stream` and returns the
+// launch status without synchronising.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "zg_common.h"
+
+namespace zg {
+
+struct FlashParams {
+  const uint16_t* q;     // bf16 [B,S,Hq,D] raw queries
+  const uint16_t* kp;    // bf16 [B,S,Hkv,D] normalised + rotated keys
+  const uint16_t* v;     // bf16 [B,S,Hkv,D]
+  const uint16_t* gate;  // bf16 [B,S,Hq,D] or null
+  const float* q_norm_w; // fp32 [D]
+  uint16_t* out;         // bf16 [B,S,Hq,D]
+  float* lse;            // fp32 [B,Hq,S] or null
+  int B, S, Hq, Hkv, window, rope_half;
+  float scale_log2;      // softmax scale * log2(e)
+  float eps;
+  long long pos_offset;
+  RopeTable tab;
+};
+
+hipError_t launch_k_prologue(const uint16_t* k, const float* w, uint16_t* kout, long long rows,
+                             int S, int Hkv, long long pos_offset, int rope_half, float eps,
+                             const RopeTable& tab, hipStream_t stream);
+
+hipError_t launch_flash_fwd(const FlashParams& p, hipStream_t stream);
+
+hipError_t launch_decode_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache,
+                                uint16_t* v_cache, const int* seq_lens, const float* w, int B,
+                                int Hkv, int cap, int ring, long long pos_offset, int rope_half,
+                                float eps, const RopeTable& tab, hipStream_t stream);
+
+struct DecodeParams {
+  const uint16_t* q;        // bf16 [B,Hq,D] raw
+  const uint16_t* k_cache;  // bf16 [B,Hkv,cap,D]
+  const uint16_t* v_cache;  // bf16 [B,Hkv,cap,D]
+  const int* seq_lens;      // int32 [B]
+  const float* q_norm_w;    // fp32 [D]
+  const uint16_t* gate;     // bf16 [B,Hq,D] or null
+  uint16_t* out;            // bf16 [B,Hq,D]
+  float* part_o;            // fp32 [B,Hq,nsplit,D]
+  float* part_ml;           // fp32 [B,Hq,nsplit,2]
+  int B, Hq, Hkv, cap, ring, window, nsplit, rope_half;
+  float scale_log2, eps;
+  long long pos_offset;
+  RopeTable tab;
+};
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+}  // namespace zg

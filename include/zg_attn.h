@@ -1,0 +1,129 @@
+/*
+ * zg_attn — gated sliding-window + global causal attention of the ZGCM-1
+ * decoder, for AMD Instinct MI355X (gfx950).  C ABI of libzgattn.so.
+ *
+ * What is computed (pages cited by title and section):
+ *  - "ZGCM-1:面向数学与智能体搜索的全开源高效基础模型" (paper.rainbus.top),
+ *    section 前置知识 › 滑动窗口注意力(SWA)与混合注意力: each token attends
+ *    only to its 128 neighbouring tokens (the sliding-window layers); global
+ *    layers at 6/12/18/24/30 of 32 attend over the whole causal prefix.
+ *    Section 核心方法: GQA with 32 query / 8 KV heads, partial RoPE ratio 0.33.
+ *  - "7B 打 235B？中关村学院把'小模型怎么活'这道题答成了一份全开源配方"
+ *    (shibing624.github.io), section 🏗️ 架构: QK normalised with RMSNorm;
+ *    the local (sliding-window) attention output is multiplied by a sigmoid
+ *    gate.
+ *
+ * Per query row i of query head h (kv head g = h / (n_q_heads/n_kv_heads)):
+ *   q' = RoPE(RMSNorm(q_i) * q_norm_w),  k'_j = RoPE(RMSNorm(k_j) * k_norm_w)
+ *   RMSNorm(x) = x / sqrt(mean(x^2) + rms_eps) over the head_dim values;
+ *   RoPE rotates dims (t, t + rope_dim/2), t < rope_dim/2, by the angle
+ *   p * rope_theta^(-2t/rope_dim) at position p = pos_offset + i; other dims
+ *   pass through.
+ *   key j visible iff j <= i and (window == 0 or i - j < window);
+ *   out_i = softmax_j(scale * q'.k'_j) V_j, then out_i *= sigmoid(gate_i)
+ *   elementwise when a gate is given;  lse_i = log sum_j exp(scale q'.k'_j).
+ *
+ * Conventions for every entry point:
+ *  - Tensor pointers are DEVICE pointers, 16-byte aligned, contiguous in the
+ *    documented layout; bf16 means IEEE bfloat16 bits.  The caller owns all
+ *    buffers; the library allocates nothing and keeps no pointer after return.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and the call returns without synchronising.  No global mutable state:
+ *    calls from several host threads are safe.
+ *  - Arguments are validated before anything is launched; on error nothing
+ *    is launched and a negative status is returned (no exceptions cross the
+ *    ABI).
+ */
+#ifndef ZG_ATTN_H
+#define ZG_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZG_OK               0
+#define ZG_ERR_INVALID     -1  /* null pointer, bad shape, misaligned pointer  */
+#define ZG_ERR_UNSUPPORTED -2  /* valid but not implemented (head_dim != 128,
+                                  rope_dim > head_dim/2, odd rope_dim, ...)    */
+#define ZG_ERR_WORKSPACE   -3  /* workspace missing or smaller than required   */
+#define ZG_ERR_HIP         -4  /* a HIP launch or runtime call failed          */
+
+typedef struct zg_attn_params {
+  int   batch;          /* B  (>= 0)                                            */
+  int   seqlen;         /* S: tokens per sequence (fwd); ignored by decode     */
+  int   n_q_heads;      /* Hq (32 in ZGCM-1)                                    */
+  int   n_kv_heads;     /* Hkv (8); Hq % Hkv == 0 and Hq/Hkv in {1,2,4,8}      */
+  int   head_dim;       /* D; must be 128                                      */
+  int   window;         /* 0 = global causal; W > 0: key j visible to query i
+                           iff 0 <= i - j < W (128 for the SWA layers)         */
+  int   rope_dim;       /* rotary dims R: even, 0 <= R <= head_dim/2 (42)      */
+  float rope_theta;     /* RoPE base (10000; 1e7 for the 256K stage)           */
+  float rms_eps;        /* RMSNorm epsilon (1e-6)                              */
+  float softmax_scale;  /* 0 -> 1/sqrt(head_dim)                               */
+  long long pos_offset; /* position of token 0 (fwd) / added to decode pos.    */
+} zg_attn_params;
+
+/* Bytes of device workspace zg_attn_fwd needs (the normalised and rotated
+ * keys K', bf16 [B,S,Hkv,D]); 0 for an invalid p.  When k_out is passed to
+ * zg_attn_fwd, K' goes there and the workspace may be NULL. */
+size_t zg_attn_fwd_workspace_size(const zg_attn_params* p);
+
+/* Prefill / training forward of one attention layer.
+ *   q     bf16 [B,S,Hq,D]   raw queries (before norm / RoPE)
+ *   k     bf16 [B,S,Hkv,D]  raw keys
+ *   v     bf16 [B,S,Hkv,D]
+ *   gate  bf16 [B,S,Hq,D]   gate logits (out *= sigmoid(gate)), or NULL
+ *   q_norm_w, k_norm_w  fp32 [D] RMSNorm weights
+ *   out   bf16 [B,S,Hq,D]   written in full
+ *   lse   fp32 [B,Hq,S]     natural-log LSE of the scaled scores, or NULL
+ *   k_out bf16 [B,S,Hkv,D]  receives K' (for filling a KV cache), or NULL
+ * S == 0 or B == 0 is valid and launches nothing. */
+int zg_attn_fwd(const zg_attn_params* p,
+                const void* q, const void* k, const void* v, const void* gate,
+                const float* q_norm_w, const float* k_norm_w,
+                void* out, float* lse, void* k_out,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Number of KV splits zg_attn_decode uses when num_splits == 0. */
+int zg_attn_decode_num_splits(const zg_attn_params* p, int cache_cap);
+
+/* Bytes of device workspace zg_attn_decode needs for `num_splits` splits
+ * (0 = the automatic choice): fp32 partial (max, sum, acc[D]) per
+ * (b, q head, split).  0 for an invalid p. */
+size_t zg_attn_decode_workspace_size(const zg_attn_params* p, int cache_cap, int num_splits);
+
+/* One decode step: one new token per sequence against a KV cache.
+ *   q         bf16 [B,Hq,D]   raw new-token queries
+ *   k_new     bf16 [B,Hkv,D]  raw new key, or NULL if the cache already holds
+ *   v_new     bf16 [B,Hkv,D]  the new token's K' and V (then both NULL)
+ *   k_cache   bf16 [B,Hkv,cache_cap,D]  K' (post norm/RoPE), updated in place
+ *   v_cache   bf16 [B,Hkv,cache_cap,D]  V, updated in place
+ *   seq_lens  device int32 [B]: tokens of each sequence INCLUDING the new
+ *             one (>= 1); the query sits at position pos_offset+len-1
+ *   ring      0: slot = position (len <= cache_cap required);
+ *             1: slot = position % cache_cap (sliding-window ring; requires
+ *                window == cache_cap)
+ *   gate      bf16 [B,Hq,D] or NULL;  out bf16 [B,Hq,D]
+ *   num_splits  KV splits per (b, kv head); 0 = automatic
+ * Visible keys: positions max(0,len-W)..len-1 (W = window, or all for 0).
+ * The new token's K' and V are written to their slot before attending.
+ * seq_lens values are read on the device; values outside [1, cache_cap] for
+ * ring == 0 are clamped to that range. */
+int zg_attn_decode(const zg_attn_params* p,
+                   const void* q, const void* k_new, const void* v_new,
+                   void* k_cache, void* v_cache, const int* seq_lens,
+                   int cache_cap, int ring, const void* gate,
+                   const float* q_norm_w, const float* k_norm_w,
+                   void* out, int num_splits,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* zg_attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZG_ATTN_H */

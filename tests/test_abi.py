@@ -1,0 +1,147 @@
+"""CPU checks of the C ABI: the library loads, exports every function that
+include/zg_attn.h declares, sizes workspaces as documented and rejects bad
+arguments before launching anything (host-side failure handling; no kernel
+runs in these tests)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "zg_attn.h")
+
+
+@pytest.fixture(scope="module")
+def bd():
+    from global_attention_zg_amd import binding
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(zg_attn_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("zg_attn_fwd", "zg_attn_decode", "zg_attn_fwd_workspace_size",
+              "zg_attn_decode_workspace_size", "zg_attn_decode_num_splits", "zg_attn_strerror"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(bd):
+    lib = ctypes.CDLL(bd.library_path())
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert set(declared_functions()) == set(bd.EXPORTED)
+
+
+def test_strerror(bd):
+    assert bd.zg_attn_strerror(0) == "ok"
+    for st in (-1, -2, -3, -4):
+        assert bd.zg_attn_strerror(st) and bd.zg_attn_strerror(st) != "unknown status"
+    assert bd.zg_attn_strerror(-99) == "unknown status"
+
+
+def _fwd(bd, p, **ptrs):
+    names = ["q", "k", "v", "gate", "qw", "kw", "out", "lse", "kout", "ws"]
+    args = [ptrs.get(n) for n in names]
+    return bd._lib.zg_attn_fwd(ctypes.byref(p), *args[:10], ptrs.get("ws_bytes", 0), None)
+
+
+FAKE = 0x10000000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, -2), ("head_dim", 0, -1), ("n_kv_heads", 3, -1), ("n_q_heads", 0, -1),
+    ("rope_dim", 43, -1), ("rope_dim", 66, -2), ("rope_dim", 130, -1), ("window", -1, -1),
+    ("batch", -1, -1), ("seqlen", -5, -1), ("rms_eps", -1.0, -1), ("softmax_scale", -0.5, -1),
+    ("rope_theta", 0.0, -1), ("rms_eps", float("nan"), -1),
+])
+def test_fwd_rejects_bad_params(bd, field, value, status):
+    p = bd.make_params(1, 64, 32, 8, 128, 128)
+    setattr(p, field, value)
+    assert _fwd(bd, p, q=FAKE, k=FAKE, v=FAKE, qw=FAKE, kw=FAKE, out=FAKE, ws=FAKE,
+                ws_bytes=1 << 30) == status
+    assert bd.zg_attn_fwd_workspace_size(p) == 0
+
+
+def test_fwd_group_size_support(bd):
+    p = bd.make_params(1, 64, 24, 8, 128, 128)   # group of 3
+    assert _fwd(bd, p) == bd.ZG_ERR_UNSUPPORTED
+    p = bd.make_params(1, 64, 32, 2, 128, 128)   # group of 16
+    assert _fwd(bd, p) == bd.ZG_ERR_UNSUPPORTED
+
+
+def test_fwd_null_and_misaligned_pointers(bd):
+    p = bd.make_params(1, 64, 32, 8, 128, 128)
+    ok = dict(q=FAKE, k=FAKE, v=FAKE, qw=FAKE, kw=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 30)
+    for name in ("q", "k", "v", "qw", "kw", "out"):
+        a = dict(ok)
+        a[name] = None
+        assert _fwd(bd, p, **a) == bd.ZG_ERR_INVALID, name
+        a[name] = FAKE + 2
+        assert _fwd(bd, p, **a) == bd.ZG_ERR_INVALID, name
+    a = dict(ok, gate=FAKE + 8)
+    assert _fwd(bd, p, **a) == bd.ZG_ERR_INVALID
+    a = dict(ok, lse=FAKE + 2)
+    assert _fwd(bd, p, **a) == bd.ZG_ERR_INVALID
+
+
+def test_fwd_workspace_rules(bd):
+    p = bd.make_params(2, 100, 32, 8, 128, 128)
+    need = bd.zg_attn_fwd_workspace_size(p)
+    assert need == 2 * 100 * 8 * 128 * 2
+    base = dict(q=FAKE, k=FAKE, v=FAKE, qw=FAKE, kw=FAKE, out=FAKE)
+    assert _fwd(bd, p, **base) == bd.ZG_ERR_WORKSPACE
+    assert _fwd(bd, p, **dict(base, ws=FAKE, ws_bytes=need - 1)) == bd.ZG_ERR_WORKSPACE
+    assert _fwd(bd, p, **dict(base, ws=FAKE + 8, ws_bytes=need)) == bd.ZG_ERR_INVALID
+
+
+def test_fwd_empty_launches_nothing(bd):
+    for B, S in ((0, 64), (1, 0), (0, 0)):
+        p = bd.make_params(B, S, 32, 8, 128, 128)
+        assert _fwd(bd, p) == bd.ZG_OK
+        assert bd.zg_attn_fwd_workspace_size(p) == 0
+
+
+def _dec(bd, p, cap, ring, num_splits=0, **ptrs):
+    names = ["q", "kn", "vn", "kc", "vc", "sl"]
+    a = [ptrs.get(n) for n in names]
+    return bd._lib.zg_attn_decode(ctypes.byref(p), *a, cap, ring, ptrs.get("gate"),
+                                  ptrs.get("qw"), ptrs.get("kw"), ptrs.get("out"), num_splits,
+                                  ptrs.get("ws"), ptrs.get("ws_bytes", 0), None)
+
+
+def test_decode_splits_and_workspace(bd):
+    p = bd.make_params(16, 0, 32, 8, 128, 0)
+    ns = bd.zg_attn_decode_num_splits(p, 262145)
+    assert 1 <= ns <= 64
+    assert bd.zg_attn_decode_workspace_size(p, 262145, 0) == 16 * 32 * ns * 130 * 4
+    assert bd.zg_attn_decode_workspace_size(p, 262145, 5) == 16 * 32 * 5 * 130 * 4
+    p2 = bd.make_params(16, 0, 32, 8, 128, 128)
+    assert bd.zg_attn_decode_num_splits(p2, 128) == 1
+    assert bd.zg_attn_decode_workspace_size(p, 0, 0) == 0
+    assert bd.zg_attn_decode_workspace_size(p, 100, 300) == 0
+
+
+def test_decode_rejects_bad_arguments(bd):
+    ok = dict(q=FAKE, kc=FAKE, vc=FAKE, sl=FAKE, qw=FAKE, kw=FAKE, out=FAKE, ws=FAKE,
+              ws_bytes=1 << 30)
+    p = bd.make_params(2, 0, 32, 8, 128, 128)
+    assert _dec(bd, p, 128, 1, **dict(ok, kn=FAKE)) == bd.ZG_ERR_INVALID      # k without v
+    assert _dec(bd, p, 64, 1, **ok) == bd.ZG_ERR_INVALID                      # window != cap
+    assert _dec(bd, p, 0, 0, **ok) == bd.ZG_ERR_INVALID
+    assert _dec(bd, p, 128, 2, **ok) == bd.ZG_ERR_INVALID
+    assert _dec(bd, p, 128, 1, num_splits=257, **ok) == bd.ZG_ERR_INVALID
+    assert _dec(bd, p, 128, 1, **dict(ok, sl=None)) == bd.ZG_ERR_INVALID
+    assert _dec(bd, p, 128, 1, **dict(ok, sl=FAKE + 2)) == bd.ZG_ERR_INVALID
+    assert _dec(bd, p, 128, 1, **dict(ok, ws=None)) == bd.ZG_ERR_WORKSPACE
+    assert _dec(bd, p, 128, 1, **dict(ok, ws_bytes=16)) == bd.ZG_ERR_WORKSPACE
+    p0 = bd.make_params(0, 0, 32, 8, 128, 128)
+    assert _dec(bd, p0, 128, 1) == bd.ZG_OK
+    pbad = bd.make_params(2, 0, 32, 8, 96, 128)
+    assert _dec(bd, pbad, 128, 1, **ok) == bd.ZG_ERR_UNSUPPORTED

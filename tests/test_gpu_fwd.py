@@ -1,0 +1,229 @@
+"""GPU parity of zg_attn_fwd (prologue + banded/global flash kernels) against
+the fp64 oracle, through the C ABI, plus the invariants of the path."""
+
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import zg_oracle as orc
+from tests import zg_cases as zc
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(autouse=True)
+def _gpu(request):
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    print(f"\n[case] {request.node.nodeid}", file=sys.stderr, flush=True)
+    yield
+    torch.cuda.synchronize()
+
+
+def _binding():
+    from global_attention_zg_amd import binding
+    return binding
+
+
+KW = dict(rope_dim=42, rope_theta=10000.0, rms_eps=1e-6)
+
+
+def run_gpu(c, window, gated=True, want_lse=True, poison=True, k_out=False, **kw):
+    bd = _binding()
+    q, k, v = (zc.to_dev(c[n], torch) for n in ("q", "k", "v"))
+    g = zc.to_dev(c["gate"], torch) if gated else None
+    gq = torch.from_numpy(c["gq"]).cuda()
+    gk = torch.from_numpy(c["gk"]).cuda()
+    out = torch.empty_like(q)
+    B, S, Hq, _ = q.shape
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda") if want_lse else None
+    if poison:
+        out.fill_(float("nan"))
+        if lse is not None:
+            lse.fill_(float("nan"))
+    ko = torch.full_like(k, float("nan")) if k_out else None
+    args = dict(KW)
+    args.update(kw)
+    bd.zg_attn_fwd(q, k, v, g, gq, gk, window=window, out=out, lse=lse, k_out=ko, **args)
+    torch.cuda.synchronize()
+    res = dict(out=out.float().cpu().numpy().astype(np.float64),
+               lse=None if lse is None else lse.cpu().numpy().astype(np.float64))
+    if k_out:
+        res["k_out"] = ko.float().cpu().numpy().astype(np.float64)
+    res["raw_out"] = out
+    return res
+
+
+def run_oracle(c, window, gated=True, rows=None, **kw):
+    args = dict(KW)
+    args.update(kw)
+    return orc.attention_fwd(zc.f64(c["q"]), zc.f64(c["k"]), zc.f64(c["v"]),
+                             zc.f64(c["gate"]) if gated else None, c["gq"].astype(np.float64),
+                             c["gk"].astype(np.float64), window=window, rows=rows, **args)
+
+
+def check_lse(got, ref, what):
+    d = np.abs(got - ref)
+    assert np.all(np.isfinite(got)), what
+    assert float(d.max()) <= 2e-2, f"{what}: lse max abs {d.max():.3e}"
+
+
+# --------------------------------------------------------------------------
+# small and ragged shapes: full element-by-element parity
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("window,gated", [(128, True), (0, False), (0, True), (37, True)])
+@pytest.mark.parametrize("B,S,Hq,Hkv", [(2, 1000, 8, 2), (1, 513, 4, 1)])
+def test_fwd_parity_ragged(B, S, Hq, Hkv, window, gated):
+    c = zc.fwd_case(101, B, S, Hq, Hkv, gated=True)
+    g = run_gpu(c, window, gated)
+    o, l = run_oracle(c, window, gated)
+    zc.compare(g["out"], o, f"out W={window}")
+    check_lse(g["lse"], l, f"lse W={window}")
+
+
+@pytest.mark.parametrize("S", [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257])
+@pytest.mark.parametrize("window", [128, 0])
+def test_fwd_parity_odd_lengths(S, window):
+    c = zc.fwd_case(102, 1, S, 8, 2, gated=True)
+    g = run_gpu(c, window, gated=window > 0)
+    o, l = run_oracle(c, window, gated=window > 0)
+    zc.compare(g["out"], o, f"S={S} W={window}")
+    check_lse(g["lse"], l, f"S={S}")
+
+
+@pytest.mark.parametrize("grp", [1, 2, 4, 8])
+def test_fwd_parity_group_sizes(grp):
+    Hkv = 2
+    c = zc.fwd_case(103, 1, 300, Hkv * grp, Hkv, gated=True)
+    for window in (128, 0):
+        g = run_gpu(c, window, gated=True)
+        o, l = run_oracle(c, window, gated=True)
+        zc.compare(g["out"], o, f"grp={grp} W={window}")
+
+
+def test_fwd_tiny_pair_config():
+    """B1 S512, 4 query / 1 KV head, W=128 gated and the global layer on the
+    same inputs."""
+    c = zc.fwd_case(1, 1, 512, 4, 1, gated=True)
+    for window, gated in ((128, True), (0, False)):
+        g = run_gpu(c, window, gated)
+        o, l = run_oracle(c, window, gated)
+        zc.compare(g["out"], o, f"tiny W={window}")
+        check_lse(g["lse"], l, f"tiny W={window}")
+
+
+def test_fwd_large_position_offset():
+    c = zc.fwd_case(104, 1, 200, 8, 2, gated=True)
+    for window in (128, 0):
+        g = run_gpu(c, window, pos_offset=262000)
+        o, l = run_oracle(c, window, pos_offset=262000)
+        zc.compare(g["out"], o, "pos_offset")
+
+
+def test_fwd_theta_and_scale_options():
+    c = zc.fwd_case(105, 1, 160, 8, 2, gated=True)
+    for kw in (dict(rope_theta=1e7), dict(rope_dim=0), dict(rope_dim=64),
+               dict(softmax_scale=0.05), dict(rms_eps=0.25)):
+        g = run_gpu(c, 64, **kw)
+        o, l = run_oracle(c, 64, **kw)
+        zc.compare(g["out"], o, str(kw))
+        check_lse(g["lse"], l, str(kw))
+
+
+def test_k_out_is_normalised_rotated_keys():
+    """The prologue's K' (returned through k_out) matches the oracle's norm +
+    RoPE of the keys to bf16 rounding."""
+    c = zc.fwd_case(106, 2, 150, 8, 2, gated=True)
+    g = run_gpu(c, 128, k_out=True, pos_offset=77)
+    kn = orc.rms_norm(zc.f64(c["k"]), c["gk"].astype(np.float64), 1e-6)
+    ref = np.stack([orc.apply_partial_rope(kn[b], 77 + np.arange(150), 42, 10000.0)
+                    for b in range(2)])
+    d = np.abs(g["k_out"] - ref)
+    assert np.all(d <= 2.0 ** -8 * np.abs(ref) + 1e-5), float(d.max())
+
+
+# --------------------------------------------------------------------------
+# invariants on the GPU path
+# --------------------------------------------------------------------------
+def test_gate_plus_inf_is_bitwise_ungated():
+    c = zc.fwd_case(107, 1, 300, 8, 2, gated=True)
+    c_inf = dict(c)
+    c_inf["gate"] = np.full_like(c["gate"], 0x7F80)  # bf16 +inf
+    a = run_gpu(c, 128, gated=False)["raw_out"]
+    b = run_gpu(c_inf, 128, gated=True)["raw_out"]
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    c_ninf = dict(c)
+    c_ninf["gate"] = np.full_like(c["gate"], 0xFF80)  # bf16 -inf
+    z = run_gpu(c_ninf, 128, gated=True)["raw_out"]
+    assert torch.all(z.float() == 0)
+
+
+def test_window_at_least_S_is_bitwise_global():
+    c = zc.fwd_case(108, 2, 333, 8, 2, gated=False)
+    a = run_gpu(c, 0, gated=False)
+    for W in (333, 334, 5000):
+        b = run_gpu(c, W, gated=False)
+        assert torch.equal(a["raw_out"].view(torch.int16), b["raw_out"].view(torch.int16))
+        assert np.array_equal(a["lse"], b["lse"])
+
+
+def test_window_one_is_gated_value():
+    c = zc.fwd_case(109, 1, 100, 8, 2, gated=True)
+    g = run_gpu(c, 1, gated=True)
+    ref = orc.attention_fwd(zc.f64(c["q"]), zc.f64(c["k"]), zc.f64(c["v"]), zc.f64(c["gate"]),
+                            c["gq"].astype(np.float64), c["gk"].astype(np.float64), window=1,
+                            **KW)[0]
+    zc.compare(g["out"], ref, "W=1")
+
+
+def test_gqa_equals_repeated_mha_on_gpu():
+    c = zc.fwd_case(110, 1, 257, 8, 2, gated=True)
+    c_mha = dict(c)
+    c_mha["k"] = np.repeat(c["k"], 4, axis=2)
+    c_mha["v"] = np.repeat(c["v"], 4, axis=2)
+    for window in (128, 0):
+        a = run_gpu(c, window)["out"]
+        b = run_gpu(c_mha, window)["out"]
+        zc.compare(a, b, f"gqa vs mha W={window}")
+
+
+def test_deterministic_and_fully_written():
+    c = zc.fwd_case(111, 2, 700, 8, 2, gated=True)
+    for window in (128, 0):
+        a = run_gpu(c, window, poison=True)
+        b = run_gpu(c, window, poison=True)
+        assert np.all(np.isfinite(a["out"])) and np.all(np.isfinite(a["lse"]))
+        assert torch.equal(a["raw_out"].view(torch.int16), b["raw_out"].view(torch.int16))
+        assert np.array_equal(a["lse"], b["lse"])
+
+
+def test_without_lse_and_with_workspace_reuse():
+    bd = _binding()
+    c = zc.fwd_case(112, 1, 256, 8, 2, gated=True)
+    q, k, v, g = (zc.to_dev(c[n], torch) for n in ("q", "k", "v", "gate"))
+    gq = torch.from_numpy(c["gq"]).cuda()
+    gk = torch.from_numpy(c["gk"]).cuda()
+    p = bd.make_params(1, 256, 8, 2, 128, 128)
+    ws = torch.empty(bd.zg_attn_fwd_workspace_size(p), dtype=torch.uint8, device="cuda")
+    o1, l1 = bd.zg_attn_fwd(q, k, v, g, gq, gk, window=128, workspace=ws)
+    assert l1 is None
+    o, _ = run_oracle(c, 128)
+    zc.compare(o1.float().cpu().numpy(), o, "no lse")
+
+
+def test_too_small_workspace_is_rejected_before_launch():
+    bd = _binding()
+    c = zc.fwd_case(113, 1, 64, 8, 2, gated=False)
+    q, k, v = (zc.to_dev(c[n], torch) for n in ("q", "k", "v"))
+    gq = torch.from_numpy(c["gq"]).cuda()
+    gk = torch.from_numpy(c["gk"]).cuda()
+    out = torch.full_like(q, 3.0)
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(bd.ZgAttnError) as e:
+        bd.zg_attn_fwd(q, k, v, None, gq, gk, window=0, out=out, workspace=ws)
+    assert e.value.status == bd.ZG_ERR_WORKSPACE
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == 3.0)
