@@ -172,6 +172,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-components", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["swa4k", "global16k", "decode", "block_global"],
+                    default=None, help="time one workload only (for profiling runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="with --only: first run a plain 1 GiB device copy, the reference "
+                         "for scaling the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -181,6 +186,16 @@ def main():
     import torch
     from global_attention_zg_amd import binding as bd
     torch.cuda.set_device(0)
+    if args.only:
+        if args.copy_calibration:
+            src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+            dst = torch.empty_like(src)
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            del src, dst
+        print(json.dumps({"only": args.only, "components": run_components(torch, bd, args.only,
+                                                                          args.steps)}))
+        return
 
     # ---- the 256K 5:1 block: five gated SWA layers + one global layer
     S, B, Hq, Hkv = 262144, 1, 32, 8
@@ -246,29 +261,7 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_components:
-        comps = {}
-        log("component: gated SWA B4 S4096")
-        l2 = Layer(torch, bd, 2, 0, 4, 4096, 32, 8, 128, True)
-        for _ in range(3):
-            l2()
-        t = time_events(torch, l2, 20)
-        comps["swa_4k_b4"] = {"ms": round(t * 1e3, 4), "tflops": round(l2.flops / t / 1e12, 2),
-                              "tokens_per_s": round(4 * 4096 / t, 1),
-                              "hbm_gbs_alg": round(l2.alg_bytes / t / 1e9, 1),
-                              "frac_hbm": round(l2.alg_bytes / t / 1e9 / PEAK_HBM_GBS, 4)}
-        del l2
-        log("component: global S16384")
-        l3 = Layer(torch, bd, 3, 0, 1, 16384, 32, 8, 0, False)
-        for _ in range(2):
-            l3()
-        t = time_events(torch, l3, 10)
-        comps["global_16k"] = {"ms": round(t * 1e3, 4), "tflops": round(l3.flops / t / 1e12, 2),
-                               "tokens_per_s": round(16384 / t, 1),
-                               "frac_mfma": round(l3.flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
-        del l3
-        torch.cuda.empty_cache()
-        comps.update(decode_components(torch, bd))
-        result["components"] = comps
+        result["components"] = run_components(torch, bd, None, 20)
 
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle, bounded sample)")
@@ -278,7 +271,45 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def decode_components(torch, bd):
+def run_components(torch, bd, only, iters):
+    """Per-workload timings: gated SWA B4xS4096, global S16384, decode at 256K."""
+    comps = {}
+    if only in (None, "swa4k"):
+        log("component: gated SWA B4 S4096")
+        l2 = Layer(torch, bd, 2, 0, 4, 4096, 32, 8, 128, True)
+        for _ in range(3):
+            l2()
+        t = time_events(torch, l2, iters)
+        comps["swa_4k_b4"] = {"ms": round(t * 1e3, 4), "tflops": round(l2.flops / t / 1e12, 2),
+                              "tokens_per_s": round(4 * 4096 / t, 1),
+                              "hbm_gbs_alg": round(l2.alg_bytes / t / 1e9, 1),
+                              "frac_hbm": round(l2.alg_bytes / t / 1e9 / PEAK_HBM_GBS, 4)}
+        del l2
+    if only in (None, "global16k"):
+        log("component: global S16384")
+        l3 = Layer(torch, bd, 3, 0, 1, 16384, 32, 8, 0, False)
+        for _ in range(2):
+            l3()
+        t = time_events(torch, l3, max(1, iters // 2))
+        comps["global_16k"] = {"ms": round(t * 1e3, 4), "tflops": round(l3.flops / t / 1e12, 2),
+                               "tokens_per_s": round(16384 / t, 1),
+                               "frac_mfma": round(l3.flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del l3
+    torch.cuda.empty_cache()
+    if only in (None, "decode"):
+        comps.update(decode_components(torch, bd, max(1, iters // 2)))
+    if only == "block_global":
+        log("global layer of the 256K block")
+        lg = Layer(torch, bd, 4, 5, 1, 262144, 32, 8, 0, False)
+        lg()
+        t = time_events(torch, lg, max(1, iters // 2))
+        comps["block_global_256k"] = {"ms": round(t * 1e3, 3),
+                                      "tflops": round(lg.flops / t / 1e12, 2)}
+        del lg
+    return comps
+
+
+def decode_components(torch, bd, iters):
     """One decode step of the block's two layer kinds at 256K: B16, one new
     token at position 262144 against the global layer's 262145-key cache and
     the SWA layer's 128-slot ring."""
@@ -308,7 +339,7 @@ def decode_components(torch, bd):
 
         for _ in range(2):
             fn()
-        t = time_events(torch, fn, 10)
+        t = time_events(torch, fn, iters)
         keys = min(L, cap)
         alg = B * Hkv * keys * D * 2 * 2 + (q.numel() * 2 + o.numel()) * 2
         flops = B * Hq * keys * FLOP_PER_PAIR

@@ -15,7 +15,12 @@
 //
 //   S^T = K' Q'^T  (v_mfma_f32_32x32x16_bf16, A = K' tile rows from LDS,
 //                   B = the wave's normalised + rotated Q' in registers)
-//   O^T += V^T P^T (A = V^T tile from LDS, B = P in registers)
+//   O^T += V^T P^T (A = V^T read from the row-major V tile with the gfx950
+//                   transposing LDS load ds_read_b64_tr_b16, B = P in registers)
+//
+// K' and V tiles are staged row-major in LDS with 272-byte and 288-byte row
+// strides: every LDS store and every MFMA operand read is free of bank
+// conflicts, and every LDS address is a per-lane base plus an immediate.
 //
 // Only KV tiles that intersect the causal band of the workgroup's queries are
 // visited: for a window W that is ceil((32 + W - 1) / 64) tiles, for the
@@ -24,6 +29,8 @@
 // epilogue.  Softmax runs in fp32 on raw scores with exp2(fma(s, c, -m c)),
 // c = scale*log2(e), and lazy rescaling of the accumulator (only when the
 // running max grows by more than 2^8 in exp2 units).
+
+#include <type_traits>
 
 #include "zg_common.h"
 #include "zg_launch.h"
@@ -34,13 +41,17 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBN = 64;             // keys per KV tile
-constexpr int kKsStride = kD + 8;   // bf16 per K' row in LDS (272 B: 16-B aligned, skewed banks)
-constexpr int kVtStride = kBN + 8;  // bf16 per V^T row in LDS (144 B)
-constexpr int kKsElems = kBN * kKsStride;
-constexpr int kVtElems = kD * kVtStride;
-constexpr int kBufElems = kKsElems + kVtElems;  // one K'+V^T stage: 35840 B
-constexpr float kRescaleThreshold = 8.0f;       // log2 units
+constexpr int kBN = 64;                          // keys per KV tile
+constexpr int kKsStride = kD + 8;                // bf16 per K' row in LDS (272 B)
+constexpr int kVsStride = kD + 16;               // bf16 per V row in LDS (288 B)
+constexpr int kKsBytes = kBN * kKsStride * 2;    // 17408 per stage
+constexpr int kVsBytes = kBN * kVsStride * 2;    // 18432 per stage
+constexpr int kVOff = 2 * kKsBytes;              // V stages follow both K stages
+constexpr int kSmemBytes = 2 * kKsBytes + 2 * kVsBytes;  // 71680
+constexpr float kRescaleThreshold = 8.0f;        // exp2 units
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 struct Geo {
   int heads_per_wg;  // query heads per workgroup (= waves sharing positions)
@@ -50,20 +61,120 @@ struct Geo {
   int n_bhg;         // B * Hkv * hgroups
 };
 
-// Row of the 32-key block that MFMA row m reads: swaps bits 2 and 3 of m so
-// that output registers 8t..8t+7 of lane half h hold keys 16t+8h .. 16t+8h+7,
-// i.e. exactly the B operand of the P.V product for k-step t.
-__device__ __forceinline__ int key_row_of(int m) {
-  return (m & 16) | ((m & 4) << 1) | ((m & 8) >> 1) | (m & 3);
-}
-// Row of V^T (a head dim) that MFMA row m of output block bd reads: chosen so
-// that output register r of lane half h holds dim 64h + 16bd + r.
-__device__ __forceinline__ int dim_row_of(int bd, int m) {
-  return ((m >> 2) & 1) * 64 + bd * 16 + (m >> 3) * 4 + (m & 3);
+__device__ __forceinline__ bf16x8 lds_read_b128(const lds_u8* p) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(p);
 }
 
+// Two transposing 8-byte LDS loads -> one 8 x bf16 MFMA operand.
+__device__ __forceinline__ bf16x8 lds_read_tr2(const lds_u8* p0, const lds_u8* p1) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) i16x4*>(const_cast<lds_u8*>(p0)));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) i16x4*>(const_cast<lds_u8*>(p1)));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+struct TileState {
+  f32x16 acc[4];
+  float m_run;   // running max of raw scores (this lane's query row)
+  float l_run;   // this lane's partial sum of P (its half of the keys)
+};
+
+// S^T = K' Q'^T for one 64-key tile (two 32-key blocks).  Lane (q = l%32,
+// h = l/32): register r of block blk holds key kt + 32 blk + 8 (r/4) + 4 h + r%4.
+__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const lds_u8* kread,
+                                        const bf16x8 (&qf)[8]) {
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    s[blk] = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const bf16x8 a = lds_read_b128(kread + blk * 32 * kKsStride * 2 + kk * 16);
+      s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[blk], 0, 0, 0);
+    }
+  }
+}
+
+// Masked-out keys -> -inf: visible iff 0 <= qm - key < lim.
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int kt, int qm, int lim, int half) {
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int dq = qm - (kt + blk * 32 + 8 * (r >> 2) + 4 * half + (r & 3));
+      s[blk][r] = (unsigned)dq < (unsigned)lim ? s[blk][r] : -INFINITY;
+    }
+  }
+}
+
+// Running max update with lazy rescaling of the accumulator; returns -m*c.
+__device__ __forceinline__ float softmax_max(TileState& st, const f32x16 (&s)[2], float c,
+                                             float rescale_raw) {
+  float mx = -INFINITY;
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
+  mx = pair_max32(mx);
+  const float m_new = fmaxf(st.m_run, mx);
+  if (__builtin_amdgcn_ballot_w64(m_new > st.m_run + rescale_raw)) {
+    const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2((st.m_run - m_new) * c);
+#pragma unroll
+    for (int bd = 0; bd < 4; ++bd) st.acc[bd] *= alpha;
+    st.l_run *= alpha;
+    st.m_run = m_new;
+  }
+  return st.m_run == -INFINITY ? 0.0f : -st.m_run * c;
+}
+
+// P = exp2(s c - m c) packed to bf16 (the PV B operand), row sums from the
+// rounded values the MFMA multiplies.
+__device__ __forceinline__ void softmax_exp(TileState& st, const f32x16 (&s)[2], float c,
+                                            float neg_mc, bf16x8 (&pf)[2][2]) {
+  const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(__builtin_fmaf(s[blk][8 * t + e], c, neg_mc));
+      pf[blk][t] = pack_bf16x8(pv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bf16x2 pr = {pf[blk][t][2 * e], pf[blk][t][2 * e + 1]};
+        st.l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, st.l_run, false);
+      }
+    }
+  }
+}
+
+// O^T += V^T P^T.  k-step t of block blk covers keys 32blk+16t .. +15; this
+// lane half supplies keys 4h+0..3 (first transposing load) and 8+4h+0..3.
+// O^T register r of block bd holds dim 32 bd + 8 (r/4) + 4 h + r%4.
+__device__ __forceinline__ void pv_tile(TileState& st, const lds_u8* vread,
+                                        const bf16x8 (&pf)[2][2]) {
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+#pragma unroll
+      for (int bd = 0; bd < 4; ++bd) {
+        const lds_u8* p0 = vread + (blk * 32 + 16 * t) * kVsStride * 2 + 64 * bd;
+        const bf16x8 a = lds_read_tr2(p0, p0 + 8 * kVsStride * 2);
+        st.acc[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[blk][t], st.acc[bd], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// BANDED: sliding-window layer (window > 0); otherwise global causal.
+template <bool BANDED>
 __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(FlashParams p, Geo geo) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kBufElems];
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kSmemBytes];
+  lds_u8* smem = (lds_u8*)smem_raw;  // generic -> LDS address space
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -76,7 +187,7 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(FlashParams p, G
   const int bid = blockIdx.x;
   const int bhg = bid % geo.n_bhg;
   int pb = bid / geo.n_bhg;
-  if (p.window == 0) pb = geo.n_pos_blocks - 1 - pb;  // longest causal rows first
+  if (!BANDED) pb = geo.n_pos_blocks - 1 - pb;  // longest causal rows first
   const int hg = bhg % geo.hgroups;
   const int bgi = bhg / geo.hgroups;
   const int g = bgi % p.Hkv;
@@ -85,10 +196,14 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(FlashParams p, G
   const int i0w = pb * geo.pos_per_wg;
   const int qi = i0w + (wv / geo.heads_per_wg) * 32 + qcol;
   const bool qok = qi < p.S;
+  // Rows past the end are padding: give them row S-1's visibility so that the
+  // wave-wide lazy-rescale vote is the same as for any window >= S.
+  const int qm = min(qi, p.S - 1);
+  const int lim = BANDED ? min(p.window, qm + 1) : qm + 1;
   const int hi = min(p.S, i0w + geo.pos_per_wg);
-  const int lo = p.window > 0 ? max(0, i0w - p.window + 1) : 0;
+  const int lo = BANDED ? max(0, i0w - p.window + 1) : 0;
   const int nt = (hi - lo + kBN - 1) / kBN;
-  const int kfirst = hi - nt * kBN;  // tiles end exactly at the last query; may start < 0
+  const int kfirst = hi - nt * kBN;  // tiles end exactly at the last query; only tile 0 may start < 0
 
   // ---- fused query prologue: RMSNorm (+ weight), partial RoPE, -> bf16 B operand
   const long long qrow = ((long long)b * p.S + (qok ? qi : 0)) * p.Hq + head;
@@ -116,7 +231,7 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(FlashParams p, G
     if (p.rope_half > 0 && half == 0) {
       // rotary dims (all < 64) live in the lane-half-0 registers; go through a
       // private LDS row so the partner dim can be addressed at run time.
-      float* qs = reinterpret_cast<float*>(smem) + (wv * 32 + qcol) * 65;
+      float* qs = reinterpret_cast<float*>(smem_raw) + (wv * 32 + qcol) * 65;
 #pragma unroll
       for (int d = 0; d < 64; ++d) qs[d] = x[d];
       const long long pos = p.pos_offset + qi;
@@ -124,11 +239,11 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(FlashParams p, G
 #pragma unroll
       for (int t = 0; t < kMaxRopeHalf; ++t) {
         if (t < rh) {
-          float c, s;
-          rope_cos_sin(p.tab, t, pos, c, s);
+          float cc, sn;
+          rope_cos_sin(p.tab, t, pos, cc, sn);
           const float a = qs[t], bb = qs[t + rh];
-          qs[t] = a * c - bb * s;
-          qs[t + rh] = bb * c + a * s;
+          qs[t] = a * cc - bb * sn;
+          qs[t + rh] = bb * cc + a * sn;
         }
       }
 #pragma unroll
@@ -139,169 +254,125 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(FlashParams p, G
   }
   __syncthreads();  // the prologue's LDS rows are reused by the KV tiles
 
-  // ---- KV tile staging: global -> registers -> LDS (K' row-major, V transposed)
+  // ---- KV tile staging: global -> registers -> LDS (both row-major,
+  // double-buffered; the next tile's loads are in flight during this tile)
   const long long kvstride = (long long)p.Hkv * kD;
   const uint16_t* kbase = p.kp + (long long)b * p.S * kvstride + g * kD;
   const uint16_t* vbase = p.v + (long long)b * p.S * kvstride + g * kD;
-  const int lc = tid & 15;   // 16-byte column chunk
-  const int lr = tid >> 4;   // 0..15
+  const int lc = tid & 15;  // 16-byte column chunk
+  const int lr = tid >> 4;  // 0..15: rows lr, lr+16, lr+32, lr+48
   u32x4 kreg[4], vreg[4];
-
-  auto gload = [&](int kt) {
+  // Keys below 0 (only in the lowest tile) load row 0 instead; they are masked out.
+  auto gload_k = [&](int kt) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = kt + lr + 16 * j;
-      kreg[j] = key >= 0 ? ld16(kbase + key * kvstride + 8 * lc) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = kt + 4 * lr + j;
-      vreg[j] = key >= 0 ? ld16(vbase + key * kvstride + 8 * lc) : u32x4{0, 0, 0, 0};
-    }
+    for (int j = 0; j < 4; ++j)
+      kreg[j] = ld16(kbase + (long long)max(kt + lr + 16 * j, 0) * kvstride + 8 * lc);
   };
-  auto sstore = [&](int buf) {
-    uint16_t* Ks = smem + buf * kBufElems;
-    uint16_t* Vt = Ks + kKsElems;
+  auto gload_v = [&](int kt) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) st16(Ks + (lr + 16 * j) * kKsStride + 8 * lc, kreg[j]);
+    for (int j = 0; j < 4; ++j)
+      vreg[j] = ld16(vbase + (long long)max(kt + lr + 16 * j, 0) * kvstride + 8 * lc);
+  };
+  auto sstore_k = [&](int stg) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int wd = i >> 1;
-      uint32_t a, c;
-      if (i & 1) {
-        a = (vreg[0][wd] >> 16) | (vreg[1][wd] & 0xffff0000u);
-        c = (vreg[2][wd] >> 16) | (vreg[3][wd] & 0xffff0000u);
-      } else {
-        a = (vreg[0][wd] & 0xffffu) | (vreg[1][wd] << 16);
-        c = (vreg[2][wd] & 0xffffu) | (vreg[3][wd] << 16);
-      }
-      uint2 pr = {a, c};
-      *reinterpret_cast<uint2*>(Vt + (8 * lc + i) * kVtStride + 4 * lr) = pr;
-    }
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+          smem + stg * kKsBytes + (lr + 16 * j) * kKsStride * 2 + 16 * lc) = kreg[j];
+  };
+  auto sstore_v = [&](int stg) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+          smem + kVOff + stg * kVsBytes + (lr + 16 * j) * kVsStride * 2 + 16 * lc) = vreg[j];
   };
 
-  f32x16 acc[4];
+  TileState st;
 #pragma unroll
-  for (int bd = 0; bd < 4; ++bd) acc[bd] = f32x16{};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  const int mrow = lane & 31;
-  const int krow = key_row_of(mrow);
-  const float rescale_raw = kRescaleThreshold / p.scale_log2;  // threshold in raw score units
+  for (int bd = 0; bd < 4; ++bd) st.acc[bd] = f32x16{};
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
+  const float c = p.scale_log2;
+  const float rescale_raw = kRescaleThreshold / c;  // threshold in raw score units
+  // per-lane LDS read bases: K' row (q%32) at column 64h; V rows 4h + i/4 at
+  // dims 16 (group parity) + 4 (i%4) for the transposing loads
+  const lds_u8* kread = smem + qcol * kKsStride * 2 + 128 * half;
+  const int gi = lane & 15;
+  const lds_u8* vread = smem + kVOff + (4 * half + (gi >> 2)) * kVsStride * 2 +
+                        (16 * ((lane >> 4) & 1) + 4 * (gi & 3)) * 2;
 
-  gload(kfirst);
-  sstore(0);
-  __syncthreads();
+  // Tiles are visited in descending key order, j = 0 .. nt-1 covering keys
+  // [kt(j), kt(j) + 64), kt(j) = kfirst + 64 (nt-1-j): the causal diagonal
+  // comes first and sets a good running max early.  Masked tiles: every tile
+  // of a windowed layer; for the global layer the tiles crossing the
+  // workgroup's first query, and the lowest tile if it starts below key 0.
+  auto kt_of = [&](int j) { return kfirst + (nt - 1 - j) * kBN; };
+  auto masked = [&](int j) {
+    const int kt = kt_of(j);
+    return BANDED || kt < 0 || kt + kBN - 1 > i0w;
+  };
 
-  for (int t = 0; t < nt; ++t) {
-    const int kt = kfirst + t * kBN;
-    if (t + 1 < nt) gload(kt + kBN);
-    const uint16_t* Ks = smem + (t & 1) * kBufElems;
-    const uint16_t* Vt = Ks + kKsElems;
-
-    // S^T for two 32-key blocks
+  int stage = 0;
+  auto step = [&](int j, auto mask_tag) {
+    const int kt = kt_of(j);
+    if (j + 1 < nt) {
+      gload_k(kt_of(j + 1));
+      gload_v(kt_of(j + 1));
+    }
     f32x16 s[2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      s[blk] = f32x16{};
-      const uint16_t* kr = Ks + (blk * 32 + krow) * kKsStride + 64 * half;
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + 8 * kk);
-        s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[blk], 0, 0, 0);
-      }
-    }
-
-    // mask (raw scores), running max in raw units; exp2 argument is one FMA
-    // fma(s, c, -m*c) so that masked and unmasked tiles round identically
-    const bool need_mask = p.window > 0 || kt < 0 || kt + kBN - 1 > i0w;
-    float mx = -INFINITY;
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = s[blk][r];
-        if (need_mask) {
-          const int j = kt + blk * 32 + 16 * (r >> 3) + 8 * half + (r & 7);
-          const bool vis = j >= 0 && j <= qi && (p.window == 0 || qi - j < p.window);
-          v = vis ? v : -INFINITY;
-        }
-        s[blk][r] = v;
-        mx = fmaxf(mx, v);
-      }
-    }
-    mx = pair_max32(mx);
-    const float m_new = fmaxf(m_run, mx);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run + rescale_raw)) {
-      const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2((m_run - m_new) * p.scale_log2);
-#pragma unroll
-      for (int bd = 0; bd < 4; ++bd) acc[bd] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-    }
-    const float neg_mc = m_run == -INFINITY ? 0.0f : -m_run * p.scale_log2;
-
+    qk_tile(s, kread + stage * kKsBytes, qf);
+    if (decltype(mask_tag)::value) mask_tile(s, kt, qm, lim, half);
+    const float neg_mc = softmax_max(st, s, c, rescale_raw);
     bf16x8 pf[2][2];
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      float pv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pv[r] = fast_exp2(__builtin_fmaf(s[blk][r], p.scale_log2, neg_mc));
-        l_run += pv[r];
-      }
-      pf[blk][0] = pack_bf16x8(pv);
-      pf[blk][1] = pack_bf16x8(pv + 8);
+    softmax_exp(st, s, c, neg_mc, pf);
+    pv_tile(st, vread + stage * kVsBytes, pf);
+    if (j + 1 < nt) {
+      sstore_k(stage ^ 1);
+      sstore_v(stage ^ 1);
     }
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-        for (int bd = 0; bd < 4; ++bd) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              Vt + dim_row_of(bd, mrow) * kVtStride + blk * 32 + 16 * tt + 8 * half);
-          acc[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[blk][tt], acc[bd], 0, 0, 0);
-        }
-      }
-    }
-
-    if (t + 1 < nt) sstore((t + 1) & 1);
+    stage ^= 1;
     __syncthreads();
-  }
+  };
 
-  // ---- epilogue: normalise, gate, store
-  const float l_tot = pair_sum32(l_run);
+  gload_k(kt_of(0));
+  gload_v(kt_of(0));
+  sstore_k(0);
+  sstore_v(0);
+  __syncthreads();
+  int j = 0;
+  for (; j < nt && masked(j); ++j) step(j, std::true_type{});   // diagonal / band
+  for (; j < nt && !masked(j); ++j) step(j, std::false_type{});
+  for (; j < nt; ++j) step(j, std::true_type{});                // lowest tile below key 0
+
+  // ---- epilogue: normalise, gate, store (register r of block bd, lane half
+  // h -> dim 32 bd + 8 (r/4) + 4 h + r%4: four runs of 4 dims per block)
+  const float l_tot = pair_sum32(st.l_run);
   const float inv = 1.0f / l_tot;
   if (qok) {
-    uint16_t* dst = p.out + qrow * kD + 64 * half;
-    const uint16_t* gsrc = p.gate ? p.gate + qrow * kD + 64 * half : nullptr;
+    uint16_t* dst = p.out + qrow * kD + 4 * half;
+    const uint16_t* gsrc = p.gate ? p.gate + qrow * kD + 4 * half : nullptr;
 #pragma unroll
     for (int bd = 0; bd < 4; ++bd) {
-      float o[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[r] = acc[bd][r] * inv;
-      if (gsrc) {
-        float gv[16];
-        unpack_bf16x8(ld16(gsrc + 16 * bd), gv);
-        unpack_bf16x8(ld16(gsrc + 16 * bd + 8), gv + 8);
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float o[4];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[r] *= sigmoidf_(gv[r]);
+        for (int e = 0; e < 4; ++e) o[e] = st.acc[bd][4 * q4 + e] * inv;
+        const int off = 32 * bd + 8 * q4;
+        if (gsrc) {
+          const uint2 gg = *reinterpret_cast<const uint2*>(gsrc + off);
+          o[0] *= sigmoidf_(bf_lo(gg.x));
+          o[1] *= sigmoidf_(bf_hi(gg.x));
+          o[2] *= sigmoidf_(bf_lo(gg.y));
+          o[3] *= sigmoidf_(bf_hi(gg.y));
+        }
+        uint2 w;
+        w.x = pack_bf16x2(o[0], o[1]);
+        w.y = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<uint2*>(dst + off) = w;
       }
-      u32x4 w0, w1;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        w0[i] = pack_bf16x2(o[2 * i], o[2 * i + 1]);
-        w1[i] = pack_bf16x2(o[8 + 2 * i], o[8 + 2 * i + 1]);
-      }
-      st16(dst + 16 * bd, w0);
-      st16(dst + 16 * bd + 8, w1);
     }
     if (p.lse && half == 0)
-      p.lse[((long long)b * p.Hq + head) * p.S + qi] =
-          (m_run * p.scale_log2 + __log2f(l_tot)) * kLn2;
+      p.lse[((long long)b * p.Hq + head) * p.S + qi] = (st.m_run * c + __log2f(l_tot)) * kLn2;
   }
 }
 
@@ -318,8 +389,12 @@ hipError_t launch_flash_fwd(const FlashParams& p, hipStream_t stream) {
   geo.n_bhg = p.B * p.Hkv * geo.hgroups;
   const long long blocks = (long long)geo.n_pos_blocks * geo.n_bhg;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(flash_fwd_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p,
-                     geo);
+  if (p.window > 0)
+    hipLaunchKernelGGL(flash_fwd_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       p, geo);
+  else
+    hipLaunchKernelGGL(flash_fwd_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       p, geo);
   return hipGetLastError();
 }
 
