@@ -18,9 +18,11 @@
 //   O^T += V^T P^T (A = V^T read from the row-major V tile with the gfx950
 //                   transposing LDS load ds_read_b64_tr_b16, B = P in registers)
 //
-// K' and V tiles are staged row-major in LDS with 272-byte and 288-byte row
-// strides: every LDS store and every MFMA operand read is free of bank
-// conflicts, and every LDS address is a per-lane base plus an immediate.
+// K' and V tiles go from global memory straight into LDS (global_load_lds,
+// no register staging), row-major with 256-byte rows whose 16-byte chunks
+// are XOR-swizzled by row: chunk ^ (row & 15) for K', chunk ^ ((row & 3) << 2)
+// for V.  With the 64-bank LDS every MFMA operand read is then free of bank
+// conflicts, and each read address is a per-lane base plus an immediate.
 //
 // Only KV tiles that intersect the causal band of the workgroup's queries are
 // visited: for a window W that is ceil((32 + W - 1) / 64) tiles, for the
@@ -41,13 +43,13 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kBN = 64;                          // keys per KV tile
-constexpr int kKsStride = kD + 8;                // bf16 per K' row in LDS (272 B)
-constexpr int kVsStride = kD + 16;               // bf16 per V row in LDS (288 B)
-constexpr int kKsBytes = kBN * kKsStride * 2;    // 17408 per stage
-constexpr int kVsBytes = kBN * kVsStride * 2;    // 18432 per stage
-constexpr int kVOff = 2 * kKsBytes;              // V stages follow both K stages
-constexpr int kSmemBytes = 2 * kKsBytes + 2 * kVsBytes;  // 71680
+constexpr int kBN = 32;                          // keys per KV tile (one MFMA block)
+constexpr int kRowBytes = kD * 2;                // 256-byte K'/V rows in LDS, 16-byte chunks XOR-swizzled
+constexpr int kTileBytes = kBN * kRowBytes;      // 8192 per K' or V stage
+constexpr int kVOff = 2 * kTileBytes;            // V stages follow both K' stages
+constexpr int kTilesBytes = 4 * kTileBytes;      // 32768: two stages of K' and V
+constexpr int kQScratchBytes = kWaves * 32 * 65 * 4;  // query-prologue RoPE rows (reused)
+constexpr int kSmemBytes = kTilesBytes > kQScratchBytes ? kTilesBytes : kQScratchBytes;
 constexpr float kRescaleThreshold = 8.0f;        // exp2 units
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
@@ -82,42 +84,40 @@ struct TileState {
   float l_run;   // this lane's partial sum of P (its half of the keys)
 };
 
-// S^T = K' Q'^T for one 64-key tile (two 32-key blocks).  Lane (q = l%32,
-// h = l/32): register r of block blk holds key kt + 32 blk + 8 (r/4) + 4 h + r%4.
-__device__ __forceinline__ void qk_tile(f32x16 (&s)[2], const lds_u8* kread,
-                                        const bf16x8 (&qf)[8]) {
+// S^T = K' Q'^T for one 32-key block.  Lane (q = l%32, h = l/32): register r
+// holds key kblk + 8 (r/4) + 4 h + r%4.  kblk_lds points at the block's first
+// K' row in LDS; kread_off is this lane's swizzled offset of row q%32, chunk
+// 8h, and k-step kk is reached by XOR with kk << 4.
+__device__ __forceinline__ void qk_blk(f32x16& s, const lds_u8* kblk_lds, uint32_t kread_off,
+                                       const bf16x8 (&qf)[8]) {
+  s = f32x16{};
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    s[blk] = f32x16{};
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const bf16x8 a = lds_read_b128(kread + blk * 32 * kKsStride * 2 + kk * 16);
-      s[blk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s[blk], 0, 0, 0);
-    }
+  for (int kk = 0; kk < 8; ++kk) {
+    const bf16x8 a = lds_read_b128(kblk_lds + (kread_off ^ (uint32_t)(kk << 4)));
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[kk], s, 0, 0, 0);
   }
 }
 
 // Masked-out keys -> -inf: visible iff 0 <= qm - key < lim.
-__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int kt, int qm, int lim, int half) {
+__device__ __forceinline__ void mask_blk(f32x16& s, int kblk, int qm, int lim, int half) {
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int dq = qm - (kt + blk * 32 + 8 * (r >> 2) + 4 * half + (r & 3));
-      s[blk][r] = (unsigned)dq < (unsigned)lim ? s[blk][r] : -INFINITY;
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int dq = qm - (kblk + 8 * (r >> 2) + 4 * half + (r & 3));
+    s[r] = (unsigned)dq < (unsigned)lim ? s[r] : -INFINITY;
   }
 }
 
-// Running max update with lazy rescaling of the accumulator; returns -m*c.
-__device__ __forceinline__ float softmax_max(TileState& st, const f32x16 (&s)[2], float c,
-                                             float rescale_raw) {
+// Row max of the raw scores of one block (both lane halves of the row).
+__device__ __forceinline__ float blk_max(const f32x16& s) {
   float mx = -INFINITY;
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk][r]);
-  mx = pair_max32(mx);
+  for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+  return pair_max32(mx);
+}
+
+// Running max update with lazy rescaling of the accumulator; returns -m*c.
+__device__ __forceinline__ float softmax_rescale(TileState& st, float mx, float c,
+                                                 float rescale_raw) {
   const float m_new = fmaxf(st.m_run, mx);
   if (__builtin_amdgcn_ballot_w64(m_new > st.m_run + rescale_raw)) {
     const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2((st.m_run - m_new) * c);
@@ -129,50 +129,46 @@ __device__ __forceinline__ float softmax_max(TileState& st, const f32x16 (&s)[2]
   return st.m_run == -INFINITY ? 0.0f : -st.m_run * c;
 }
 
-// P = exp2(s c - m c) packed to bf16 (the PV B operand), row sums from the
-// rounded values the MFMA multiplies.
-__device__ __forceinline__ void softmax_exp(TileState& st, const f32x16 (&s)[2], float c,
-                                            float neg_mc, bf16x8 (&pf)[2][2]) {
+// P = exp2(s c - m c) packed to bf16 (the PV B operand for the block's two
+// 16-key k-steps), row sums from the rounded values the MFMA multiplies.
+__device__ __forceinline__ void exp_blk(TileState& st, const f32x16& s, float c, float neg_mc,
+                                        bf16x8 (&pf)[2]) {
   const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
+  for (int t = 0; t < 2; ++t) {
+    float pv[8];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      float pv[8];
+    for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(__builtin_fmaf(s[8 * t + e], c, neg_mc));
+    pf[t] = pack_bf16x8(pv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = fast_exp2(__builtin_fmaf(s[blk][8 * t + e], c, neg_mc));
-      pf[blk][t] = pack_bf16x8(pv);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bf16x2 pr = {pf[blk][t][2 * e], pf[blk][t][2 * e + 1]};
-        st.l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, st.l_run, false);
-      }
+    for (int e = 0; e < 4; ++e) {
+      const bf16x2 pr = {pf[t][2 * e], pf[t][2 * e + 1]};
+      st.l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, one2, st.l_run, false);
     }
   }
 }
 
-// O^T += V^T P^T.  k-step t of block blk covers keys 32blk+16t .. +15; this
-// lane half supplies keys 4h+0..3 (first transposing load) and 8+4h+0..3.
-// O^T register r of block bd holds dim 32 bd + 8 (r/4) + 4 h + r%4.
-__device__ __forceinline__ void pv_tile(TileState& st, const lds_u8* vread,
-                                        const bf16x8 (&pf)[2][2]) {
+// O^T += V^T P^T for one 32-key block.  k-step t covers keys 16t .. 16t+15 of
+// the block; this lane half supplies keys 4h+0..3 (first transposing load)
+// and 8+4h+0..3.  O^T register r of block bd holds dim 32 bd + 8 (r/4) + 4 h
+// + r%4.  vread[bd]: this lane's swizzled address for dim block bd in the
+// block's V row 4h + i/4 (i = lane % 16).
+__device__ __forceinline__ void pv_blk(TileState& st, const lds_u8* (&vread)[4], int row0,
+                                       const bf16x8 (&pf)[2]) {
 #pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
+  for (int t = 0; t < 2; ++t) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int bd = 0; bd < 4; ++bd) {
-        const lds_u8* p0 = vread + (blk * 32 + 16 * t) * kVsStride * 2 + 64 * bd;
-        const bf16x8 a = lds_read_tr2(p0, p0 + 8 * kVsStride * 2);
-        st.acc[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[blk][t], st.acc[bd], 0, 0, 0);
-      }
+    for (int bd = 0; bd < 4; ++bd) {
+      const lds_u8* p0 = vread[bd] + (row0 + 16 * t) * kRowBytes;
+      const bf16x8 a = lds_read_tr2(p0, p0 + 8 * kRowBytes);
+      st.acc[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[t], st.acc[bd], 0, 0, 0);
     }
   }
 }
 
 // BANDED: sliding-window layer (window > 0); otherwise global causal.
 template <bool BANDED>
-__global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(FlashParams p, Geo geo) {
+__global__ __launch_bounds__(kThreads, 3) void flash_fwd_kernel(FlashParams p, Geo geo) {
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kSmemBytes];
   lds_u8* smem = (lds_u8*)smem_raw;  // generic -> LDS address space
 
@@ -200,10 +196,8 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(FlashParams p, G
   // wave-wide lazy-rescale vote is the same as for any window >= S.
   const int qm = min(qi, p.S - 1);
   const int lim = BANDED ? min(p.window, qm + 1) : qm + 1;
-  const int hi = min(p.S, i0w + geo.pos_per_wg);
-  const int lo = BANDED ? max(0, i0w - p.window + 1) : 0;
-  const int nt = (hi - lo + kBN - 1) / kBN;
-  const int kfirst = hi - nt * kBN;  // tiles end exactly at the last query; only tile 0 may start < 0
+  const int hi = min(p.S, i0w + geo.pos_per_wg);      // keys < hi
+  const int lo = BANDED ? max(0, i0w - p.window + 1) : 0;  // keys >= lo
 
   // ---- fused query prologue: RMSNorm (+ weight), partial RoPE, -> bf16 B operand
   const long long qrow = ((long long)b * p.S + (qok ? qi : 0)) * p.Hq + head;
@@ -254,37 +248,57 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(FlashParams p, G
   }
   __syncthreads();  // the prologue's LDS rows are reused by the KV tiles
 
-  // ---- KV tile staging: global -> registers -> LDS (both row-major,
-  // double-buffered; the next tile's loads are in flight during this tile)
+  // ---- KV tile staging: global -> LDS directly (global_load_lds_dwordx4),
+  // double-buffered, tile t in stage t&1.  Wave wv fills 1 KB blocks
+  // 2wv, 2wv+1 (rows 4n..4n+3) of each 8 KB tile: lane L writes physical
+  // chunk L%16 of row 4n + L/16 and so fetches the logical chunk that the
+  // row's swizzle places there.
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);  // wave-uniform copy
   const long long kvstride = (long long)p.Hkv * kD;
   const uint16_t* kbase = p.kp + (long long)b * p.S * kvstride + g * kD;
   const uint16_t* vbase = p.v + (long long)b * p.S * kvstride + g * kD;
-  const int lc = tid & 15;  // 16-byte column chunk
-  const int lr = tid >> 4;  // 0..15: rows lr, lr+16, lr+32, lr+48
-  u32x4 kreg[4], vreg[4];
-  // Keys below 0 (only in the lowest tile) load row 0 instead; they are masked out.
-  auto gload_k = [&](int kt) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  uint32_t row_off[2], kchunk[2];
+  int lrow[2];
+  const uint32_t vchunk = 16u * ((lane & 15) ^ (((lane >> 4) & 3) << 2));
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      kreg[j] = ld16(kbase + (long long)max(kt + lr + 16 * j, 0) * kvstride + 8 * lc);
-  };
-  auto gload_v = [&](int kt) {
+  for (int j = 0; j < 2; ++j) {
+    lrow[j] = 4 * (2 * wvu + j) + (lane >> 4);
+    row_off[j] = (uint32_t)(lrow[j] * kvstride * 2);
+    kchunk[j] = 16u * ((lane & 15) ^ (lrow[j] & 15));
+  }
+  // tile t -> stage t&1; keys >= S (only in the top tile) load key S-1 and
+  // are masked out
+  auto gload = [&](int t) {
+    const int stg = t & 1;
+    if (t * kBN + kBN <= p.S) {
+      const unsigned char* kb = (const unsigned char*)(kbase + (long long)t * kBN * kvstride);
+      const unsigned char* vb = (const unsigned char*)(vbase + (long long)t * kBN * kvstride);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      vreg[j] = ld16(vbase + (long long)max(kt + lr + 16 * j, 0) * kvstride + 8 * lc);
-  };
-  auto sstore_k = [&](int stg) {
+      for (int j = 0; j < 2; ++j) {
+        __builtin_amdgcn_global_load_lds(kb + row_off[j] + kchunk[j],
+                                         (lds_void*)(smem + stg * kTileBytes + (2 * wvu + j) * 1024),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vb + row_off[j] + vchunk,
+                                         (lds_void*)(smem + kVOff + stg * kTileBytes + (2 * wvu + j) * 1024),
+                                         16, 0, 0);
+      }
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
-          smem + stg * kKsBytes + (lr + 16 * j) * kKsStride * 2 + 16 * lc) = kreg[j];
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t off = (uint32_t)(min(t * kBN + lrow[j], p.S - 1) * kvstride * 2);
+        __builtin_amdgcn_global_load_lds((const unsigned char*)kbase + off + kchunk[j],
+                                         (lds_void*)(smem + stg * kTileBytes + (2 * wvu + j) * 1024),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const unsigned char*)vbase + off + vchunk,
+                                         (lds_void*)(smem + kVOff + stg * kTileBytes + (2 * wvu + j) * 1024),
+                                         16, 0, 0);
+      }
+    }
   };
-  auto sstore_v = [&](int stg) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
-          smem + kVOff + stg * kVsBytes + (lr + 16 * j) * kVsStride * 2 + 16 * lc) = vreg[j];
-  };
+  // this wave's direct-to-LDS loads have landed (vmcnt(0)); a barrier then
+  // publishes them to the workgroup
+  auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
   TileState st;
 #pragma unroll
@@ -293,55 +307,47 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(FlashParams p, G
   st.l_run = 0.f;
   const float c = p.scale_log2;
   const float rescale_raw = kRescaleThreshold / c;  // threshold in raw score units
-  // per-lane LDS read bases: K' row (q%32) at column 64h; V rows 4h + i/4 at
-  // dims 16 (group parity) + 4 (i%4) for the transposing loads
-  const lds_u8* kread = smem + qcol * kKsStride * 2 + 128 * half;
+  // per-lane LDS read offsets: K' row q%32 at logical chunk 8h; V rows
+  // 4h + i/4 at dims 32bd + 16 (group parity) + 4 (i%4) for the transposing loads
+  const uint32_t kread_off = qcol * kRowBytes + ((uint32_t)((8 * half) ^ (qcol & 15)) << 4);
   const int gi = lane & 15;
-  const lds_u8* vread = smem + kVOff + (4 * half + (gi >> 2)) * kVsStride * 2 +
-                        (16 * ((lane >> 4) & 1) + 4 * (gi & 3)) * 2;
+  const int vq = gi >> 2;
+  const int vlow = 2 * ((lane >> 4) & 1) + ((gi & 3) >> 1);
+  const lds_u8* vread0[4];
+  const lds_u8* vread1[4];
+#pragma unroll
+  for (int bd = 0; bd < 4; ++bd) {
+    const int off = (4 * half + vq) * kRowBytes + (((bd ^ vq) << 2 | vlow) << 4) + 8 * (gi & 1);
+    vread0[bd] = smem + kVOff + off;
+    vread1[bd] = smem + kVOff + kTileBytes + off;
+  }
 
-  // Tiles are visited in descending key order, j = 0 .. nt-1 covering keys
-  // [kt(j), kt(j) + 64), kt(j) = kfirst + 64 (nt-1-j): the causal diagonal
-  // comes first and sets a good running max early.  Masked tiles: every tile
-  // of a windowed layer; for the global layer the tiles crossing the
-  // workgroup's first query, and the lowest tile if it starts below key 0.
-  auto kt_of = [&](int j) { return kfirst + (nt - 1 - j) * kBN; };
-  auto masked = [&](int j) {
-    const int kt = kt_of(j);
-    return BANDED || kt < 0 || kt + kBN - 1 > i0w;
-  };
-
-  int stage = 0;
+  // 32-key tiles aligned to key 0, visited from the diagonal down: tile
+  // t = t_hi - j holds keys [32t, 32t + 32).  Masked tiles: every tile of a
+  // windowed layer; for the global layer the tiles reaching past the
+  // workgroup's first query.
+  const int t_hi = (hi - 1) / kBN;
+  const int nt = t_hi - lo / kBN + 1;
   auto step = [&](int j, auto mask_tag) {
-    const int kt = kt_of(j);
-    if (j + 1 < nt) {
-      gload_k(kt_of(j + 1));
-      gload_v(kt_of(j + 1));
-    }
-    f32x16 s[2];
-    qk_tile(s, kread + stage * kKsBytes, qf);
-    if (decltype(mask_tag)::value) mask_tile(s, kt, qm, lim, half);
-    const float neg_mc = softmax_max(st, s, c, rescale_raw);
-    bf16x8 pf[2][2];
-    softmax_exp(st, s, c, neg_mc, pf);
-    pv_tile(st, vread + stage * kVsBytes, pf);
-    if (j + 1 < nt) {
-      sstore_k(stage ^ 1);
-      sstore_v(stage ^ 1);
-    }
-    stage ^= 1;
+    const int t = t_hi - j;
+    if (j + 1 < nt) gload(t - 1);
+    f32x16 s;
+    qk_blk(s, smem + (t & 1) * kTileBytes, kread_off, qf);
+    if (decltype(mask_tag)::value) mask_blk(s, t * kBN, qm, lim, half);
+    const float neg_mc = softmax_rescale(st, blk_max(s), c, rescale_raw);
+    bf16x8 pf[2];
+    exp_blk(st, s, c, neg_mc, pf);
+    pv_blk(st, (t & 1) ? vread1 : vread0, 0, pf);
+    wait_loads();
     __syncthreads();
   };
 
-  gload_k(kt_of(0));
-  gload_v(kt_of(0));
-  sstore_k(0);
-  sstore_v(0);
+  gload(t_hi);
+  wait_loads();
   __syncthreads();
   int j = 0;
-  for (; j < nt && masked(j); ++j) step(j, std::true_type{});   // diagonal / band
-  for (; j < nt && !masked(j); ++j) step(j, std::false_type{});
-  for (; j < nt; ++j) step(j, std::true_type{});                // lowest tile below key 0
+  for (; j < nt && (BANDED || (t_hi - j) * kBN + kBN - 1 > i0w); ++j) step(j, std::true_type{});
+  for (; j < nt; ++j) step(j, std::false_type{});
 
   // ---- epilogue: normalise, gate, store (register r of block bd, lane half
   // h -> dim 32 bd + 8 (r/4) + 4 h + r%4: four runs of 4 dims per block)
