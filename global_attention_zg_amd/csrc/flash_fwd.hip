@@ -46,13 +46,30 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBN = 32;                          // keys per KV tile (one MFMA block)
 constexpr int kRowBytes = kD * 2;                // 256-byte K'/V rows in LDS, 16-byte chunks XOR-swizzled
 constexpr int kTileBytes = kBN * kRowBytes;      // 8192 per K' or V stage
-constexpr int kVOff = 2 * kTileBytes;            // V stages follow both K' stages
-constexpr int kTilesBytes = 4 * kTileBytes;      // 32768: two stages of K' and V
+// LDS ring depth: the windowed kernel keeps loads two tiles ahead (three
+// stages), the global kernel, which runs three workgroups per CU, one tile
+// ahead (two stages).  K' stages come first, then the V stages.
+template <bool BANDED> struct Ring {
+  static constexpr int kStages = BANDED ? 3 : 2;
+  static constexpr int kVOff = kStages * kTileBytes;
+  static constexpr int kTilesBytes = 2 * kStages * kTileBytes;
+};
 constexpr int kQScratchBytes = kWaves * 32 * 65 * 4;  // query-prologue RoPE rows (reused)
-constexpr int kSmemBytes = kTilesBytes > kQScratchBytes ? kTilesBytes : kQScratchBytes;
+constexpr int kSmemGlobal =
+    Ring<false>::kTilesBytes > kQScratchBytes ? Ring<false>::kTilesBytes : kQScratchBytes;  // 33280
+// Windowed layers also stage their query rows (8 KB per wave) behind the
+// tiles, and after the loop their fp32 output rows (16 KB per wave) for
+// coalesced stores.
+constexpr int kQRegion = Ring<true>::kTilesBytes;
+constexpr int kSmemBanded = Ring<true>::kTilesBytes + kWaves * 32 * kRowBytes;  // 81920
+static_assert(kWaves * 32 * 128 * 4 <= kSmemBanded, "output staging must fit");
 constexpr float kRescaleThreshold = 8.0f;        // exp2 units
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// s_waitcnt immediate for "at most n vector-memory loads outstanding" (lgkm
+// and exp counters left at their maxima): vmcnt is bits [3:0] and [15:14].
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 struct Geo {
@@ -167,10 +184,15 @@ __device__ __forceinline__ void pv_blk(TileState& st, const lds_u8* (&vread)[4],
 }
 
 // BANDED: sliding-window layer (window > 0); otherwise global causal.
-template <bool BANDED>
-__global__ __launch_bounds__(kThreads, 3) void flash_fwd_kernel(FlashParams p, Geo geo) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kSmemBytes];
+// RH: rope_dim / 2 when known at compile time (0 or 21: the rotation runs in
+// registers), -1 for any other rope_dim (rotation through LDS).
+template <bool BANDED, int RH>
+__global__ __launch_bounds__(kThreads, BANDED ? 2 : 3) void flash_fwd_kernel(FlashParams p,
+                                                                               Geo geo) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[BANDED ? kSmemBanded : kSmemGlobal];
   lds_u8* smem = (lds_u8*)smem_raw;  // generic -> LDS address space
+  constexpr int NS = Ring<BANDED>::kStages;
+  constexpr int kVOff = Ring<BANDED>::kVOff;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -199,60 +221,15 @@ __global__ __launch_bounds__(kThreads, 3) void flash_fwd_kernel(FlashParams p, G
   const int hi = min(p.S, i0w + geo.pos_per_wg);      // keys < hi
   const int lo = BANDED ? max(0, i0w - p.window + 1) : 0;  // keys >= lo
 
-  // ---- fused query prologue: RMSNorm (+ weight), partial RoPE, -> bf16 B operand
-  const long long qrow = ((long long)b * p.S + (qok ? qi : 0)) * p.Hq + head;
-  bf16x8 qf[8];
-  {
-    float x[64];
-    const uint16_t* src = p.q + qrow * kD + 64 * half;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      u32x4 u = qok ? ld16(src + 8 * j) : u32x4{0, 0, 0, 0};
-      unpack_bf16x8(u, x + 8 * j);
-    }
-    float ss = 0.f;
-#pragma unroll
-    for (int d = 0; d < 64; ++d) ss += x[d] * x[d];
-    ss = pair_sum32(ss);
-    const float r = 1.0f / sqrtf(ss * (1.0f / kD) + p.eps);
-    const float* wsrc = p.q_norm_w + 64 * half;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      u32x4 wv4 = ld16(wsrc + 4 * j);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) x[4 * j + i] *= r * __uint_as_float(wv4[i]);
-    }
-    if (p.rope_half > 0 && half == 0) {
-      // rotary dims (all < 64) live in the lane-half-0 registers; go through a
-      // private LDS row so the partner dim can be addressed at run time.
-      float* qs = reinterpret_cast<float*>(smem_raw) + (wv * 32 + qcol) * 65;
-#pragma unroll
-      for (int d = 0; d < 64; ++d) qs[d] = x[d];
-      const long long pos = p.pos_offset + qi;
-      const int rh = p.rope_half;
-#pragma unroll
-      for (int t = 0; t < kMaxRopeHalf; ++t) {
-        if (t < rh) {
-          float cc, sn;
-          rope_cos_sin(p.tab, t, pos, cc, sn);
-          const float a = qs[t], bb = qs[t + rh];
-          qs[t] = a * cc - bb * sn;
-          qs[t + rh] = bb * cc + a * sn;
-        }
-      }
-#pragma unroll
-      for (int d = 0; d < 64; ++d) x[d] = qs[d];
-    }
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qf[kk] = pack_bf16x8(x + 8 * kk);
-  }
-  __syncthreads();  // the prologue's LDS rows are reused by the KV tiles
 
-  // ---- KV tile staging: global -> LDS directly (global_load_lds_dwordx4),
-  // double-buffered, tile t in stage t&1.  Wave wv fills 1 KB blocks
-  // 2wv, 2wv+1 (rows 4n..4n+3) of each 8 KB tile: lane L writes physical
-  // chunk L%16 of row 4n + L/16 and so fetches the logical chunk that the
-  // row's swizzle places there.
+  const long long qrow = ((long long)b * p.S + (qok ? qi : 0)) * p.Hq + head;
+  bf16x8 qf[8];  // this wave's Q' rows: the B operand of every S MFMA
+
+  // ---- KV tile staging: global -> LDS directly (global_load_lds_dwordx4)
+  // into a ring of NS stages, so that a tile's loads have NS - 1 tiles of
+  // compute to arrive.  Wave wv fills 1 KB blocks 2wv, 2wv+1 (rows 4n..4n+3)
+  // of each 8 KB tile: lane L writes physical chunk L%16 of row 4n + L/16 and
+  // so fetches the logical chunk that the row's swizzle places there.
   const int wvu = __builtin_amdgcn_readfirstlane(wv);  // wave-uniform copy
   const long long kvstride = (long long)p.Hkv * kD;
   const uint16_t* kbase = p.kp + (long long)b * p.S * kvstride + g * kD;
@@ -267,10 +244,9 @@ __global__ __launch_bounds__(kThreads, 3) void flash_fwd_kernel(FlashParams p, G
     row_off[j] = (uint32_t)(lrow[j] * kvstride * 2);
     kchunk[j] = 16u * ((lane & 15) ^ (lrow[j] & 15));
   }
-  // tile t -> stage t&1; keys >= S (only in the top tile) load key S-1 and
-  // are masked out
-  auto gload = [&](int t) {
-    const int stg = t & 1;
+  // tile -> stage stg; keys >= S (only in the top tile) load key S-1 and are
+  // masked out
+  auto gload = [&](int t, int stg) {
     if (t * kBN + kBN <= p.S) {
       const unsigned char* kb = (const unsigned char*)(kbase + (long long)t * kBN * kvstride);
       const unsigned char* vb = (const unsigned char*)(vbase + (long long)t * kBN * kvstride);
@@ -296,9 +272,10 @@ __global__ __launch_bounds__(kThreads, 3) void flash_fwd_kernel(FlashParams p, G
       }
     }
   };
-  // this wave's direct-to-LDS loads have landed (vmcnt(0)); a barrier then
-  // publishes them to the workgroup
-  auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
+  // vmcnt(0) / vmcnt(4): all / all but the latest tile's four of this wave's
+  // direct-to-LDS loads have landed; a barrier then publishes them.
+  auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); };
+  auto wait_loads_but_one_tile = [] { __builtin_amdgcn_s_waitcnt(waitcnt_vm(4)); };
 
   TileState st;
 #pragma unroll
@@ -313,13 +290,11 @@ __global__ __launch_bounds__(kThreads, 3) void flash_fwd_kernel(FlashParams p, G
   const int gi = lane & 15;
   const int vq = gi >> 2;
   const int vlow = 2 * ((lane >> 4) & 1) + ((gi & 3) >> 1);
-  const lds_u8* vread0[4];
-  const lds_u8* vread1[4];
+  const lds_u8* vread0[4];  // stage 0; stage k adds k * kTileBytes
 #pragma unroll
   for (int bd = 0; bd < 4; ++bd) {
     const int off = (4 * half + vq) * kRowBytes + (((bd ^ vq) << 2 | vlow) << 4) + 8 * (gi & 1);
     vread0[bd] = smem + kVOff + off;
-    vread1[bd] = smem + kVOff + kTileBytes + off;
   }
 
   // 32-key tiles aligned to key 0, visited from the diagonal down: tile
@@ -328,32 +303,204 @@ __global__ __launch_bounds__(kThreads, 3) void flash_fwd_kernel(FlashParams p, G
   // workgroup's first query.
   const int t_hi = (hi - 1) / kBN;
   const int nt = t_hi - lo / kBN + 1;
+  // tile j lives in stage j % NS; loads for tile j + NS - 1 are issued while
+  // tile j is computed, into the stage tile j - 1 used
+  int stg = 0;
   auto step = [&](int j, auto mask_tag) {
     const int t = t_hi - j;
-    if (j + 1 < nt) gload(t - 1);
+    const int stg_ahead = stg == 0 ? NS - 1 : stg - 1;  // (j + NS - 1) % NS
+    const bool issue = j + NS - 1 < nt;
+    if (issue) gload(t - (NS - 1), stg_ahead);
     f32x16 s;
-    qk_blk(s, smem + (t & 1) * kTileBytes, kread_off, qf);
+    qk_blk(s, smem + stg * kTileBytes, kread_off, qf);
     if (decltype(mask_tag)::value) mask_blk(s, t * kBN, qm, lim, half);
     const float neg_mc = softmax_rescale(st, blk_max(s), c, rescale_raw);
     bf16x8 pf[2];
     exp_blk(st, s, c, neg_mc, pf);
-    pv_blk(st, (t & 1) ? vread1 : vread0, 0, pf);
-    wait_loads();
+    const lds_u8* vr[4];
+#pragma unroll
+    for (int bd = 0; bd < 4; ++bd) vr[bd] = vread0[bd] + stg * kTileBytes;
+    pv_blk(st, vr, 0, pf);
+    // tile j+1 must have landed; with three stages tile j+2's loads may
+    // still fly
+    if (NS > 2 && issue) wait_loads_but_one_tile();
+    else wait_loads();
     __syncthreads();
+    stg = stg == NS - 1 ? 0 : stg + 1;
   };
 
-  gload(t_hi);
-  wait_loads();
+  // Start-up.  With the rotation in registers (RH >= 0) the first two K'/V
+  // tiles, and on a gated windowed layer the gate rows, are requested before
+  // the query rows so their latencies overlap; the generic rotation needs LDS
+  // first.
+  auto first_loads = [&] {
+    gload(t_hi, 0);
+    if (NS > 2 && nt > 1) gload(t_hi - 1, 1);
+  };
+  // Windowed layers move their query, gate and output rows in whole 256-byte
+  // rows (16 lanes per row): each wave's 32 query rows go straight to LDS,
+  // and lane L prefetches 8 gate values of row 4k + L/16 (k = 0..7) in the
+  // layout of the coalesced output stores.
+  const int wrow0 = i0w + (wv / geo.heads_per_wg) * 32;  // this wave's first query row
+  const bool gate_pre = BANDED && p.gate != nullptr;
+  u32x4 gco[8];
+  if (BANDED) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int row = 4 * n + (lane >> 4);
+      const long long qr = ((long long)b * p.S + min(wrow0 + row, p.S - 1)) * p.Hq + head;
+      __builtin_amdgcn_global_load_lds(p.q + qr * kD + 8 * ((lane & 15) ^ (row & 15)),
+                                       (lds_void*)(smem + kQRegion + wv * 32 * kRowBytes + n * 1024),
+                                       16, 0, 0);
+    }
+  }
+  if (BANDED || RH >= 0) first_loads();
+  if (gate_pre) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const long long gr = ((long long)b * p.S + min(wrow0 + 4 * k + (lane >> 4), p.S - 1)) * p.Hq + head;
+      gco[k] = ld16(p.gate + gr * kD + 8 * (lane & 15));
+    }
+  }
+  // ---- fused query prologue: RMSNorm (+ weight), partial RoPE, -> bf16 B operand
+  {
+    float x[64];
+    if (BANDED) {
+      // this wave's 32 query rows arrived in LDS (row q%32, chunks swizzled
+      // by row); wait for them: the loads issued after them (4 per tile, 8
+      // of gate) may still fly
+      if (nt > 1) {
+        if (gate_pre) __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+      } else {
+        if (gate_pre) __builtin_amdgcn_s_waitcnt(waitcnt_vm(12));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+      }
+      const lds_u8* qr = smem + kQRegion + wv * 32 * kRowBytes + qcol * kRowBytes;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bf16x8 v = lds_read_b128(qr + (((8 * half + j) ^ (qcol & 15)) << 4));
+        unpack_bf16x8(__builtin_bit_cast(u32x4, v), x + 8 * j);
+      }
+    } else {
+      const uint16_t* src = p.q + qrow * kD + 64 * half;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        u32x4 u = qok ? ld16(src + 8 * j) : u32x4{0, 0, 0, 0};
+        unpack_bf16x8(u, x + 8 * j);
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int d = 0; d < 64; ++d) ss += x[d] * x[d];
+    ss = pair_sum32(ss);
+    const float r = 1.0f / sqrtf(ss * (1.0f / kD) + p.eps);
+    const float* wsrc = p.q_norm_w + 64 * half;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      u32x4 wv4 = ld16(wsrc + 4 * j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[4 * j + i] *= r * __uint_as_float(wv4[i]);
+    }
+    if (RH > 0 && half == 0) {
+      // rotary pairs (t, t + RH), all in this lane's registers
+      const long long pos = p.pos_offset + qi;
+      float y[2 * (RH > 0 ? RH : 1)];
+#pragma unroll
+      for (int t = 0; t < RH; ++t) {
+        float cc, sn;
+        rope_cos_sin(p.tab, t, pos, cc, sn);
+        y[t] = x[t] * cc - x[t + RH] * sn;
+        y[t + RH] = x[t + RH] * cc + x[t] * sn;
+      }
+#pragma unroll
+      for (int d = 0; d < 2 * RH; ++d) x[d] = y[d];
+    } else if (RH < 0 && p.rope_half > 0 && half == 0) {
+      // any rope_dim <= 64: the rotary dims live in the lane-half-0 registers;
+      // go through a private LDS row so the partner dim is addressable
+      // (windowed layers: behind the tiles in flight, in the wave's own query rows' region,
+      // which it has already read)
+      float* qs = reinterpret_cast<float*>(smem_raw + (BANDED ? kQRegion + wv * 32 * kRowBytes : 0)) +
+                  (BANDED ? qcol * 64 : (wv * 32 + qcol) * 65);
+#pragma unroll
+      for (int d = 0; d < 64; ++d) qs[d] = x[d];
+      const long long pos = p.pos_offset + qi;
+      const int rh = p.rope_half;
+#pragma unroll
+      for (int t = 0; t < kMaxRopeHalf; ++t) {
+        if (t < rh) {
+          float cc, sn;
+          rope_cos_sin(p.tab, t, pos, cc, sn);
+          const float a = qs[t], bb = qs[t + rh];
+          qs[t] = a * cc - bb * sn;
+          qs[t + rh] = bb * cc + a * sn;
+        }
+      }
+#pragma unroll
+      for (int d = 0; d < 64; ++d) x[d] = qs[d];
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qf[kk] = pack_bf16x8(x + 8 * kk);
+  }
+  if (!BANDED && RH < 0) {
+    __syncthreads();  // the prologue's LDS rows are reused by the KV tiles
+    first_loads();
+  }
+  if (NS > 2 && nt > 1) wait_loads_but_one_tile();
+  else wait_loads();
   __syncthreads();
   int j = 0;
   for (; j < nt && (BANDED || (t_hi - j) * kBN + kBN - 1 > i0w); ++j) step(j, std::true_type{});
-  for (; j < nt; ++j) step(j, std::false_type{});
+  if (!BANDED)
+    for (; j < nt; ++j) step(j, std::false_type{});
 
   // ---- epilogue: normalise, gate, store (register r of block bd, lane half
   // h -> dim 32 bd + 8 (r/4) + 4 h + r%4: four runs of 4 dims per block)
   const float l_tot = pair_sum32(st.l_run);
   const float inv = 1.0f / l_tot;
-  if (qok) {
+  if (p.lse && qok && half == 0)
+    p.lse[((long long)b * p.Hq + head) * p.S + qi] = (st.m_run * c + __log2f(l_tot)) * kLn2;
+  if (BANDED) {
+    // fp32 rows to LDS (the tiles are dead: every wave passed the last
+    // barrier), 16-byte chunk c of row q at chunk c ^ q; then row-coalesced
+    // gate and store, lane L handling dims 8(L%16).. of row 4k + L/16.
+    lds_u8* orow = smem + wv * 32 * 512;
+#pragma unroll
+    for (int bd = 0; bd < 4; ++bd) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = st.acc[bd][4 * q4 + e] * inv;
+        const int ch = 8 * bd + 2 * q4 + half;
+        *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(
+            orow + qcol * 512 + ((ch ^ qcol) << 4)) = o;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int row = 4 * k + (lane >> 4);
+      const int ch0 = 2 * (lane & 15);
+      const f32x4 a = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+          orow + row * 512 + ((ch0 ^ row) << 4));
+      const f32x4 a2 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+          orow + row * 512 + (((ch0 + 1) ^ row) << 4));
+      float o[8] = {a[0], a[1], a[2], a[3], a2[0], a2[1], a2[2], a2[3]};
+      if (gate_pre) {
+        float gv[8];
+        unpack_bf16x8(gco[k], gv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] *= sigmoidf_(gv[e]);
+      }
+      if (wrow0 + row < p.S) {
+        const long long orw = ((long long)b * p.S + wrow0 + row) * p.Hq + head;
+        u32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
+        st16(p.out + orw * kD + 8 * (lane & 15), w);
+      }
+    }
+  } else if (qok) {
     uint16_t* dst = p.out + qrow * kD + 4 * half;
     const uint16_t* gsrc = p.gate ? p.gate + qrow * kD + 4 * half : nullptr;
 #pragma unroll
@@ -377,8 +524,6 @@ __global__ __launch_bounds__(kThreads, 3) void flash_fwd_kernel(FlashParams p, G
         *reinterpret_cast<uint2*>(dst + off) = w;
       }
     }
-    if (p.lse && half == 0)
-      p.lse[((long long)b * p.Hq + head) * p.S + qi] = (st.m_run * c + __log2f(l_tot)) * kLn2;
   }
 }
 
@@ -395,12 +540,18 @@ hipError_t launch_flash_fwd(const FlashParams& p, hipStream_t stream) {
   geo.n_bhg = p.B * p.Hkv * geo.hgroups;
   const long long blocks = (long long)geo.n_pos_blocks * geo.n_bhg;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (p.window > 0)
-    hipLaunchKernelGGL(flash_fwd_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                       p, geo);
-  else
-    hipLaunchKernelGGL(flash_fwd_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                       p, geo);
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  const bool banded = p.window > 0;
+  if (p.rope_half == 21) {
+    if (banded) hipLaunchKernelGGL((flash_fwd_kernel<true, 21>), grid, block, 0, stream, p, geo);
+    else hipLaunchKernelGGL((flash_fwd_kernel<false, 21>), grid, block, 0, stream, p, geo);
+  } else if (p.rope_half == 0) {
+    if (banded) hipLaunchKernelGGL((flash_fwd_kernel<true, 0>), grid, block, 0, stream, p, geo);
+    else hipLaunchKernelGGL((flash_fwd_kernel<false, 0>), grid, block, 0, stream, p, geo);
+  } else {
+    if (banded) hipLaunchKernelGGL((flash_fwd_kernel<true, -1>), grid, block, 0, stream, p, geo);
+    else hipLaunchKernelGGL((flash_fwd_kernel<false, -1>), grid, block, 0, stream, p, geo);
+  }
   return hipGetLastError();
 }
 
