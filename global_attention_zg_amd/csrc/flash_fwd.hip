@@ -7,11 +7,13 @@
 // share 8 KV heads.  Page "7B 打 235B？…全开源配方" (shibing624.github.io),
 // section 🏗️ 架构: the local attention output is multiplied by a sigmoid gate.
 //
-// One 256-thread workgroup = one KV head g and a block of query positions; its
-// four waves are four query heads of g's group (GQA packing: every K/V tile
-// in LDS feeds 4 x 32 query rows).  Each wave owns 32 query rows; lane l owns
-// query row l%32 and the half l/32 of everything else, so the online softmax
-// needs one cross-half exchange per tile and no other cross-lane traffic.
+// A workgroup serves one KV head g and a block of query positions; each wave
+// is one query head of g's group at 32 positions (GQA packing: every K'/V
+// tile in LDS feeds all of the workgroup's waves).  Windowed layers use four
+// waves (the four heads at 32 positions), global layers eight (the four
+// heads at 64 positions).  Lane l owns query row l%32 and the half l/32 of
+// everything else, so the online softmax needs one cross-half exchange per
+// tile and no other cross-lane traffic.
 //
 //   S^T = K' Q'^T  (v_mfma_f32_32x32x16_bf16, A = K' tile rows from LDS,
 //                   B = the wave's normalised + rotated Q' in registers)
@@ -19,18 +21,22 @@
 //                   transposing LDS load ds_read_b64_tr_b16, B = P in registers)
 //
 // K' and V tiles go from global memory straight into LDS (global_load_lds,
-// no register staging), row-major with 256-byte rows whose 16-byte chunks
-// are XOR-swizzled by row: chunk ^ (row & 15) for K', chunk ^ ((row & 3) << 2)
-// for V.  With the 64-bank LDS every MFMA operand read is then free of bank
-// conflicts, and each read address is a per-lane base plus an immediate.
+// no register staging) through a ring of three stages, row-major with
+// 256-byte rows whose 16-byte chunks are XOR-swizzled by row: chunk ^ (row &
+// 15) for K', chunk ^ ((row & 3) << 2) for V.  With the 64-bank LDS every
+// MFMA operand read is then free of bank conflicts, and each read address is
+// a per-lane base plus an immediate.
 //
 // Only KV tiles that intersect the causal band of the workgroup's queries are
-// visited: for a window W that is ceil((32 + W - 1) / 64) tiles, for the
-// global layer every tile up to the diagonal.  The query prologue (RMSNorm +
-// partial RoPE) is fused into the Q load; the sigmoid gate is fused into the
-// epilogue.  Softmax runs in fp32 on raw scores with exp2(fma(s, c, -m c)),
-// c = scale*log2(e), and lazy rescaling of the accumulator (only when the
-// running max grows by more than 2^8 in exp2 units).
+// visited: for a window W that is ceil((32 + W - 1) / 32) + 1 tiles at most,
+// for the global layer every tile up to the diagonal.  The query prologue
+// (RMSNorm + partial RoPE) is fused into the Q load; the sigmoid gate is
+// fused into the epilogue.  Softmax runs in fp32 on raw scores with
+// exp2(fma(s, c, -m c)), c = scale*log2(e), and lazy rescaling of the
+// accumulator (only when the running max grows by more than 2^8 in exp2
+// units).  In the global kernel the two waves that share a SIMD alternate
+// between an MFMA phase and a softmax phase, so that one wave's softmax
+// (VALU) runs under the other's matrix work.
 
 #include <type_traits>
 
@@ -41,36 +47,90 @@ namespace zg {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+// Windowed layers: 4 waves per workgroup (the four query heads of a KV group
+// at 32 positions).  Global layers: 8 waves, the same four heads at 64
+// positions, so that each K'/V tile copied into LDS feeds twice the work; the
+// two waves that share a SIMD (w and w + 4) alternate MFMA and softmax phases.
+template <bool BANDED> struct Cfg {
+  static constexpr int kWaves = BANDED ? 4 : 8;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kBlocksPerWave = 8 / kWaves;  // 1 KB blocks of each tile a wave copies
+  static constexpr int kCopies = 2 * kBlocksPerWave;  // its K' + V copies per tile
+};
 constexpr int kBN = 32;                          // keys per KV tile (one MFMA block)
 constexpr int kRowBytes = kD * 2;                // 256-byte K'/V rows in LDS, 16-byte chunks XOR-swizzled
 constexpr int kTileBytes = kBN * kRowBytes;      // 8192 per K' or V stage
-// LDS ring depth: the windowed kernel keeps loads two tiles ahead (three
-// stages), the global kernel, which runs three workgroups per CU, one tile
-// ahead (two stages).  K' stages come first, then the V stages.
+// LDS ring of three stages per K' and V: copies fly two tiles ahead.  K'
+// stages come first, then the V stages.
 template <bool BANDED> struct Ring {
-  static constexpr int kStages = BANDED ? 3 : 2;
+  static constexpr int kStages = 3;
   static constexpr int kVOff = kStages * kTileBytes;
   static constexpr int kTilesBytes = 2 * kStages * kTileBytes;
 };
-constexpr int kQScratchBytes = kWaves * 32 * 65 * 4;  // query-prologue RoPE rows (reused)
+constexpr int kQScratchBytes = Cfg<false>::kWaves * 32 * 65 * 4;  // query-prologue RoPE rows (reused)
 constexpr int kSmemGlobal =
-    Ring<false>::kTilesBytes > kQScratchBytes ? Ring<false>::kTilesBytes : kQScratchBytes;  // 33280
+    Ring<false>::kTilesBytes > kQScratchBytes ? Ring<false>::kTilesBytes : kQScratchBytes;  // 66560
 // Windowed layers also stage their query rows (8 KB per wave) behind the
 // tiles, and after the loop their fp32 output rows (16 KB per wave) for
 // coalesced stores.
 constexpr int kQRegion = Ring<true>::kTilesBytes;
-constexpr int kSmemBanded = Ring<true>::kTilesBytes + kWaves * 32 * kRowBytes;  // 81920
-static_assert(kWaves * 32 * 128 * 4 <= kSmemBanded, "output staging must fit");
+constexpr int kSmemBanded = Ring<true>::kTilesBytes + Cfg<true>::kWaves * 32 * kRowBytes;  // 81920
+static_assert(Cfg<true>::kWaves * 32 * 128 * 4 <= kSmemBanded, "output staging must fit");
 constexpr float kRescaleThreshold = 8.0f;        // exp2 units
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
-// s_waitcnt immediate for "at most n vector-memory loads outstanding" (lgkm
-// and exp counters left at their maxima): vmcnt is bits [3:0] and [15:14].
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// Global -> LDS copies are issued as inline asm, so that the compiler does not
+// track them: it would otherwise place a vmcnt(0) wait in front of every LDS
+// read that it cannot prove disjoint from an in-flight copy, which serialises
+// the tile ring.  Every wait for copied data is explicit below (in-order
+// completion of vector loads makes "at most N outstanding" exact), and M0 is
+// written only here.
+__device__ __forceinline__ uint32_t lds_addr(const lds_u8* p) { return (uint32_t)(uintptr_t)p; }
+
+// 16 bytes per lane from a per-lane 64-bit address to LDS base + 16 * lane.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds)
+               : "memory");
+}
+
+// Same, from a wave-uniform base plus a per-lane 32-bit byte offset.
+__device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base),
+               "s"(lds)
+               : "memory");
+}
+
+// At most N of this wave's vector loads still in flight.
+template <int N> __device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// At most N vector loads in flight and this wave's LDS accesses done, then
+// the workgroup barrier.
+template <int N> __device__ __forceinline__ void sync_tiles() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Phase boundaries of the global kernel: the barrier (after at most N vector
+// loads in flight, and with LGKM also drained) fenced on both sides against
+// the instruction scheduler, so that no ALU or MFMA work moves across.
+template <int N, bool LGKM> __device__ __forceinline__ void phase_sync() {
+  __builtin_amdgcn_sched_barrier(0);
+  if (LGKM) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+// An empty asm that consumes x: x is computed before this point (keeps the
+// compiler from sinking a phase's results into the next phase).
+template <typename T> __device__ __forceinline__ void pin(const T& x) { asm volatile("" ::"v"(x)); }
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
 
 struct Geo {
   int heads_per_wg;  // query heads per workgroup (= waves sharing positions)
@@ -183,11 +243,46 @@ __device__ __forceinline__ void pv_blk(TileState& st, const lds_u8* (&vread)[4],
   }
 }
 
+// Split forms of qk_blk / pv_blk for the software-pipelined global loop: the
+// LDS operand reads are issued early, into registers, and the MFMAs run
+// back to back once they have landed.
+__device__ __forceinline__ void load_kops(bf16x8 (&ka)[8], const lds_u8* kblk_lds, uint32_t kread_off) {
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) ka[kk] = lds_read_b128(kblk_lds + (kread_off ^ (uint32_t)(kk << 4)));
+}
+
+__device__ __forceinline__ void qk_mfma(f32x16& s, const bf16x8 (&ka)[8], const bf16x8 (&qf)[8]) {
+  s = f32x16{};
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[kk], s, 0, 0, 0);
+}
+
+// va[4 t + bd]: the A operand of k-step t, dim block bd
+__device__ __forceinline__ void load_vops(bf16x8 (&va)[8], const lds_u8* const (&vread)[4]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int bd = 0; bd < 4; ++bd) {
+      const lds_u8* p0 = vread[bd] + 16 * t * kRowBytes;
+      va[4 * t + bd] = lds_read_tr2(p0, p0 + 8 * kRowBytes);
+    }
+  }
+}
+
+__device__ __forceinline__ void pv_mfma(TileState& st, const bf16x8 (&va)[8], const bf16x8 (&pf)[2]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int bd = 0; bd < 4; ++bd)
+      st.acc[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[4 * t + bd], pf[t], st.acc[bd], 0, 0, 0);
+  }
+}
+
 // BANDED: sliding-window layer (window > 0); otherwise global causal.
 // RH: rope_dim / 2 when known at compile time (0 or 21: the rotation runs in
 // registers), -1 for any other rope_dim (rotation through LDS).
 template <bool BANDED, int RH>
-__global__ __launch_bounds__(kThreads, BANDED ? 2 : 3) void flash_fwd_kernel(FlashParams p,
+__global__ __launch_bounds__(Cfg<BANDED>::kThreads, 2) void flash_fwd_kernel(FlashParams p,
                                                                                Geo geo) {
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[BANDED ? kSmemBanded : kSmemGlobal];
   lds_u8* smem = (lds_u8*)smem_raw;  // generic -> LDS address space
@@ -227,55 +322,46 @@ __global__ __launch_bounds__(kThreads, BANDED ? 2 : 3) void flash_fwd_kernel(Fla
 
   // ---- KV tile staging: global -> LDS directly (global_load_lds_dwordx4)
   // into a ring of NS stages, so that a tile's loads have NS - 1 tiles of
-  // compute to arrive.  Wave wv fills 1 KB blocks 2wv, 2wv+1 (rows 4n..4n+3)
-  // of each 8 KB tile: lane L writes physical chunk L%16 of row 4n + L/16 and
-  // so fetches the logical chunk that the row's swizzle places there.
+  // compute to arrive.  Wave wv fills the BPW 1 KB blocks BPW wv + j (rows
+  // 4n..4n+3) of each 8 KB tile: lane L writes physical chunk L%16 of row
+  // 4n + L/16 and so fetches the logical chunk that the row's swizzle places
+  // there.
+  constexpr int BPW = Cfg<BANDED>::kBlocksPerWave;
   const int wvu = __builtin_amdgcn_readfirstlane(wv);  // wave-uniform copy
   const long long kvstride = (long long)p.Hkv * kD;
   const uint16_t* kbase = p.kp + (long long)b * p.S * kvstride + g * kD;
   const uint16_t* vbase = p.v + (long long)b * p.S * kvstride + g * kD;
-  typedef __attribute__((address_space(3))) void lds_void;
   uint32_t row_off[2], kchunk[2];
   int lrow[2];
   const uint32_t vchunk = 16u * ((lane & 15) ^ (((lane >> 4) & 3) << 2));
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    lrow[j] = 4 * (2 * wvu + j) + (lane >> 4);
+  for (int j = 0; j < BPW; ++j) {
+    lrow[j] = 4 * (BPW * wvu + j) + (lane >> 4);
     row_off[j] = (uint32_t)(lrow[j] * kvstride * 2);
     kchunk[j] = 16u * ((lane & 15) ^ (lrow[j] & 15));
   }
   // tile -> stage stg; keys >= S (only in the top tile) load key S-1 and are
   // masked out
   auto gload = [&](int t, int stg) {
+    const unsigned char* kb = (const unsigned char*)(kbase + (long long)t * kBN * kvstride);
+    const unsigned char* vb = (const unsigned char*)(vbase + (long long)t * kBN * kvstride);
+    const uint32_t kl = lds_addr(smem + stg * kTileBytes + BPW * wvu * 1024);
+    const uint32_t vl = kl + kVOff;
     if (t * kBN + kBN <= p.S) {
-      const unsigned char* kb = (const unsigned char*)(kbase + (long long)t * kBN * kvstride);
-      const unsigned char* vb = (const unsigned char*)(vbase + (long long)t * kBN * kvstride);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        __builtin_amdgcn_global_load_lds(kb + row_off[j] + kchunk[j],
-                                         (lds_void*)(smem + stg * kTileBytes + (2 * wvu + j) * 1024),
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vb + row_off[j] + vchunk,
-                                         (lds_void*)(smem + kVOff + stg * kTileBytes + (2 * wvu + j) * 1024),
-                                         16, 0, 0);
+      for (int j = 0; j < BPW; ++j) {
+        dma16_s(kb, row_off[j] + kchunk[j], kl + j * 1024);
+        dma16_s(vb, row_off[j] + vchunk, vl + j * 1024);
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const uint32_t off = (uint32_t)(min(t * kBN + lrow[j], p.S - 1) * kvstride * 2);
-        __builtin_amdgcn_global_load_lds((const unsigned char*)kbase + off + kchunk[j],
-                                         (lds_void*)(smem + stg * kTileBytes + (2 * wvu + j) * 1024),
-                                         16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const unsigned char*)vbase + off + vchunk,
-                                         (lds_void*)(smem + kVOff + stg * kTileBytes + (2 * wvu + j) * 1024),
-                                         16, 0, 0);
+      for (int j = 0; j < BPW; ++j) {
+        const uint32_t off = (uint32_t)((min(t * kBN + lrow[j], p.S - 1) - t * kBN) * kvstride * 2);
+        dma16_s(kb, off + kchunk[j], kl + j * 1024);
+        dma16_s(vb, off + vchunk, vl + j * 1024);
       }
     }
   };
-  // vmcnt(0) / vmcnt(4): all / all but the latest tile's four of this wave's
-  // direct-to-LDS loads have landed; a barrier then publishes them.
-  auto wait_loads = [] { __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); };
-  auto wait_loads_but_one_tile = [] { __builtin_amdgcn_s_waitcnt(waitcnt_vm(4)); };
 
   TileState st;
 #pragma unroll
@@ -321,11 +407,10 @@ __global__ __launch_bounds__(kThreads, BANDED ? 2 : 3) void flash_fwd_kernel(Fla
 #pragma unroll
     for (int bd = 0; bd < 4; ++bd) vr[bd] = vread0[bd] + stg * kTileBytes;
     pv_blk(st, vr, 0, pf);
-    // tile j+1 must have landed; with three stages tile j+2's loads may
-    // still fly
-    if (NS > 2 && issue) wait_loads_but_one_tile();
-    else wait_loads();
-    __syncthreads();
+    // tile j+1 must have landed; with three stages tile j+2's four copies
+    // may still fly
+    if (NS > 2 && issue) sync_tiles<4>();
+    else sync_tiles<0>();
     stg = stg == NS - 1 ? 0 : stg + 1;
   };
 
@@ -335,7 +420,7 @@ __global__ __launch_bounds__(kThreads, BANDED ? 2 : 3) void flash_fwd_kernel(Fla
   // first.
   auto first_loads = [&] {
     gload(t_hi, 0);
-    if (NS > 2 && nt > 1) gload(t_hi - 1, 1);
+    if (nt > 1) gload(t_hi - 1, 1);
   };
   // Windowed layers move their query, gate and output rows in whole 256-byte
   // rows (16 lanes per row): each wave's 32 query rows go straight to LDS,
@@ -349,9 +434,8 @@ __global__ __launch_bounds__(kThreads, BANDED ? 2 : 3) void flash_fwd_kernel(Fla
     for (int n = 0; n < 8; ++n) {
       const int row = 4 * n + (lane >> 4);
       const long long qr = ((long long)b * p.S + min(wrow0 + row, p.S - 1)) * p.Hq + head;
-      __builtin_amdgcn_global_load_lds(p.q + qr * kD + 8 * ((lane & 15) ^ (row & 15)),
-                                       (lds_void*)(smem + kQRegion + wv * 32 * kRowBytes + n * 1024),
-                                       16, 0, 0);
+      dma16(p.q + qr * kD + 8 * ((lane & 15) ^ (row & 15)),
+            lds_addr(smem + kQRegion + wvu * 32 * kRowBytes + n * 1024));
     }
   }
   if (BANDED || RH >= 0) first_loads();
@@ -370,11 +454,11 @@ __global__ __launch_bounds__(kThreads, BANDED ? 2 : 3) void flash_fwd_kernel(Fla
       // by row); wait for them: the loads issued after them (4 per tile, 8
       // of gate) may still fly
       if (nt > 1) {
-        if (gate_pre) __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));
+        if (gate_pre) wait_vm<16>();
+        else wait_vm<8>();
       } else {
-        if (gate_pre) __builtin_amdgcn_s_waitcnt(waitcnt_vm(12));
-        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));
+        if (gate_pre) wait_vm<12>();
+        else wait_vm<4>();
       }
       const lds_u8* qr = smem + kQRegion + wv * 32 * kRowBytes + qcol * kRowBytes;
 #pragma unroll
@@ -446,13 +530,79 @@ __global__ __launch_bounds__(kThreads, BANDED ? 2 : 3) void flash_fwd_kernel(Fla
     __syncthreads();  // the prologue's LDS rows are reused by the KV tiles
     first_loads();
   }
-  if (NS > 2 && nt > 1) wait_loads_but_one_tile();
-  else wait_loads();
-  __syncthreads();
-  int j = 0;
-  for (; j < nt && (BANDED || (t_hi - j) * kBN + kBN - 1 > i0w); ++j) step(j, std::true_type{});
-  if (!BANDED)
-    for (; j < nt; ++j) step(j, std::false_type{});
+  // tile 0 must have landed (loads issued after it: tile 1's copies, and on
+  // gated windowed layers the eight gate rows)
+  constexpr int kCopies = Cfg<BANDED>::kCopies;
+  if (BANDED && gate_pre) {
+    if (nt > 1) sync_tiles<kCopies + 8>();
+    else sync_tiles<8>();
+  } else {
+    if (nt > 1) sync_tiles<kCopies>();
+    else sync_tiles<0>();
+  }
+  if constexpr (BANDED) {
+    for (int j = 0; j < nt; ++j) step(j, std::true_type{});
+  } else {
+    // Global layers: the two waves on each SIMD (w and w + 4) take turns.
+    // Every wave runs the same sequence of phases separated by barriers:
+    // MFMA phase k (PV of tile k-1 while the K' operand reads of tile k fly,
+    // then QK' of tile k and the V operand reads of tile k) and softmax
+    // phase k (scores of tile k -> P).  Wave w + 4 passes one extra barrier
+    // first and wave w one extra at the end, so that one runs its MFMA
+    // phase while the other runs its softmax phase.
+    //
+    // Tile k+2 is copied into the stage of tile k-1 at the top of softmax
+    // phase k: every wave has finished reading tile k-1 by then (its reads
+    // end with the lgkmcnt(0) before the barrier closing softmax phase k-1).
+    // Barriers after an MFMA phase wait for every copy in flight (tile k+1),
+    // those after a softmax phase for all but the copies just issued, so
+    // tile k+1 has landed for every wave before the barrier that opens
+    // either wave's MFMA phase k+1.
+    const bool second = wvu >= 4;
+    bf16x8 ka[8], va[8], pf[2];
+    f32x16 s;
+    auto qk_part = [&](int stg) {
+      qk_mfma(s, ka, qf);
+      const lds_u8* vr[4];
+#pragma unroll
+      for (int bd = 0; bd < 4; ++bd) vr[bd] = vread0[bd] + stg * kTileBytes;
+      load_vops(va, vr);
+    };
+    auto v_phase = [&](int k) {
+      const int t = t_hi - k;
+      if (t * kBN + kBN - 1 > wrow0) mask_blk(s, t * kBN, qm, lim, half);
+      const float neg_mc = softmax_rescale(st, blk_max(s), c, rescale_raw);
+      exp_blk(st, s, c, neg_mc, pf);
+      pin(pf[0]);
+      pin(pf[1]);
+      pin(st.l_run);
+    };
+    if (second) phase_barrier();
+    load_kops(ka, smem, kread_off);
+    qk_part(0);
+    phase_sync<0, false>();
+    int sk = 0;  // stage of tile k
+    for (int k = 0; k < nt; ++k) {
+      const int s1 = sk == 2 ? 0 : sk + 1;  // tile k+1
+      const int s2 = s1 == 2 ? 0 : s1 + 1;  // tile k+2 (held tile k-1)
+      if (k + 2 < nt) gload(t_hi - (k + 2), s2);
+      v_phase(k);
+      if (k + 2 < nt) phase_sync<kCopies, true>();
+      else phase_sync<0, true>();
+      if (k + 1 < nt) {
+        load_kops(ka, smem + s1 * kTileBytes, kread_off);
+        pv_mfma(st, va, pf);
+        // keep the next V operand reads below the MFMAs that consume the
+        // current ones (otherwise both sets are live at once)
+        __builtin_amdgcn_sched_barrier(0);
+        qk_part(s1);
+        phase_sync<0, false>();
+      }
+      sk = s1;
+    }
+    pv_mfma(st, va, pf);
+    if (!second) phase_barrier();
+  }
 
   // ---- epilogue: normalise, gate, store (register r of block bd, lane half
   // h -> dim 32 bd + 8 (r/4) + 4 h + r%4: four runs of 4 dims per block)
@@ -532,16 +682,17 @@ __global__ __launch_bounds__(kThreads, BANDED ? 2 : 3) void flash_fwd_kernel(Fla
 hipError_t launch_flash_fwd(const FlashParams& p, hipStream_t stream) {
   if (p.B == 0 || p.S == 0) return hipSuccess;
   const int grp = p.Hq / p.Hkv;
+  const bool banded = p.window > 0;
+  const int waves = banded ? Cfg<true>::kWaves : Cfg<false>::kWaves;
   Geo geo;
-  geo.heads_per_wg = grp < kWaves ? grp : kWaves;
+  geo.heads_per_wg = grp < waves ? grp : waves;
   geo.hgroups = grp / geo.heads_per_wg;
-  geo.pos_per_wg = 32 * kWaves / geo.heads_per_wg;
+  geo.pos_per_wg = 32 * waves / geo.heads_per_wg;
   geo.n_pos_blocks = (p.S + geo.pos_per_wg - 1) / geo.pos_per_wg;
   geo.n_bhg = p.B * p.Hkv * geo.hgroups;
   const long long blocks = (long long)geo.n_pos_blocks * geo.n_bhg;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks), block(kThreads);
-  const bool banded = p.window > 0;
+  const dim3 grid((unsigned)blocks), block(64 * waves);
   if (p.rope_half == 21) {
     if (banded) hipLaunchKernelGGL((flash_fwd_kernel<true, 21>), grid, block, 0, stream, p, geo);
     else hipLaunchKernelGGL((flash_fwd_kernel<false, 21>), grid, block, 0, stream, p, geo);
