@@ -41,6 +41,9 @@ __all__ = [
     "attention_fwd",
     "decode_group",
     "attention_decode",
+    "rope_bwd",
+    "rms_norm_bwd",
+    "attention_bwd",
     "kv_cache_bytes_per_token",
     "kv_cache_bytes",
     "layer_schedule",
@@ -279,6 +282,125 @@ def attention_decode(q, k_new, v_new, k_cache, v_cache, seq_lens, *, ring: bool,
                 slot = (L - 1) % cap if ring else L - 1
                 k_after[b, g, slot] = ka
     return out, lse, k_after
+
+
+# ---------------------------------------------------------------------------
+# Training backward: the derivative of steps 1-7.
+#
+# The pages measure the model in training ([RB] 前置知识 and the throughput
+# ablation of the architecture section; [SB] 🏗️ 架构), but define only the
+# forward computation.  The functions below are that forward's derivative by
+# the chain rule, written out step by step; nothing in them is taken from
+# the pages beyond the forward definitions above.
+# ---------------------------------------------------------------------------
+def rope_bwd(dy: np.ndarray, positions: np.ndarray, rope_dim: int,
+             theta: float) -> np.ndarray:
+    """Gradient through apply_partial_rope: each rotary pair (j, j+R/2) was
+    rotated by phi_j, so its gradient is rotated back by -phi_j (the
+    rotation is orthogonal); the other dims pass through."""
+    dy = np.asarray(dy, dtype=np.float64)
+    dx = dy.copy()
+    if rope_dim == 0:
+        return dx
+    half = rope_dim // 2
+    phi = rope_angles(positions, rope_dim, theta)
+    c = np.cos(phi)[:, None, :]
+    s = np.sin(phi)[:, None, :]
+    d1 = dy[..., :half]
+    d2 = dy[..., half:rope_dim]
+    dx[..., :half] = d1 * c + d2 * s
+    dx[..., half:rope_dim] = d2 * c - d1 * s
+    return dx
+
+
+def rms_norm_bwd(x: np.ndarray, gamma: np.ndarray, eps: float, dxhat: np.ndarray):
+    """Gradient through rms_norm over the last axis.
+
+    With r = (mean(x^2) + eps)^(-1/2) and x_hat = x r gamma:
+        dx     = r (gamma * dx_hat) - x r^3 mean(gamma * dx_hat * x)
+        dgamma = sum over rows of dx_hat * x * r
+    Returns (dx, dgamma).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    gamma = np.asarray(gamma, dtype=np.float64)
+    dxhat = np.asarray(dxhat, dtype=np.float64)
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    gd = dxhat * gamma
+    dx = r * gd - x * r ** 3 * np.mean(gd * x, axis=-1, keepdims=True)
+    dgamma = np.sum((dxhat * x * r).reshape(-1, x.shape[-1]), axis=0)
+    return dx, dgamma
+
+
+def attention_bwd(q, k, v, gate, q_norm_w, k_norm_w, dout, *, window: int,
+                  rope_dim: int, rope_theta: float, rms_eps: float,
+                  softmax_scale: float = 0.0, pos_offset: int = 0, chunk: int = 1024):
+    """Gradients of L = sum(dout * Y) for the layer Y = attention_fwd(...)[0].
+
+    Returns a dict with dq, dk, dv (shapes of q, k, v), dgate (shape of gate,
+    or None), dq_norm_w and dk_norm_w ([D]).  Per query head h (kv head g):
+        sig = sigmoid(G);  dO = dY * sig;  dG = dY * O * sig * (1 - sig)
+        P = softmax(tau q' k'^T over the visible keys)
+        dV_g += P^T dO;  dP = dO V^T;  Dr = rowsum(dO * O)
+        dS = P * (dP - Dr);  dq' = tau dS K';  dk'_g += tau dS^T Q'
+    then back through RoPE (rope_bwd) and RMSNorm (rms_norm_bwd).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    assert Hq % Hkv == 0
+    grp = Hq // Hkv
+    tau = softmax_scale if softmax_scale > 0 else 1.0 / math.sqrt(D)
+    pos = pos_offset + np.arange(S, dtype=np.int64)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dgate = None if gate is None else np.zeros(np.shape(gate), dtype=np.float64)
+    dwq = np.zeros(D)
+    dwk = np.zeros(D)
+    for b in range(B):
+        qp = apply_partial_rope(rms_norm(q[b], q_norm_w, rms_eps), pos, rope_dim, rope_theta)
+        kp = apply_partial_rope(rms_norm(k[b], k_norm_w, rms_eps), pos, rope_dim, rope_theta)
+        dqp = np.zeros_like(qp)
+        dkp = np.zeros_like(kp)
+        for c0 in range(0, S, chunk):
+            ridx = np.arange(c0, min(S, c0 + chunk))
+            lo = 0 if window == 0 else max(0, c0 - window + 1)
+            hi = int(ridx[-1]) + 1
+            jj = np.arange(lo, hi)
+            mask = visible(ridx[:, None], jj[None, :], window)
+            for g in range(Hkv):
+                kg = kp[lo:hi, g, :]
+                vg = v[b, lo:hi, g, :]
+                for hh in range(grp):
+                    h = g * grp + hh
+                    s = np.where(mask, tau * (qp[ridx, h, :] @ kg.T), -np.inf)
+                    e = np.exp(s - np.max(s, axis=1, keepdims=True))
+                    P = e / np.sum(e, axis=1, keepdims=True)
+                    o = P @ vg
+                    dy = dout[b, ridx, h, :]
+                    if gate is not None:
+                        sg = _sigmoid(np.asarray(gate[b, ridx, h, :], dtype=np.float64))
+                        do = dy * sg
+                        dgate[b, ridx, h, :] = dy * o * sg * (1.0 - sg)
+                    else:
+                        do = dy
+                    dv[b, lo:hi, g, :] += P.T @ do
+                    dP = do @ vg.T
+                    dr = np.sum(do * o, axis=1, keepdims=True)
+                    dS = P * (dP - dr)
+                    dqp[ridx, h, :] += tau * (dS @ kg)
+                    dkp[lo:hi, g, :] += tau * (dS.T @ qp[ridx, h, :])
+        dqh = rope_bwd(dqp, pos, rope_dim, rope_theta)
+        dkh = rope_bwd(dkp, pos, rope_dim, rope_theta)
+        dq[b], gq = rms_norm_bwd(q[b], q_norm_w, rms_eps, dqh)
+        dk[b], gk = rms_norm_bwd(k[b], k_norm_w, rms_eps, dkh)
+        dwq += gq
+        dwk += gk
+    return {"dq": dq, "dk": dk, "dv": dv, "dgate": dgate,
+            "dq_norm_w": dwq, "dk_norm_w": dwk}
 
 
 # ---------------------------------------------------------------------------
