@@ -61,6 +61,11 @@ def _load():
     lib.zg_attn_decode_workspace_size.restype = sz
     lib.zg_attn_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, i, i, vp, vp, vp, vp, i, vp, sz, vp]
     lib.zg_attn_decode.restype = i
+    lib.zg_attn_bwd_workspace_size.argtypes = [P]
+    lib.zg_attn_bwd_workspace_size.restype = sz
+    lib.zg_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                sz, vp]
+    lib.zg_attn_bwd.restype = i
     lib.zg_attn_strerror.argtypes = [i]
     lib.zg_attn_strerror.restype = ctypes.c_char_p
     return lib
@@ -69,7 +74,8 @@ def _load():
 _lib = _load()
 
 EXPORTED = ("zg_attn_fwd_workspace_size", "zg_attn_fwd", "zg_attn_decode_num_splits",
-            "zg_attn_decode_workspace_size", "zg_attn_decode", "zg_attn_strerror")
+            "zg_attn_decode_workspace_size", "zg_attn_decode", "zg_attn_bwd_workspace_size",
+            "zg_attn_bwd", "zg_attn_strerror")
 
 
 def library_path() -> str:
@@ -128,6 +134,43 @@ def zg_attn_fwd(q, k, v, gate, q_norm_w, k_norm_w, *, window, rope_dim=42, rope_
                           _ptr(workspace) if k_out is None else None, ws_bytes, _stream(stream))
     _check(st)
     return out, lse
+
+
+def zg_attn_bwd_workspace_size(p: Params) -> int:
+    return int(_lib.zg_attn_bwd_workspace_size(ctypes.byref(p)))
+
+
+def zg_attn_bwd(q, k, v, gate, q_norm_w, k_norm_w, out, lse, dout, *, window, rope_dim=42,
+                rope_theta=10000.0, rms_eps=1e-6, softmax_scale=0.0, pos_offset=0, dq=None,
+                dk=None, dv=None, dgate=None, dq_norm_w=None, dk_norm_w=None, workspace=None,
+                stream=None):
+    """Gradients of sum(dout * out) for out, lse = zg_attn_fwd(...) with the same
+    inputs.  Returns a dict: dq, dk, dv, dgate (None when gate is None),
+    dq_norm_w, dk_norm_w."""
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    p = make_params(B, S, Hq, Hkv, D, window, rope_dim, rope_theta, rms_eps, softmax_scale,
+                    pos_offset)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if gate is not None and dgate is None:
+        dgate = torch.empty_like(gate)
+    if dq_norm_w is None:
+        dq_norm_w = torch.empty(D, dtype=torch.float32, device=q.device)
+    if dk_norm_w is None:
+        dk_norm_w = torch.empty(D, dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = zg_attn_bwd_workspace_size(p)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.zg_attn_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(q_norm_w),
+                          _ptr(k_norm_w), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                          _ptr(dv), _ptr(dgate), _ptr(dq_norm_w), _ptr(dk_norm_w),
+                          _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st)
+    return {"dq": dq, "dk": dk, "dv": dv, "dgate": dgate if gate is not None else None,
+            "dq_norm_w": dq_norm_w, "dk_norm_w": dk_norm_w}
 
 
 def zg_attn_decode_num_splits(p: Params, cache_cap: int) -> int:

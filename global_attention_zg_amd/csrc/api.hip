@@ -64,6 +64,31 @@ int auto_splits(const zg_attn_params* p, int cache_cap) {
   return (int)s;
 }
 
+// Backward workspace: 256-byte aligned segments, in this order.
+struct BwdLayout {
+  size_t qp, kp, dO, lse2, dvec, dqp, dkp, part, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+BwdLayout bwd_layout(const zg_attn_params* p) {
+  const size_t B = (size_t)p->batch, S = (size_t)p->seqlen, Hq = (size_t)p->n_q_heads,
+               Hkv = (size_t)p->n_kv_heads;
+  const size_t Spad = (S + zg::kBwdRowPad - 1) / zg::kBwdRowPad * zg::kBwdRowPad;
+  BwdLayout l;
+  size_t off = 0;
+  l.qp = off;   off += align256(B * S * Hq * kD * 2);
+  l.kp = off;   off += align256(B * S * Hkv * kD * 2);
+  l.dO = off;   off += align256(B * S * Hq * kD * 2);
+  l.lse2 = off; off += align256(B * Hq * Spad * 4);
+  l.dvec = off; off += align256(B * Hq * Spad * 4);
+  l.dqp = off;  off += align256(B * S * Hq * kD * 4);
+  l.dkp = off;  off += align256(B * S * Hkv * kD * 4);
+  l.part = off; off += align256((size_t)2 * zg::kBwdParts * kD * 4);
+  l.total = off;
+  return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,6 +154,94 @@ int zg_attn_fwd(const zg_attn_params* p, const void* q, const void* k, const voi
   fp.pos_offset = p->pos_offset;
   fp.tab = tab;
   return hip_status(zg::launch_flash_fwd(fp, s));
+}
+
+size_t zg_attn_bwd_workspace_size(const zg_attn_params* p) {
+  if (check_params(p) != ZG_OK) return 0;
+  return bwd_layout(p).total;
+}
+
+int zg_attn_bwd(const zg_attn_params* p, const void* q, const void* k, const void* v,
+                const void* gate, const float* q_norm_w, const float* k_norm_w, const void* out,
+                const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dgate,
+                float* dq_norm_w, float* dk_norm_w, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  int st = check_params(p);
+  if (st != ZG_OK) return st;
+  if ((long long)p->seqlen * p->n_q_heads > 0x7fffffffLL) return ZG_ERR_UNSUPPORTED;
+  if (p->batch == 0 || p->seqlen == 0) return ZG_OK;
+  if (!q || !k || !v || !q_norm_w || !k_norm_w || !out || !lse || !dout || !dq || !dk || !dv ||
+      !dq_norm_w || !dk_norm_w)
+    return ZG_ERR_INVALID;
+  if ((gate == nullptr) != (dgate == nullptr)) return ZG_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_norm_w) ||
+      !aligned16(k_norm_w) || !aligned16(out) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || (gate && (!aligned16(gate) || !aligned16(dgate))) ||
+      (reinterpret_cast<uintptr_t>(lse) & 3u) || (reinterpret_cast<uintptr_t>(dq_norm_w) & 3u) ||
+      (reinterpret_cast<uintptr_t>(dk_norm_w) & 3u))
+    return ZG_ERR_INVALID;
+  const BwdLayout L = bwd_layout(p);
+  if (!workspace || workspace_bytes < L.total) return ZG_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ZG_ERR_INVALID;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  uint16_t* qp = reinterpret_cast<uint16_t*>(ws + L.qp);
+  uint16_t* kp = reinterpret_cast<uint16_t*>(ws + L.kp);
+  uint16_t* dO = gate ? reinterpret_cast<uint16_t*>(ws + L.dO)
+                      : const_cast<uint16_t*>(static_cast<const uint16_t*>(dout));
+  float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
+  float* dvec = reinterpret_cast<float*>(ws + L.dvec);
+  float* dqp = reinterpret_cast<float*>(ws + L.dqp);
+  float* dkp = reinterpret_cast<float*>(ws + L.dkp);
+  float* part_q = reinterpret_cast<float*>(ws + L.part);
+  float* part_k = part_q + (size_t)zg::kBwdParts * kD;
+  const int B = p->batch, S = p->seqlen, Hq = p->n_q_heads, Hkv = p->n_kv_heads;
+  const int Spad = (S + zg::kBwdRowPad - 1) / zg::kBwdRowPad * zg::kBwdRowPad;
+  const zg::RopeTable tab = make_rope_table(p);
+  const int rh = p->rope_dim / 2;
+
+  hipError_t e = zg::launch_bwd_prep(static_cast<const uint16_t*>(dout),
+                                     static_cast<const uint16_t*>(out),
+                                     static_cast<const uint16_t*>(gate), lse, dO,
+                                     static_cast<uint16_t*>(dgate), lse2, dvec, B, S, Spad, Hq, s);
+  if (e != hipSuccess) return ZG_ERR_HIP;
+  e = zg::launch_k_prologue(static_cast<const uint16_t*>(q), q_norm_w, qp, (long long)B * S * Hq, S,
+                            Hq, p->pos_offset, rh, p->rms_eps, tab, s);
+  if (e != hipSuccess) return ZG_ERR_HIP;
+  e = zg::launch_k_prologue(static_cast<const uint16_t*>(k), k_norm_w, kp, (long long)B * S * Hkv,
+                            S, Hkv, p->pos_offset, rh, p->rms_eps, tab, s);
+  if (e != hipSuccess) return ZG_ERR_HIP;
+  zg::BwdParams bp{};
+  bp.qp = qp;
+  bp.kp = kp;
+  bp.v = static_cast<const uint16_t*>(v);
+  bp.dO = dO;
+  bp.lse2 = lse2;
+  bp.dvec = dvec;
+  bp.dqp = dqp;
+  bp.dkp = dkp;
+  bp.dv = static_cast<uint16_t*>(dv);
+  bp.B = B;
+  bp.S = S;
+  bp.Spad = Spad;
+  bp.Hq = Hq;
+  bp.Hkv = Hkv;
+  bp.window = p->window;
+  bp.scale_log2 = scale_log2(p);
+  bp.scale = (float)(p->softmax_scale > 0.f ? (double)p->softmax_scale : 1.0 / sqrt((double)kD));
+  if (zg::launch_bwd_dq(bp, s) != hipSuccess) return ZG_ERR_HIP;
+  if (zg::launch_bwd_dkv(bp, s) != hipSuccess) return ZG_ERR_HIP;
+  e = zg::launch_prologue_bwd(static_cast<const uint16_t*>(q), dqp, q_norm_w,
+                              static_cast<uint16_t*>(dq), part_q, (long long)B * S * Hq, S, Hq,
+                              p->pos_offset, rh, p->rms_eps, tab, s);
+  if (e != hipSuccess) return ZG_ERR_HIP;
+  e = zg::launch_prologue_bwd(static_cast<const uint16_t*>(k), dkp, k_norm_w,
+                              static_cast<uint16_t*>(dk), part_k, (long long)B * S * Hkv, S, Hkv,
+                              p->pos_offset, rh, p->rms_eps, tab, s);
+  if (e != hipSuccess) return ZG_ERR_HIP;
+  if (zg::launch_reduce_parts(part_q, dq_norm_w, s) != hipSuccess) return ZG_ERR_HIP;
+  return hip_status(zg::launch_reduce_parts(part_k, dk_norm_w, s));
 }
 
 int zg_attn_decode_num_splits(const zg_attn_params* p, int cache_cap) {

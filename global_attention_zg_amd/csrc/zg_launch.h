@@ -54,4 +54,39 @@ struct DecodeParams {
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
+
+// Training backward.  Q' / K' are the normalised + rotated rows recomputed by
+// launch_k_prologue; dO = dY * sigmoid(G) (dY itself on an ungated layer).
+struct BwdParams {
+  const uint16_t* qp;   // bf16 [B,S,Hq,D]   Q'
+  const uint16_t* kp;   // bf16 [B,S,Hkv,D]  K'
+  const uint16_t* v;    // bf16 [B,S,Hkv,D]
+  const uint16_t* dO;   // bf16 [B,S,Hq,D]
+  const float* lse2;    // fp32 [B,Hq,Spad]  LSE * log2(e); +inf for rows >= S
+  const float* dvec;    // fp32 [B,Hq,Spad]  rowsum(dY * Y); 0 for rows >= S
+  float* dqp;           // fp32 [B,S,Hq,D]   dL/dQ'
+  float* dkp;           // fp32 [B,S,Hkv,D]  dL/dK'
+  uint16_t* dv;         // bf16 [B,S,Hkv,D]
+  int B, S, Spad, Hq, Hkv, window;
+  float scale_log2;     // softmax scale * log2(e)
+  float scale;          // softmax scale
+};
+
+// Row padding of the LSE / D vectors (a multiple of every query block).
+constexpr int kBwdRowPad = 128;
+// Number of per-block partial sums of each RMSNorm weight gradient.
+constexpr int kBwdParts = 512;
+
+hipError_t launch_bwd_prep(const uint16_t* dy, const uint16_t* y, const uint16_t* gate,
+                           const float* lse, uint16_t* dO, uint16_t* dgate, float* lse2,
+                           float* dvec, int B, int S, int Spad, int Hq, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream);
+hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t stream);
+// dx = d(prologue)/dx^T dy' for rows of `heads` heads; partial weight
+// gradients go to part[kBwdParts][D], then dw = sum of the parts.
+hipError_t launch_prologue_bwd(const uint16_t* x, const float* dyp, const float* w, uint16_t* dx,
+                               float* part, long long rows, int S, int heads, long long pos_offset,
+                               int rope_half, float eps, const RopeTable& tab, hipStream_t stream);
+hipError_t launch_reduce_parts(const float* part, float* dw, hipStream_t stream);
+
 }  // namespace zg

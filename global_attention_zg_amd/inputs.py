@@ -19,6 +19,7 @@ CHUNK = 1 << 22
 
 # tensor ids
 T_Q, T_K, T_V, T_GATE, T_GQ, T_GK, T_KCACHE, T_VCACHE, T_KNEW, T_VNEW = range(10)
+T_DOUT = 10  # upstream gradient dL/dout of the training backward
 
 
 def _threads() -> int:

@@ -119,6 +119,35 @@ int zg_attn_decode(const zg_attn_params* p,
                    void* out, int num_splits,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace zg_attn_bwd needs (recomputed Q' and K', dO,
+ * per-row LSE*log2(e) and rowsum(dY*Y), fp32 dL/dQ' and dL/dK', and the
+ * partial sums of the two weight gradients); 0 for an invalid p. */
+size_t zg_attn_bwd_workspace_size(const zg_attn_params* p);
+
+/* Training backward of one attention layer: the gradients of
+ * L = sum(dout * out) for out = zg_attn_fwd(...) with the same p and inputs.
+ * The pages define only the forward; this is its derivative by the chain
+ * rule (gate, softmax attention, RoPE rotation transposed, RMSNorm).
+ *   q, k, v, gate, q_norm_w, k_norm_w   the forward's inputs (gate may be NULL)
+ *   out   bf16 [B,S,Hq,D]  the forward's output (gated)
+ *   lse   fp32 [B,Hq,S]    the forward's LSE (required)
+ *   dout  bf16 [B,S,Hq,D]  dL/dout
+ *   dq    bf16 [B,S,Hq,D], dk, dv bf16 [B,S,Hkv,D]   gradients of q, k, v
+ *   dgate bf16 [B,S,Hq,D]  gradient of the gate logits; required iff gate
+ *   dq_norm_w, dk_norm_w  fp32 [D] weight gradients (overwritten, not
+ *         accumulated)
+ * dq, dk, dv, dgate and the weight gradients are written in full; the
+ * summation order is fixed, so repeated calls give identical bits.
+ * S == 0 or B == 0 is valid and launches nothing (the weight-gradient
+ * buffers are then left as they are; the gradient is zero). */
+int zg_attn_bwd(const zg_attn_params* p,
+                const void* q, const void* k, const void* v, const void* gate,
+                const float* q_norm_w, const float* k_norm_w,
+                const void* out, const float* lse, const void* dout,
+                void* dq, void* dk, void* dv, void* dgate,
+                float* dq_norm_w, float* dk_norm_w,
+                void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* zg_attn_strerror(int status);
 

@@ -145,3 +145,48 @@ def test_decode_rejects_bad_arguments(bd):
     assert _dec(bd, p0, 128, 1) == bd.ZG_OK
     pbad = bd.make_params(2, 0, 32, 8, 96, 128)
     assert _dec(bd, pbad, 128, 1, **ok) == bd.ZG_ERR_UNSUPPORTED
+
+
+def _bwd(bd, p, **ptrs):
+    names = ["q", "k", "v", "gate", "qw", "kw", "out", "lse", "dout", "dq", "dk", "dv", "dgate",
+             "dqw", "dkw", "ws"]
+    args = [ptrs.get(n) for n in names]
+    return bd._lib.zg_attn_bwd(ctypes.byref(p), *args, ptrs.get("ws_bytes", 0), None)
+
+
+def test_bwd_workspace_size_formula(bd):
+    B, S, Hq, Hkv, D = 2, 300, 32, 8, 128
+    p = bd.make_params(B, S, Hq, Hkv, D, 128)
+    a = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    spad = (S + 127) // 128 * 128
+    want = (a(B * S * Hq * D * 2) + a(B * S * Hkv * D * 2) + a(B * S * Hq * D * 2)
+            + 2 * a(B * Hq * spad * 4) + a(B * S * Hq * D * 4) + a(B * S * Hkv * D * 4)
+            + a(2 * 512 * D * 4))
+    assert bd.zg_attn_bwd_workspace_size(p) == want
+    p.head_dim = 64
+    assert bd.zg_attn_bwd_workspace_size(p) == 0
+
+
+def test_bwd_rejects_bad_arguments(bd):
+    p = bd.make_params(1, 64, 32, 8, 128, 128)
+    full = dict(q=FAKE, k=FAKE, v=FAKE, qw=FAKE, kw=FAKE, out=FAKE, lse=FAKE, dout=FAKE, dq=FAKE,
+                dk=FAKE, dv=FAKE, dqw=FAKE, dkw=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    for missing in ("q", "out", "lse", "dout", "dq", "dk", "dv", "dqw", "dkw"):
+        args = dict(full)
+        args[missing] = None
+        assert _bwd(bd, p, **args) == bd.ZG_ERR_INVALID, missing
+    # gate and dgate come together
+    assert _bwd(bd, p, **dict(full, gate=FAKE)) == bd.ZG_ERR_INVALID
+    assert _bwd(bd, p, **dict(full, dgate=FAKE)) == bd.ZG_ERR_INVALID
+    # misaligned tensor
+    assert _bwd(bd, p, **dict(full, dq=FAKE + 8)) == bd.ZG_ERR_INVALID
+    # workspace missing or short
+    assert _bwd(bd, p, **dict(full, ws=None)) == bd.ZG_ERR_WORKSPACE
+    need = bd.zg_attn_bwd_workspace_size(p)
+    assert _bwd(bd, p, **dict(full, ws_bytes=need - 1)) == bd.ZG_ERR_WORKSPACE
+    # bad params are checked first
+    p.rope_dim = 43
+    assert _bwd(bd, p, **full) == bd.ZG_ERR_INVALID
+    # empty problem: valid, nothing launched
+    q = bd.make_params(0, 64, 32, 8, 128, 0)
+    assert _bwd(bd, q) == bd.ZG_OK

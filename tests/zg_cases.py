@@ -57,3 +57,29 @@ def compare(got, ref, what=""):
     assert max_abs <= MAX_ABS and rms <= REL_RMS, \
         f"{what}: max_abs {max_abs:.3e} (<= {MAX_ABS}), rel_rms {rms:.3e} (<= {REL_RMS})"
     return max_abs, rms
+
+
+# Gradient bar of the training backward (relative, per tensor): the backward
+# multiplies bf16-rounded Q', K', dO, P and dS (unit roundoff 2^-9 each) and
+# accumulates in fp32, so a gradient carries a few roundoffs of relative
+# error that partly cancel over the sums; measured 0.3-0.5% RMS.
+GRAD_REL_RMS = 1e-2
+GRAD_MAX_REL = 2e-2
+
+
+def compare_grad(got, ref, what=""):
+    """Return (max_err / max|ref|, rel_rms) and assert the gradient bar."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite gradient"
+    d = got - ref
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    if scale == 0.0:
+        assert float(np.max(np.abs(got))) == 0.0, f"{what}: expected an exact zero"
+        return 0.0, 0.0
+    max_rel = float(np.max(np.abs(d))) / scale
+    rms = float(np.sqrt(np.sum(d * d) / np.sum(ref * ref)))
+    assert rms <= GRAD_REL_RMS and max_rel <= GRAD_MAX_REL, \
+        f"{what}: max_err/max|ref| {max_rel:.3e} (<= {GRAD_MAX_REL}), rel_rms {rms:.3e} (<= {GRAD_REL_RMS})"
+    return max_rel, rms
