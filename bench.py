@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 FLOP_PER_PAIR = 4 * 128     # QK^T and PV, 2 flop per MAC, head dim 128
+BWD_FLOP_PER_PAIR = 10 * 128  # backward: S, dP, dV, dK, dQ products (algorithmic count)
 D = 128
 KW = dict(rope_dim=42, rope_theta=10000.0, rms_eps=1e-6)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flash_fwd_global_256k_traffic.json")
@@ -89,6 +90,36 @@ class Layer:
     def __call__(self):
         self.bd.zg_attn_fwd(self.q, self.k, self.v, self.g, self.gq, self.gk, window=self.window,
                             out=self.out, workspace=self.ws, **KW)
+
+
+class BwdLayer:
+    """A forward layer plus what its training backward reads and writes."""
+
+    def __init__(self, torch, bd, tag, B, S, Hq, Hkv, window, gated):
+        from global_attention_zg_amd import inputs
+        self.f = Layer(torch, bd, tag, 0, B, S, Hq, Hkv, window, gated)
+        f = self.f
+        self.dout = dev_tensor(torch, (tag, 0, inputs.T_DOUT), (B, S, Hq, D))
+        self.lse = torch.empty((B, Hq, S), dtype=torch.float32, device="cuda")
+        bd.zg_attn_fwd(f.q, f.k, f.v, f.g, f.gq, f.gk, window=window, out=f.out, lse=self.lse,
+                       workspace=f.ws, **KW)
+        self.grads = dict(dq=torch.empty_like(f.q), dk=torch.empty_like(f.k),
+                          dv=torch.empty_like(f.v),
+                          dgate=None if f.g is None else torch.empty_like(f.g),
+                          dq_norm_w=torch.empty(D, dtype=torch.float32, device="cuda"),
+                          dk_norm_w=torch.empty(D, dtype=torch.float32, device="cuda"))
+        p = bd.make_params(B, S, Hq, Hkv, D, window)
+        self.ws = torch.empty(bd.zg_attn_bwd_workspace_size(p), dtype=torch.uint8, device="cuda")
+        self.bd = bd
+        self.flops = B * Hq * inband_pairs(S, window) * BWD_FLOP_PER_PAIR
+        nq = f.q.numel() * (4 + (2 if gated else 0))  # q, out, dout, dq (+ gate, dgate)
+        nk = f.k.numel() * 4                           # k, v, dk, dv
+        self.alg_bytes = (nq + nk) * 2 + self.lse.numel() * 4
+
+    def __call__(self):
+        f = self.f
+        self.bd.zg_attn_bwd(f.q, f.k, f.v, f.g, f.gq, f.gk, f.out, self.lse, self.dout,
+                            window=f.window, workspace=self.ws, **self.grads, **KW)
 
 
 def time_events(torch, fn, iters):
@@ -172,7 +203,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-components", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["swa4k", "global16k", "decode", "block_global"],
+    ap.add_argument("--only", choices=["swa4k", "global16k", "decode", "block_global", "bwd"],
                     default=None, help="time one workload only (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="with --only: first run a plain 1 GiB device copy, the reference "
@@ -298,6 +329,8 @@ def run_components(torch, bd, only, iters):
     torch.cuda.empty_cache()
     if only in (None, "decode"):
         comps.update(decode_components(torch, bd, max(1, iters // 2)))
+    if only in (None, "bwd"):
+        comps.update(bwd_components(torch, bd, max(1, iters // 2)))
     if only == "block_global":
         log("global layer of the 256K block")
         lg = Layer(torch, bd, 4, 5, 1, 262144, 32, 8, 0, False)
@@ -307,6 +340,30 @@ def run_components(torch, bd, only, iters):
                                       "tflops": round(lg.flops / t / 1e12, 2)}
         del lg
     return comps
+
+
+def bwd_components(torch, bd, iters):
+    """Training backward of the gated SWA layer at B4 S4096 (HBM-bound) and of
+    a global layer at S16384 (MFMA-bound)."""
+    out = {}
+    for kind, tag, B, S, window, gated in (("bwd_swa_4k_b4", 6, 4, 4096, 128, True),
+                                           ("bwd_global_16k", 7, 1, 16384, 0, False)):
+        log(f"component: {kind}")
+        l = BwdLayer(torch, bd, tag, B, S, 32, 8, window, gated)
+        for _ in range(2):
+            l()
+        t = time_events(torch, l, iters)
+        r = {"ms": round(t * 1e3, 4), "tflops": round(l.flops / t / 1e12, 2),
+             "tokens_per_s": round(B * S / t, 1)}
+        if window:
+            r["hbm_gbs_alg"] = round(l.alg_bytes / t / 1e9, 1)
+            r["frac_hbm"] = round(l.alg_bytes / t / 1e9 / PEAK_HBM_GBS, 4)
+        else:
+            r["frac_mfma"] = round(l.flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)
+        out[kind] = r
+        del l
+        torch.cuda.empty_cache()
+    return out
 
 
 def decode_components(torch, bd, iters):

@@ -306,16 +306,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
 // every (query head of the group, 32-query tile) whose queries can see its
 // keys; per tile and wave, with this lane's key in column l % 32:
 //   S  = Q' K'^T  (A = Q' rows, ds_read_b128; B = K' in registers)
-//   dP = dO V^T   (A = dO rows, ds_read_b128; B = V in registers)
+//   dP = dO V^T   (A = dO rows; B = V rows of the block, both ds_read_b128)
 //   P = exp2(S c - lse2), dS = P (dP - Dr)
 //   dV^T += dO^T P, dK^T += Q'^T dS  (A by transposing reads; B = P, dS)
-// Q'/dO tiles and the tile's lse2 / Dr come through a two-stage ring of
-// untracked copies (five per wave and tile).
+// The block's V rows sit in LDS for the whole kernel (keeping them in
+// registers would leave room for one wave per SIMD only); Q'/dO tiles and
+// the tile's lse2 / Dr come through a two-stage ring of untracked copies
+// (five per wave and tile).
 // ---------------------------------------------------------------------------
 constexpr int kDkvStage = 2 * kTileB + 256;  // Q', dO, lse2[32], Dr[32]
+constexpr int kDkvV = 2 * kDkvStage;         // V rows of the key block, 4 x 8 KB
 
-__global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[2 * kDkvStage];
+__global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[2 * kDkvStage + 4 * kTileB];
   lds_u8* smem = (lds_u8*)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -371,21 +374,34 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdParams p) {
       dma16(src, sb + 2 * kTileB + 64 * wvu);
     }
   };
+  // ---- the wave's 32 V rows -> LDS (8 copies of 1 KB: rows 4n + L/16 of
+  // its slice, swizzled; rows past S read row S-1 and are never visible)
+  {
+    const long long vstride = (long long)p.Hkv * kD;
+    const int r0 = kb0 + 32 * wvu;
+    const unsigned char* vb =
+        (const unsigned char*)(p.v + ((long long)b * p.S + min(r0, p.S - 1)) * vstride + g * kD);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int rl = 4 * n + (lane >> 4);  // row within the wave's slice
+      const uint32_t off = (uint32_t)((min(r0 + rl, p.S - 1) - min(r0, p.S - 1)) * vstride * 2) +
+                           16u * ((uint32_t)(lane & 15) ^ swz(rl));
+      dma16_s(vb, off, lds_addr(smem + kDkvV + wvu * kTileB + n * 1024));
+    }
+  }
   gload(0, 0);
   if (ntile > 1) gload(1, 1);
 
-  // ---- this lane's key: K' and V as B operands (dims 64 half + 8kk ..)
-  bf16x8 kf[8], vf[8];
+  // ---- this lane's key: K' as the B operand (dims 64 half + 8kk ..)
+  bf16x8 kf[8];
   {
     const long long krow = ((long long)b * p.S + (kok ? kj : 0)) * p.Hkv + g;
     const uint16_t* ks = p.kp + krow * kD + 64 * half;
-    const uint16_t* vs = p.v + krow * kD + 64 * half;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < 8; ++j)
       kf[j] = __builtin_bit_cast(bf16x8, kok ? ld16(ks + 8 * j) : u32x4{0, 0, 0, 0});
-      vf[j] = __builtin_bit_cast(bf16x8, kok ? ld16(vs + 8 * j) : u32x4{0, 0, 0, 0});
-    }
   }
+  const lds_u8* vblk = smem + kDkvV + wvu * kTileB;  // this wave's V rows
   const float c = p.scale_log2;
   const uint32_t bread = (uint32_t)qcol * kRowB + (((uint32_t)(8 * half) ^ swz(qcol)) << 4);
   const TrOffsets tro = tr_offsets(lane);
@@ -414,7 +430,8 @@ __global__ __launch_bounds__(256, 1) void bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
       dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(ot + (bread ^ (uint32_t)(kk << 4))),
-                                                   vf[kk], dp, 0, 0, 0);
+                                                   lds_read_b128(vblk + (bread ^ (uint32_t)(kk << 4))),
+                                                   dp, 0, 0, 0);
     // register r: query q0 + 8(r/4) + 4 half + r%4, key kj
     float pr[16], ds[16];
 #pragma unroll
