@@ -36,7 +36,9 @@ BWD_FLOP_PER_PAIR = 10 * 128  # backward: S, dP, dV, dK, dQ products (algorithmi
 D = 128
 KW = dict(rope_dim=42, rope_theta=10000.0, rms_eps=1e-6)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flash_fwd_global_256k_traffic.json")
-FLASH_SRC = os.path.join(ROOT, "global_attention_zg_amd", "csrc", "flash_fwd.hip")
+# sources the flash kernel is compiled from (the traffic summary is keyed by their hash)
+FLASH_SRCS = [os.path.join(ROOT, "global_attention_zg_amd", "csrc", f)
+              for f in ("flash_fwd.hip", "zg_common.h", "zg_lds.h")]
 
 
 def inband_pairs(S, W):
@@ -136,8 +138,11 @@ def time_events(torch, fn, iters):
 
 
 def flash_source_hash():
-    with open(FLASH_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in FLASH_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def read_traffic():

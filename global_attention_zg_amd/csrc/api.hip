@@ -37,8 +37,12 @@ int check_params(const zg_attn_params* p) {
 zg::RopeTable make_rope_table(const zg_attn_params* p) {
   zg::RopeTable t{};
   const int half = p->rope_dim / 2;
-  for (int i = 0; i < half; ++i)
-    t.rev[i] = pow((double)p->rope_theta, -2.0 * i / (double)p->rope_dim) / (2.0 * M_PI);
+  const long double two_pi = 2.0L * acosl(-1.0L);
+  for (int i = 0; i < half; ++i) {
+    // revolutions per position, < 1/(2 pi), as a 0.64 fixed-point fraction
+    const long double rev = powl((long double)p->rope_theta, -2.0L * i / (long double)p->rope_dim) / two_pi;
+    t.frac[i] = (uint64_t)(ldexpl(rev, 64) + 0.5L);
+  }
   return t;
 }
 

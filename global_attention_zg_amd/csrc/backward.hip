@@ -505,6 +505,7 @@ __global__ __launch_bounds__(256) void prologue_bwd_kernel(const uint16_t* __res
                                                            int S, int heads, long long pos_offset,
                                                            int rope_half, float eps, RopeTable tab) {
   __shared__ float rowbuf[16][kD + 4];
+  __shared__ float cs[16][kMaxRopeHalf], sn[16][kMaxRopeHalf];
   const int slot = threadIdx.x >> 4, c16 = threadIdx.x & 15;
   float wl[8];
   {
@@ -535,12 +536,17 @@ __global__ __launch_bounds__(256) void prologue_bwd_kernel(const uint16_t* __res
 #pragma unroll
       for (int e = 0; e < 8; ++e) xv[e] = dyv[e] = 0.f;
     }
+    const long long pos = pos_offset + (row / heads) % S;
     if (R > 0) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) rowbuf[slot][8 * c16 + e] = dyv[e];
+      // the block's first row of each position computes its angles, one per
+      // lane t % 16, for all rows of that position
+      if ((int)(row % heads) == 0 || slot == 0)
+        for (int t = c16; t < rope_half; t += 16) rope_cos_sin(tab, t, pos, cs[slot][t], sn[slot][t]);
     }
     __syncthreads();
-    const long long pos = pos_offset + (row / heads) % S;
+    const int ref = slot - (int)min(row % heads, (long long)slot);
     float dh[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -548,10 +554,9 @@ __global__ __launch_bounds__(256) void prologue_bwd_kernel(const uint16_t* __res
       dh[e] = dyv[e];
       if (d < R) {
         const int t = d < rope_half ? d : d - rope_half;
-        float cs, sn;
-        rope_cos_sin(tab, t, pos, cs, sn);
-        if (d < rope_half) dh[e] = dyv[e] * cs + rowbuf[slot][d + rope_half] * sn;
-        else dh[e] = dyv[e] * cs - rowbuf[slot][d - rope_half] * sn;
+        const float c = cs[ref][t], s = sn[ref][t];
+        if (d < rope_half) dh[e] = dyv[e] * c + rowbuf[slot][d + rope_half] * s;
+        else dh[e] = dyv[e] * c - rowbuf[slot][d - rope_half] * s;
       }
     }
     float ss = 0.f, dot = 0.f;

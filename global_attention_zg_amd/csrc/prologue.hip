@@ -22,10 +22,16 @@ namespace {
 constexpr int kRowsPerBlock = 16;
 
 // Normalise + rotate one row held as 8 values per lane (lane c16 = 0..15 of
-// the row owns dims 8*c16 .. 8*c16+7).  `xs` is the row's LDS scratch.
+// the row owns dims 8*c16 .. 8*c16+7).  `xs` is the row's LDS scratch.  The
+// rotary cosines / sines live in per-row LDS tables; rows at the same
+// position (the heads of one token) share them: the block's first row of
+// each position (`own` true) fills its table, one angle per lane t % 16, and
+// every row reads the table `cs_r` / `sn_r` of that first row.  Every thread
+// of the block calls this together (one barrier).
 __device__ __forceinline__ void norm_rope_row(float* x, int c16, const float* w, float eps,
                                               int rope_half, const RopeTable& tab,
-                                              long long pos, float* xs) {
+                                              long long pos, float* xs, bool own, float* cs_w,
+                                              float* sn_w, const float* cs_r, const float* sn_r) {
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
@@ -43,6 +49,8 @@ __device__ __forceinline__ void norm_rope_row(float* x, int c16, const float* w,
   if (rope_half == 0) return;
 #pragma unroll
   for (int i = 0; i < 8; ++i) xs[8 * c16 + i] = x[i];
+  if (own)
+    for (int t = c16; t < rope_half; t += 16) rope_cos_sin(tab, t, pos, cs_w[t], sn_w[t]);
   __syncthreads();
   const int R = 2 * rope_half;
 #pragma unroll
@@ -50,8 +58,7 @@ __device__ __forceinline__ void norm_rope_row(float* x, int c16, const float* w,
     const int d = 8 * c16 + i;
     if (d < R) {
       const int t = d < rope_half ? d : d - rope_half;
-      float c, s;
-      rope_cos_sin(tab, t, pos, c, s);
+      const float c = cs_r[t], s = sn_r[t];
       if (d < rope_half)
         x[i] = x[i] * c - xs[d + rope_half] * s;
       else
@@ -67,6 +74,7 @@ __global__ __launch_bounds__(256) void k_prologue_kernel(const uint16_t* __restr
                                                          long long pos_offset, int rope_half,
                                                          float eps, RopeTable tab) {
   __shared__ float xs[kRowsPerBlock][kD];
+  __shared__ float cs[kRowsPerBlock][kMaxRopeHalf], sn[kRowsPerBlock][kMaxRopeHalf];
   const int lrow = threadIdx.x / 16;
   const int c16 = threadIdx.x % 16;
   const long long row = (long long)blockIdx.x * kRowsPerBlock + lrow;
@@ -79,7 +87,12 @@ __global__ __launch_bounds__(256) void k_prologue_kernel(const uint16_t* __restr
     for (int i = 0; i < 8; ++i) x[i] = 0.f;
   }
   const long long s = (row / Hkv) % S;
-  norm_rope_row(x, c16, w, eps, rope_half, tab, pos_offset + s, xs[lrow]);
+  // rows are (b, s, head): the first row of each position in the block
+  // computes the angles for all of them
+  const int hh = (int)(row % Hkv);
+  const int ref = lrow - min(hh, lrow);
+  norm_rope_row(x, c16, w, eps, rope_half, tab, pos_offset + s, xs[lrow], ref == lrow, cs[lrow],
+                sn[lrow], cs[ref], sn[ref]);
   if (ok) {
     u32x4 o;
 #pragma unroll
@@ -96,6 +109,7 @@ __global__ __launch_bounds__(256) void decode_append_kernel(
     const int* __restrict__ seq_lens, const float* __restrict__ w, int rows, int Hkv,
     int cap, int ring, long long pos_offset, int rope_half, float eps, RopeTable tab) {
   __shared__ float xs[kRowsPerBlock][kD];
+  __shared__ float cs[kRowsPerBlock][kMaxRopeHalf], sn[kRowsPerBlock][kMaxRopeHalf];
   const int lrow = threadIdx.x / 16;
   const int c16 = threadIdx.x % 16;
   const int row = blockIdx.x * kRowsPerBlock + lrow;  // b * Hkv + g
@@ -114,7 +128,10 @@ __global__ __launch_bounds__(256) void decode_append_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = 0.f;
   }
-  norm_rope_row(x, c16, w, eps, rope_half, tab, pos_offset + L - 1, xs[lrow]);
+  // rows are (b, kv head): one position per b
+  const int ref = lrow - min(row % Hkv, lrow);
+  norm_rope_row(x, c16, w, eps, rope_half, tab, pos_offset + L - 1, xs[lrow], ref == lrow,
+                cs[lrow], sn[lrow], cs[ref], sn[ref]);
   if (ok) {
     u32x4 o;
 #pragma unroll

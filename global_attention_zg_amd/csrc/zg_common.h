@@ -17,22 +17,28 @@ constexpr int kMaxRopeHalf = 32; // rope_dim <= head_dim / 2
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-// Revolutions per position of each rotary pair t: theta^(-2t/R) / (2*pi),
-// computed in double on the host.  Angles are formed in double and reduced
-// to [-1/2, 1/2] revolution before the float sine/cosine, so that positions
-// up to 2^31 keep ~1e-7 rad accuracy.
+// Revolutions per position of each rotary pair t, theta^(-2t/R) / (2*pi), as
+// a 0.64 fixed-point fraction (computed on the host in extended precision).
+// The angle of position p is then frac(p * rev) = (p * F mod 2^64) / 2^64,
+// exact modular integer arithmetic for any 64-bit p; its top 32 bits, read
+// as a signed number, give the angle reduced to [-1/2, 1/2) revolution with
+// an error below 2^-32 revolution.
 struct RopeTable {
-  double rev[kMaxRopeHalf];
+  uint64_t frac[kMaxRopeHalf];
 };
 
 __device__ __forceinline__ void rope_cos_sin(const RopeTable& tab, int t, long long pos,
                                              float& c, float& s) {
-  double r = (double)pos * tab.rev[t];
-  r -= rint(r);
-  float f = (float)r;
+  const uint64_t f = tab.frac[t];
+  const uint64_t p = (uint64_t)pos;
+  const uint32_t pl = (uint32_t)p, ph = (uint32_t)(p >> 32);
+  const uint32_t fl = (uint32_t)f, fh = (uint32_t)(f >> 32);
+  // bits 32..63 of p * f (the carry out of bits 0..31 is dropped: < 2^-32)
+  const uint32_t top = __umulhi(pl, fl) + pl * fh + ph * fl;
+  const float r = (float)(int32_t)top * 2.3283064365386963e-10f;  // * 2^-32
   // v_sin_f32 / v_cos_f32 take their argument in revolutions.
-  s = __builtin_amdgcn_sinf(f);
-  c = __builtin_amdgcn_cosf(f);
+  s = __builtin_amdgcn_sinf(r);
+  c = __builtin_amdgcn_cosf(r);
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
