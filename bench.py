@@ -399,17 +399,51 @@ def decode_components(torch, bd, iters):
             bd.zg_attn_decode(q, kn, vn, kc, vc, sl, ring=ring, window=window, gate=g,
                               q_norm_w=gq, k_norm_w=gk, out=o, workspace=ws, **KW)
 
-        for _ in range(2):
-            fn()
-        t = time_events(torch, fn, iters)
-        keys = min(L, cap)
-        alg = B * Hkv * keys * D * 2 * 2 + (q.numel() * 2 + o.numel()) * 2
-        flops = B * Hq * keys * FLOP_PER_PAIR
-        out[kind] = {"ms": round(t * 1e3, 4), "tokens_per_s": round(B / t, 1),
-                     "hbm_gbs_alg": round(alg / t / 1e9, 1),
-                     "frac_hbm": round(alg / t / 1e9 / PEAK_HBM_GBS, 4),
-                     "tflops": round(flops / t / 1e12, 3),
-                     "splits": bd.zg_attn_decode_num_splits(p, cap)}
+        def record(name, fn, cap):
+            for _ in range(2):
+                fn()
+            t = time_events(torch, fn, iters)
+            keys = min(L, cap)
+            alg = B * Hkv * keys * D * 2 * 2 + (q.numel() * 2 + o.numel()) * 2
+            flops = B * Hq * keys * FLOP_PER_PAIR
+            out[name] = {"ms": round(t * 1e3, 4), "tokens_per_s": round(B / t, 1),
+                         "hbm_gbs_alg": round(alg / t / 1e9, 1),
+                         "frac_hbm": round(alg / t / 1e9 / PEAK_HBM_GBS, 4),
+                         "tflops": round(flops / t / 1e12, 3),
+                         "splits": bd.zg_attn_decode_num_splits(p, cap)}
+
+        record(kind, fn, cap)
+        if not ring:
+            # the same step over a paged copy of the cache: 64-token pages in
+            # a scrambled order
+            log(f"component: {kind}_paged")
+            P = 64
+            mp = (L + P - 1) // P
+            gen = torch.Generator().manual_seed(5)
+            bt = torch.randperm(B * mp, generator=gen).view(B, mp).to(torch.int32).cuda()
+            pools = []
+            for c in (kc, vc):
+                pool = torch.empty((B * mp, Hkv, P, D), dtype=torch.bfloat16, device="cuda")
+                full = L // P
+                for b in range(B):
+                    src = c[b, :, :full * P].view(Hkv, full, P, D).transpose(0, 1)
+                    pool.index_copy_(0, bt[b, :full].long(), src)
+                    if L % P:
+                        pool[int(bt[b, full]), :, :L % P] = c[b, :, full * P:L]
+                pools.append(pool)
+            o_ref = o.clone()
+            o_pg = torch.empty_like(o)
+
+            def fn_paged():
+                bd.zg_attn_decode_paged(q, kn, vn, pools[0], pools[1], bt, sl, window=window,
+                                        gate=g, q_norm_w=gq, k_norm_w=gk, out=o_pg, workspace=ws,
+                                        **KW)
+
+            record(kind + "_paged", fn_paged, mp * P)
+            out[kind + "_paged"]["page_size"] = P
+            out[kind + "_paged"]["equals_contiguous"] = bool(
+                torch.equal(o_pg.view(torch.int16), o_ref.view(torch.int16)))
+            del pools
         del kc, vc
         torch.cuda.empty_cache()
     return out

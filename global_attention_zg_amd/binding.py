@@ -61,6 +61,11 @@ def _load():
     lib.zg_attn_decode_workspace_size.restype = sz
     lib.zg_attn_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, i, i, vp, vp, vp, vp, i, vp, sz, vp]
     lib.zg_attn_decode.restype = i
+    lib.zg_attn_decode_paged.argtypes = [P, vp, vp, vp, vp, vp, i, vp, i, i, vp, vp, vp, vp, vp,
+                                         i, vp, sz, vp]
+    lib.zg_attn_decode_paged.restype = i
+    lib.zg_attn_kv_write_pages.argtypes = [P, vp, vp, vp, vp, i, vp, i, i, vp]
+    lib.zg_attn_kv_write_pages.restype = i
     lib.zg_attn_bwd_workspace_size.argtypes = [P]
     lib.zg_attn_bwd_workspace_size.restype = sz
     lib.zg_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -74,8 +79,9 @@ def _load():
 _lib = _load()
 
 EXPORTED = ("zg_attn_fwd_workspace_size", "zg_attn_fwd", "zg_attn_decode_num_splits",
-            "zg_attn_decode_workspace_size", "zg_attn_decode", "zg_attn_bwd_workspace_size",
-            "zg_attn_bwd", "zg_attn_strerror")
+            "zg_attn_decode_workspace_size", "zg_attn_decode", "zg_attn_kv_write_pages",
+            "zg_attn_decode_paged", "zg_attn_bwd_workspace_size", "zg_attn_bwd",
+            "zg_attn_strerror")
 
 
 def library_path() -> str:
@@ -200,5 +206,45 @@ def zg_attn_decode(q, k_new, v_new, k_cache, v_cache, seq_lens, *, ring, window,
                              _ptr(v_cache), _ptr(seq_lens), cap, int(ring), _ptr(gate),
                              _ptr(q_norm_w), _ptr(k_norm_w), _ptr(out), num_splits,
                              _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st)
+    return out
+
+
+def zg_attn_kv_write_pages(k_prime, v, k_pages, v_pages, block_table, *, stream=None):
+    """k_prime / v [B,S,Hkv,128] (K' from zg_attn_fwd's k_out, and V) into the
+    page pool k_pages / v_pages [num_pages,Hkv,page_size,128]; block_table
+    int32 [B,max_pages] on the device."""
+    B, S, Hkv, D = k_prime.shape
+    num_pages, _, page_size, _ = k_pages.shape
+    p = make_params(B, S, Hkv, Hkv, D)
+    st = _lib.zg_attn_kv_write_pages(ctypes.byref(p), _ptr(k_prime), _ptr(v), _ptr(k_pages),
+                                     _ptr(v_pages), num_pages, _ptr(block_table),
+                                     block_table.shape[1], page_size, _stream(stream))
+    _check(st)
+
+
+def zg_attn_decode_paged(q, k_new, v_new, k_pages, v_pages, block_table, seq_lens, *, window,
+                         gate, q_norm_w, k_norm_w, rope_dim=42, rope_theta=10000.0, rms_eps=1e-6,
+                         softmax_scale=0.0, pos_offset=0, num_splits=0, out=None,
+                         workspace=None, stream=None):
+    """zg_attn_decode over a page pool [num_pages,Hkv,page_size,128] with an
+    int32 block table [B,max_pages].  Returns out."""
+    B, Hq, D = q.shape
+    num_pages, Hkv, page_size, _ = k_pages.shape
+    max_pages = block_table.shape[1]
+    cap = max_pages * page_size
+    p = make_params(B, 0, Hq, Hkv, D, window, rope_dim, rope_theta, rms_eps, softmax_scale,
+                    pos_offset)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        nbytes = zg_attn_decode_workspace_size(p, cap, num_splits)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.zg_attn_decode_paged(ctypes.byref(p), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                   _ptr(k_pages), _ptr(v_pages), num_pages, _ptr(block_table),
+                                   max_pages, page_size, _ptr(seq_lens), _ptr(gate),
+                                   _ptr(q_norm_w), _ptr(k_norm_w), _ptr(out), num_splits,
+                                   _ptr(workspace), ws_bytes, _stream(stream))
     _check(st)
     return out

@@ -95,6 +95,82 @@ BwdLayout bwd_layout(const zg_attn_params* p) {
 
 }  // namespace
 
+// Shared body of the contiguous and the paged decode.
+static int decode_impl(const zg_attn_params* p, const void* q, const void* k_new,
+                       const void* v_new, void* k_cache, void* v_cache, const int* seq_lens,
+                       int cache_cap, int ring, const zg::CacheMap& map, const void* gate,
+                       const float* q_norm_w, const float* k_norm_w, void* out, int num_splits,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_params(p);
+  if (st != ZG_OK) return st;
+  if (cache_cap < 1 || num_splits < 0 || num_splits > 256) return ZG_ERR_INVALID;
+  if (ring && p->window != cache_cap) return ZG_ERR_INVALID;
+  if ((k_new == nullptr) != (v_new == nullptr)) return ZG_ERR_INVALID;
+  if (p->batch == 0) return ZG_OK;
+  if (!q || !k_cache || !v_cache || !seq_lens || !q_norm_w || !k_norm_w || !out)
+    return ZG_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q_norm_w) ||
+      !aligned16(k_norm_w) || !aligned16(out) || (gate && !aligned16(gate)) ||
+      (k_new && (!aligned16(k_new) || !aligned16(v_new))) ||
+      (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
+    return ZG_ERR_INVALID;
+  const int ns = num_splits ? num_splits : auto_splits(p, cache_cap);
+  const size_t need = (size_t)p->batch * p->n_q_heads * ns * (kD + 2) * sizeof(float);
+  if (!workspace || workspace_bytes < need) return ZG_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ZG_ERR_INVALID;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const zg::RopeTable tab = make_rope_table(p);
+  if (k_new) {
+    hipError_t e = zg::launch_decode_append(
+        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), seq_lens, k_norm_w,
+        p->batch, p->n_kv_heads, cache_cap, ring, map, p->pos_offset, p->rope_dim / 2,
+        p->rms_eps, tab, s);
+    if (e != hipSuccess) return ZG_ERR_HIP;
+  }
+  zg::DecodeParams dp{};
+  dp.q = static_cast<const uint16_t*>(q);
+  dp.k_cache = static_cast<const uint16_t*>(k_cache);
+  dp.v_cache = static_cast<const uint16_t*>(v_cache);
+  dp.seq_lens = seq_lens;
+  dp.q_norm_w = q_norm_w;
+  dp.gate = static_cast<const uint16_t*>(gate);
+  dp.out = static_cast<uint16_t*>(out);
+  float* ws = static_cast<float*>(workspace);
+  dp.part_o = ws;
+  dp.part_ml = ws + (size_t)p->batch * p->n_q_heads * ns * kD;
+  dp.B = p->batch;
+  dp.Hq = p->n_q_heads;
+  dp.Hkv = p->n_kv_heads;
+  dp.cap = cache_cap;
+  dp.ring = ring;
+  dp.window = p->window;
+  dp.nsplit = ns;
+  dp.rope_half = p->rope_dim / 2;
+  dp.scale_log2 = scale_log2(p);
+  dp.eps = p->rms_eps;
+  dp.pos_offset = p->pos_offset;
+  dp.map = map;
+  dp.tab = tab;
+  return hip_status(zg::launch_decode(dp, s));
+}
+
+// Page-pool arguments: page_size a power of two in [32, 65536], a table of
+// max_pages >= 1 entries per sequence, at least one page, and a slot count
+// (max_pages * page_size) that fits an int.
+static int check_pages(int num_pages, const int* block_table, int max_pages, int page_size,
+                       zg::CacheMap& map) {
+  if (num_pages < 1 || !block_table || max_pages < 1) return ZG_ERR_INVALID;
+  if (page_size < 32 || page_size > 65536 || (page_size & (page_size - 1))) return ZG_ERR_INVALID;
+  if ((long long)max_pages * page_size > 0x7fffffffLL) return ZG_ERR_INVALID;
+  if (reinterpret_cast<uintptr_t>(block_table) & 3u) return ZG_ERR_INVALID;
+  int sh = 0;
+  while ((1 << sh) < page_size) ++sh;
+  map = zg::CacheMap{block_table, max_pages, sh, num_pages};
+  return ZG_OK;
+}
+
 extern "C" {
 
 const char* zg_attn_strerror(int status) {
@@ -263,59 +339,44 @@ int zg_attn_decode(const zg_attn_params* p, const void* q, const void* k_new, co
                    void* k_cache, void* v_cache, const int* seq_lens, int cache_cap, int ring,
                    const void* gate, const float* q_norm_w, const float* k_norm_w, void* out,
                    int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (ring != 0 && ring != 1) return ZG_ERR_INVALID;
+  const zg::CacheMap contiguous{nullptr, 0, 0, 0};
+  return decode_impl(p, q, k_new, v_new, k_cache, v_cache, seq_lens, cache_cap, ring, contiguous,
+                     gate, q_norm_w, k_norm_w, out, num_splits, workspace, workspace_bytes,
+                     stream);
+}
+
+int zg_attn_decode_paged(const zg_attn_params* p, const void* q, const void* k_new,
+                         const void* v_new, void* k_pages, void* v_pages, int num_pages,
+                         const int* block_table, int max_pages, int page_size,
+                         const int* seq_lens, const void* gate, const float* q_norm_w,
+                         const float* k_norm_w, void* out, int num_splits, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  zg::CacheMap map{};
+  const int st = check_pages(num_pages, block_table, max_pages, page_size, map);
+  if (st != ZG_OK) return st;
+  return decode_impl(p, q, k_new, v_new, k_pages, v_pages, seq_lens, max_pages * page_size, 0,
+                     map, gate, q_norm_w, k_norm_w, out, num_splits, workspace, workspace_bytes,
+                     stream);
+}
+
+int zg_attn_kv_write_pages(const zg_attn_params* p, const void* k_prime, const void* v,
+                           void* k_pages, void* v_pages, int num_pages, const int* block_table,
+                           int max_pages, int page_size, void* stream) {
   int st = check_params(p);
   if (st != ZG_OK) return st;
-  if (cache_cap < 1 || num_splits < 0 || num_splits > 256 || (ring != 0 && ring != 1))
+  zg::CacheMap map{};
+  st = check_pages(num_pages, block_table, max_pages, page_size, map);
+  if (st != ZG_OK) return st;
+  if ((long long)p->seqlen > (long long)max_pages * page_size) return ZG_ERR_INVALID;
+  if (p->batch == 0 || p->seqlen == 0) return ZG_OK;
+  if (!k_prime || !v || !k_pages || !v_pages) return ZG_ERR_INVALID;
+  if (!aligned16(k_prime) || !aligned16(v) || !aligned16(k_pages) || !aligned16(v_pages))
     return ZG_ERR_INVALID;
-  if (ring && p->window != cache_cap) return ZG_ERR_INVALID;
-  if ((k_new == nullptr) != (v_new == nullptr)) return ZG_ERR_INVALID;
-  if (p->batch == 0) return ZG_OK;
-  if (!q || !k_cache || !v_cache || !seq_lens || !q_norm_w || !k_norm_w || !out)
-    return ZG_ERR_INVALID;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(q_norm_w) ||
-      !aligned16(k_norm_w) || !aligned16(out) || (gate && !aligned16(gate)) ||
-      (k_new && (!aligned16(k_new) || !aligned16(v_new))) ||
-      (reinterpret_cast<uintptr_t>(seq_lens) & 3u))
-    return ZG_ERR_INVALID;
-  const int ns = num_splits ? num_splits : auto_splits(p, cache_cap);
-  const size_t need = (size_t)p->batch * p->n_q_heads * ns * (kD + 2) * sizeof(float);
-  if (!workspace || workspace_bytes < need) return ZG_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return ZG_ERR_INVALID;
-
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const zg::RopeTable tab = make_rope_table(p);
-  if (k_new) {
-    hipError_t e = zg::launch_decode_append(
-        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), seq_lens, k_norm_w,
-        p->batch, p->n_kv_heads, cache_cap, ring, p->pos_offset, p->rope_dim / 2, p->rms_eps,
-        tab, s);
-    if (e != hipSuccess) return ZG_ERR_HIP;
-  }
-  zg::DecodeParams dp{};
-  dp.q = static_cast<const uint16_t*>(q);
-  dp.k_cache = static_cast<const uint16_t*>(k_cache);
-  dp.v_cache = static_cast<const uint16_t*>(v_cache);
-  dp.seq_lens = seq_lens;
-  dp.q_norm_w = q_norm_w;
-  dp.gate = static_cast<const uint16_t*>(gate);
-  dp.out = static_cast<uint16_t*>(out);
-  float* ws = static_cast<float*>(workspace);
-  dp.part_o = ws;
-  dp.part_ml = ws + (size_t)p->batch * p->n_q_heads * ns * kD;
-  dp.B = p->batch;
-  dp.Hq = p->n_q_heads;
-  dp.Hkv = p->n_kv_heads;
-  dp.cap = cache_cap;
-  dp.ring = ring;
-  dp.window = p->window;
-  dp.nsplit = ns;
-  dp.rope_half = p->rope_dim / 2;
-  dp.scale_log2 = scale_log2(p);
-  dp.eps = p->rms_eps;
-  dp.pos_offset = p->pos_offset;
-  dp.tab = tab;
-  return hip_status(zg::launch_decode(dp, s));
+  return hip_status(zg::launch_kv_write_pages(
+      static_cast<const uint16_t*>(k_prime), static_cast<const uint16_t*>(v),
+      static_cast<uint16_t*>(k_pages), static_cast<uint16_t*>(v_pages), p->batch, p->seqlen,
+      p->n_kv_heads, map, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -16,6 +16,11 @@
 // O^T += V^T P^T with the V slice transposed through a wave-private LDS tile.
 // Each workgroup writes an unnormalised partial (max, sum, acc[128]) per query
 // head; the merge kernel combines the splits and applies the gate.
+//
+// The cache is either one contiguous [cap, 128] slab per (b, kv head) or a
+// pool of fixed-size pages addressed through a per-sequence page table (the
+// PAGED instance); both read the same keys in the same order, so they give
+// the same bits.
 
 #include "zg_common.h"
 #include "zg_launch.h"
@@ -40,6 +45,7 @@ constexpr int kQnBytes = kMaxGroup * kD * 4;                  // 4096
 constexpr int kRedOBytes = kWaves * kMaxGroup * kD * 4;       // 16384 (inside the Vt area)
 static_assert(kRedOBytes <= kVtBytes, "reduction area must fit in the V^T area");
 
+template <bool PAGED>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kVtBytes + kQsBytes + kQnBytes];
   __shared__ float red_m[kWaves][16];
@@ -107,10 +113,18 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   for (int kk = 0; kk < 4; ++kk)
     qf[kk] = *reinterpret_cast<const bf16x8*>(qs + col * kQsStride + 32 * kk + 8 * kg);
 
-  // ---- stream the split's keys
+  // ---- stream the split's keys.  Cache row of key `key` relative to the
+  // cache base: a contiguous slab per (b, kv head), or the key's page slot
+  // (a wave's 32-key slice spans at most two pages, looked up once per
+  // slice: pa for the slice's first key, pb for its last)
   const long long slab = ((long long)b * p.Hkv + g) * p.cap * kD;
-  const uint16_t* kb = p.k_cache + slab;
-  const uint16_t* vb = p.v_cache + slab;
+  const int psh = p.map.page_shift;
+  auto row_off = [&](int key, int pa, int pb, int base) -> long long {
+    if (!PAGED) return slab + (long long)key * kD;
+    const int pg = (key >> psh) == (base >> psh) ? pa : pb;
+    return (((long long)pg * p.Hkv + g) << psh) * kD + (long long)(key & ((1 << psh) - 1)) * kD;
+  };
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
   uint16_t* vt = vt_all + wv * kD * kVtwStride;
   f32x4 o[8];
 #pragma unroll
@@ -122,15 +136,20 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const float rescale_raw = kRescaleThreshold / p.scale_log2;
 
   for (int it = 0; it < nit; ++it) {
-    const int base = start + it * kKeysPerIter + wv * kKeysPerWave;
+    const int base = start + it * kKeysPerIter + wvu * kKeysPerWave;  // wave-uniform
+    int pa = 0, pb = 0;
+    if (PAGED && base < end) {
+      pa = p.map.page(b, base);
+      pb = p.map.page(b, min(base + kKeysPerWave - 1, end - 1));
+    }
     bf16x8 kf[2][4];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int key = base + krel + 4 * blk;
+      const long long ro = key < end ? row_off(key, pa, pb, base) : 0;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        u32x4 u = key < end ? ld16(kb + (long long)key * kD + 32 * kk + 8 * kg)
-                            : u32x4{0, 0, 0, 0};
+        u32x4 u = key < end ? ld16(p.k_cache + ro + 32 * kk + 8 * kg) : u32x4{0, 0, 0, 0};
         kf[blk][kk] = __builtin_bit_cast(bf16x8, u);
       }
     }
@@ -138,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int key = base + 8 * kg + j;
-      vr[j] = key < end ? ld16(vb + (long long)key * kD + 8 * col) : u32x4{0, 0, 0, 0};
+      vr[j] = key < end ? ld16(p.v_cache + row_off(key, pa, pb, base) + 8 * col) : u32x4{0, 0, 0, 0};
     }
 
     f32x4 s[2];
@@ -272,7 +291,12 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (p.B == 0) return hipSuccess;
   const long long blocks = (long long)p.B * p.Hkv * p.nsplit;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(decode_split_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, p);
+  if (p.map.block_table)
+    hipLaunchKernelGGL(decode_split_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL(decode_split_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0,
+                       stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(p.B * p.Hq), dim3(64), 0, stream, p);

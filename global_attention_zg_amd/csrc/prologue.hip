@@ -107,7 +107,8 @@ __global__ __launch_bounds__(256) void decode_append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
     const int* __restrict__ seq_lens, const float* __restrict__ w, int rows, int Hkv,
-    int cap, int ring, long long pos_offset, int rope_half, float eps, RopeTable tab) {
+    int cap, int ring, CacheMap map, long long pos_offset, int rope_half, float eps,
+    RopeTable tab) {
   __shared__ float xs[kRowsPerBlock][kD];
   __shared__ float cs[kRowsPerBlock][kMaxRopeHalf], sn[kRowsPerBlock][kMaxRopeHalf];
   const int lrow = threadIdx.x / 16;
@@ -136,10 +137,39 @@ __global__ __launch_bounds__(256) void decode_append_kernel(
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-    const long long dst = ((long long)row * cap + slot) * kD + 8 * c16;
+    long long dst;
+    if (map.block_table) {  // slot L-1 of its page
+      const int pg = map.page(b, slot);
+      dst = ((((long long)pg * Hkv + row % Hkv) << map.page_shift) + (slot & ((1 << map.page_shift) - 1))) * kD + 8 * c16;
+    } else {
+      dst = ((long long)row * cap + slot) * kD + 8 * c16;
+    }
     st16(k_cache + dst, o);
     st16(v_cache + dst, vv);
   }
+}
+
+// Prefill -> paged cache: token s of sequence b (rows of [B,S,Hkv,D]) goes
+// to slot s % page_size of page block_table[b][s / page_size].  16 lanes per
+// row, 16 bytes each.
+__global__ __launch_bounds__(256) void kv_write_pages_kernel(const uint16_t* __restrict__ kp,
+                                                             const uint16_t* __restrict__ v,
+                                                             uint16_t* __restrict__ k_pages,
+                                                             uint16_t* __restrict__ v_pages,
+                                                             long long rows, int S, int Hkv,
+                                                             CacheMap map) {
+  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);  // (b*S + s)*Hkv + g
+  const int c16 = threadIdx.x & 15;
+  if (row >= rows) return;
+  const int g = (int)(row % Hkv);
+  const long long bs = row / Hkv;
+  const int s = (int)(bs % S);
+  const long long b = bs / S;
+  const int pg = map.page(b, s);
+  const long long dst =
+      ((((long long)pg * Hkv + g) << map.page_shift) + (s & ((1 << map.page_shift) - 1))) * kD + 8 * c16;
+  st16(k_pages + dst, ld16(kp + row * kD + 8 * c16));
+  st16(v_pages + dst, ld16(v + row * kD + 8 * c16));
 }
 
 }  // namespace
@@ -156,14 +186,27 @@ hipError_t launch_k_prologue(const uint16_t* k, const float* w, uint16_t* kout, 
 
 hipError_t launch_decode_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache,
                                 uint16_t* v_cache, const int* seq_lens, const float* w, int B,
-                                int Hkv, int cap, int ring, long long pos_offset, int rope_half,
-                                float eps, const RopeTable& tab, hipStream_t stream) {
+                                int Hkv, int cap, int ring, const CacheMap& map,
+                                long long pos_offset, int rope_half, float eps,
+                                const RopeTable& tab, hipStream_t stream) {
   const int rows = B * Hkv;
   if (rows == 0) return hipSuccess;
   const int blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
   hipLaunchKernelGGL(decode_append_kernel, dim3(blocks), dim3(256), 0, stream, k_new, v_new,
-                     k_cache, v_cache, seq_lens, w, rows, Hkv, cap, ring, pos_offset, rope_half,
-                     eps, tab);
+                     k_cache, v_cache, seq_lens, w, rows, Hkv, cap, ring, map, pos_offset,
+                     rope_half, eps, tab);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_write_pages(const uint16_t* kp, const uint16_t* v, uint16_t* k_pages,
+                                 uint16_t* v_pages, int B, int S, int Hkv, const CacheMap& map,
+                                 hipStream_t stream) {
+  const long long rows = (long long)B * S * Hkv;
+  if (rows == 0) return hipSuccess;
+  const long long blocks = (rows + 15) / 16;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(kv_write_pages_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, kp, v,
+                     k_pages, v_pages, rows, S, Hkv, map);
   return hipGetLastError();
 }
 

@@ -31,15 +31,42 @@ hipError_t launch_k_prologue(const uint16_t* k, const float* w, uint16_t* kout, 
 
 hipError_t launch_flash_fwd(const FlashParams& p, hipStream_t stream);
 
+// Where a sequence's cache rows live.  Contiguous: one slab [cap, D] per
+// (b, kv head).  Paged (block_table != null): token t of sequence b is slot
+// t % page_size of page block_table[b * max_pages + t / page_size], and a
+// page holds [Hkv, page_size, D]; page_size is a power of two >= 32.
+// Paged KV cache: page table row b lists the pages of sequence b; key slot t
+// sits in page table[b][t >> page_shift], row t & (page_size-1) of that
+// page's [Hkv, page_size, D] block.  Page ids are clamped into [0, num_pages)
+// so a bad table entry cannot address memory outside the pool.
+struct CacheMap {
+  const int* block_table;  // int32 [B, max_pages], or null: contiguous slabs
+  int max_pages;
+  int page_shift;  // log2(page_size)
+  int num_pages;
+
+  __device__ __forceinline__ int page(long long b, int slot) const {
+    const int pg = block_table[b * max_pages + (slot >> page_shift)];
+    return (int)min((unsigned)pg, (unsigned)(num_pages - 1));
+  }
+};
+
 hipError_t launch_decode_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache,
                                 uint16_t* v_cache, const int* seq_lens, const float* w, int B,
-                                int Hkv, int cap, int ring, long long pos_offset, int rope_half,
-                                float eps, const RopeTable& tab, hipStream_t stream);
+                                int Hkv, int cap, int ring, const CacheMap& map,
+                                long long pos_offset, int rope_half, float eps,
+                                const RopeTable& tab, hipStream_t stream);
+
+// Copy K' and V of a prefill (bf16 [B,S,Hkv,D]) into a paged cache: token s
+// of sequence b goes to its page slot (CacheMap).
+hipError_t launch_kv_write_pages(const uint16_t* kp, const uint16_t* v, uint16_t* k_pages,
+                                 uint16_t* v_pages, int B, int S, int Hkv, const CacheMap& map,
+                                 hipStream_t stream);
 
 struct DecodeParams {
   const uint16_t* q;        // bf16 [B,Hq,D] raw
-  const uint16_t* k_cache;  // bf16 [B,Hkv,cap,D]
-  const uint16_t* v_cache;  // bf16 [B,Hkv,cap,D]
+  const uint16_t* k_cache;  // bf16 [B,Hkv,cap,D], or pages [num_pages,Hkv,page,D]
+  const uint16_t* v_cache;  // bf16, same layout as k_cache
   const int* seq_lens;      // int32 [B]
   const float* q_norm_w;    // fp32 [D]
   const uint16_t* gate;     // bf16 [B,Hq,D] or null
@@ -49,6 +76,7 @@ struct DecodeParams {
   int B, Hq, Hkv, cap, ring, window, nsplit, rope_half;
   float scale_log2, eps;
   long long pos_offset;
+  CacheMap map;             // block_table == null: contiguous slabs
   RopeTable tab;
 };
 

@@ -119,6 +119,46 @@ int zg_attn_decode(const zg_attn_params* p,
                    void* out, int num_splits,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* Paged KV cache (a serving layout for the global layers' cache, whose size
+ * at 256K tokens the structured-data table of the ZGCM-1 page, row
+ * "256K 上下文推理 KV 缓存", quantifies): a pool of num_pages pages, each
+ * bf16 [Hkv, page_size, D] for K' and the same for V, so k_pages/v_pages are
+ * bf16 [num_pages, Hkv, page_size, D].  block_table is device int32
+ * [B, max_pages]: token slot t of sequence b lives in page
+ * block_table[b*max_pages + t/page_size], row t % page_size.
+ *   page_size   a power of two in [32, 65536]
+ *   max_pages   table entries per sequence (>= 1); max_pages * page_size
+ *               is the per-sequence capacity and must fit an int
+ * Table entries are read on the device; an entry outside [0, num_pages) is
+ * clamped into that range (the result is then meaningless, but no access
+ * leaves the pool).  Pages shared by several sequences are allowed for
+ * reading; two sequences must not append into the same page slot. */
+
+/* Copy a prefill's K' (zg_attn_fwd's k_out) and V, both bf16 [B,S,Hkv,D]
+ * with B = p->batch and S = p->seqlen, into the page pool: token s of
+ * sequence b goes to slot s.  S <= max_pages * page_size is required.
+ * S == 0 or B == 0 is valid and launches nothing. */
+int zg_attn_kv_write_pages(const zg_attn_params* p,
+                           const void* k_prime, const void* v,
+                           void* k_pages, void* v_pages, int num_pages,
+                           const int* block_table, int max_pages, int page_size,
+                           void* stream);
+
+/* zg_attn_decode over a paged cache: identical arguments and semantics to
+ * the ring == 0 case of zg_attn_decode with cache_cap = max_pages *
+ * page_size, except that key slot t is read from (and the new token's K' and
+ * V written to) its page as described above.  The workspace is
+ * zg_attn_decode_workspace_size(p, max_pages * page_size, num_splits).  For
+ * equal inputs the output is bit-identical to zg_attn_decode's. */
+int zg_attn_decode_paged(const zg_attn_params* p,
+                         const void* q, const void* k_new, const void* v_new,
+                         void* k_pages, void* v_pages, int num_pages,
+                         const int* block_table, int max_pages, int page_size,
+                         const int* seq_lens, const void* gate,
+                         const float* q_norm_w, const float* k_norm_w,
+                         void* out, int num_splits,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace zg_attn_bwd needs (recomputed Q' and K', dO,
  * per-row LSE*log2(e) and rowsum(dY*Y), fp32 dL/dQ' and dL/dK', and the
  * partial sums of the two weight gradients); 0 for an invalid p. */

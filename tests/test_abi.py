@@ -28,7 +28,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("zg_attn_fwd", "zg_attn_decode", "zg_attn_fwd_workspace_size",
-              "zg_attn_decode_workspace_size", "zg_attn_decode_num_splits", "zg_attn_strerror"):
+              "zg_attn_decode_workspace_size", "zg_attn_decode_num_splits", "zg_attn_strerror",
+              "zg_attn_decode_paged", "zg_attn_kv_write_pages", "zg_attn_bwd"):
         assert n in names
 
 
@@ -190,3 +191,53 @@ def test_bwd_rejects_bad_arguments(bd):
     # empty problem: valid, nothing launched
     q = bd.make_params(0, 64, 32, 8, 128, 0)
     assert _bwd(bd, q) == bd.ZG_OK
+
+
+def _dec_paged(bd, p, num_pages, max_pages, page_size, num_splits=0, **ptrs):
+    a = [ptrs.get(n) for n in ("q", "kn", "vn", "kp", "vp")]
+    return bd._lib.zg_attn_decode_paged(ctypes.byref(p), *a, num_pages, ptrs.get("bt"),
+                                        max_pages, page_size, ptrs.get("sl"), ptrs.get("gate"),
+                                        ptrs.get("qw"), ptrs.get("kw"), ptrs.get("out"),
+                                        num_splits, ptrs.get("ws"), ptrs.get("ws_bytes", 0), None)
+
+
+def _write_pages(bd, p, num_pages, max_pages, page_size, **ptrs):
+    a = [ptrs.get(n) for n in ("kp_in", "v_in", "kp", "vp")]
+    return bd._lib.zg_attn_kv_write_pages(ctypes.byref(p), *a, num_pages, ptrs.get("bt"),
+                                          max_pages, page_size, None)
+
+
+def test_paged_decode_rejects_bad_arguments(bd):
+    ok = dict(q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, qw=FAKE, kw=FAKE, out=FAKE, ws=FAKE,
+              ws_bytes=1 << 30)
+    p = bd.make_params(2, 0, 32, 8, 128, 0)
+    for page_size in (16, 48, 100, 1 << 17):                       # not a power of two in range
+        assert _dec_paged(bd, p, 8, 4, page_size, **ok) == bd.ZG_ERR_INVALID, page_size
+    assert _dec_paged(bd, p, 0, 4, 64, **ok) == bd.ZG_ERR_INVALID  # empty pool
+    assert _dec_paged(bd, p, 8, 0, 64, **ok) == bd.ZG_ERR_INVALID  # empty table row
+    assert _dec_paged(bd, p, 8, 1 << 16, 1 << 16, **ok) == bd.ZG_ERR_INVALID  # > int slots
+    assert _dec_paged(bd, p, 8, 4, 64, **dict(ok, bt=None)) == bd.ZG_ERR_INVALID
+    assert _dec_paged(bd, p, 8, 4, 64, **dict(ok, bt=FAKE + 2)) == bd.ZG_ERR_INVALID
+    assert _dec_paged(bd, p, 8, 4, 64, **dict(ok, kp=FAKE + 8)) == bd.ZG_ERR_INVALID
+    assert _dec_paged(bd, p, 8, 4, 64, **dict(ok, kn=FAKE)) == bd.ZG_ERR_INVALID  # k without v
+    assert _dec_paged(bd, p, 8, 4, 64, num_splits=257, **ok) == bd.ZG_ERR_INVALID
+    # workspace sized for cap = max_pages * page_size
+    need = bd.zg_attn_decode_workspace_size(p, 4 * 64, 0)
+    assert _dec_paged(bd, p, 8, 4, 64, **dict(ok, ws_bytes=need - 1)) == bd.ZG_ERR_WORKSPACE
+    p0 = bd.make_params(0, 0, 32, 8, 128, 0)
+    assert _dec_paged(bd, p0, 8, 4, 64, bt=FAKE) == bd.ZG_OK
+    pbad = bd.make_params(2, 0, 32, 8, 128, 0)
+    pbad.rope_dim = 43
+    assert _dec_paged(bd, pbad, 8, 4, 64, **ok) == bd.ZG_ERR_INVALID
+
+
+def test_write_pages_rejects_bad_arguments(bd):
+    ok = dict(kp_in=FAKE, v_in=FAKE, kp=FAKE, vp=FAKE, bt=FAKE)
+    p = bd.make_params(2, 300, 8, 8, 128)
+    assert _write_pages(bd, p, 16, 9, 32, **ok) == bd.ZG_ERR_INVALID     # 288 slots < 300
+    assert _write_pages(bd, p, 16, 10, 24, **ok) == bd.ZG_ERR_INVALID
+    assert _write_pages(bd, p, 16, 10, 32, **dict(ok, v_in=None)) == bd.ZG_ERR_INVALID
+    assert _write_pages(bd, p, 16, 10, 32, **dict(ok, vp=FAKE + 4)) == bd.ZG_ERR_INVALID
+    assert _write_pages(bd, p, 0, 10, 32, **ok) == bd.ZG_ERR_INVALID
+    for B, S in ((0, 300), (2, 0)):
+        assert _write_pages(bd, bd.make_params(B, S, 8, 8, 128), 16, 10, 32, bt=FAKE) == bd.ZG_OK
