@@ -208,7 +208,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--no-components", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["swa4k", "global16k", "decode", "block_global", "bwd"],
+    ap.add_argument("--only",
+                    choices=["swa4k", "global16k", "decode", "block_global", "bwd", "varlen"],
                     default=None, help="time one workload only (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="with --only: first run a plain 1 GiB device copy, the reference "
@@ -334,6 +335,8 @@ def run_components(torch, bd, only, iters):
     torch.cuda.empty_cache()
     if only in (None, "decode"):
         comps.update(decode_components(torch, bd, max(1, iters // 2)))
+    if only in (None, "varlen"):
+        comps.update(varlen_components(torch, bd, max(1, iters // 2)))
     if only in (None, "bwd"):
         comps.update(bwd_components(torch, bd, max(1, iters // 2)))
     if only == "block_global":
@@ -345,6 +348,49 @@ def run_components(torch, bd, only, iters):
                                       "tflops": round(lg.flops / t / 1e12, 2)}
         del lg
     return comps
+
+
+VARLEN_LENS_SEED = 9
+
+
+def varlen_components(torch, bd, iters):
+    """A packed serving batch: 16 prompts of seeded lengths in 1..8192, 32/8
+    heads, through the gated SWA layer and the global layer."""
+    from global_attention_zg_amd import inputs
+    lens = [int(x) for x in np.random.default_rng(VARLEN_LENS_SEED).integers(1, 8193, size=16)]
+    T = sum(lens)
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32, device="cuda")
+    q = dev_tensor(torch, (8, 0, inputs.T_Q), (T, 32, D))
+    k = dev_tensor(torch, (8, 0, inputs.T_K), (T, 8, D))
+    v = dev_tensor(torch, (8, 0, inputs.T_V), (T, 8, D))
+    g = dev_tensor(torch, (8, 0, inputs.T_GATE), (T, 32, D))
+    gq = norm_w(torch, (8, 0, inputs.T_GQ))
+    gk = norm_w(torch, (8, 0, inputs.T_GK))
+    o = torch.empty_like(q)
+    ws = torch.empty(T * 8 * D * 2, dtype=torch.uint8, device="cuda")
+    out = {}
+    for kind, window, gate in (("varlen_swa_16x", 128, g), ("varlen_global_16x", 0, None)):
+        log(f"component: {kind}")
+
+        def fn():
+            bd.zg_attn_fwd_varlen(q, k, v, gate, gq, gk, cu, max(lens), window=window, out=o,
+                                  workspace=ws, **KW)
+
+        for _ in range(2):
+            fn()
+        t = time_events(torch, fn, iters)
+        flops = 32 * sum(inband_pairs(n, window) for n in lens) * FLOP_PER_PAIR
+        r = {"ms": round(t * 1e3, 4), "tokens": T, "tokens_per_s": round(T / t, 1),
+             "tflops": round(flops / t / 1e12, 2)}
+        if window:
+            alg = (q.numel() * 3 + k.numel() * 2) * 2  # q, gate, out, k, v
+            r["hbm_gbs_alg"] = round(alg / t / 1e9, 1)
+            r["frac_hbm"] = round(alg / t / 1e9 / PEAK_HBM_GBS, 4)
+        else:
+            r["frac_mfma"] = round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)
+        out[kind] = r
+    out["varlen_lens"] = lens
+    return out
 
 
 def bwd_components(torch, bd, iters):

@@ -55,6 +55,11 @@ def _load():
     lib.zg_attn_fwd_workspace_size.restype = sz
     lib.zg_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.zg_attn_fwd.restype = i
+    ll = ctypes.c_longlong
+    lib.zg_attn_fwd_varlen_workspace_size.argtypes = [P, ll]
+    lib.zg_attn_fwd_varlen_workspace_size.restype = sz
+    lib.zg_attn_fwd_varlen.argtypes = [P, vp, ll, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.zg_attn_fwd_varlen.restype = i
     lib.zg_attn_decode_num_splits.argtypes = [P, i]
     lib.zg_attn_decode_num_splits.restype = i
     lib.zg_attn_decode_workspace_size.argtypes = [P, i, i]
@@ -78,7 +83,8 @@ def _load():
 
 _lib = _load()
 
-EXPORTED = ("zg_attn_fwd_workspace_size", "zg_attn_fwd", "zg_attn_decode_num_splits",
+EXPORTED = ("zg_attn_fwd_workspace_size", "zg_attn_fwd", "zg_attn_fwd_varlen_workspace_size",
+            "zg_attn_fwd_varlen", "zg_attn_decode_num_splits",
             "zg_attn_decode_workspace_size", "zg_attn_decode", "zg_attn_kv_write_pages",
             "zg_attn_decode_paged", "zg_attn_bwd_workspace_size", "zg_attn_bwd",
             "zg_attn_strerror")
@@ -138,6 +144,39 @@ def zg_attn_fwd(q, k, v, gate, q_norm_w, k_norm_w, *, window, rope_dim=42, rope_
     st = _lib.zg_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(q_norm_w),
                           _ptr(k_norm_w), _ptr(out), _ptr(lse), _ptr(k_out),
                           _ptr(workspace) if k_out is None else None, ws_bytes, _stream(stream))
+    _check(st)
+    return out, lse
+
+
+def zg_attn_fwd_varlen_workspace_size(p: Params, total_tokens: int) -> int:
+    return int(_lib.zg_attn_fwd_varlen_workspace_size(ctypes.byref(p), total_tokens))
+
+
+def zg_attn_fwd_varlen(q, k, v, gate, q_norm_w, k_norm_w, cu_seqlens, max_seqlen, *, window,
+                       rope_dim=42, rope_theta=10000.0, rms_eps=1e-6, softmax_scale=0.0,
+                       pos_offset=0, out=None, lse=None, want_lse=False, k_out=None,
+                       workspace=None, stream=None):
+    """Packed batch: q [T,Hq,128], k/v [T,Hkv,128], gate [T,Hq,128] or None;
+    cu_seqlens int32 [B+1] on the device.  Returns (out, lse [Hq,T] or None)."""
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    B = cu_seqlens.numel() - 1
+    p = make_params(B, max_seqlen, Hq, Hkv, D, window, rope_dim, rope_theta, rms_eps,
+                    softmax_scale, pos_offset)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
+    ws_bytes = 0
+    if k_out is None:
+        ws_bytes = zg_attn_fwd_varlen_workspace_size(p, T)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.zg_attn_fwd_varlen(ctypes.byref(p), _ptr(cu_seqlens), T, _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(gate), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(out), _ptr(lse),
+                                 _ptr(k_out), _ptr(workspace) if k_out is None else None,
+                                 ws_bytes, _stream(stream))
     _check(st)
     return out, lse
 

@@ -213,7 +213,7 @@ __device__ __forceinline__ void pv_mfma(TileState& st, const bf16x8 (&va)[8], co
 // BANDED: sliding-window layer (window > 0); otherwise global causal.
 // RH: rope_dim / 2 when known at compile time (0 or 21: the rotation runs in
 // registers), -1 for any other rope_dim (rotation through LDS).
-template <bool BANDED, int RH>
+template <bool BANDED, int RH, bool PACKED>
 __global__ __launch_bounds__(Cfg<BANDED>::kThreads, 2) void flash_fwd_kernel(FlashParams p,
                                                                                Geo geo) {
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[BANDED ? kSmemBanded : kSmemGlobal];
@@ -239,17 +239,32 @@ __global__ __launch_bounds__(Cfg<BANDED>::kThreads, 2) void flash_fwd_kernel(Fla
   const int b = bgi / p.Hkv;
   const int head = g * grp + hg * geo.heads_per_wg + (wv % geo.heads_per_wg);
   const int i0w = pb * geo.pos_per_wg;
+  // This workgroup's sequence is rows [tok0, tok0 + S) of the token-major
+  // layout: tok0 = b * S for fixed-length batches; with cu_seqlens the
+  // offsets are clamped into [0, total) and the length to the grid's S.
+  int S = p.S;
+  long long tok0 = (long long)b * p.S;
+  long long lse0 = (long long)b * p.Hq * p.S, lse_hs = p.S;
+  if constexpr (PACKED) {
+    const long long c0 = min(max((long long)p.cu_seqlens[b], 0LL), p.total);
+    const long long c1 = min(max((long long)p.cu_seqlens[b + 1], c0), p.total);
+    tok0 = c0;
+    S = (int)min(c1 - c0, (long long)p.S);
+    lse0 = tok0;
+    lse_hs = p.total;
+    if (i0w >= S) return;  // whole workgroup: past the end of a short sequence
+  }
   const int qi = i0w + (wv / geo.heads_per_wg) * 32 + qcol;
-  const bool qok = qi < p.S;
+  const bool qok = qi < S;
   // Rows past the end are padding: give them row S-1's visibility so that the
   // wave-wide lazy-rescale vote is the same as for any window >= S.
-  const int qm = min(qi, p.S - 1);
+  const int qm = min(qi, S - 1);
   const int lim = BANDED ? min(p.window, qm + 1) : qm + 1;
-  const int hi = min(p.S, i0w + geo.pos_per_wg);      // keys < hi
+  const int hi = min(S, i0w + geo.pos_per_wg);      // keys < hi
   const int lo = BANDED ? max(0, i0w - p.window + 1) : 0;  // keys >= lo
 
 
-  const long long qrow = ((long long)b * p.S + (qok ? qi : 0)) * p.Hq + head;
+  const long long qrow = (tok0 + (qok ? qi : 0)) * p.Hq + head;
   bf16x8 qf[8];  // this wave's Q' rows: the B operand of every S MFMA
 
   // ---- KV tile staging: global -> LDS directly (global_load_lds_dwordx4)
@@ -261,8 +276,8 @@ __global__ __launch_bounds__(Cfg<BANDED>::kThreads, 2) void flash_fwd_kernel(Fla
   constexpr int BPW = Cfg<BANDED>::kBlocksPerWave;
   const int wvu = __builtin_amdgcn_readfirstlane(wv);  // wave-uniform copy
   const long long kvstride = (long long)p.Hkv * kD;
-  const uint16_t* kbase = p.kp + (long long)b * p.S * kvstride + g * kD;
-  const uint16_t* vbase = p.v + (long long)b * p.S * kvstride + g * kD;
+  const uint16_t* kbase = p.kp + tok0 * kvstride + g * kD;
+  const uint16_t* vbase = p.v + tok0 * kvstride + g * kD;
   uint32_t row_off[2], kchunk[2];
   int lrow[2];
   const uint32_t vchunk = 16u * ((lane & 15) ^ (((lane >> 4) & 3) << 2));
@@ -279,7 +294,7 @@ __global__ __launch_bounds__(Cfg<BANDED>::kThreads, 2) void flash_fwd_kernel(Fla
     const unsigned char* vb = (const unsigned char*)(vbase + (long long)t * kBN * kvstride);
     const uint32_t kl = lds_addr(smem + stg * kTileBytes + BPW * wvu * 1024);
     const uint32_t vl = kl + kVOff;
-    if (t * kBN + kBN <= p.S) {
+    if (t * kBN + kBN <= S) {
 #pragma unroll
       for (int j = 0; j < BPW; ++j) {
         dma16_s(kb, row_off[j] + kchunk[j], kl + j * 1024);
@@ -288,7 +303,7 @@ __global__ __launch_bounds__(Cfg<BANDED>::kThreads, 2) void flash_fwd_kernel(Fla
     } else {
 #pragma unroll
       for (int j = 0; j < BPW; ++j) {
-        const uint32_t off = (uint32_t)((min(t * kBN + lrow[j], p.S - 1) - t * kBN) * kvstride * 2);
+        const uint32_t off = (uint32_t)((min(t * kBN + lrow[j], S - 1) - t * kBN) * kvstride * 2);
         dma16_s(kb, off + kchunk[j], kl + j * 1024);
         dma16_s(vb, off + vchunk, vl + j * 1024);
       }
@@ -365,7 +380,7 @@ __global__ __launch_bounds__(Cfg<BANDED>::kThreads, 2) void flash_fwd_kernel(Fla
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
       const int row = 4 * n + (lane >> 4);
-      const long long qr = ((long long)b * p.S + min(wrow0 + row, p.S - 1)) * p.Hq + head;
+      const long long qr = (tok0 + min(wrow0 + row, S - 1)) * p.Hq + head;
       dma16(p.q + qr * kD + 8 * ((lane & 15) ^ (row & 15)),
             lds_addr(smem + kQRegion + wvu * 32 * kRowBytes + n * 1024));
     }
@@ -374,7 +389,7 @@ __global__ __launch_bounds__(Cfg<BANDED>::kThreads, 2) void flash_fwd_kernel(Fla
   if (gate_pre) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const long long gr = ((long long)b * p.S + min(wrow0 + 4 * k + (lane >> 4), p.S - 1)) * p.Hq + head;
+      const long long gr = (tok0 + min(wrow0 + 4 * k + (lane >> 4), S - 1)) * p.Hq + head;
       gco[k] = ld16(p.gate + gr * kD + 8 * (lane & 15));
     }
   }
@@ -541,7 +556,7 @@ __global__ __launch_bounds__(Cfg<BANDED>::kThreads, 2) void flash_fwd_kernel(Fla
   const float l_tot = pair_sum32(st.l_run);
   const float inv = 1.0f / l_tot;
   if (p.lse && qok && half == 0)
-    p.lse[((long long)b * p.Hq + head) * p.S + qi] = (st.m_run * c + __log2f(l_tot)) * kLn2;
+    p.lse[lse0 + head * lse_hs + qi] = (st.m_run * c + __log2f(l_tot)) * kLn2;
   if (BANDED) {
     // fp32 rows to LDS (the tiles are dead: every wave passed the last
     // barrier), 16-byte chunk c of row q at chunk c ^ q; then row-coalesced
@@ -574,8 +589,8 @@ __global__ __launch_bounds__(Cfg<BANDED>::kThreads, 2) void flash_fwd_kernel(Fla
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] *= sigmoidf_(gv[e]);
       }
-      if (wrow0 + row < p.S) {
-        const long long orw = ((long long)b * p.S + wrow0 + row) * p.Hq + head;
+      if (wrow0 + row < S) {
+        const long long orw = (tok0 + wrow0 + row) * p.Hq + head;
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
@@ -609,6 +624,15 @@ __global__ __launch_bounds__(Cfg<BANDED>::kThreads, 2) void flash_fwd_kernel(Fla
   }
 }
 
+template <int RH, bool PACKED>
+void launch_variant(bool banded, dim3 grid, dim3 block, hipStream_t stream, const FlashParams& p,
+                    const Geo& geo) {
+  if (banded)
+    hipLaunchKernelGGL((flash_fwd_kernel<true, RH, PACKED>), grid, block, 0, stream, p, geo);
+  else
+    hipLaunchKernelGGL((flash_fwd_kernel<false, RH, PACKED>), grid, block, 0, stream, p, geo);
+}
+
 }  // namespace
 
 hipError_t launch_flash_fwd(const FlashParams& p, hipStream_t stream) {
@@ -625,15 +649,14 @@ hipError_t launch_flash_fwd(const FlashParams& p, hipStream_t stream) {
   const long long blocks = (long long)geo.n_pos_blocks * geo.n_bhg;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(64 * waves);
-  if (p.rope_half == 21) {
-    if (banded) hipLaunchKernelGGL((flash_fwd_kernel<true, 21>), grid, block, 0, stream, p, geo);
-    else hipLaunchKernelGGL((flash_fwd_kernel<false, 21>), grid, block, 0, stream, p, geo);
-  } else if (p.rope_half == 0) {
-    if (banded) hipLaunchKernelGGL((flash_fwd_kernel<true, 0>), grid, block, 0, stream, p, geo);
-    else hipLaunchKernelGGL((flash_fwd_kernel<false, 0>), grid, block, 0, stream, p, geo);
+  if (p.cu_seqlens) {
+    if (p.rope_half == 21) launch_variant<21, true>(banded, grid, block, stream, p, geo);
+    else if (p.rope_half == 0) launch_variant<0, true>(banded, grid, block, stream, p, geo);
+    else launch_variant<-1, true>(banded, grid, block, stream, p, geo);
   } else {
-    if (banded) hipLaunchKernelGGL((flash_fwd_kernel<true, -1>), grid, block, 0, stream, p, geo);
-    else hipLaunchKernelGGL((flash_fwd_kernel<false, -1>), grid, block, 0, stream, p, geo);
+    if (p.rope_half == 21) launch_variant<21, false>(banded, grid, block, stream, p, geo);
+    else if (p.rope_half == 0) launch_variant<0, false>(banded, grid, block, stream, p, geo);
+    else launch_variant<-1, false>(banded, grid, block, stream, p, geo);
   }
   return hipGetLastError();
 }

@@ -71,8 +71,9 @@ __global__ __launch_bounds__(256) void k_prologue_kernel(const uint16_t* __restr
                                                          const float* __restrict__ w,
                                                          uint16_t* __restrict__ kout,
                                                          long long rows, int S, int Hkv,
-                                                         long long pos_offset, int rope_half,
-                                                         float eps, RopeTable tab) {
+                                                         const int* __restrict__ cu_seqlens,
+                                                         int nseq, long long pos_offset,
+                                                         int rope_half, float eps, RopeTable tab) {
   __shared__ float xs[kRowsPerBlock][kD];
   __shared__ float cs[kRowsPerBlock][kMaxRopeHalf], sn[kRowsPerBlock][kMaxRopeHalf];
   const int lrow = threadIdx.x / 16;
@@ -86,7 +87,20 @@ __global__ __launch_bounds__(256) void k_prologue_kernel(const uint16_t* __restr
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = 0.f;
   }
-  const long long s = (row / Hkv) % S;
+  // position of the row's token within its sequence
+  const long long tok = row / Hkv;
+  long long s;
+  if (cu_seqlens) {  // packed: the last sequence b with cu_seqlens[b] <= tok
+    int lo = 0, hi = nseq;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cu_seqlens[mid] <= tok) lo = mid;
+      else hi = mid;
+    }
+    s = max(tok - (long long)cu_seqlens[lo], 0LL);
+  } else {
+    s = tok % S;
+  }
   // rows are (b, s, head): the first row of each position in the block
   // computes the angles for all of them
   const int hh = (int)(row % Hkv);
@@ -176,11 +190,13 @@ __global__ __launch_bounds__(256) void kv_write_pages_kernel(const uint16_t* __r
 
 hipError_t launch_k_prologue(const uint16_t* k, const float* w, uint16_t* kout, long long rows,
                              int S, int Hkv, long long pos_offset, int rope_half, float eps,
-                             const RopeTable& tab, hipStream_t stream) {
+                             const RopeTable& tab, hipStream_t stream, const int* cu_seqlens,
+                             int nseq) {
   if (rows == 0) return hipSuccess;
   const long long blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_prologue_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k, w,
-                     kout, rows, S, Hkv, pos_offset, rope_half, eps, tab);
+                     kout, rows, S, Hkv, cu_seqlens, nseq, pos_offset, rope_half, eps, tab);
   return hipGetLastError();
 }
 

@@ -17,17 +17,28 @@ struct FlashParams {
   const uint16_t* gate;  // bf16 [B,S,Hq,D] or null
   const float* q_norm_w; // fp32 [D]
   uint16_t* out;         // bf16 [B,S,Hq,D]
-  float* lse;            // fp32 [B,Hq,S] or null
+  float* lse;            // fp32 [B,Hq,S], or [Hq,total] when packed; or null
   int B, S, Hq, Hkv, window, rope_half;
   float scale_log2;      // softmax scale * log2(e)
   float eps;
   long long pos_offset;
   RopeTable tab;
+  // Packed variable-length batch: rows [cu_seqlens[b], cu_seqlens[b+1]) of
+  // the token-major tensors form sequence b; S is then the longest length
+  // (it sizes the grid) and total the number of rows.  Null: B fixed-length
+  // sequences of S tokens.
+  const int* cu_seqlens;
+  long long total;
 };
 
+// Rows are (token, head) of a token-major [tokens, H, D] tensor.  Token t
+// sits at position pos_offset + (t mod S), or, with cu_seqlens (int32
+// [nseq + 1] on the device), pos_offset + t - cu_seqlens[b] for the sequence
+// b that holds it.
 hipError_t launch_k_prologue(const uint16_t* k, const float* w, uint16_t* kout, long long rows,
                              int S, int Hkv, long long pos_offset, int rope_half, float eps,
-                             const RopeTable& tab, hipStream_t stream);
+                             const RopeTable& tab, hipStream_t stream,
+                             const int* cu_seqlens = nullptr, int nseq = 0);
 
 hipError_t launch_flash_fwd(const FlashParams& p, hipStream_t stream);
 

@@ -86,6 +86,30 @@ int zg_attn_fwd(const zg_attn_params* p,
                 void* out, float* lse, void* k_out,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Packed variable-length prefill: the same attention as zg_attn_fwd over a
+ * batch of sequences of different lengths stored back to back, as a server
+ * batches prompts (the ZGCM-1 page's structured-data table, row
+ * "256K 上下文推理 KV 缓存", and its section 核心方法 describe the serving
+ * setting; the pages fix no batching format, so this is the common
+ * cumulative-offsets one).
+ *   p->batch      number of sequences B
+ *   p->seqlen     an upper bound on every length (sizes the grid); rows of a
+ *                 longer sequence past p->seqlen are not computed
+ *   cu_seqlens    device int32 [B+1]: sequence b is rows
+ *                 [cu_seqlens[b], cu_seqlens[b+1]) (0 = cu_seqlens[0] <= ...
+ *                 <= cu_seqlens[B] = total_tokens); empty sequences allowed.
+ *                 Read on the device and clamped into [0, total_tokens].
+ *   q, gate, out  bf16 [total_tokens,Hq,D];  k, v, k_out bf16 [total_tokens,Hkv,D]
+ *   lse           fp32 [Hq,total_tokens] or NULL
+ * Token s of every sequence sits at position pos_offset + s.  Each sequence's
+ * rows are bit-identical to zg_attn_fwd on that sequence alone. */
+size_t zg_attn_fwd_varlen_workspace_size(const zg_attn_params* p, long long total_tokens);
+int zg_attn_fwd_varlen(const zg_attn_params* p, const int* cu_seqlens, long long total_tokens,
+                       const void* q, const void* k, const void* v, const void* gate,
+                       const float* q_norm_w, const float* k_norm_w,
+                       void* out, float* lse, void* k_out,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Number of KV splits zg_attn_decode uses when num_splits == 0. */
 int zg_attn_decode_num_splits(const zg_attn_params* p, int cache_cap);
 

@@ -241,3 +241,31 @@ def test_write_pages_rejects_bad_arguments(bd):
     assert _write_pages(bd, p, 0, 10, 32, **ok) == bd.ZG_ERR_INVALID
     for B, S in ((0, 300), (2, 0)):
         assert _write_pages(bd, bd.make_params(B, S, 8, 8, 128), 16, 10, 32, bt=FAKE) == bd.ZG_OK
+
+
+def _fwd_varlen(bd, p, total, **ptrs):
+    names = ["q", "k", "v", "gate", "qw", "kw", "out", "lse", "kout", "ws"]
+    args = [ptrs.get(n) for n in names]
+    return bd._lib.zg_attn_fwd_varlen(ctypes.byref(p), ptrs.get("cu"), total, *args,
+                                      ptrs.get("ws_bytes", 0), None)
+
+
+def test_fwd_varlen_workspace_and_rejects(bd):
+    p = bd.make_params(3, 4096, 32, 8, 128, 128)
+    assert bd.zg_attn_fwd_varlen_workspace_size(p, 5000) == 5000 * 8 * 128 * 2
+    assert bd.zg_attn_fwd_varlen_workspace_size(p, -1) == 0
+    full = dict(cu=FAKE, q=FAKE, k=FAKE, v=FAKE, qw=FAKE, kw=FAKE, out=FAKE, ws=FAKE,
+                ws_bytes=5000 * 8 * 128 * 2)
+    assert _fwd_varlen(bd, p, 5000, **dict(full, cu=None)) == bd.ZG_ERR_INVALID
+    assert _fwd_varlen(bd, p, 5000, **dict(full, cu=FAKE + 2)) == bd.ZG_ERR_INVALID
+    assert _fwd_varlen(bd, p, -5, **full) == bd.ZG_ERR_INVALID
+    assert _fwd_varlen(bd, p, 5000, **dict(full, k=None)) == bd.ZG_ERR_INVALID
+    assert _fwd_varlen(bd, p, 5000, **dict(full, out=FAKE + 8)) == bd.ZG_ERR_INVALID
+    assert _fwd_varlen(bd, p, 5000, **dict(full, ws_bytes=5000 * 8 * 128 * 2 - 1)) == \
+        bd.ZG_ERR_WORKSPACE
+    # empty batch, empty grid or no tokens: valid, nothing launched
+    assert _fwd_varlen(bd, bd.make_params(0, 4096, 32, 8, 128, 0), 0) == bd.ZG_OK
+    assert _fwd_varlen(bd, bd.make_params(3, 0, 32, 8, 128, 0), 0, cu=FAKE) == bd.ZG_OK
+    assert _fwd_varlen(bd, p, 0, cu=FAKE) == bd.ZG_OK
+    p.n_kv_heads = 3
+    assert _fwd_varlen(bd, p, 5000, **full) == bd.ZG_ERR_INVALID
