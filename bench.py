@@ -209,7 +209,8 @@ def main():
     ap.add_argument("--no-components", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only",
-                    choices=["swa4k", "global16k", "decode", "block_global", "bwd", "varlen"],
+                    choices=["swa4k", "global16k", "decode", "decode_block", "block_global", "bwd",
+                             "varlen"],
                     default=None, help="time one workload only (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="with --only: first run a plain 1 GiB device copy, the reference "
@@ -335,6 +336,8 @@ def run_components(torch, bd, only, iters):
     torch.cuda.empty_cache()
     if only in (None, "decode"):
         comps.update(decode_components(torch, bd, max(1, iters // 2)))
+    if only in (None, "decode", "decode_block"):
+        comps.update(decode_block_components(torch, bd, max(1, iters // 2)))
     if only in (None, "varlen"):
         comps.update(varlen_components(torch, bd, max(1, iters // 2)))
     if only in (None, "bwd"):
@@ -348,6 +351,80 @@ def run_components(torch, bd, only, iters):
                                       "tflops": round(lg.flops / t / 1e12, 2)}
         del lg
     return comps
+
+
+class DecodeLayer:
+    """One layer's decode step, B16 at one new token per sequence: a gated
+    SWA layer against its 128-slot ring, or the global layer against a cache
+    of `cap` keys."""
+
+    def __init__(self, torch, bd, tag, layer, L, swa):
+        from global_attention_zg_amd import inputs
+        B, Hq, Hkv = 16, 32, 8
+        self.cap, self.ring, self.window = (128, True, 128) if swa else (L, False, 0)
+        key = lambda t: (tag, layer, t)  # noqa: E731
+        self.kc = dev_tensor(torch, key(inputs.T_KCACHE), (B, Hkv, self.cap, D))
+        self.vc = dev_tensor(torch, key(inputs.T_VCACHE), (B, Hkv, self.cap, D))
+        self.q = dev_tensor(torch, key(inputs.T_Q), (B, Hq, D))
+        self.kn = dev_tensor(torch, key(inputs.T_KNEW), (B, Hkv, D))
+        self.vn = dev_tensor(torch, key(inputs.T_VNEW), (B, Hkv, D))
+        self.g = dev_tensor(torch, key(inputs.T_GATE), (B, Hq, D)) if swa else None
+        self.gq = norm_w(torch, key(inputs.T_GQ))
+        self.gk = norm_w(torch, key(inputs.T_GK))
+        self.sl = torch.full((B,), L, dtype=torch.int32, device="cuda")
+        self.out = torch.empty_like(self.q)
+        p = bd.make_params(B, 0, Hq, Hkv, D, self.window)
+        self.ws = torch.empty(max(16, bd.zg_attn_decode_workspace_size(p, self.cap, 0)),
+                              dtype=torch.uint8, device="cuda")
+        self.bd = bd
+
+    def __call__(self):
+        self.bd.zg_attn_decode(self.q, self.kn, self.vn, self.kc, self.vc, self.sl,
+                               ring=self.ring, window=self.window, gate=self.g,
+                               q_norm_w=self.gq, k_norm_w=self.gk, out=self.out,
+                               workspace=self.ws, **KW)
+
+
+def decode_block_components(torch, bd, iters):
+    """One decode step of a whole 5:1 block (five gated SWA layers, then the
+    global layer), B16, issued eagerly and replayed from a captured HIP graph
+    (the same six launches sequences without host overhead), at a 256K and a
+    4K context."""
+    out = {}
+    for kind, L in (("decode_block_256k", 262145), ("decode_block_4k", 4097)):
+        log(f"component: {kind}")
+        layers = [DecodeLayer(torch, bd, 10, i, L, swa=(i < 5)) for i in range(6)]
+
+        def step():
+            for layer in layers:
+                layer()
+
+        for _ in range(2):
+            step()
+        t_eager = time_events(torch, step, iters)
+        ref = [layer.out.clone() for layer in layers]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        graph.replay()
+        torch.cuda.synchronize()
+        same = all(torch.equal(a.view(torch.int16), layer.out.view(torch.int16))
+                   for a, layer in zip(ref, layers))
+        t_graph = time_events(torch, graph.replay, iters)
+        keys = 16 * 8 * (L + 5 * 128)
+        alg = keys * D * 2 * 2
+        out[kind] = {"ms_eager": round(t_eager * 1e3, 4), "ms_graph": round(t_graph * 1e3, 4),
+                     "tokens_per_s_graph": round(16 / t_graph, 1),
+                     "hbm_gbs_alg_graph": round(alg / t_graph / 1e9, 1),
+                     "graph_equals_eager": bool(same)}
+        del graph, layers
+        torch.cuda.empty_cache()
+    return out
 
 
 VARLEN_LENS_SEED = 9

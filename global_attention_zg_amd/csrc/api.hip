@@ -172,7 +172,12 @@ static int decode_impl(const zg_attn_params* p, const void* q, const void* k_new
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const zg::RopeTable tab = make_rope_table(p);
-  if (k_new) {
+  zg::DecodeParams dp{};
+  if (k_new && ns == 1) {  // the single-split kernel appends the token itself
+    dp.k_new = static_cast<const uint16_t*>(k_new);
+    dp.v_new = static_cast<const uint16_t*>(v_new);
+    dp.k_norm_w = k_norm_w;
+  } else if (k_new) {
     hipError_t e = zg::launch_decode_append(
         static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
         static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), seq_lens, k_norm_w,
@@ -180,7 +185,6 @@ static int decode_impl(const zg_attn_params* p, const void* q, const void* k_new
         p->rms_eps, tab, s);
     if (e != hipSuccess) return ZG_ERR_HIP;
   }
-  zg::DecodeParams dp{};
   dp.q = static_cast<const uint16_t*>(q);
   dp.k_cache = static_cast<const uint16_t*>(k_cache);
   dp.v_cache = static_cast<const uint16_t*>(v_cache);

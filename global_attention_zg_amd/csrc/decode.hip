@@ -24,6 +24,7 @@
 
 #include "zg_common.h"
 #include "zg_launch.h"
+#include "zg_norm_rope.h"
 
 namespace zg {
 
@@ -44,8 +45,12 @@ constexpr int kQsBytes = 16 * kQsStride * 2;                  // 4352
 constexpr int kQnBytes = kMaxGroup * kD * 4;                  // 4096
 constexpr int kRedOBytes = kWaves * kMaxGroup * kD * 4;       // 16384 (inside the Vt area)
 static_assert(kRedOBytes <= kVtBytes, "reduction area must fit in the V^T area");
+static_assert(16 * (kD + 2 * kMaxRopeHalf) * 4 <= kVtBytes, "append scratch must fit in the V^T area");
 
-template <bool PAGED>
+// FUSED: the launch has one split per (b, kv head), so this workgroup owns
+// the whole key range: it appends the new token itself, before reading the
+// cache, and writes the normalised, gated output instead of a partial.
+template <bool PAGED, bool FUSED>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kVtBytes + kQsBytes + kQnBytes];
   __shared__ float red_m[kWaves][16];
@@ -78,12 +83,82 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const int start = min(hi, lo + split * chunk);
   const int end = min(hi, start + chunk);
 
-  // ---- query prologue for the group's heads (RMSNorm, partial RoPE)
   const long long pos = p.pos_offset + L - 1;
-  for (int c = wv; c < grp; c += kWaves) {
-    const uint16_t* src = p.q + ((long long)b * p.Hq + g * grp + c) * kD;
-    float x0 = __uint_as_float((uint32_t)src[lane] << 16);
-    float x1 = __uint_as_float((uint32_t)src[64 + lane] << 16);
+  const int psh = p.map.page_shift;
+  // raw query rows c = wv, wv + 4 of the group (loaded up front: their
+  // latency overlaps the append) and, for the single-split epilogue, the gate
+  // values of this thread's output elements
+  float xq[2][2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = wv + kWaves * j;
+    const uint16_t* src = p.q + ((long long)b * p.Hq + g * grp + min(c, grp - 1)) * kD;
+    xq[j][0] = __uint_as_float((uint32_t)src[lane] << 16);
+    xq[j][1] = __uint_as_float((uint32_t)src[64 + lane] << 16);
+  }
+  float gpre[kMaxGroup * kD / kThreads];
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int j = 0; j < kMaxGroup * kD / kThreads; ++j) {
+      const int idx = tid + j * kThreads;
+      gpre[j] = 0.f;
+      if (p.gate && idx < grp * kD)
+        gpre[j] = __uint_as_float(
+            (uint32_t)p.gate[((long long)b * p.Hq + g * grp) * kD + idx] << 16);
+    }
+  }
+  if constexpr (FUSED) {
+    if (p.k_new) {
+      // the new key, normalised and rotated by the same row code as the
+      // append kernel, and the new value, into slot len-1 (or its ring
+      // slot); 16 lanes per row, only the first row is real.  The V^T area
+      // is free until the key loop.
+      float* xs = reinterpret_cast<float*>(smem);
+      float* cs = xs + 16 * kD;
+      float* sn = cs + 16 * kMaxRopeHalf;
+      const int lrow = tid >> 4, c16 = tid & 15;
+      const long long row = (long long)b * p.Hkv + g;
+      float x[8];
+      u32x4 vv = {0, 0, 0, 0};
+      if (lrow == 0) {
+        unpack_bf16x8(ld16(p.k_new + row * kD + 8 * c16), x);
+        vv = ld16(p.v_new + row * kD + 8 * c16);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = 0.f;
+      }
+      norm_rope_row(x, c16, p.k_norm_w, p.eps, p.rope_half, p.tab, pos, xs + lrow * kD, true,
+                    cs + lrow * kMaxRopeHalf, sn + lrow * kMaxRopeHalf, cs + lrow * kMaxRopeHalf,
+                    sn + lrow * kMaxRopeHalf);
+      if (lrow == 0) {
+        u32x4 o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+        const int slot = p.ring ? (L - 1) % p.cap : L - 1;
+        long long dst;
+        if (PAGED) {
+          const int pg = p.map.page(b, slot);
+          dst = ((((long long)pg * p.Hkv + g) << psh) + (slot & ((1 << psh) - 1))) * kD;
+        } else {
+          dst = (row * p.cap + slot) * kD;
+        }
+        st16(const_cast<uint16_t*>(p.k_cache) + dst + 8 * c16, o);
+        st16(const_cast<uint16_t*>(p.v_cache) + dst + 8 * c16, vv);
+      }
+      // The key loop below reads the slot back.  All waves of the workgroup
+      // share the CU's vector cache, so the barrier's workgroup-scope
+      // release / acquire (stores complete first) is enough; the slot's
+      // cache lines belong to this (b, kv head) alone.
+      __syncthreads();
+    }
+  }
+
+  // ---- query prologue for the group's heads (RMSNorm, partial RoPE)
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = wv + kWaves * j;
+    if (c >= grp) break;
+    const float x0 = xq[j][0], x1 = xq[j][1];
     float ss = x0 * x0 + x1 * x1;
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
@@ -118,7 +193,6 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   // (a wave's 32-key slice spans at most two pages, looked up once per
   // slice: pa for the slice's first key, pb for its last)
   const long long slab = ((long long)b * p.Hkv + g) * p.cap * kD;
-  const int psh = p.map.page_shift;
   auto row_off = [&](int key, int pa, int pb, int base) -> long long {
     if (!PAGED) return slab + (long long)key * kD;
     const int pg = (key >> psh) == (base >> psh) ? pa : pb;
@@ -236,7 +310,10 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         red_o[(wv * kMaxGroup + col) * kD + 16 * db + 4 * kg + e] = o[db][e];
   }
   __syncthreads();
-  for (int idx = tid; idx < grp * kD; idx += kThreads) {
+#pragma unroll
+  for (int j = 0; j < kMaxGroup * kD / kThreads; ++j) {
+    const int idx = tid + j * kThreads;
+    if (idx >= grp * kD) break;
     const int c = idx / kD, d = idx % kD;
     float M = -INFINITY;
 #pragma unroll
@@ -249,11 +326,19 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
       acc += f * red_o[(w2 * kMaxGroup + c) * kD + d];
       lsum += f * red_l[w2][c];
     }
-    const long long pi = ((long long)b * p.Hq + g * grp + c) * p.nsplit + split;
-    p.part_o[pi * kD + d] = acc;
-    if (d == 0) {
-      p.part_ml[2 * pi] = M;
-      p.part_ml[2 * pi + 1] = lsum;
+    if constexpr (FUSED) {
+      // what the merge computes for one split (its weight is exactly 1)
+      const long long oi = ((long long)b * p.Hq + g * grp + c) * kD + d;
+      float o = acc * (1.0f / lsum);
+      if (p.gate) o *= sigmoidf_(gpre[j]);
+      p.out[oi] = __builtin_bit_cast(uint16_t, (__bf16)o);
+    } else {
+      const long long pi = ((long long)b * p.Hq + g * grp + c) * p.nsplit + split;
+      p.part_o[pi * kD + d] = acc;
+      if (d == 0) {
+        p.part_ml[2 * pi] = M;
+        p.part_ml[2 * pi + 1] = lsum;
+      }
     }
   }
 }
@@ -291,12 +376,14 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (p.B == 0) return hipSuccess;
   const long long blocks = (long long)p.B * p.Hkv * p.nsplit;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  if (p.map.block_table)
-    hipLaunchKernelGGL(decode_split_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, p);
-  else
-    hipLaunchKernelGGL(decode_split_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                       stream, p);
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  if (p.nsplit == 1) {
+    if (p.map.block_table) hipLaunchKernelGGL((decode_split_kernel<true, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((decode_split_kernel<false, true>), grid, block, 0, stream, p);
+    return hipGetLastError();
+  }
+  if (p.map.block_table) hipLaunchKernelGGL((decode_split_kernel<true, false>), grid, block, 0, stream, p);
+  else hipLaunchKernelGGL((decode_split_kernel<false, false>), grid, block, 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(p.B * p.Hq), dim3(64), 0, stream, p);

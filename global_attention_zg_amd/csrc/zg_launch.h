@@ -88,6 +88,11 @@ struct DecodeParams {
   float scale_log2, eps;
   long long pos_offset;
   CacheMap map;             // block_table == null: contiguous slabs
+  // With a single split the split kernel is the whole step: it appends the
+  // new token (when k_new is given), attends and writes `out` itself.
+  const uint16_t* k_new;    // bf16 [B,Hkv,D] raw, or null
+  const uint16_t* v_new;    // bf16 [B,Hkv,D]
+  const float* k_norm_w;    // fp32 [D]
   RopeTable tab;
 };
 

@@ -163,6 +163,24 @@ def test_decode_equals_last_row_of_prefill(window):
     zc.compare(_f(od), _f(out[:, S - 1]), "decode vs gpu prefill last row")
 
 
+@pytest.mark.parametrize("ring,window,cap,lens", [
+    (0, 0, 300, [1, 2, 150, 300]),
+    (1, 128, 128, [1, 129, 1000]),
+])
+def test_single_split_appends_the_same_bits(ring, window, cap, lens):
+    """With one split the attention kernel appends the new token itself; the
+    cache it leaves is bit-identical to the one the separate append kernel
+    (used with several splits) writes, and both outputs meet the bar."""
+    c = dec_case(207, len(lens), 8, 2, cap)
+    o1, k1, v1 = run_gpu(c, lens, ring, window, num_splits=1)
+    o2, k2, v2 = run_gpu(c, lens, ring, window, num_splits=2)
+    assert torch.equal(k1.view(torch.int16), k2.view(torch.int16))
+    assert torch.equal(v1.view(torch.int16), v2.view(torch.int16))
+    o, _, _ = run_oracle(c, lens, ring, window)
+    zc.compare(_f(o1), o, "one split")
+    zc.compare(_f(o2), o, "two splits")
+
+
 def test_decode_deterministic():
     lens = [1000, 17, 512]
     c = dec_case(205, 3, 8, 2, 1024)

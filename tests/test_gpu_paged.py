@@ -120,7 +120,7 @@ def run_pair(c, lens, window, page_size, max_pages, num_pages, num_splits, seed)
     (256, 4, 0, [255, 256, 257, 1024]),
     (1024, 2, 0, [1, 2048]),
 ])
-@pytest.mark.parametrize("num_splits", [0, 3])
+@pytest.mark.parametrize("num_splits", [0, 1, 3])
 def test_paged_equals_contiguous_bitwise(page_size, max_pages, window, lens, num_splits):
     cap = page_size * max_pages
     c = dec_case(301, len(lens), 8, 2, cap)
