@@ -34,6 +34,8 @@ import numpy as np
 
 __all__ = [
     "bf16_bits_to_f64",
+    "linear",
+    "qkvg_proj",
     "rms_norm",
     "rope_angles",
     "apply_partial_rope",
@@ -401,6 +403,43 @@ def attention_bwd(q, k, v, gate, q_norm_w, k_norm_w, dout, *, window: int,
         dwk += gk
     return {"dq": dq, "dk": dk, "dv": dv, "dgate": dgate,
             "dq_norm_w": dwq, "dk_norm_w": dwk}
+
+
+# ---------------------------------------------------------------------------
+# The projections on either side of the attention
+# ([RB] 核心方法 and [SB] 🏗️ 架构: hidden size 4096, 32 query / 8 KV heads of
+# 128 dims; [SB] 🏗️ 架构: the local output is multiplied by a sigmoid gate)
+# ---------------------------------------------------------------------------
+def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """y = x W^T for a weight stored [out_features, in_features].
+
+    Reading: the pages name the layer sizes only; a bias-free linear map with
+    the weight stored output-major is the plainest form of a Transformer
+    projection.  x [T, in], w [out, in] -> y [T, out], in float64.
+    """
+    return np.asarray(x, dtype=np.float64) @ np.asarray(w, dtype=np.float64).T
+
+
+def qkvg_proj(x: np.ndarray, w: np.ndarray, n_q_heads: int, n_kv_heads: int,
+              head_dim: int, gated: bool):
+    """The fused input projection of one attention layer.
+
+    Reading: the rows of w stack W_q (n_q_heads * head_dim rows), W_k and
+    W_v (n_kv_heads * head_dim rows each) and, on a gated layer, W_g
+    (n_q_heads * head_dim rows: the gate has the output's shape, since it
+    multiplies the attention output elementwise).  Column h * head_dim + d of
+    each part is head h, dim d.  Returns (q [T,Hq,D], k [T,Hkv,D], v, g or
+    None).
+    """
+    y = linear(x, w)
+    T = y.shape[0]
+    nq, nk = n_q_heads * head_dim, n_kv_heads * head_dim
+    assert y.shape[1] == 2 * nq + 2 * nk if gated else nq + 2 * nk
+    q = y[:, :nq].reshape(T, n_q_heads, head_dim)
+    k = y[:, nq:nq + nk].reshape(T, n_kv_heads, head_dim)
+    v = y[:, nq + nk:nq + 2 * nk].reshape(T, n_kv_heads, head_dim)
+    g = y[:, nq + 2 * nk:].reshape(T, n_q_heads, head_dim) if gated else None
+    return q, k, v, g
 
 
 # ---------------------------------------------------------------------------
