@@ -71,6 +71,10 @@ def _load():
     lib.zg_attn_decode_paged.restype = i
     lib.zg_attn_kv_write_pages.argtypes = [P, vp, vp, vp, vp, i, vp, i, i, vp]
     lib.zg_attn_kv_write_pages.restype = i
+    lib.zg_linear.argtypes = [i, i, i, vp, vp, vp, vp]
+    lib.zg_linear.restype = i
+    lib.zg_qkvg_proj.argtypes = [P, i, vp, vp, vp, vp, vp, vp, vp]
+    lib.zg_qkvg_proj.restype = i
     lib.zg_attn_bwd_workspace_size.argtypes = [P]
     lib.zg_attn_bwd_workspace_size.restype = sz
     lib.zg_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -87,7 +91,7 @@ EXPORTED = ("zg_attn_fwd_workspace_size", "zg_attn_fwd", "zg_attn_fwd_varlen_wor
             "zg_attn_fwd_varlen", "zg_attn_decode_num_splits",
             "zg_attn_decode_workspace_size", "zg_attn_decode", "zg_attn_kv_write_pages",
             "zg_attn_decode_paged", "zg_attn_bwd_workspace_size", "zg_attn_bwd",
-            "zg_attn_strerror")
+            "zg_linear", "zg_qkvg_proj", "zg_attn_strerror")
 
 
 def library_path() -> str:
@@ -287,3 +291,31 @@ def zg_attn_decode_paged(q, k_new, v_new, k_pages, v_pages, block_table, seq_len
                                    _ptr(workspace), ws_bytes, _stream(stream))
     _check(st)
     return out
+
+
+def zg_linear(x, w, out=None, stream=None):
+    """y = x w^T: x [M,K], w [N,K] bf16 on the device -> y [M,N] bf16."""
+    M, K = x.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=x.dtype, device=x.device)
+    _check(_lib.zg_linear(M, N, K, _ptr(x), _ptr(w), _ptr(out), _stream(stream)))
+    return out
+
+
+def zg_qkvg_proj(x, w, n_q_heads, n_kv_heads, gated, *, q=None, k=None, v=None, gate=None,
+                 stream=None):
+    """x [T,hidden] bf16, w [Nw,hidden] stacking W_q, W_k, W_v (and W_g when
+    gated).  Returns (q [T,Hq,128], k [T,Hkv,128], v, gate or None)."""
+    T, hidden = x.shape
+    D = 128
+    p = make_params(1, T, n_q_heads, n_kv_heads, D)
+    dev = x.device
+    q = torch.empty((T, n_q_heads, D), dtype=x.dtype, device=dev) if q is None else q
+    k = torch.empty((T, n_kv_heads, D), dtype=x.dtype, device=dev) if k is None else k
+    v = torch.empty((T, n_kv_heads, D), dtype=x.dtype, device=dev) if v is None else v
+    if gated and gate is None:
+        gate = torch.empty((T, n_q_heads, D), dtype=x.dtype, device=dev)
+    _check(_lib.zg_qkvg_proj(ctypes.byref(p), hidden, _ptr(x), _ptr(w), _ptr(q), _ptr(k),
+                             _ptr(v), _ptr(gate if gated else None), _stream(stream)))
+    return q, k, v, (gate if gated else None)

@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libzgattn.so")
-SOURCES = ["prologue.hip", "flash_fwd.hip", "decode.hip", "backward.hip", "api.hip"]
+SOURCES = ["prologue.hip", "flash_fwd.hip", "decode.hip", "backward.hip", "gemm.hip", "api.hip"]
 ARCH = "gfx950"
 
 

@@ -415,4 +415,58 @@ int zg_attn_kv_write_pages(const zg_attn_params* p, const void* k_prime, const v
       p->n_kv_heads, map, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int zg_linear(int M, int N, int K, const void* x, const void* w, void* y, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return ZG_ERR_INVALID;
+  if (M == 0 || N == 0) return ZG_OK;
+  if (N % 256 || K % 32 || K == 0) return ZG_ERR_UNSUPPORTED;
+  if ((long long)K * 2 * 256 > 0x7fffffffLL) return ZG_ERR_UNSUPPORTED;
+  if (!x || !w || !y) return ZG_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y)) return ZG_ERR_INVALID;
+  zg::GemmParams gp{};
+  gp.a = static_cast<const uint16_t*>(x);
+  gp.b = static_cast<const uint16_t*>(w);
+  gp.M = M;
+  gp.N = N;
+  gp.K = K;
+  gp.lda = K;
+  gp.ldb = K;
+  gp.seg[0] = zg::GemmSeg{static_cast<uint16_t*>(y), 0, N};
+  gp.nseg = 1;
+  return hip_status(zg::launch_gemm_bf16_tn(gp, reinterpret_cast<hipStream_t>(stream)));
+}
+
+int zg_qkvg_proj(const zg_attn_params* p, int hidden, const void* x, const void* w, void* q,
+                 void* k, void* v, void* gate, void* stream) {
+  int st = check_params(p);
+  if (st != ZG_OK) return st;
+  if (hidden < 0) return ZG_ERR_INVALID;
+  const long long T = (long long)p->batch * p->seqlen;
+  if (T == 0) return ZG_OK;
+  if (T > 0x7fffffffLL) return ZG_ERR_UNSUPPORTED;
+  const int nq = p->n_q_heads * kD, nk = p->n_kv_heads * kD;
+  if (nk % 256 || hidden % 32 || hidden == 0) return ZG_ERR_UNSUPPORTED;
+  if ((long long)hidden * 2 * 256 > 0x7fffffffLL) return ZG_ERR_UNSUPPORTED;
+  if (!x || !w || !q || !k || !v) return ZG_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(q) || !aligned16(k) || !aligned16(v) ||
+      (gate && !aligned16(gate)))
+    return ZG_ERR_INVALID;
+  zg::GemmParams gp{};
+  gp.a = static_cast<const uint16_t*>(x);
+  gp.b = static_cast<const uint16_t*>(w);
+  gp.M = (int)T;
+  gp.N = 2 * nk + (gate ? 2 * nq : nq);
+  gp.K = hidden;
+  gp.lda = hidden;
+  gp.ldb = hidden;
+  gp.seg[0] = zg::GemmSeg{static_cast<uint16_t*>(q), 0, nq};
+  gp.seg[1] = zg::GemmSeg{static_cast<uint16_t*>(k), nq, nk};
+  gp.seg[2] = zg::GemmSeg{static_cast<uint16_t*>(v), nq + nk, nk};
+  gp.nseg = 3;
+  if (gate) {
+    gp.seg[3] = zg::GemmSeg{static_cast<uint16_t*>(gate), nq + 2 * nk, nq};
+    gp.nseg = 4;
+  }
+  return hip_status(zg::launch_gemm_bf16_tn(gp, reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -1,0 +1,197 @@
+// The projections on either side of the attention: y = x W^T with bf16
+// operands, fp32 accumulation on MFMA and bf16 results.
+//
+// Page "ZGCM-1:面向数学与智能体搜索的全开源高效基础模型" (paper.rainbus.top),
+// section 核心方法, and page "7B 打 235B？中关村学院把'小模型怎么活'这道题答成了
+// 一份全开源配方" (shibing624.github.io), section 🏗️ 架构: hidden size 4096,
+// 32 query and 8 KV heads of 128 dims, and a sigmoid gate of the output's
+// shape on the sliding-window layers.  The input projection of a layer is one
+// GEMM against the stacked weight [W_q; W_k; W_v; W_g] (10240 x 4096 on a
+// gated layer) whose epilogue writes q, k, v and the gate logits straight
+// into the four token-major tensors the attention kernels read; the output
+// projection is the same kernel with one output.
+//
+// Both operands are K-contiguous ("TN"): x is [M, K] and W is [N, K], row
+// major, which is exactly the per-lane layout of both MFMA operands (8
+// consecutive k of one row per lane).
+//
+// Workgroup tile 256 x 256, K step 32, four-stage LDS ring (128 KB), eight
+// waves in a 2 (M) x 4 (N) grid, each wave 128 x 64 = 4 x 2 blocks of
+// v_mfma_f32_32x32x16_bf16.  Tiles move global -> LDS with untracked
+// global_load_lds_dwordx4 copies, three K steps ahead; LDS rows are 64 bytes
+// with their four 16-byte chunks XOR-swizzled by (row / 4) % 4, which makes
+// every MFMA operand read conflict-free under the 64-bank LDS.
+
+#include "zg_common.h"
+#include "zg_launch.h"
+#include "zg_lds.h"
+
+namespace zg {
+
+namespace {
+
+constexpr int kGBM = 256, kGBN = 256, kGBK = 32;
+constexpr int kGStages = 4;
+constexpr int kGWaves = 8;
+constexpr int kGThreads = 64 * kGWaves;
+constexpr int kGRowBytes = kGBK * 2;                  // 64
+constexpr int kGTileA = kGBM * kGRowBytes;            // 16384
+constexpr int kGTileB = kGBN * kGRowBytes;            // 16384
+constexpr int kGStageBytes = kGTileA + kGTileB;       // 32768
+constexpr int kGSmem = kGStages * kGStageBytes;       // 131072
+constexpr int kGCopies = 4;                           // copies per wave per K step
+static_assert(kGTileA / 1024 == 2 * kGWaves && kGTileB / 1024 == 2 * kGWaves,
+              "each wave copies two 1 KB blocks of A and two of B per K step");
+
+// Chunk swizzle of a 64-byte LDS row.
+__device__ __forceinline__ int gswz(int row) { return (row >> 2) & 3; }
+
+__global__ __launch_bounds__(kGThreads, 1) void gemm_bf16_tn_kernel(GemmParams p) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kGSmem];
+  lds_u8* smem = (lds_u8*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;
+  const int wvu = __builtin_amdgcn_readfirstlane(wv);
+  const int wm = wvu & 1;   // M half of the tile
+  const int wn = wvu >> 1;  // N quarter of the tile
+
+  // ---- tile of this workgroup.  Consecutive workgroup ids go to different
+  // XCDs; each XCD is given a contiguous range of tiles, walked in groups of
+  // kGroupM tile rows so that the workgroups resident on one XCD share A
+  // panels and W panels in its L2.
+  const int ntiles = p.tiles_m * p.tiles_n;
+  const int bid = blockIdx.x;
+  int lin = bid;
+  if (ntiles % 8 == 0) lin = (bid % 8) * (ntiles / 8) + bid / 8;
+  constexpr int kGroupM = 4;
+  const int per_group = kGroupM * p.tiles_n;
+  const int grp = lin / per_group;
+  const int first_m = grp * kGroupM;
+  const int gsize = min(p.tiles_m - first_m, kGroupM);
+  const int tm = first_m + (lin % per_group) % gsize;
+  const int tn = (lin % per_group) / gsize;
+  const int m0 = tm * kGBM;
+  const int n0 = tn * kGBN;
+
+  // ---- copies: block j (0, 1) of this wave covers rows 16 (2 wv + j) ..
+  // +15 of the A (resp. W) tile; lane L writes physical chunk L % 4 of row
+  // L / 4 of the block and fetches the logical chunk stored there.
+  const unsigned char* abase = reinterpret_cast<const unsigned char*>(p.a) +
+                               (long long)m0 * p.lda * 2;
+  const unsigned char* bbase = reinterpret_cast<const unsigned char*>(p.b) +
+                               (long long)n0 * p.ldb * 2;
+  uint32_t aoff[2], boff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 16 * (2 * wvu + j) + (lane >> 2);
+    const int lc = (lane & 3) ^ gswz(row);
+    const int arow = min(row, p.M - 1 - m0);  // rows past M repeat row M-1
+    aoff[j] = (uint32_t)(arow * p.lda * 2 + lc * 16);
+    boff[j] = (uint32_t)(row * p.ldb * 2 + lc * 16);
+  }
+  auto issue = [&](int ks, int stg) {
+    const unsigned char* ak = abase + (long long)ks * kGBK * 2;
+    const unsigned char* bk = bbase + (long long)ks * kGBK * 2;
+    const uint32_t la = lds_addr(smem + stg * kGStageBytes) + (2 * wvu) * 1024;
+    const uint32_t lb = la + kGTileA;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16_s(ak, aoff[j], la + j * 1024);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16_s(bk, boff[j], lb + j * 1024);
+  };
+
+  // ---- operand reads: lane l reads row l % 32 of a 32-row block, logical
+  // chunk 2 kk + l / 32 (kk = 0, 1: the two 16-k halves of the K step)
+  const int r32 = lane & 31;
+  const int hsel = lane >> 5;
+  uint32_t ard[4][2], brd[2][2];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+    const int row = wm * 128 + mb * 32 + r32;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      ard[mb][kk] = row * kGRowBytes + (((2 * kk + hsel) ^ gswz(row)) << 4);
+  }
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int row = wn * 64 + nb * 32 + r32;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+      brd[nb][kk] = kGTileA + row * kGRowBytes + (((2 * kk + hsel) ^ gswz(row)) << 4);
+  }
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{};
+
+  const int nk = p.K / kGBK;
+#pragma unroll
+  for (int s = 0; s < kGStages - 1; ++s)
+    if (s < nk) issue(s, s);
+
+  for (int ks = 0; ks < nk; ++ks) {
+    // step ks has landed for every wave; the groups of steps ks+1, ks+2 may
+    // still fly.  Every wave's reads of step ks-1 are done (lgkmcnt(0)), so
+    // its stage can be refilled.
+    if (ks + 2 < nk) sync_tiles<2 * kGCopies>();
+    else if (ks + 1 < nk) sync_tiles<kGCopies>();
+    else sync_tiles<0>();
+    if (ks + kGStages - 1 < nk) issue(ks + kGStages - 1, (ks + kGStages - 1) % kGStages);
+    const lds_u8* st = smem + (ks % kGStages) * kGStageBytes;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 af[4], bfr[2];
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) af[mb] = lds_read_b128(st + ard[mb][kk]);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) bfr[nb] = lds_read_b128(st + brd[nb][kk]);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+    }
+  }
+
+  // ---- epilogue: the N tile lies in one output segment; register r of
+  // block (mb, nb) holds row 8 (r/4) + 4 (l/32) + r%4, column l % 32
+  int sg = 0;
+#pragma unroll
+  for (int i = 1; i < kGemmMaxSegs; ++i)
+    if (i < p.nseg && n0 >= p.seg[i].n0) sg = i;
+  uint16_t* out = p.seg[sg].ptr;
+  const long long ld = p.seg[sg].ld;
+  const int ncol0 = n0 - p.seg[sg].n0 + wn * 64 + r32;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = m0 + wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * hsel + (r & 3);
+      if (row < p.M) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          out[row * ld + ncol0 + nb * 32] = __builtin_bit_cast(uint16_t, (__bf16)acc[mb][nb][r]);
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_bf16_tn(GemmParams p, hipStream_t stream) {
+  if (p.M == 0) return hipSuccess;
+  if (p.N % kGBN || p.K % kGBK || p.K < kGBK || p.nseg < 1 || p.nseg > kGemmMaxSegs)
+    return hipErrorInvalidValue;
+  p.tiles_m = (p.M + kGBM - 1) / kGBM;
+  p.tiles_n = p.N / kGBN;
+  const long long blocks = (long long)p.tiles_m * p.tiles_n;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(gemm_bf16_tn_kernel, dim3((unsigned)blocks), dim3(kGThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace zg

@@ -99,6 +99,28 @@ struct DecodeParams {
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 
 
+// Projections: C = A B^T with A [M, K] and B [N, K] bf16 row major (row
+// strides lda, ldb elements); output columns [seg[i].n0, seg[i+1].n0) go to
+// seg[i].ptr with row stride seg[i].ld.  Segment starts are sorted and
+// multiples of 256; N is a multiple of 256 and K of 32.
+constexpr int kGemmMaxSegs = 4;
+struct GemmSeg {
+  uint16_t* ptr;
+  int n0;
+  int ld;
+};
+struct GemmParams {
+  const uint16_t* a;
+  const uint16_t* b;
+  int M, N, K;
+  int lda, ldb;
+  GemmSeg seg[kGemmMaxSegs];
+  int nseg;
+  int tiles_m, tiles_n;  // set by the launcher
+};
+
+hipError_t launch_gemm_bf16_tn(GemmParams p, hipStream_t stream);
+
 // Training backward.  Q' / K' are the normalised + rotated rows recomputed by
 // launch_k_prologue; dO = dY * sigmoid(G) (dY itself on an ungated layer).
 struct BwdParams {

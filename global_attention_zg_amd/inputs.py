@@ -20,6 +20,7 @@ CHUNK = 1 << 22
 # tensor ids
 T_Q, T_K, T_V, T_GATE, T_GQ, T_GK, T_KCACHE, T_VCACHE, T_KNEW, T_VNEW = range(10)
 T_DOUT = 10  # upstream gradient dL/dout of the training backward
+T_X, T_W = 11, 12  # layer input (hidden states) and a projection weight
 
 
 def _threads() -> int:
@@ -66,6 +67,20 @@ def normal_bf16_bits(key, total: int, start: int = 0, stop: int | None = None,
         with ThreadPoolExecutor(_threads()) as ex:
             list(ex.map(work, range(c0, c1)))
     return res
+
+
+def scaled_normal_bf16_bits(key, total: int, scale: float) -> np.ndarray:
+    """bf16 bits of N(0, scale^2) values: the float32 draws of ``key`` times
+    ``scale``, rounded once to bf16 (a projection weight with fan-in n uses
+    scale = n ** -0.5, so that its outputs are again of unit variance)."""
+    out = np.empty(total, dtype=np.uint16)
+    for c in range((total + CHUNK - 1) // CHUNK):
+        lo = c * CHUNK
+        ln = min(CHUNK, total - lo)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_BASE, *key, c])))
+        out[lo:lo + ln] = _round_bf16_bits(g.standard_normal(ln, dtype=np.float32)
+                                           * np.float32(scale))
+    return out
 
 
 def norm_weight(key, D: int) -> np.ndarray:

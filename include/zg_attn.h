@@ -183,6 +183,32 @@ int zg_attn_decode_paged(const zg_attn_params* p,
                          void* out, int num_splits,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- The projections on either side of the attention ----------------------
+ * Page "ZGCM-1:面向数学与智能体搜索的全开源高效基础模型", section 核心方法, and
+ * page "7B 打 235B？…", section 🏗️ 架构: hidden size 4096 feeding 32 query
+ * and 8 KV heads of 128 dims; the sliding-window output is multiplied by a
+ * sigmoid gate of its own shape, whose logits come from the layer input
+ * (reading: a linear projection, since the gate's formula did not survive
+ * on the page).  Weights are stored [out_features, in_features] (a bias-free
+ * linear map y = x W^T); bf16 operands and results, fp32 accumulation.
+ * Neither call allocates or needs a workspace. */
+
+/* y bf16 [M,N] = x bf16 [M,K] . w bf16 [N,K]^T (the output projection is
+ * M = tokens, N = hidden, K = n_q_heads * head_dim).  N must be a multiple of
+ * 256 and K a positive multiple of 32 (else ZG_ERR_UNSUPPORTED); M is any
+ * size >= 0.  M == 0 or N == 0 is valid and launches nothing. */
+int zg_linear(int M, int N, int K, const void* x, const void* w, void* y, void* stream);
+
+/* The fused input projection of one layer for T = p->batch * p->seqlen
+ * tokens: x bf16 [T,hidden]; w bf16 [Nw,hidden] stacking W_q (Hq*D rows),
+ * W_k and W_v (Hkv*D rows each) and, when gate != NULL, W_g (Hq*D rows), so
+ * Nw = 2*Hkv*D + Hq*D (+ Hq*D).  One GEMM writes q bf16 [T,Hq,D], k and v
+ * bf16 [T,Hkv,D] and gate bf16 [T,Hq,D]: the layouts zg_attn_fwd reads.
+ * Requires Hkv*D a multiple of 256 (even n_kv_heads) and hidden a positive
+ * multiple of 32 (else ZG_ERR_UNSUPPORTED). */
+int zg_qkvg_proj(const zg_attn_params* p, int hidden, const void* x, const void* w,
+                 void* q, void* k, void* v, void* gate, void* stream);
+
 /* Bytes of device workspace zg_attn_bwd needs (recomputed Q' and K', dO,
  * per-row LSE*log2(e) and rowsum(dY*Y), fp32 dL/dQ' and dL/dK', and the
  * partial sums of the two weight gradients); 0 for an invalid p. */

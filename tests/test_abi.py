@@ -22,7 +22,7 @@ def bd():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(zg_attn_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(zg_[a-z_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
@@ -269,3 +269,25 @@ def test_fwd_varlen_workspace_and_rejects(bd):
     assert _fwd_varlen(bd, p, 0, cu=FAKE) == bd.ZG_OK
     p.n_kv_heads = 3
     assert _fwd_varlen(bd, p, 5000, **full) == bd.ZG_ERR_INVALID
+
+
+def test_projection_argument_rules(bd):
+    lin = bd._lib.zg_linear
+    assert lin(0, 256, 64, None, None, None, None) == bd.ZG_OK          # nothing to do
+    assert lin(5, 0, 64, None, None, None, None) == bd.ZG_OK
+    assert lin(-1, 256, 64, FAKE, FAKE, FAKE, None) == bd.ZG_ERR_INVALID
+    assert lin(5, 200, 64, FAKE, FAKE, FAKE, None) == bd.ZG_ERR_UNSUPPORTED  # N % 256
+    assert lin(5, 256, 48, FAKE, FAKE, FAKE, None) == bd.ZG_ERR_UNSUPPORTED  # K % 32
+    assert lin(5, 256, 64, None, FAKE, FAKE, None) == bd.ZG_ERR_INVALID
+    assert lin(5, 256, 64, FAKE, FAKE, FAKE + 8, None) == bd.ZG_ERR_INVALID
+    proj = bd._lib.zg_qkvg_proj
+    p = bd.make_params(2, 100, 32, 8, 128)
+    args = [FAKE] * 5
+    assert proj(ctypes.byref(p), 4096, None, *args[1:], None, None) == bd.ZG_ERR_INVALID
+    assert proj(ctypes.byref(p), 4010, *args, None, None) == bd.ZG_ERR_UNSUPPORTED  # hidden % 32
+    assert proj(ctypes.byref(p), 4096, *args[:4], None, None, None) == bd.ZG_ERR_INVALID  # no v
+    assert proj(ctypes.byref(p), 4096, *args, FAKE + 4, None) == bd.ZG_ERR_INVALID  # gate
+    p1 = bd.make_params(2, 100, 4, 1, 128)   # Hkv * D = 128: not a whole 256-column tile
+    assert proj(ctypes.byref(p1), 4096, *args, None, None) == bd.ZG_ERR_UNSUPPORTED
+    p0 = bd.make_params(0, 100, 32, 8, 128)
+    assert proj(ctypes.byref(p0), 4096, None, None, None, None, None, None, None) == bd.ZG_OK
