@@ -210,7 +210,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only",
                     choices=["swa4k", "global16k", "decode", "decode_block", "block_global", "bwd",
-                             "varlen"],
+                             "varlen", "proj"],
                     default=None, help="time one workload only (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="with --only: first run a plain 1 GiB device copy, the reference "
@@ -338,6 +338,8 @@ def run_components(torch, bd, only, iters):
         comps.update(decode_components(torch, bd, max(1, iters // 2)))
     if only in (None, "decode", "decode_block"):
         comps.update(decode_block_components(torch, bd, max(1, iters // 2)))
+    if only in (None, "proj"):
+        comps.update(proj_components(torch, bd, max(1, iters // 2)))
     if only in (None, "varlen"):
         comps.update(varlen_components(torch, bd, max(1, iters // 2)))
     if only in (None, "bwd"):
@@ -423,6 +425,43 @@ def decode_block_components(torch, bd, iters):
                      "hbm_gbs_alg_graph": round(alg / t_graph / 1e9, 1),
                      "graph_equals_eager": bool(same)}
         del graph, layers
+        torch.cuda.empty_cache()
+    return out
+
+
+def proj_components(torch, bd, iters):
+    """The projections around the attention at the model's sizes (hidden
+    4096, 32/8 heads of 128): the gated layer's fused q/k/v/gate input
+    projection (N 10240) and the output projection (N 4096), at 16K and 64K
+    tokens."""
+    from global_attention_zg_amd import inputs
+    out = {}
+    hidden, Hq, Hkv = 4096, 32, 8
+    for T in (16384, 65536):
+        x = dev_tensor(torch, (11, T, inputs.T_X), (T, hidden))
+        for kind, N in (("qkvg", 2 * Hkv * D + 2 * Hq * D), ("o", hidden)):
+            name = f"proj_{kind}_{T // 1024}k"
+            log(f"component: {name}")
+            w = dev_tensor(torch, (11, N, inputs.T_W), (N, hidden))
+            if kind == "qkvg":
+                q = torch.empty((T, Hq, D), dtype=torch.bfloat16, device="cuda")
+                k = torch.empty((T, Hkv, D), dtype=torch.bfloat16, device="cuda")
+                v = torch.empty_like(k)
+                g = torch.empty_like(q)
+                fn = lambda: bd.zg_qkvg_proj(x, w, Hq, Hkv, True, q=q, k=k, v=v,  # noqa: E731
+                                             gate=g)
+            else:
+                y = torch.empty((T, hidden), dtype=torch.bfloat16, device="cuda")
+                fn = lambda: bd.zg_linear(x, w, out=y)  # noqa: E731
+            for _ in range(2):
+                fn()
+            t = time_events(torch, fn, iters)
+            flops = 2.0 * T * N * hidden
+            out[name] = {"ms": round(t * 1e3, 4), "tflops": round(flops / t / 1e12, 1),
+                         "frac_mfma": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "M": T, "N": N, "K": hidden}
+            del w
+        del x
         torch.cuda.empty_cache()
     return out
 

@@ -30,24 +30,44 @@ namespace zg {
 
 namespace {
 
-constexpr int kGBM = 256, kGBN = 256, kGBK = 32;
-constexpr int kGStages = 4;
-constexpr int kGWaves = 8;
-constexpr int kGThreads = 64 * kGWaves;
-constexpr int kGRowBytes = kGBK * 2;                  // 64
-constexpr int kGTileA = kGBM * kGRowBytes;            // 16384
-constexpr int kGTileB = kGBN * kGRowBytes;            // 16384
-constexpr int kGStageBytes = kGTileA + kGTileB;       // 32768
-constexpr int kGSmem = kGStages * kGStageBytes;       // 131072
-constexpr int kGCopies = 4;                           // copies per wave per K step
-static_assert(kGTileA / 1024 == 2 * kGWaves && kGTileB / 1024 == 2 * kGWaves,
-              "each wave copies two 1 KB blocks of A and two of B per K step");
+constexpr int kGBM = 256, kGBN = 256;
 
-// Chunk swizzle of a 64-byte LDS row.
-__device__ __forceinline__ int gswz(int row) { return (row >> 2) & 3; }
+// K step BK (32 or 64) and ring depth: BK * 2 bytes per LDS row, rows of A
+// then W per stage.  A 1 KB copy covers 1024 / (2 BK) rows.
+template <int BK, int W> struct GCfg {
+  static constexpr int kRowBytes = BK * 2;
+  static constexpr int kChunks = kRowBytes / 16;            // 16-byte chunks per row
+  static constexpr int kStages = BK == 32 ? 4 : 2;
+  static constexpr int kTileA = kGBM * kRowBytes;
+  static constexpr int kTileB = kGBN * kRowBytes;
+  static constexpr int kStageBytes = kTileA + kTileB;
+  static constexpr int kSmem = kStages * kStageBytes;     // 131072
+  static constexpr int kBlocksPerWave = kTileA / 1024 / W;  // per operand
+  static constexpr int kCopies = 2 * kBlocksPerWave;
+  static constexpr int kRowsPerCopy = 1024 / kRowBytes;
+  // chunk swizzle: rows that share a 256-byte bank window, and successive
+  // windows, get distinct chunk positions
+  __device__ static int swz(int row) {
+    return BK == 32 ? (row >> 2) & 3 : (row >> 1) & 7;
+  }
+};
 
-__global__ __launch_bounds__(kGThreads, 1) void gemm_bf16_tn_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kGSmem];
+// W waves in a 2 (M) x W/2 (N) grid: a wave computes 128 x 512/W, i.e.
+// 4 x NB blocks of 32 x 32 (W = 8: two waves per SIMD, 128 accumulator
+// registers each; W = 4: one wave per SIMD, 256, which the compiler may keep
+// in the accumulation registers).
+template <int BK, int W>
+__global__ __launch_bounds__(64 * W, 1) void gemm_bf16_tn_kernel(GemmParams p) {
+  using C = GCfg<BK, W>;
+  constexpr int NB = 16 / W;  // 32-column blocks per wave: 256 / (W / 2) columns
+  static_assert(NB * 32 * (W / 2) == kGBN && 4 * 32 * 2 == kGBM, "waves must tile 256 x 256");
+  constexpr int kGStages = C::kStages;
+  constexpr int kGStageBytes = C::kStageBytes;
+  constexpr int kGTileA = C::kTileA;
+  constexpr int kGRowBytes = C::kRowBytes;
+  constexpr int kGCopies = C::kCopies;
+  constexpr int BPW = C::kBlocksPerWave;
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[C::kSmem];
   lds_u8* smem = (lds_u8*)smem_raw;
 
   const int tid = threadIdx.x;
@@ -75,84 +95,86 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_bf16_tn_kernel(GemmParams p
   const int m0 = tm * kGBM;
   const int n0 = tn * kGBN;
 
-  // ---- copies: block j (0, 1) of this wave covers rows 16 (2 wv + j) ..
-  // +15 of the A (resp. W) tile; lane L writes physical chunk L % 4 of row
-  // L / 4 of the block and fetches the logical chunk stored there.
+  // ---- copies: block j of this wave covers rows R (BPW wv + j) .. +R-1 of
+  // the A (resp. W) tile (R rows per 1 KB); lane L writes physical chunk
+  // L % chunks of row L / chunks of the block and fetches the logical chunk
+  // stored there.
   const unsigned char* abase = reinterpret_cast<const unsigned char*>(p.a) +
                                (long long)m0 * p.lda * 2;
   const unsigned char* bbase = reinterpret_cast<const unsigned char*>(p.b) +
                                (long long)n0 * p.ldb * 2;
-  uint32_t aoff[2], boff[2];
+  uint32_t aoff[BPW], boff[BPW];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = 16 * (2 * wvu + j) + (lane >> 2);
-    const int lc = (lane & 3) ^ gswz(row);
+  for (int j = 0; j < BPW; ++j) {
+    const int row = C::kRowsPerCopy * (BPW * wvu + j) + lane / C::kChunks;
+    const int lc = (lane % C::kChunks) ^ C::swz(row);
     const int arow = min(row, p.M - 1 - m0);  // rows past M repeat row M-1
     aoff[j] = (uint32_t)(arow * p.lda * 2 + lc * 16);
     boff[j] = (uint32_t)(row * p.ldb * 2 + lc * 16);
   }
   auto issue = [&](int ks, int stg) {
-    const unsigned char* ak = abase + (long long)ks * kGBK * 2;
-    const unsigned char* bk = bbase + (long long)ks * kGBK * 2;
-    const uint32_t la = lds_addr(smem + stg * kGStageBytes) + (2 * wvu) * 1024;
+    const unsigned char* ak = abase + (long long)ks * BK * 2;
+    const unsigned char* bk = bbase + (long long)ks * BK * 2;
+    const uint32_t la = lds_addr(smem + stg * kGStageBytes) + (BPW * wvu) * 1024;
     const uint32_t lb = la + kGTileA;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) dma16_s(ak, aoff[j], la + j * 1024);
+    for (int j = 0; j < BPW; ++j) dma16_s(ak, aoff[j], la + j * 1024);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) dma16_s(bk, boff[j], lb + j * 1024);
+    for (int j = 0; j < BPW; ++j) dma16_s(bk, boff[j], lb + j * 1024);
   };
 
   // ---- operand reads: lane l reads row l % 32 of a 32-row block, logical
-  // chunk 2 kk + l / 32 (kk = 0, 1: the two 16-k halves of the K step)
+  // chunk 2 kk + l / 32 (kk: the 16-k slices of the K step)
   const int r32 = lane & 31;
   const int hsel = lane >> 5;
-  uint32_t ard[4][2], brd[2][2];
+  constexpr int KK = BK / 16;
+  uint32_t ard[4][KK], brd[NB][KK];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     const int row = wm * 128 + mb * 32 + r32;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-      ard[mb][kk] = row * kGRowBytes + (((2 * kk + hsel) ^ gswz(row)) << 4);
+    for (int kk = 0; kk < KK; ++kk)
+      ard[mb][kk] = row * kGRowBytes + (((2 * kk + hsel) ^ C::swz(row)) << 4);
   }
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int row = wn * 64 + nb * 32 + r32;
+  for (int nb = 0; nb < NB; ++nb) {
+    const int row = wn * 32 * NB + nb * 32 + r32;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
-      brd[nb][kk] = kGTileA + row * kGRowBytes + (((2 * kk + hsel) ^ gswz(row)) << 4);
+    for (int kk = 0; kk < KK; ++kk)
+      brd[nb][kk] = kGTileA + row * kGRowBytes + (((2 * kk + hsel) ^ C::swz(row)) << 4);
   }
 
-  f32x16 acc[4][2];
+  f32x16 acc[4][NB];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = f32x16{};
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x16{};
 
-  const int nk = p.K / kGBK;
+  const int nk = p.K / BK;
 #pragma unroll
   for (int s = 0; s < kGStages - 1; ++s)
     if (s < nk) issue(s, s);
 
   for (int ks = 0; ks < nk; ++ks) {
-    // step ks has landed for every wave; the groups of steps ks+1, ks+2 may
-    // still fly.  Every wave's reads of step ks-1 are done (lgkmcnt(0)), so
-    // its stage can be refilled.
-    if (ks + 2 < nk) sync_tiles<2 * kGCopies>();
-    else if (ks + 1 < nk) sync_tiles<kGCopies>();
+    // step ks has landed for every wave; the groups of the following steps
+    // (up to kGStages - 2 of them) may still fly.  Every wave's reads of step
+    // ks-1 are done (lgkmcnt(0)), so its stage can be refilled.
+    if (kGStages >= 4 && ks + 2 < nk) sync_tiles<2 * kGCopies>();
+    else if (kGStages >= 3 && ks + 1 < nk) sync_tiles<kGCopies>();
     else sync_tiles<0>();
     if (ks + kGStages - 1 < nk) issue(ks + kGStages - 1, (ks + kGStages - 1) % kGStages);
     const lds_u8* st = smem + (ks % kGStages) * kGStageBytes;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      bf16x8 af[4], bfr[2];
+    for (int kk = 0; kk < KK; ++kk) {
+      bf16x8 af[4], bfr[NB];
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) af[mb] = lds_read_b128(st + ard[mb][kk]);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) bfr[nb] = lds_read_b128(st + brd[nb][kk]);
+      for (int nb = 0; nb < NB; ++nb) bfr[nb] = lds_read_b128(st + brd[nb][kk]);
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
     }
   }
@@ -165,7 +187,7 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_bf16_tn_kernel(GemmParams p
     if (i < p.nseg && n0 >= p.seg[i].n0) sg = i;
   uint16_t* out = p.seg[sg].ptr;
   const long long ld = p.seg[sg].ld;
-  const int ncol0 = n0 - p.seg[sg].n0 + wn * 64 + r32;
+  const int ncol0 = n0 - p.seg[sg].n0 + wn * 32 * NB + r32;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
@@ -173,24 +195,30 @@ __global__ __launch_bounds__(kGThreads, 1) void gemm_bf16_tn_kernel(GemmParams p
       const int row = m0 + wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * hsel + (r & 3);
       if (row < p.M) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
           out[row * ld + ncol0 + nb * 32] = __builtin_bit_cast(uint16_t, (__bf16)acc[mb][nb][r]);
       }
     }
   }
 }
 
+constexpr int kGemmWaves = 8;
+
 }  // namespace
 
 hipError_t launch_gemm_bf16_tn(GemmParams p, hipStream_t stream) {
   if (p.M == 0) return hipSuccess;
-  if (p.N % kGBN || p.K % kGBK || p.K < kGBK || p.nseg < 1 || p.nseg > kGemmMaxSegs)
+  if (p.N % kGBN || p.K % 32 || p.K < 32 || p.nseg < 1 || p.nseg > kGemmMaxSegs)
     return hipErrorInvalidValue;
   p.tiles_m = (p.M + kGBM - 1) / kGBM;
   p.tiles_n = p.N / kGBN;
   const long long blocks = (long long)p.tiles_m * p.tiles_n;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(gemm_bf16_tn_kernel, dim3((unsigned)blocks), dim3(kGThreads), 0, stream, p);
+  constexpr int W = kGemmWaves;
+  if (p.K % 64 == 0)
+    hipLaunchKernelGGL((gemm_bf16_tn_kernel<64, W>), dim3((unsigned)blocks), dim3(64 * W), 0, stream, p);
+  else
+    hipLaunchKernelGGL((gemm_bf16_tn_kernel<32, W>), dim3((unsigned)blocks), dim3(64 * W), 0, stream, p);
   return hipGetLastError();
 }
 
