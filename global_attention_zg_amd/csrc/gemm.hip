@@ -151,31 +151,71 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_tn_kernel(GemmParams p) {
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x16{};
 
   const int nk = p.K / BK;
+  auto mfmas = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[NB]) {
 #pragma unroll
-  for (int s = 0; s < kGStages - 1; ++s)
-    if (s < nk) issue(s, s);
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+  };
+  auto load_ops = [&](bf16x8 (&af)[4], bf16x8 (&bfr)[NB], const lds_u8* st, int kk) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) af[mb] = lds_read_b128(st + ard[mb][kk]);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) bfr[nb] = lds_read_b128(st + brd[nb][kk]);
+  };
 
-  for (int ks = 0; ks < nk; ++ks) {
-    // step ks has landed for every wave; the groups of the following steps
-    // (up to kGStages - 2 of them) may still fly.  Every wave's reads of step
-    // ks-1 are done (lgkmcnt(0)), so its stage can be refilled.
-    if (kGStages >= 4 && ks + 2 < nk) sync_tiles<2 * kGCopies>();
-    else if (kGStages >= 3 && ks + 1 < nk) sync_tiles<kGCopies>();
+  if constexpr (kGStages == 2) {
+    // Two stages, software-pipelined: the operands of slice kk+1 are read
+    // while the MFMAs of slice kk run, also across steps.  At the last
+    // slice of step ks every wave has issued (and, at the barrier, received)
+    // all its reads of step ks, and step ks+1 has landed: after the barrier
+    // the copies of step ks+2 refill stage ks % 2 and slice 0 of step ks+1 is
+    // read, under the last MFMAs of step ks.
+    static_assert(KK % 2 == 0, "operand buffers alternate per slice");
+    bf16x8 af[2][4], bfr[2][NB];
+    issue(0, 0);
+    if (nk > 1) issue(1, 1);
+    if (nk > 1) sync_tiles<kGCopies>();
     else sync_tiles<0>();
-    if (ks + kGStages - 1 < nk) issue(ks + kGStages - 1, (ks + kGStages - 1) % kGStages);
-    const lds_u8* st = smem + (ks % kGStages) * kGStageBytes;
+    load_ops(af[0], bfr[0], smem, 0);
+    for (int ks = 0; ks < nk; ++ks) {
+      const lds_u8* st = smem + (ks & 1) * kGStageBytes;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      bf16x8 af[4], bfr[NB];
+      for (int kk = 0; kk < KK; ++kk) {
+        const int cur = kk & 1, nxt = cur ^ 1;
+        if (kk + 1 < KK) {
+          load_ops(af[nxt], bfr[nxt], st, kk + 1);
+        } else if (ks + 1 < nk) {
+          sync_tiles<0>();
+          if (ks + 2 < nk) issue(ks + 2, ks & 1);
+          load_ops(af[nxt], bfr[nxt], smem + ((ks + 1) & 1) * kGStageBytes, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(af[cur], bfr[cur]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) af[mb] = lds_read_b128(st + ard[mb][kk]);
+    for (int s = 0; s < kGStages - 1; ++s)
+      if (s < nk) issue(s, s);
+
+    for (int ks = 0; ks < nk; ++ks) {
+      // step ks has landed for every wave; the groups of the following
+      // steps (up to kGStages - 2 of them) may still fly.  Every wave's reads
+      // of step ks-1 are done (lgkmcnt(0)), so its stage can be refilled.
+      if (kGStages >= 4 && ks + 2 < nk) sync_tiles<2 * kGCopies>();
+      else if (kGStages >= 3 && ks + 1 < nk) sync_tiles<kGCopies>();
+      else sync_tiles<0>();
+      if (ks + kGStages - 1 < nk) issue(ks + kGStages - 1, (ks + kGStages - 1) % kGStages);
+      const lds_u8* st = smem + (ks % kGStages) * kGStageBytes;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) bfr[nb] = lds_read_b128(st + brd[nb][kk]);
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+      for (int kk = 0; kk < KK; ++kk) {
+        bf16x8 af[4], bfr[NB];
+        load_ops(af, bfr, st, kk);
+        mfmas(af, bfr);
+      }
     }
   }
 
