@@ -210,7 +210,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only",
                     choices=["swa4k", "global16k", "decode", "decode_block", "block_global", "bwd",
-                             "varlen", "proj"],
+                             "varlen", "proj", "variants"],
                     default=None, help="time one workload only (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="with --only: first run a plain 1 GiB device copy, the reference "
@@ -338,6 +338,8 @@ def run_components(torch, bd, only, iters):
         comps.update(decode_components(torch, bd, max(1, iters // 2)))
     if only in (None, "decode", "decode_block"):
         comps.update(decode_block_components(torch, bd, max(1, iters // 2)))
+    if only in (None, "variants"):
+        comps.update(variant_components(torch, bd, max(1, iters // 2)))
     if only in (None, "proj"):
         comps.update(proj_components(torch, bd, max(1, iters // 2)))
     if only in (None, "varlen"):
@@ -426,6 +428,49 @@ def decode_block_components(torch, bd, iters):
                      "graph_equals_eager": bool(same)}
         del graph, layers
         torch.cuda.empty_cache()
+    return out
+
+
+def variant_components(torch, bd, iters):
+    """The ablation's other configurations: the 1:1 / 3:1 / 5:1 interleave
+    arms and full attention over the 32 attention layers at 64K tokens
+    (composed from the measured time of one gated SWA layer and one global
+    layer at that length), and sliding windows other than 128 (B4 S4096)."""
+    out = {}
+    S = 65536
+    log("component: variants (64K layers)")
+    times = {}
+    for kind, window, gated in (("swa", 128, True), ("global", 0, False)):
+        l = Layer(torch, bd, 12, 0 if gated else 1, 1, S, 32, 8, window, gated)
+        for _ in range(2):
+            l()
+        times[kind] = time_events(torch, l, iters)
+        del l
+        torch.cuda.empty_cache()
+    arms = {}
+    for name, period in (("1:1", 2), ("3:1", 4), ("5:1", 6), ("full", 1)):
+        n_global = 32 // period
+        t = (32 - n_global) * times["swa"] + n_global * times["global"]
+        arms[name] = {"global_layers": n_global, "ms_32_layers": round(t * 1e3, 3),
+                      "tokens_per_s": round(S / t, 1)}
+    for name in ("1:1", "3:1", "5:1"):
+        arms[name]["speedup_vs_full"] = round(arms["full"]["ms_32_layers"] /
+                                              arms[name]["ms_32_layers"], 3)
+    out["interleave_arms_64k"] = {"swa_layer_ms": round(times["swa"] * 1e3, 4),
+                                  "global_layer_ms": round(times["global"] * 1e3, 4),
+                                  "arms": arms}
+    for W in (64, 256, 512, 1024):
+        log(f"component: swa W{W} B4 S4096")
+        l = Layer(torch, bd, 13, W, 4, 4096, 32, 8, W, True)
+        for _ in range(2):
+            l()
+        t = time_events(torch, l, iters)
+        out[f"swa_w{W}_4k_b4"] = {"ms": round(t * 1e3, 4), "tflops": round(l.flops / t / 1e12, 2),
+                                  "hbm_gbs_alg": round(l.alg_bytes / t / 1e9, 1),
+                                  "frac_hbm": round(l.alg_bytes / t / 1e9 / PEAK_HBM_GBS, 4),
+                                  "frac_mfma": round(l.flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del l
+    torch.cuda.empty_cache()
     return out
 
 

@@ -227,3 +227,14 @@ def test_too_small_workspace_is_rejected_before_launch():
     assert e.value.status == bd.ZG_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert torch.all(out.float() == 3.0)
+
+
+@pytest.mark.parametrize("window", [256, 1000])
+def test_fwd_wider_windows(window):
+    """Sliding windows other than the pages' 128 (the ablation's other
+    configurations): several tiles of band per query block."""
+    c = zc.fwd_case(150 + window, 1, 2100, 8, 2, gated=True)
+    got = run_gpu(c, window, gated=True)
+    ref_out, ref_lse = run_oracle(c, window, gated=True)
+    zc.compare(got["out"], ref_out, f"W{window}")
+    check_lse(got["lse"], ref_lse, f"W{window}")

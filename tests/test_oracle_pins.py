@@ -374,3 +374,18 @@ def test_inband_pair_count_matches_enumeration():
         i = np.arange(S)[:, None]
         j = np.arange(S)[None, :]
         assert orc.inband_pairs(S, W) == int(orc.visible(i, j, W).sum())
+
+
+def test_layer_schedule_ratio_variants():
+    """The architecture ablation's interleave arms (1:1, 3:1, 5:1 local to
+    global; [RB] 前置知识 and the throughput ablation, [SB] 🏗️ 架构): every
+    period-th layer global.  The 5:1 arm must reproduce the pages' layers and
+    their 5.0 GiB cache at 256K; the other arms follow in closed form."""
+    for period, n_global in ((2, 16), (4, 8), (6, 5)):
+        sched = orc.layer_schedule(32, period)
+        glob = [i + 1 for i, t in enumerate(sched) if t == "global"]
+        assert glob == list(range(period, 33, period))
+        assert len(glob) == n_global == 32 // period
+        gib = orc.kv_cache_bytes(n_global, 8, 128, 2, 262144) / 2**30
+        assert gib == 4.0 * n_global / 4  # 4 KiB per token per global layer, 256K tokens
+    assert orc.kv_cache_bytes(32 // 6, 8, 128, 2, 262144) / 2**30 == 5.0
