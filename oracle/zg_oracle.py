@@ -36,6 +36,9 @@ __all__ = [
     "bf16_bits_to_f64",
     "linear",
     "qkvg_proj",
+    "E4M3_MAX",
+    "e4m3_decode",
+    "quantize_e4m3",
     "rms_norm",
     "rope_angles",
     "apply_partial_rope",
@@ -440,6 +443,52 @@ def qkvg_proj(x: np.ndarray, w: np.ndarray, n_q_heads: int, n_kv_heads: int,
     v = y[:, nq + nk:nq + 2 * nk].reshape(T, n_kv_heads, head_dim)
     g = y[:, nq + 2 * nk:].reshape(T, n_q_heads, head_dim) if gated else None
     return q, k, v, g
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) matrix multiplies
+# ([RB] 前置知识 › FP8 混合精度训练与 TWEO: forward matrix multiplies in E4M3
+# with per-tensor scaling factors)
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Values of E4M3 codes (OCP: sign, 4 exponent bits with bias 7, 3
+    mantissa bits; exponent 0 is subnormal; 0x7F / 0xFF are NaN, there are no
+    infinities).  float64."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0**-9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return s * mag
+
+
+def quantize_e4m3(x: np.ndarray, scale: float):
+    """E4M3 codes and values of x * scale.
+
+    Reading: the product is formed in float32 (the precision of the kernel
+    that takes the decision), then clamped to [-448, 448] and rounded to the
+    nearest E4M3 value with ties to even; the sign of a value that rounds to
+    zero is kept (negative zero).  Returns (codes uint8, values float64).
+    """
+    v = (np.asarray(x, dtype=np.float32) * np.float32(scale)).astype(np.float64)
+    v = np.clip(v, -E4M3_MAX, E4M3_MAX)
+    neg = np.signbit(v)
+    a = np.abs(v)
+    # binade exponent of a (exact: frexp), the subnormal grid below 2^-6
+    _, ex = np.frexp(np.maximum(a, 2.0**-6))
+    quantum = np.exp2(ex - 1 - 3.0)
+    q = np.round(a / quantum) * quantum  # exact scaling; numpy rounds ties to even
+    # encode
+    _, qex = np.frexp(np.where(q > 0, q, 1.0))
+    normal = q >= 2.0**-6
+    E = np.where(normal, qex - 1 + 7, 0)
+    M = np.where(normal, q / np.exp2(qex - 1.0) * 8 - 8, q / 2.0**-9)
+    codes = (np.where(neg, 0x80, 0) | (E.astype(np.int64) << 3) | M.astype(np.int64))
+    return codes.astype(np.uint8), np.where(neg, -q, q)
 
 
 # ---------------------------------------------------------------------------
