@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0  # dense FP8 MFMA, MI355X spec
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 FLOP_PER_PAIR = 4 * 128     # QK^T and PV, 2 flop per MAC, head dim 128
 BWD_FLOP_PER_PAIR = 10 * 128  # backward: S, dP, dV, dK, dQ products (algorithmic count)
@@ -505,7 +506,25 @@ def proj_components(torch, bd, iters):
             out[name] = {"ms": round(t * 1e3, 4), "tflops": round(flops / t / 1e12, 1),
                          "frac_mfma": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4),
                          "M": T, "N": N, "K": hidden}
-            del w
+            # the same product with E4M3 operands (per-tensor scales; the
+            # weight quantized once, the activations per call)
+            log(f"component: {name}_fp8")
+            wq = bd.zg_quantize_fp8(w, 32.0 * hidden ** 0.5)
+            xq = torch.empty((T, hidden), dtype=torch.uint8, device="cuda")
+            yq = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+            osc = 1.0 / (32.0 * 32.0 * hidden ** 0.5)
+            fq = lambda: bd.zg_linear_fp8(xq, wq, osc, out=yq)  # noqa: E731
+            fz = lambda: bd.zg_quantize_fp8(x, 32.0, out=xq)  # noqa: E731
+            fz()
+            for _ in range(2):
+                fq()
+            tq = time_events(torch, fq, iters)
+            tz = time_events(torch, fz, iters)
+            out[name + "_fp8"] = {"ms": round(tq * 1e3, 4), "tflops": round(flops / tq / 1e12, 1),
+                                  "frac_fp8_mfma": round(flops / tq / 1e12 / PEAK_FP8_TFLOPS, 4),
+                                  "quantize_x_ms": round(tz * 1e3, 4),
+                                  "M": T, "N": N, "K": hidden}
+            del w, wq, xq, yq
         del x
         torch.cuda.empty_cache()
     return out

@@ -75,6 +75,10 @@ def _load():
     lib.zg_linear.restype = i
     lib.zg_qkvg_proj.argtypes = [P, i, vp, vp, vp, vp, vp, vp, vp]
     lib.zg_qkvg_proj.restype = i
+    lib.zg_quantize_fp8.argtypes = [ctypes.c_longlong, vp, ctypes.c_float, vp, vp]
+    lib.zg_quantize_fp8.restype = i
+    lib.zg_linear_fp8.argtypes = [i, i, i, vp, vp, ctypes.c_float, vp, vp]
+    lib.zg_linear_fp8.restype = i
     lib.zg_attn_bwd_workspace_size.argtypes = [P]
     lib.zg_attn_bwd_workspace_size.restype = sz
     lib.zg_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -91,7 +95,8 @@ EXPORTED = ("zg_attn_fwd_workspace_size", "zg_attn_fwd", "zg_attn_fwd_varlen_wor
             "zg_attn_fwd_varlen", "zg_attn_decode_num_splits",
             "zg_attn_decode_workspace_size", "zg_attn_decode", "zg_attn_kv_write_pages",
             "zg_attn_decode_paged", "zg_attn_bwd_workspace_size", "zg_attn_bwd",
-            "zg_linear", "zg_qkvg_proj", "zg_attn_strerror")
+            "zg_linear", "zg_qkvg_proj", "zg_quantize_fp8", "zg_linear_fp8",
+            "zg_attn_strerror")
 
 
 def library_path() -> str:
@@ -319,3 +324,22 @@ def zg_qkvg_proj(x, w, n_q_heads, n_kv_heads, gated, *, q=None, k=None, v=None, 
     _check(_lib.zg_qkvg_proj(ctypes.byref(p), hidden, _ptr(x), _ptr(w), _ptr(q), _ptr(k),
                              _ptr(v), _ptr(gate if gated else None), _stream(stream)))
     return q, k, v, (gate if gated else None)
+
+
+def zg_quantize_fp8(x, scale, out=None, stream=None):
+    """bf16 tensor -> uint8 tensor of E4M3 codes of x * scale (same shape)."""
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    _check(_lib.zg_quantize_fp8(x.numel(), _ptr(x), float(scale), _ptr(out), _stream(stream)))
+    return out
+
+
+def zg_linear_fp8(xq, wq, out_scale, out=None, stream=None):
+    """E4M3 codes xq [M,K], wq [N,K] (uint8) -> y [M,N] bf16 = out_scale * xq . wq^T."""
+    M, K = xq.shape
+    N = wq.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _check(_lib.zg_linear_fp8(M, N, K, _ptr(xq), _ptr(wq), float(out_scale), _ptr(out),
+                              _stream(stream)))
+    return out

@@ -435,6 +435,39 @@ int zg_linear(int M, int N, int K, const void* x, const void* w, void* y, void* 
   return hip_status(zg::launch_gemm_bf16_tn(gp, reinterpret_cast<hipStream_t>(stream)));
 }
 
+int zg_quantize_fp8(long long n, const void* x, float scale, void* q, void* stream) {
+  if (n < 0 || !(isfinite(scale) && scale > 0.f)) return ZG_ERR_INVALID;
+  if (n == 0) return ZG_OK;
+  if (n % 8) return ZG_ERR_UNSUPPORTED;
+  if (!x || !q || !aligned16(x) || (reinterpret_cast<uintptr_t>(q) & 7u)) return ZG_ERR_INVALID;
+  return hip_status(zg::launch_quantize_fp8(static_cast<const uint16_t*>(x),
+                                            static_cast<uint8_t*>(q), n, scale,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
+int zg_linear_fp8(int M, int N, int K, const void* xq, const void* wq, float out_scale, void* y,
+                  void* stream) {
+  if (M < 0 || N < 0 || K < 0 || !isfinite(out_scale)) return ZG_ERR_INVALID;
+  if (M == 0 || N == 0) return ZG_OK;
+  if (N % 256 || K % 128 || K == 0) return ZG_ERR_UNSUPPORTED;
+  if ((long long)K * 256 > 0x7fffffffLL) return ZG_ERR_UNSUPPORTED;
+  if (!xq || !wq || !y) return ZG_ERR_INVALID;
+  if (!aligned16(xq) || !aligned16(wq) || !aligned16(y)) return ZG_ERR_INVALID;
+  zg::GemmParams gp{};
+  gp.a = static_cast<const uint16_t*>(xq);
+  gp.b = static_cast<const uint16_t*>(wq);
+  gp.M = M;
+  gp.N = N;
+  gp.K = K;
+  gp.lda = K;
+  gp.ldb = K;
+  gp.seg[0] = zg::GemmSeg{static_cast<uint16_t*>(y), 0, N};
+  gp.nseg = 1;
+  gp.fp8 = 1;
+  gp.out_scale = out_scale;
+  return hip_status(zg::launch_gemm_bf16_tn(gp, reinterpret_cast<hipStream_t>(stream)));
+}
+
 int zg_qkvg_proj(const zg_attn_params* p, int hidden, const void* x, const void* w, void* q,
                  void* k, void* v, void* gate, void* stream) {
   int st = check_params(p);

@@ -32,12 +32,13 @@ namespace {
 
 constexpr int kGBM = 256, kGBN = 256;
 
-// K step BK (32 or 64) and ring depth: BK * 2 bytes per LDS row, rows of A
-// then W per stage.  A 1 KB copy covers 1024 / (2 BK) rows.
-template <int BK, int W> struct GCfg {
-  static constexpr int kRowBytes = BK * 2;
+// LDS rows of ROWB bytes (64 or 128) per K step: a K step is ROWB / 2
+// bf16 or ROWB fp8 elements.  Rows of A then W per stage; a 1 KB copy covers
+// 1024 / ROWB rows.
+template <int ROWB, int W> struct GCfg {
+  static constexpr int kRowBytes = ROWB;
   static constexpr int kChunks = kRowBytes / 16;            // 16-byte chunks per row
-  static constexpr int kStages = BK == 32 ? 4 : 2;
+  static constexpr int kStages = ROWB == 64 ? 4 : 2;
   static constexpr int kTileA = kGBM * kRowBytes;
   static constexpr int kTileB = kGBN * kRowBytes;
   static constexpr int kStageBytes = kTileA + kTileB;
@@ -48,7 +49,37 @@ template <int BK, int W> struct GCfg {
   // chunk swizzle: rows that share a 256-byte bank window, and successive
   // windows, get distinct chunk positions
   __device__ static int swz(int row) {
-    return BK == 32 ? (row >> 2) & 3 : (row >> 1) & 7;
+    return ROWB == 64 ? (row >> 2) & 3 : (row >> 1) & 7;
+  }
+};
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// The MFMA of each element type: bf16 v_mfma_f32_32x32x16_bf16 (16 k per
+// instruction, 16 bytes per lane) or FP8 E4M3 v_mfma_scale_f32_32x32x64_f8f6f4
+// (64 k, 32 bytes per lane: row l % 32, k 32 (l / 32) + 4 d + byte j of dword
+// d, probe-confirmed; block scales fixed at 1).  CPL: 16-byte chunks per lane
+// per instruction.
+template <bool FP8> struct GOp;
+template <> struct GOp<false> {
+  typedef bf16x8 T;
+  static constexpr int CPL = 1;
+  __device__ static T read(const lds_u8* st, const uint32_t (&a)[1]) { return lds_read_b128(st + a[0]); }
+  __device__ static f32x16 mma(const T& a, const T& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct GOp<true> {
+  typedef i32x8 T;
+  static constexpr int CPL = 2;
+  __device__ static T read(const lds_u8* st, const uint32_t (&a)[2]) {
+    const u32x4 lo = __builtin_bit_cast(u32x4, lds_read_b128(st + a[0]));
+    const u32x4 hi = __builtin_bit_cast(u32x4, lds_read_b128(st + a[1]));
+    return T{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+  }
+  __device__ static f32x16 mma(const T& a, const T& b, const f32x16& c) {
+    // formats 0 / 0: E4M3 for A and B; E8M0 block scales 127 = 1.0
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
   }
 };
 
@@ -56,9 +87,12 @@ template <int BK, int W> struct GCfg {
 // 4 x NB blocks of 32 x 32 (W = 8: two waves per SIMD, 128 accumulator
 // registers each; W = 4: one wave per SIMD, 256, which the compiler may keep
 // in the accumulation registers).
-template <int BK, int W>
+template <int ROWB, int W, bool FP8>
 __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_tn_kernel(GemmParams p) {
-  using C = GCfg<BK, W>;
+  using C = GCfg<ROWB, W>;
+  using O = GOp<FP8>;
+  using OT = typename O::T;
+  constexpr int EB = FP8 ? 1 : 2;  // bytes per element
   constexpr int NB = 16 / W;  // 32-column blocks per wave: 256 / (W / 2) columns
   static_assert(NB * 32 * (W / 2) == kGBN && 4 * 32 * 2 == kGBM, "waves must tile 256 x 256");
   constexpr int kGStages = C::kStages;
@@ -100,21 +134,21 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_tn_kernel(GemmParams p) {
   // L % chunks of row L / chunks of the block and fetches the logical chunk
   // stored there.
   const unsigned char* abase = reinterpret_cast<const unsigned char*>(p.a) +
-                               (long long)m0 * p.lda * 2;
+                               (long long)m0 * p.lda * EB;
   const unsigned char* bbase = reinterpret_cast<const unsigned char*>(p.b) +
-                               (long long)n0 * p.ldb * 2;
+                               (long long)n0 * p.ldb * EB;
   uint32_t aoff[BPW], boff[BPW];
 #pragma unroll
   for (int j = 0; j < BPW; ++j) {
     const int row = C::kRowsPerCopy * (BPW * wvu + j) + lane / C::kChunks;
     const int lc = (lane % C::kChunks) ^ C::swz(row);
     const int arow = min(row, p.M - 1 - m0);  // rows past M repeat row M-1
-    aoff[j] = (uint32_t)(arow * p.lda * 2 + lc * 16);
-    boff[j] = (uint32_t)(row * p.ldb * 2 + lc * 16);
+    aoff[j] = (uint32_t)(arow * p.lda * EB + lc * 16);
+    boff[j] = (uint32_t)(row * p.ldb * EB + lc * 16);
   }
   auto issue = [&](int ks, int stg) {
-    const unsigned char* ak = abase + (long long)ks * BK * 2;
-    const unsigned char* bk = bbase + (long long)ks * BK * 2;
+    const unsigned char* ak = abase + (long long)ks * ROWB;
+    const unsigned char* bk = bbase + (long long)ks * ROWB;
     const uint32_t la = lds_addr(smem + stg * kGStageBytes) + (BPW * wvu) * 1024;
     const uint32_t lb = la + kGTileA;
 #pragma unroll
@@ -124,24 +158,30 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_tn_kernel(GemmParams p) {
   };
 
   // ---- operand reads: lane l reads row l % 32 of a 32-row block, logical
-  // chunk 2 kk + l / 32 (kk: the 16-k slices of the K step)
+  // chunks 2 CPL kk + CPL (l / 32) + c (kk: the slices of the K step that
+  // one MFMA consumes)
   const int r32 = lane & 31;
   const int hsel = lane >> 5;
-  constexpr int KK = BK / 16;
-  uint32_t ard[4][KK], brd[NB][KK];
+  constexpr int CPL = O::CPL;
+  constexpr int KK = C::kChunks / (2 * CPL);
+  uint32_t ard[4][KK][CPL], brd[NB][KK][CPL];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
     const int row = wm * 128 + mb * 32 + r32;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      ard[mb][kk] = row * kGRowBytes + (((2 * kk + hsel) ^ C::swz(row)) << 4);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        ard[mb][kk][c] = row * kGRowBytes + (((2 * CPL * kk + CPL * hsel + c) ^ C::swz(row)) << 4);
   }
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int row = wn * 32 * NB + nb * 32 + r32;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      brd[nb][kk] = kGTileA + row * kGRowBytes + (((2 * kk + hsel) ^ C::swz(row)) << 4);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c)
+        brd[nb][kk][c] = kGTileA + row * kGRowBytes + (((2 * CPL * kk + CPL * hsel + c) ^ C::swz(row)) << 4);
   }
 
   f32x16 acc[4][NB];
@@ -150,22 +190,21 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_tn_kernel(GemmParams p) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x16{};
 
-  const int nk = p.K / BK;
-  auto mfmas = [&](const bf16x8 (&af)[4], const bf16x8 (&bfr)[NB]) {
+  const int nk = p.K / (ROWB / EB);
+  auto mfmas = [&](const OT (&af)[4], const OT (&bfr)[NB]) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+      for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = O::mma(af[mb], bfr[nb], acc[mb][nb]);
   };
-  auto load_ops = [&](bf16x8 (&af)[4], bf16x8 (&bfr)[NB], const lds_u8* st, int kk) {
+  auto load_ops = [&](OT (&af)[4], OT (&bfr)[NB], const lds_u8* st, int kk) {
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) af[mb] = lds_read_b128(st + ard[mb][kk]);
+    for (int mb = 0; mb < 4; ++mb) af[mb] = O::read(st, ard[mb][kk]);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) bfr[nb] = lds_read_b128(st + brd[nb][kk]);
+    for (int nb = 0; nb < NB; ++nb) bfr[nb] = O::read(st, brd[nb][kk]);
   };
 
-  if constexpr (kGStages == 2) {
+  if constexpr (kGStages == 2 && !FP8) {
     // Two stages, software-pipelined: the operands of slice kk+1 are read
     // while the MFMAs of slice kk run, also across steps.  At the last
     // slice of step ks every wave has issued (and, at the barrier, received)
@@ -173,7 +212,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_tn_kernel(GemmParams p) {
     // the copies of step ks+2 refill stage ks % 2 and slice 0 of step ks+1 is
     // read, under the last MFMAs of step ks.
     static_assert(KK % 2 == 0, "operand buffers alternate per slice");
-    bf16x8 af[2][4], bfr[2][NB];
+    OT af[2][4], bfr[2][NB];
     issue(0, 0);
     if (nk > 1) issue(1, 1);
     if (nk > 1) sync_tiles<kGCopies>();
@@ -201,6 +240,8 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_tn_kernel(GemmParams p) {
     for (int s = 0; s < kGStages - 1; ++s)
       if (s < nk) issue(s, s);
 
+    // (FP8 takes this loop with two stages: its operands are twice the
+    // registers of bf16's, too many to double-buffer)
     for (int ks = 0; ks < nk; ++ks) {
       // step ks has landed for every wave; the groups of the following
       // steps (up to kGStages - 2 of them) may still fly.  Every wave's reads
@@ -212,7 +253,7 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_tn_kernel(GemmParams p) {
       const lds_u8* st = smem + (ks % kGStages) * kGStageBytes;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        bf16x8 af[4], bfr[NB];
+        OT af[4], bfr[NB];
         load_ops(af, bfr, st, kk);
         mfmas(af, bfr);
       }
@@ -236,7 +277,8 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_tn_kernel(GemmParams p) {
       if (row < p.M) {
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
-          out[row * ld + ncol0 + nb * 32] = __builtin_bit_cast(uint16_t, (__bf16)acc[mb][nb][r]);
+          out[row * ld + ncol0 + nb * 32] =
+              __builtin_bit_cast(uint16_t, (__bf16)(FP8 ? acc[mb][nb][r] * p.out_scale : acc[mb][nb][r]));
       }
     }
   }
@@ -244,21 +286,56 @@ __global__ __launch_bounds__(64 * W, 1) void gemm_bf16_tn_kernel(GemmParams p) {
 
 constexpr int kGemmWaves = 8;
 
+// bf16 -> FP8 E4M3: q = RNE(clamp(x * scale, -448, 448)), the product taken
+// in fp32.  The conversion instruction does not saturate (its overflow is
+// NaN), hence the explicit clamp.  8 elements per lane.
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __restrict__ x,
+                                                           uint8_t* __restrict__ q, long long n8,
+                                                           float scale) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  float v[8];
+  unpack_bf16x8(ld16(x + 8 * i), v);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = fminf(fmaxf(v[e] * scale, -448.0f), 448.0f);
+  int w0 = 0, w1 = 0;
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], w0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w0, true);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], w1, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], w1, true);
+  *reinterpret_cast<uint2*>(q + 8 * i) = make_uint2((uint32_t)w0, (uint32_t)w1);
+}
+
 }  // namespace
+
+hipError_t launch_quantize_fp8(const uint16_t* x, uint8_t* q, long long n, float scale,
+                               hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  if (n % 8) return hipErrorInvalidValue;
+  const long long n8 = n / 8;
+  const long long blocks = (n8 + 255) / 256;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(quantize_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, x, q, n8,
+                     scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_gemm_bf16_tn(GemmParams p, hipStream_t stream) {
   if (p.M == 0) return hipSuccess;
-  if (p.N % kGBN || p.K % 32 || p.K < 32 || p.nseg < 1 || p.nseg > kGemmMaxSegs)
+  if (p.N % kGBN || p.K % (p.fp8 ? 128 : 32) || p.K < 32 || p.nseg < 1 || p.nseg > kGemmMaxSegs)
     return hipErrorInvalidValue;
   p.tiles_m = (p.M + kGBM - 1) / kGBM;
   p.tiles_n = p.N / kGBN;
   const long long blocks = (long long)p.tiles_m * p.tiles_n;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   constexpr int W = kGemmWaves;
-  if (p.K % 64 == 0)
-    hipLaunchKernelGGL((gemm_bf16_tn_kernel<64, W>), dim3((unsigned)blocks), dim3(64 * W), 0, stream, p);
+  const dim3 grid((unsigned)blocks), block(64 * W);
+  if (p.fp8)
+    hipLaunchKernelGGL((gemm_bf16_tn_kernel<128, W, true>), grid, block, 0, stream, p);
+  else if (p.K % 64 == 0)
+    hipLaunchKernelGGL((gemm_bf16_tn_kernel<128, W, false>), grid, block, 0, stream, p);
   else
-    hipLaunchKernelGGL((gemm_bf16_tn_kernel<32, W>), dim3((unsigned)blocks), dim3(64 * W), 0, stream, p);
+    hipLaunchKernelGGL((gemm_bf16_tn_kernel<64, W, false>), grid, block, 0, stream, p);
   return hipGetLastError();
 }
 

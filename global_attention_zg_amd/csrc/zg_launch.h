@@ -116,10 +116,15 @@ struct GemmParams {
   int lda, ldb;
   GemmSeg seg[kGemmMaxSegs];
   int nseg;
+  int fp8;           // operands are FP8 E4M3 bytes (K a multiple of 128)
+  float out_scale;   // fp8: results are multiplied by this before rounding
   int tiles_m, tiles_n;  // set by the launcher
 };
 
 hipError_t launch_gemm_bf16_tn(GemmParams p, hipStream_t stream);
+// n bf16 values -> FP8 E4M3 bytes, q = RNE(clamp(x * scale, +-448)); n % 8 == 0
+hipError_t launch_quantize_fp8(const uint16_t* x, uint8_t* q, long long n, float scale,
+                               hipStream_t stream);
 
 // Training backward.  Q' / K' are the normalised + rotated rows recomputed by
 // launch_k_prologue; dO = dY * sigmoid(G) (dY itself on an ungated layer).

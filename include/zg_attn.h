@@ -209,6 +209,30 @@ int zg_linear(int M, int N, int K, const void* x, const void* w, void* y, void* 
 int zg_qkvg_proj(const zg_attn_params* p, int hidden, const void* x, const void* w,
                  void* q, void* k, void* v, void* gate, void* stream);
 
+/* ---- FP8 (E4M3) projections ------------------------------------------------
+ * Page "ZGCM-1:面向数学与智能体搜索的全开源高效基础模型", section 前置知识 ›
+ * FP8 混合精度训练与 TWEO: the forward matrix multiplies run in 8-bit floating
+ * point E4M3 with per-tensor scaling factors (the pages update them from the
+ * maximum seen over the last 1024 steps; choosing the factor is the
+ * caller's).  E4M3 here is the OCP format: bias 7, no infinities, largest
+ * finite value 448. */
+
+/* q uint8 [n] = E4M3 code of x * scale for x bf16 [n]: the product is taken
+ * in fp32, clamped to [-448, 448] and rounded to nearest, ties to even (so
+ * a value that would overflow saturates).  n a multiple of 8 (else
+ * ZG_ERR_UNSUPPORTED); scale finite and > 0; x 16-byte and q 8-byte
+ * aligned. */
+int zg_quantize_fp8(long long n, const void* x, float scale, void* q, void* stream);
+
+/* y bf16 [M,N] = out_scale * (xq [M,K] . wq [N,K]^T) for E4M3 operands
+ * (quantized with scales s_x and s_w, pass out_scale = 1 / (s_x s_w)); the
+ * exact products are accumulated in fp32 on the gfx950 FP8 matrix cores
+ * (twice the bf16 rate) and the scaled sum is rounded once to bf16.  N a
+ * multiple of 256 and K a positive multiple of 128 (else
+ * ZG_ERR_UNSUPPORTED); M any size >= 0. */
+int zg_linear_fp8(int M, int N, int K, const void* xq, const void* wq, float out_scale,
+                  void* y, void* stream);
+
 /* Bytes of device workspace zg_attn_bwd needs (recomputed Q' and K', dO,
  * per-row LSE*log2(e) and rowsum(dY*Y), fp32 dL/dQ' and dL/dK', and the
  * partial sums of the two weight gradients); 0 for an invalid p. */

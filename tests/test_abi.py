@@ -22,7 +22,7 @@ def bd():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(zg_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(zg_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_entry_points():
@@ -291,3 +291,20 @@ def test_projection_argument_rules(bd):
     assert proj(ctypes.byref(p1), 4096, *args, None, None) == bd.ZG_ERR_UNSUPPORTED
     p0 = bd.make_params(0, 100, 32, 8, 128)
     assert proj(ctypes.byref(p0), 4096, None, None, None, None, None, None, None) == bd.ZG_OK
+
+
+def test_fp8_argument_rules(bd):
+    qz = bd._lib.zg_quantize_fp8
+    assert qz(0, None, 1.0, None, None) == bd.ZG_OK
+    assert qz(-8, FAKE, 1.0, FAKE, None) == bd.ZG_ERR_INVALID
+    assert qz(8, FAKE, 0.0, FAKE, None) == bd.ZG_ERR_INVALID          # scale must be > 0
+    assert qz(8, FAKE, float("inf"), FAKE, None) == bd.ZG_ERR_INVALID
+    assert qz(12, FAKE, 1.0, FAKE, None) == bd.ZG_ERR_UNSUPPORTED     # n % 8
+    assert qz(8, FAKE + 8, 1.0, FAKE, None) == bd.ZG_ERR_INVALID      # x alignment
+    assert qz(8, FAKE, 1.0, FAKE + 4, None) == bd.ZG_ERR_INVALID      # q alignment
+    lf = bd._lib.zg_linear_fp8
+    assert lf(0, 256, 128, None, None, 1.0, None, None) == bd.ZG_OK
+    assert lf(5, 256, 64, FAKE, FAKE, 1.0, FAKE, None) == bd.ZG_ERR_UNSUPPORTED   # K % 128
+    assert lf(5, 100, 128, FAKE, FAKE, 1.0, FAKE, None) == bd.ZG_ERR_UNSUPPORTED  # N % 256
+    assert lf(5, 256, 128, FAKE, None, 1.0, FAKE, None) == bd.ZG_ERR_INVALID
+    assert lf(5, 256, 128, FAKE, FAKE, float("nan"), FAKE, None) == bd.ZG_ERR_INVALID
