@@ -625,12 +625,12 @@ def decode_components(torch, bd, iters):
             bd.zg_attn_decode(q, kn, vn, kc, vc, sl, ring=ring, window=window, gate=g,
                               q_norm_w=gq, k_norm_w=gk, out=o, workspace=ws, **KW)
 
-        def record(name, fn, cap):
+        def record(name, fn, cap, elem_bytes=2):
             for _ in range(2):
                 fn()
             t = time_events(torch, fn, iters)
             keys = min(L, cap)
-            alg = B * Hkv * keys * D * 2 * 2 + (q.numel() * 2 + o.numel()) * 2
+            alg = B * Hkv * keys * D * 2 * elem_bytes + (q.numel() * 2 + o.numel()) * 2
             flops = B * Hq * keys * FLOP_PER_PAIR
             out[name] = {"ms": round(t * 1e3, 4), "tokens_per_s": round(B / t, 1),
                          "hbm_gbs_alg": round(alg / t / 1e9, 1),
@@ -670,6 +670,22 @@ def decode_components(torch, bd, iters):
             out[kind + "_paged"]["equals_contiguous"] = bool(
                 torch.equal(o_pg.view(torch.int16), o_ref.view(torch.int16)))
             del pools
+        # the same step over an E4M3 copy of the cache (per-tensor scales 16:
+        # the N(0,1) entries then span the format's normal range)
+        log(f"component: {kind}_fp8")
+        kc8 = bd.zg_quantize_fp8(kc, 16.0)
+        vc8 = bd.zg_quantize_fp8(vc, 16.0)
+        o8 = torch.empty_like(o)
+
+        def fn_fp8():
+            bd.zg_attn_decode_fp8(q, kn, vn, kc8, vc8, sl, ring=ring, window=window,
+                                  k_scale=16.0, v_scale=16.0, gate=g, q_norm_w=gq, k_norm_w=gk,
+                                  out=o8, workspace=ws, **KW)
+
+        record(kind + "_fp8", fn_fp8, cap, elem_bytes=1)
+        out[kind + "_fp8"]["max_abs_vs_bf16_cache"] = round(
+            float((o8.float() - o.float()).abs().max()), 5)
+        del kc8, vc8
         del kc, vc
         torch.cuda.empty_cache()
     return out

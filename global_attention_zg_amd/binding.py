@@ -69,6 +69,13 @@ def _load():
     lib.zg_attn_decode_paged.argtypes = [P, vp, vp, vp, vp, vp, i, vp, i, i, vp, vp, vp, vp, vp,
                                          i, vp, sz, vp]
     lib.zg_attn_decode_paged.restype = i
+    f = ctypes.c_float
+    lib.zg_attn_decode_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, i, i, f, f, vp, vp, vp, vp, i,
+                                       vp, sz, vp]
+    lib.zg_attn_decode_fp8.restype = i
+    lib.zg_attn_decode_paged_fp8.argtypes = [P, vp, vp, vp, vp, vp, i, vp, i, i, vp, f, f, vp, vp,
+                                             vp, vp, i, vp, sz, vp]
+    lib.zg_attn_decode_paged_fp8.restype = i
     lib.zg_attn_kv_write_pages.argtypes = [P, vp, vp, vp, vp, i, vp, i, i, vp]
     lib.zg_attn_kv_write_pages.restype = i
     lib.zg_linear.argtypes = [i, i, i, vp, vp, vp, vp]
@@ -96,7 +103,7 @@ EXPORTED = ("zg_attn_fwd_workspace_size", "zg_attn_fwd", "zg_attn_fwd_varlen_wor
             "zg_attn_decode_workspace_size", "zg_attn_decode", "zg_attn_kv_write_pages",
             "zg_attn_decode_paged", "zg_attn_bwd_workspace_size", "zg_attn_bwd",
             "zg_linear", "zg_qkvg_proj", "zg_quantize_fp8", "zg_linear_fp8",
-            "zg_attn_strerror")
+            "zg_attn_decode_fp8", "zg_attn_decode_paged_fp8", "zg_attn_strerror")
 
 
 def library_path() -> str:
@@ -294,6 +301,60 @@ def zg_attn_decode_paged(q, k_new, v_new, k_pages, v_pages, block_table, seq_len
                                    max_pages, page_size, _ptr(seq_lens), _ptr(gate),
                                    _ptr(q_norm_w), _ptr(k_norm_w), _ptr(out), num_splits,
                                    _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st)
+    return out
+
+
+def zg_attn_decode_fp8(q, k_new, v_new, k_cache, v_cache, seq_lens, *, ring, window, k_scale,
+                       v_scale, gate, q_norm_w, k_norm_w, rope_dim=42, rope_theta=10000.0,
+                       rms_eps=1e-6, softmax_scale=0.0, pos_offset=0, num_splits=0, out=None,
+                       workspace=None, stream=None):
+    """zg_attn_decode over an E4M3 cache: k_cache / v_cache uint8 [B,Hkv,cap,128]
+    hold the codes of K' * k_scale and V * v_scale (updated in place).
+    Returns out (bf16 [B,Hq,128])."""
+    B, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    p = make_params(B, 0, Hq, Hkv, D, window, rope_dim, rope_theta, rms_eps, softmax_scale,
+                    pos_offset)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        nbytes = zg_attn_decode_workspace_size(p, cap, num_splits)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.zg_attn_decode_fp8(ctypes.byref(p), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                 _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), cap, int(ring),
+                                 float(k_scale), float(v_scale), _ptr(gate), _ptr(q_norm_w),
+                                 _ptr(k_norm_w), _ptr(out), num_splits, _ptr(workspace),
+                                 ws_bytes, _stream(stream))
+    _check(st)
+    return out
+
+
+def zg_attn_decode_paged_fp8(q, k_new, v_new, k_pages, v_pages, block_table, seq_lens, *,
+                             window, k_scale, v_scale, gate, q_norm_w, k_norm_w, rope_dim=42,
+                             rope_theta=10000.0, rms_eps=1e-6, softmax_scale=0.0, pos_offset=0,
+                             num_splits=0, out=None, workspace=None, stream=None):
+    """zg_attn_decode_paged over E4M3 pages uint8 [num_pages,Hkv,page_size,128].
+    Returns out."""
+    B, Hq, D = q.shape
+    num_pages, Hkv, page_size, _ = k_pages.shape
+    max_pages = block_table.shape[1]
+    cap = max_pages * page_size
+    p = make_params(B, 0, Hq, Hkv, D, window, rope_dim, rope_theta, rms_eps, softmax_scale,
+                    pos_offset)
+    if out is None:
+        out = torch.empty_like(q)
+    if workspace is None:
+        nbytes = zg_attn_decode_workspace_size(p, cap, num_splits)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.zg_attn_decode_paged_fp8(ctypes.byref(p), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                       _ptr(k_pages), _ptr(v_pages), num_pages,
+                                       _ptr(block_table), max_pages, page_size, _ptr(seq_lens),
+                                       float(k_scale), float(v_scale), _ptr(gate),
+                                       _ptr(q_norm_w), _ptr(k_norm_w), _ptr(out), num_splits,
+                                       _ptr(workspace), ws_bytes, _stream(stream))
     _check(st)
     return out
 

@@ -151,8 +151,11 @@ static int decode_impl(const zg_attn_params* p, const void* q, const void* k_new
                        const void* v_new, void* k_cache, void* v_cache, const int* seq_lens,
                        int cache_cap, int ring, const zg::CacheMap& map, const void* gate,
                        const float* q_norm_w, const float* k_norm_w, void* out, int num_splits,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       void* workspace, size_t workspace_bytes, void* stream, int fp8 = 0,
+                       float k_scale = 0.f, float v_scale = 0.f) {
   int st = check_params(p);
+  if (fp8 && !(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f))
+    return ZG_ERR_INVALID;
   if (st != ZG_OK) return st;
   if (cache_cap < 1 || num_splits < 0 || num_splits > 256) return ZG_ERR_INVALID;
   if (ring && p->window != cache_cap) return ZG_ERR_INVALID;
@@ -179,10 +182,9 @@ static int decode_impl(const zg_attn_params* p, const void* q, const void* k_new
     dp.k_norm_w = k_norm_w;
   } else if (k_new) {
     hipError_t e = zg::launch_decode_append(
-        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
-        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), seq_lens, k_norm_w,
-        p->batch, p->n_kv_heads, cache_cap, ring, map, p->pos_offset, p->rope_dim / 2,
-        p->rms_eps, tab, s);
+        static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), k_cache,
+        v_cache, seq_lens, k_norm_w, p->batch, p->n_kv_heads, cache_cap, ring, map,
+        p->pos_offset, p->rope_dim / 2, p->rms_eps, tab, fp8, k_scale, v_scale, s);
     if (e != hipSuccess) return ZG_ERR_HIP;
   }
   dp.q = static_cast<const uint16_t*>(q);
@@ -208,6 +210,14 @@ static int decode_impl(const zg_attn_params* p, const void* q, const void* k_new
   dp.pos_offset = p->pos_offset;
   dp.map = map;
   dp.tab = tab;
+  if (fp8) {
+    // scores are q'.decode(code) / k_scale: fold the division into the scale
+    dp.fp8 = 1;
+    dp.k_scale = k_scale;
+    dp.v_scale = v_scale;
+    dp.scale_log2 = (float)((double)dp.scale_log2 / (double)k_scale);
+    dp.v_inv = (float)(1.0 / (double)v_scale);
+  }
   return hip_status(zg::launch_decode(dp, s));
 }
 
@@ -394,6 +404,32 @@ int zg_attn_decode_paged(const zg_attn_params* p, const void* q, const void* k_n
   return decode_impl(p, q, k_new, v_new, k_pages, v_pages, seq_lens, max_pages * page_size, 0,
                      map, gate, q_norm_w, k_norm_w, out, num_splits, workspace, workspace_bytes,
                      stream);
+}
+
+int zg_attn_decode_fp8(const zg_attn_params* p, const void* q, const void* k_new,
+                       const void* v_new, void* k_cache, void* v_cache, const int* seq_lens,
+                       int cache_cap, int ring, float k_scale, float v_scale, const void* gate,
+                       const float* q_norm_w, const float* k_norm_w, void* out, int num_splits,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  const zg::CacheMap contiguous{nullptr, 0, 0, 0};
+  return decode_impl(p, q, k_new, v_new, k_cache, v_cache, seq_lens, cache_cap, ring, contiguous,
+                     gate, q_norm_w, k_norm_w, out, num_splits, workspace, workspace_bytes,
+                     stream, 1, k_scale, v_scale);
+}
+
+int zg_attn_decode_paged_fp8(const zg_attn_params* p, const void* q, const void* k_new,
+                             const void* v_new, void* k_pages, void* v_pages, int num_pages,
+                             const int* block_table, int max_pages, int page_size,
+                             const int* seq_lens, float k_scale, float v_scale, const void* gate,
+                             const float* q_norm_w, const float* k_norm_w, void* out,
+                             int num_splits, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  zg::CacheMap map{};
+  const int st = check_pages(num_pages, block_table, max_pages, page_size, map);
+  if (st != ZG_OK) return st;
+  return decode_impl(p, q, k_new, v_new, k_pages, v_pages, seq_lens, max_pages * page_size, 0,
+                     map, gate, q_norm_w, k_norm_w, out, num_splits, workspace, workspace_bytes,
+                     stream, 1, k_scale, v_scale);
 }
 
 int zg_attn_kv_write_pages(const zg_attn_params* p, const void* k_prime, const void* v,

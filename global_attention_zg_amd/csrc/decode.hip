@@ -20,9 +20,13 @@
 // The cache is either one contiguous [cap, 128] slab per (b, kv head) or a
 // pool of fixed-size pages addressed through a per-sequence page table (the
 // PAGED instance); both read the same keys in the same order, so they give
-// the same bits.
+// the same bits.  It holds bf16 values or, in the FP8 instance, E4M3 codes
+// with per-tensor scales, which halves the bytes a step streams (page
+// "ZGCM-1:面向数学与智能体搜索的全开源高效基础模型", section 前置知识 › FP8
+// 混合精度训练与 TWEO: the model's E4M3 format and per-tensor scaling).
 
 #include "zg_common.h"
+#include "zg_fp8.h"
 #include "zg_launch.h"
 #include "zg_norm_rope.h"
 
@@ -50,7 +54,13 @@ static_assert(16 * (kD + 2 * kMaxRopeHalf) * 4 <= kVtBytes, "append scratch must
 // FUSED: the launch has one split per (b, kv head), so this workgroup owns
 // the whole key range: it appends the new token itself, before reading the
 // cache, and writes the normalised, gated output instead of a partial.
-template <bool PAGED, bool FUSED>
+// FP8: the cache holds E4M3 codes (one byte per element).  Each code is
+// widened to bf16 in registers, which is exact, so the MFMAs and the softmax
+// are those of the bf16 cache; the launch folds 1 / k_scale into the score
+// scale and the epilogue multiplies by 1 / v_scale.  The dims of Q' and K'
+// are fed to the MFMAs in another (common) order, so that a lane reads 32
+// consecutive bytes of a key row.
+template <bool PAGED, bool FUSED, bool FP8>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kVtBytes + kQsBytes + kQnBytes];
   __shared__ float red_m[kWaves][16];
@@ -142,8 +152,17 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
         } else {
           dst = (row * p.cap + slot) * kD;
         }
-        st16(const_cast<uint16_t*>(p.k_cache) + dst + 8 * c16, o);
-        st16(const_cast<uint16_t*>(p.v_cache) + dst + 8 * c16, vv);
+        if constexpr (FP8) {
+          float vf[8];
+          unpack_bf16x8(vv, vf);
+          uint8_t* kc = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(p.k_cache));
+          uint8_t* vc = reinterpret_cast<uint8_t*>(const_cast<uint16_t*>(p.v_cache));
+          st8(kc + dst + 8 * c16, pack_e4m3x8(x, p.k_scale));
+          st8(vc + dst + 8 * c16, pack_e4m3x8(vf, p.v_scale));
+        } else {
+          st16(const_cast<uint16_t*>(p.k_cache) + dst + 8 * c16, o);
+          st16(const_cast<uint16_t*>(p.v_cache) + dst + 8 * c16, vv);
+        }
       }
       // The key loop below reads the slot back.  All waves of the workgroup
       // share the CU's vector cache, so the barrier's workgroup-scope
@@ -186,7 +205,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   bf16x8 qf[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
-    qf[kk] = *reinterpret_cast<const bf16x8*>(qs + col * kQsStride + 32 * kk + 8 * kg);
+    qf[kk] = *reinterpret_cast<const bf16x8*>(qs + col * kQsStride +
+                                              (FP8 ? 32 * kg + 8 * kk : 32 * kk + 8 * kg));
 
   // ---- stream the split's keys.  Cache row of key `key` relative to the
   // cache base: a contiguous slab per (b, kv head), or the key's page slot
@@ -209,30 +229,86 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const int krel = 8 * (mr >> 2) + (mr & 3);  // + 4*blk: key of MFMA row mr
   const float rescale_raw = kRescaleThreshold / p.scale_log2;
 
-  for (int it = 0; it < nit; ++it) {
-    const int base = start + it * kKeysPerIter + wvu * kKeysPerWave;  // wave-uniform
-    int pa = 0, pb = 0;
-    if (PAGED && base < end) {
-      pa = p.map.page(b, base);
-      pb = p.map.page(b, min(base + kKeysPerWave - 1, end - 1));
+  // The raw cache bytes of the next kDepth slices are in flight while a
+  // slice is processed, so that a wave keeps loads moving during its MFMAs
+  // and softmax.  bf16: one slice ahead, the operands themselves (64
+  // registers); FP8: two slices ahead, the codes (32 registers per slice),
+  // widened after arrival, since a slice of codes is half the bytes.
+  constexpr int kDepth = FP8 ? 2 : 1;
+  constexpr int kRawK = FP8 ? 2 : 4;  // 16-byte loads per key row and lane
+  u32x4 rk[kDepth][2][kRawK];
+  u32x4 rv16[kDepth][FP8 ? 1 : 8];
+  uint2 rv8[kDepth][FP8 ? 8 : 1];
+  // Keys past the range load row min(key, end - 1) instead: a visible,
+  // written row, so its values are finite; its score is replaced by -inf
+  // below, so it adds exact zeros (the loads need no branch).
+  auto load_slice = [&](int it2, int d) {
+    const int b2 = start + it2 * kKeysPerIter + wvu * kKeysPerWave;  // wave-uniform
+    int qa = 0, qb = 0;
+    if (PAGED && b2 < end) {
+      qa = p.map.page(b, b2);
+      qb = p.map.page(b, min(b2 + kKeysPerWave - 1, end - 1));
     }
-    bf16x8 kf[2][4];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
-      const int key = base + krel + 4 * blk;
-      const long long ro = key < end ? row_off(key, pa, pb, base) : 0;
+      const long long ro = row_off(min(b2 + krel + 4 * blk, end - 1), qa, qb, b2);
+      if constexpr (FP8) {
+        // bytes 32kg..32kg+31 of the key row: dims 32kg + 8kk + 0..7 of kf[kk]
+        const uint8_t* src = reinterpret_cast<const uint8_t*>(p.k_cache) + ro + 32 * kg;
+        rk[d][blk][0] = ld16(src);
+        rk[d][blk][1] = ld16(src + 16);
+      } else {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        u32x4 u = key < end ? ld16(p.k_cache + ro + 32 * kk + 8 * kg) : u32x4{0, 0, 0, 0};
-        kf[blk][kk] = __builtin_bit_cast(bf16x8, u);
+        for (int kk = 0; kk < 4; ++kk) rk[d][blk][kk] = ld16(p.k_cache + ro + 32 * kk + 8 * kg);
       }
     }
-    u32x4 vr[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int key = base + 8 * kg + j;
-      vr[j] = key < end ? ld16(p.v_cache + row_off(key, pa, pb, base) + 8 * col) : u32x4{0, 0, 0, 0};
+      const long long ro = row_off(min(b2 + 8 * kg + j, end - 1), qa, qb, b2);
+      if constexpr (FP8)
+        rv8[d][j] = ld8(reinterpret_cast<const uint8_t*>(p.v_cache) + ro + 8 * col);
+      else
+        rv16[d][j] = ld16(p.v_cache + ro + 8 * col);
     }
+  };
+  // Every prefetch is issued, also past the last slice (it then re-reads
+  // slice nit - 1, an L2 hit): a conditional one would make the compiler
+  // copy the buffers at the loop head, waiting for all loads in flight.
+  if (nit > 0) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) load_slice(min(d, nit - 1), d);
+  }
+
+  // With kDepth 2 an odd slice count ends with slice nit, past the range:
+  // all its keys are masked, so it adds exact zeros and leaves the max.
+  for (int it0 = 0; it0 < nit; it0 += kDepth)
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) {
+    const int it = it0 + d;
+    const int base = start + it * kKeysPerIter + wvu * kKeysPerWave;  // wave-uniform
+    bf16x8 kf[2][4];
+    u32x4 vr[8];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if constexpr (FP8) {
+          const u32x4& c = rk[d][blk][kk >> 1];
+          kf[blk][kk] = __builtin_bit_cast(
+              bf16x8, widen_e4m3x8(make_uint2(c[2 * (kk & 1)], c[2 * (kk & 1) + 1])));
+        } else {
+          kf[blk][kk] = __builtin_bit_cast(bf16x8, rk[d][blk][kk]);
+        }
+      }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (FP8) vr[j] = widen_e4m3x8(rv8[d][j]);
+      else vr[j] = rv16[d][j];
+    }
+    // the buffer's old contents are consumed before its refill is issued,
+    // so the refill lands in the same registers (no copies at the loop end)
+    __builtin_amdgcn_sched_barrier(0);
+    load_slice(min(it + kDepth, nit - 1), d);
 
     f32x4 s[2];
 #pragma unroll
@@ -326,6 +402,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
       acc += f * red_o[(w2 * kMaxGroup + c) * kD + d];
       lsum += f * red_l[w2][c];
     }
+    if constexpr (FP8) acc *= p.v_inv;
     if constexpr (FUSED) {
       // what the merge computes for one split (its weight is exactly 1)
       const long long oi = ((long long)b * p.Hq + g * grp + c) * kD + d;
@@ -370,6 +447,17 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
   dst[64 + lane] = __builtin_bit_cast(uint16_t, (__bf16)o1);
 }
 
+template <bool FUSED>
+void launch_split(const DecodeParams& p, bool paged, dim3 grid, dim3 block, hipStream_t stream) {
+  if (p.fp8) {
+    if (paged) hipLaunchKernelGGL((decode_split_kernel<true, FUSED, true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((decode_split_kernel<false, FUSED, true>), grid, block, 0, stream, p);
+  } else {
+    if (paged) hipLaunchKernelGGL((decode_split_kernel<true, FUSED, false>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((decode_split_kernel<false, FUSED, false>), grid, block, 0, stream, p);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
@@ -377,13 +465,12 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   const long long blocks = (long long)p.B * p.Hkv * p.nsplit;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks), block(kThreads);
+  const bool paged = p.map.block_table != nullptr;
   if (p.nsplit == 1) {
-    if (p.map.block_table) hipLaunchKernelGGL((decode_split_kernel<true, true>), grid, block, 0, stream, p);
-    else hipLaunchKernelGGL((decode_split_kernel<false, true>), grid, block, 0, stream, p);
+    launch_split<true>(p, paged, grid, block, stream);
     return hipGetLastError();
   }
-  if (p.map.block_table) hipLaunchKernelGGL((decode_split_kernel<true, false>), grid, block, 0, stream, p);
-  else hipLaunchKernelGGL((decode_split_kernel<false, false>), grid, block, 0, stream, p);
+  launch_split<false>(p, paged, grid, block, stream);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(p.B * p.Hq), dim3(64), 0, stream, p);

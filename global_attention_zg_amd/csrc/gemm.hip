@@ -15,14 +15,19 @@
 // major, which is exactly the per-lane layout of both MFMA operands (8
 // consecutive k of one row per lane).
 //
-// Workgroup tile 256 x 256, K step 32, four-stage LDS ring (128 KB), eight
-// waves in a 2 (M) x 4 (N) grid, each wave 128 x 64 = 4 x 2 blocks of
-// v_mfma_f32_32x32x16_bf16.  Tiles move global -> LDS with untracked
-// global_load_lds_dwordx4 copies, three K steps ahead; LDS rows are 64 bytes
-// with their four 16-byte chunks XOR-swizzled by (row / 4) % 4, which makes
-// every MFMA operand read conflict-free under the 64-bank LDS.
+// Workgroup tile 256 x 256, eight waves in a 2 (M) x 4 (N) grid, each wave
+// 128 x 64 = 4 x 2 blocks of v_mfma_f32_32x32x16_bf16, 128 KB of LDS.  Tiles
+// move global -> LDS with untracked global_load_lds_dwordx4 copies.  Two
+// instances: K step 64 (128-byte LDS rows, eight 16-byte chunks XOR-swizzled
+// by (row / 2) % 8, a two-stage ring whose next step's copies fly during the
+// current step's MFMAs) when K is a multiple of 64, else K step 32 (64-byte
+// rows, four chunks swizzled by (row / 4) % 4, a four-stage ring filled three
+// steps ahead).  Both swizzles make every MFMA operand read conflict-free
+// under the 64-bank LDS.  The FP8 instance takes E4M3 operands at K step 128
+// (128-byte rows) on v_mfma_scale_f32_32x32x64_f8f6f4.
 
 #include "zg_common.h"
+#include "zg_fp8.h"
 #include "zg_launch.h"
 #include "zg_lds.h"
 
@@ -296,14 +301,7 @@ __global__ __launch_bounds__(256) void quantize_fp8_kernel(const uint16_t* __res
   if (i >= n8) return;
   float v[8];
   unpack_bf16x8(ld16(x + 8 * i), v);
-#pragma unroll
-  for (int e = 0; e < 8; ++e) v[e] = fminf(fmaxf(v[e] * scale, -448.0f), 448.0f);
-  int w0 = 0, w1 = 0;
-  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], w0, false);
-  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w0, true);
-  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], w1, false);
-  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], w1, true);
-  *reinterpret_cast<uint2*>(q + 8 * i) = make_uint2((uint32_t)w0, (uint32_t)w1);
+  st8(q + 8 * i, pack_e4m3x8(v, scale));
 }
 
 }  // namespace

@@ -13,6 +13,7 @@
 // lane can read the partner dim of its rotary pairs.
 
 #include "zg_common.h"
+#include "zg_fp8.h"
 #include "zg_launch.h"
 #include "zg_norm_rope.h"
 
@@ -72,12 +73,15 @@ __global__ __launch_bounds__(256) void k_prologue_kernel(const uint16_t* __restr
 
 // Decode: normalise + rotate the new key of each (b, kv head) at position
 // pos_offset + len - 1 and write it, with the new value, into its cache slot.
+// FP8: the caches hold E4M3 codes of K' * k_scale and V * v_scale (one byte
+// per element, same layout).
+template <bool FP8>
 __global__ __launch_bounds__(256) void decode_append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
-    uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache,
+    void* __restrict__ k_cache, void* __restrict__ v_cache,
     const int* __restrict__ seq_lens, const float* __restrict__ w, int rows, int Hkv,
     int cap, int ring, CacheMap map, long long pos_offset, int rope_half, float eps,
-    RopeTable tab) {
+    RopeTable tab, float k_scale, float v_scale) {
   __shared__ float xs[kRowsPerBlock][kD];
   __shared__ float cs[kRowsPerBlock][kMaxRopeHalf], sn[kRowsPerBlock][kMaxRopeHalf];
   const int lrow = threadIdx.x / 16;
@@ -113,8 +117,15 @@ __global__ __launch_bounds__(256) void decode_append_kernel(
     } else {
       dst = ((long long)row * cap + slot) * kD + 8 * c16;
     }
-    st16(k_cache + dst, o);
-    st16(v_cache + dst, vv);
+    if constexpr (FP8) {
+      float vf[8];
+      unpack_bf16x8(vv, vf);
+      st8(static_cast<uint8_t*>(k_cache) + dst, pack_e4m3x8(x, k_scale));
+      st8(static_cast<uint8_t*>(v_cache) + dst, pack_e4m3x8(vf, v_scale));
+    } else {
+      st16(static_cast<uint16_t*>(k_cache) + dst, o);
+      st16(static_cast<uint16_t*>(v_cache) + dst, vv);
+    }
   }
 }
 
@@ -155,17 +166,23 @@ hipError_t launch_k_prologue(const uint16_t* k, const float* w, uint16_t* kout, 
   return hipGetLastError();
 }
 
-hipError_t launch_decode_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache,
-                                uint16_t* v_cache, const int* seq_lens, const float* w, int B,
+hipError_t launch_decode_append(const uint16_t* k_new, const uint16_t* v_new, void* k_cache,
+                                void* v_cache, const int* seq_lens, const float* w, int B,
                                 int Hkv, int cap, int ring, const CacheMap& map,
                                 long long pos_offset, int rope_half, float eps,
-                                const RopeTable& tab, hipStream_t stream) {
+                                const RopeTable& tab, int fp8, float k_scale, float v_scale,
+                                hipStream_t stream) {
   const int rows = B * Hkv;
   if (rows == 0) return hipSuccess;
   const int blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL(decode_append_kernel, dim3(blocks), dim3(256), 0, stream, k_new, v_new,
-                     k_cache, v_cache, seq_lens, w, rows, Hkv, cap, ring, map, pos_offset,
-                     rope_half, eps, tab);
+  if (fp8)
+    hipLaunchKernelGGL(decode_append_kernel<true>, dim3(blocks), dim3(256), 0, stream, k_new,
+                       v_new, k_cache, v_cache, seq_lens, w, rows, Hkv, cap, ring, map,
+                       pos_offset, rope_half, eps, tab, k_scale, v_scale);
+  else
+    hipLaunchKernelGGL(decode_append_kernel<false>, dim3(blocks), dim3(256), 0, stream, k_new,
+                       v_new, k_cache, v_cache, seq_lens, w, rows, Hkv, cap, ring, map,
+                       pos_offset, rope_half, eps, tab, k_scale, v_scale);
   return hipGetLastError();
 }
 

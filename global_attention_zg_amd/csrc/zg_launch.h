@@ -62,11 +62,14 @@ struct CacheMap {
   }
 };
 
-hipError_t launch_decode_append(const uint16_t* k_new, const uint16_t* v_new, uint16_t* k_cache,
-                                uint16_t* v_cache, const int* seq_lens, const float* w, int B,
+// fp8 != 0: the caches hold E4M3 codes (one byte per element) of
+// K' * k_scale and V * v_scale.
+hipError_t launch_decode_append(const uint16_t* k_new, const uint16_t* v_new, void* k_cache,
+                                void* v_cache, const int* seq_lens, const float* w, int B,
                                 int Hkv, int cap, int ring, const CacheMap& map,
                                 long long pos_offset, int rope_half, float eps,
-                                const RopeTable& tab, hipStream_t stream);
+                                const RopeTable& tab, int fp8, float k_scale, float v_scale,
+                                hipStream_t stream);
 
 // Copy K' and V of a prefill (bf16 [B,S,Hkv,D]) into a paged cache: token s
 // of sequence b goes to its page slot (CacheMap).
@@ -94,6 +97,11 @@ struct DecodeParams {
   const uint16_t* v_new;    // bf16 [B,Hkv,D]
   const float* k_norm_w;    // fp32 [D]
   RopeTable tab;
+  // E4M3 cache (the FP8 instance): k_cache / v_cache hold codes, one byte
+  // per element in the same layouts, of K' * k_scale and V * v_scale.  The
+  // launch folds 1 / k_scale into scale_log2; v_inv = 1 / v_scale.
+  float k_scale, v_scale, v_inv;
+  int fp8;
 };
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);

@@ -1,7 +1,7 @@
 """Seeded synthetic inputs shared by the tests, the smoke check and the benchmark.
 
 This module holds no attention arithmetic: it only draws N(0,1) numbers and
-rounds them to bf16.  Every tensor is drawn in chunks of 2**22 elements; chunk
+rounds them to bf16, or draws uniform bytes.  Every tensor is drawn in chunks of 2**22 elements; chunk
 c of tensor t for workload k, layer l comes from
 ``Generator(PCG64(SeedSequence([20260915, k, l, t, c])))``, so any slice can
 be regenerated without materialising the whole tensor.
@@ -89,3 +89,22 @@ def norm_weight(key, D: int) -> np.ndarray:
     w = (1.0 + 0.1 * g.standard_normal(D)).astype(np.float32)
     return (_round_bf16_bits(w).astype(np.uint32) << 16).view(np.float32)
 
+
+def sign_magnitude_bytes(key, total: int, lo: int, hi: int, start: int = 0,
+                         stop: int | None = None) -> np.ndarray:
+    """Elements [start, stop) of a seeded uint8 tensor ``key`` of ``total``
+    bytes: the low 7 bits uniform on [lo, hi) (0 <= lo < hi <= 128), the top
+    bit a fair coin.  Chunked and seeded like ``normal_bf16_bits``."""
+    assert 0 <= lo < hi <= 128
+    stop = total if stop is None else stop
+    assert 0 <= start <= stop <= total
+    res = np.empty(stop - start, dtype=np.uint8)
+    for c in range(start // CHUNK, (stop + CHUNK - 1) // CHUNK):
+        base = c * CHUNK
+        ln = min(CHUNK, total - base)
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_BASE, *key, c])))
+        mag = g.integers(lo, hi, ln, dtype=np.uint8)
+        sign = g.integers(0, 2, ln, dtype=np.uint8) << np.uint8(7)
+        s0, s1 = max(start, base), min(stop, base + ln)
+        res[s0 - start:s1 - start] = (mag | sign)[s0 - base:s1 - base]
+    return res

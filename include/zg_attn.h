@@ -183,6 +183,47 @@ int zg_attn_decode_paged(const zg_attn_params* p,
                          void* out, int num_splits,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- FP8 (E4M3) KV cache ----------------------------------------------------
+ * Page "ZGCM-1:面向数学与智能体搜索的全开源高效基础模型", section 前置知识 ›
+ * FP8 混合精度训练与 TWEO: E4M3 with per-tensor scaling factors is the
+ * model's matrix-multiply precision; the page's structured-data table, row
+ * "256K 上下文推理 KV 缓存", frames decode cost as the bytes of the cache.
+ * Here the cache holds one byte per element: the OCP E4M3 code (bias 7,
+ * largest finite 448, 0x7F/0xFF NaN) of K' * k_scale and of V * v_scale,
+ * with the product formed in fp32, clamped to [-448, 448] and rounded to
+ * the nearest E4M3 value, ties to even (the codes zg_quantize_fp8 writes).
+ * A cached key then stands for decode(code) / k_scale and a value for
+ * decode(code) / v_scale, and the attention is zg_attn_decode's over those
+ * values (up to fp32 rounding order): the kernel widens each code to bf16
+ * without rounding, runs the bf16 MFMAs and the fp32 softmax, and applies
+ * 1 / k_scale in the score scale and 1 / v_scale to the output.  A step
+ * reads half the bytes of a bf16 cache.
+ * Scales must be finite and > 0 (else ZG_ERR_INVALID). */
+
+/* zg_attn_decode with uint8 caches k_cache / v_cache [B,Hkv,cache_cap,D] of
+ * E4M3 codes; the new token's K' and V are quantized with k_scale / v_scale
+ * into their slot (updated in place).  Every other argument, the workspace
+ * and the clamping of seq_lens are as for zg_attn_decode. */
+int zg_attn_decode_fp8(const zg_attn_params* p,
+                       const void* q, const void* k_new, const void* v_new,
+                       void* k_cache, void* v_cache, const int* seq_lens,
+                       int cache_cap, int ring, float k_scale, float v_scale,
+                       const void* gate, const float* q_norm_w, const float* k_norm_w,
+                       void* out, int num_splits,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* zg_attn_decode_paged over uint8 page pools [num_pages,Hkv,page_size,D] of
+ * E4M3 codes (scales as for zg_attn_decode_fp8).  For equal inputs the
+ * output is bit-identical to zg_attn_decode_fp8's with ring == 0. */
+int zg_attn_decode_paged_fp8(const zg_attn_params* p,
+                             const void* q, const void* k_new, const void* v_new,
+                             void* k_pages, void* v_pages, int num_pages,
+                             const int* block_table, int max_pages, int page_size,
+                             const int* seq_lens, float k_scale, float v_scale,
+                             const void* gate, const float* q_norm_w, const float* k_norm_w,
+                             void* out, int num_splits,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- The projections on either side of the attention ----------------------
  * Page "ZGCM-1:面向数学与智能体搜索的全开源高效基础模型", section 核心方法, and
  * page "7B 打 235B？…", section 🏗️ 架构: hidden size 4096 feeding 32 query

@@ -39,6 +39,7 @@ __all__ = [
     "E4M3_MAX",
     "e4m3_decode",
     "quantize_e4m3",
+    "attention_decode_fp8",
     "rms_norm",
     "rope_angles",
     "apply_partial_rope",
@@ -63,7 +64,7 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# Step 1: QK-RMSNorm  ([SB] 🏗️ 架构: "QK 用 RMSNorm 归一化")
+# Step 1: QK-RMSNorm  ([SB] 🏗️ 架构: queries and keys are RMS-normalised)
 # ---------------------------------------------------------------------------
 def rms_norm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
     """RMSNorm over the last axis (one attention head of D values).
@@ -123,8 +124,9 @@ def apply_partial_rope(x: np.ndarray, positions: np.ndarray, rope_dim: int,
 def visible(i: np.ndarray, j: np.ndarray, window: int) -> np.ndarray:
     """Key j is visible to query i iff j <= i and (window == 0 or i - j < window).
 
-    Reading of [RB] 前置知识 ("与相邻 128 个 token"): the band holds 128 keys
-    including the query itself; window == 0 means global causal attention.
+    Reading of [RB] 前置知识 (each token sees its 128 neighbouring tokens):
+    the band holds 128 keys including the query itself; window == 0 means
+    global causal attention.
     """
     ok = j <= i
     if window > 0:
@@ -489,6 +491,52 @@ def quantize_e4m3(x: np.ndarray, scale: float):
     M = np.where(normal, q / np.exp2(qex - 1.0) * 8 - 8, q / 2.0**-9)
     codes = (np.where(neg, 0x80, 0) | (E.astype(np.int64) << 3) | M.astype(np.int64))
     return codes.astype(np.uint8), np.where(neg, -q, q)
+
+
+def attention_decode_fp8(q, k_new, v_new, k_codes, v_codes, seq_lens, *, k_scale: float,
+                         v_scale: float, ring: bool, window: int, gate, q_norm_w, k_norm_w,
+                         rope_dim: int, rope_theta: float, rms_eps: float,
+                         softmax_scale: float = 0.0, pos_offset: int = 0):
+    """Decode against a KV cache stored in E4M3 ([RB] 前置知识 › FP8 混合精度训练与
+    TWEO for the format and per-tensor scaling; the cache-size row of [RB]'s
+    structured-data table for why the cache is what decode streams).
+
+    k_codes, v_codes uint8 [B,Hkv,cap,D]: codes of K' * k_scale and
+    V * v_scale.  Reading: a cached code c stands for e4m3_decode(c) / scale;
+    the new token's K' (step 1 of ``decode_group``, in fp64) and V are
+    quantized with ``quantize_e4m3`` into their slot; the step is then
+    ``decode_group`` over the dequantized cache, with the new token already
+    in it.  Returns (out [B,Hq,D], lse [B,Hq], k_codes_after, v_codes_after).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv, cap = k_codes.shape[1], k_codes.shape[2]
+    grp = Hq // Hkv
+    kc = np.array(k_codes, dtype=np.uint8, copy=True)
+    vc = np.array(v_codes, dtype=np.uint8, copy=True)
+    out = np.zeros((B, Hq, D))
+    lse = np.zeros((B, Hq))
+    for b in range(B):
+        L = int(seq_lens[b])
+        p = pos_offset + L - 1
+        slot = (L - 1) % cap if ring else L - 1
+        for g in range(Hkv):
+            if k_new is not None:
+                kn = rms_norm(np.asarray(k_new[b, g], dtype=np.float64)[None, None, :],
+                              k_norm_w, rms_eps)
+                kn = apply_partial_rope(kn, np.array([p]), rope_dim, rope_theta)[0, 0]
+                kc[b, g, slot] = quantize_e4m3(kn, k_scale)[0]
+                vc[b, g, slot] = quantize_e4m3(np.asarray(v_new[b, g]), v_scale)[0]
+            hs = slice(g * grp, (g + 1) * grp)
+            o, ls, _ = decode_group(
+                q[b, hs], None, None, e4m3_decode(kc[b, g]) / k_scale,
+                e4m3_decode(vc[b, g]) / v_scale, L, ring=ring, window=window,
+                gate_group=None if gate is None else gate[b, hs], q_norm_w=q_norm_w,
+                k_norm_w=k_norm_w, rope_dim=rope_dim, rope_theta=rope_theta, rms_eps=rms_eps,
+                softmax_scale=softmax_scale, pos_offset=pos_offset)
+            out[b, hs] = o
+            lse[b, hs] = ls
+    return out, lse, kc, vc
 
 
 # ---------------------------------------------------------------------------

@@ -148,6 +148,45 @@ def test_decode_rejects_bad_arguments(bd):
     assert _dec(bd, pbad, 128, 1, **ok) == bd.ZG_ERR_UNSUPPORTED
 
 
+def _dec_fp8(bd, p, cap, ring, k_scale, v_scale, num_splits=0, **ptrs):
+    a = [ptrs.get(n) for n in ("q", "kn", "vn", "kc", "vc", "sl")]
+    return bd._lib.zg_attn_decode_fp8(ctypes.byref(p), *a, cap, ring, k_scale, v_scale,
+                                      ptrs.get("gate"), ptrs.get("qw"), ptrs.get("kw"),
+                                      ptrs.get("out"), num_splits, ptrs.get("ws"),
+                                      ptrs.get("ws_bytes", 0), None)
+
+
+def _dec_paged_fp8(bd, p, num_pages, max_pages, page_size, k_scale, v_scale, **ptrs):
+    a = [ptrs.get(n) for n in ("q", "kn", "vn", "kp", "vp")]
+    return bd._lib.zg_attn_decode_paged_fp8(ctypes.byref(p), *a, num_pages, ptrs.get("bt"),
+                                            max_pages, page_size, ptrs.get("sl"), k_scale,
+                                            v_scale, ptrs.get("gate"), ptrs.get("qw"),
+                                            ptrs.get("kw"), ptrs.get("out"), 0, ptrs.get("ws"),
+                                            ptrs.get("ws_bytes", 0), None)
+
+
+def test_fp8_decode_rejects_bad_arguments(bd):
+    """Every case fails validation, so nothing is launched."""
+    ok = dict(q=FAKE, kc=FAKE, vc=FAKE, sl=FAKE, qw=FAKE, kw=FAKE, out=FAKE, ws=FAKE,
+              ws_bytes=1 << 30)
+    p = bd.make_params(2, 0, 32, 8, 128, 128)
+    inf, nan = float("inf"), float("nan")
+    for ks, vs in ((0.0, 1.0), (1.0, 0.0), (-1.0, 1.0), (1.0, -3.0), (inf, 1.0), (1.0, nan)):
+        assert _dec_fp8(bd, p, 128, 1, ks, vs, **ok) == bd.ZG_ERR_INVALID, (ks, vs)
+    assert _dec_fp8(bd, p, 64, 1, 1.0, 1.0, **ok) == bd.ZG_ERR_INVALID         # window != cap
+    assert _dec_fp8(bd, p, 128, 1, 1.0, 1.0, **dict(ok, kn=FAKE)) == bd.ZG_ERR_INVALID
+    assert _dec_fp8(bd, p, 128, 1, 1.0, 1.0, **dict(ok, kc=FAKE + 8)) == bd.ZG_ERR_INVALID
+    assert _dec_fp8(bd, p, 128, 1, 1.0, 1.0, **dict(ok, ws_bytes=16)) == bd.ZG_ERR_WORKSPACE
+    p0 = bd.make_params(0, 0, 32, 8, 128, 128)
+    assert _dec_fp8(bd, p0, 128, 1, 1.0, 1.0) == bd.ZG_OK
+    okp = dict(q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, sl=FAKE, qw=FAKE, kw=FAKE, out=FAKE, ws=FAKE,
+               ws_bytes=1 << 30)
+    pg = bd.make_params(2, 0, 32, 8, 128, 0)
+    assert _dec_paged_fp8(bd, pg, 8, 4, 64, 0.0, 1.0, **okp) == bd.ZG_ERR_INVALID
+    assert _dec_paged_fp8(bd, pg, 8, 4, 48, 1.0, 1.0, **okp) == bd.ZG_ERR_INVALID
+    assert _dec_paged_fp8(bd, pg, 8, 4, 64, 1.0, 1.0, **dict(okp, bt=None)) == bd.ZG_ERR_INVALID
+
+
 def _bwd(bd, p, **ptrs):
     names = ["q", "k", "v", "gate", "qw", "kw", "out", "lse", "dout", "dq", "dk", "dv", "dgate",
              "dqw", "dkw", "ws"]

@@ -53,3 +53,109 @@ def test_rounding_error_bound_and_monotone():
     order = np.argsort(v)
     assert np.all(np.diff(vals[order]) >= 0)
     assert np.array_equal(orc.e4m3_decode(codes), vals)
+
+
+# ---------------------------------------------------------------------------
+# attention_decode_fp8: decode over an E4M3 cache, pinned by closed forms
+# ---------------------------------------------------------------------------
+D = 128
+DEC = dict(rope_dim=0, rope_theta=10000.0, rms_eps=1e-6)
+
+
+def _dec(q, kn, vn, kc, vc, lens, k_scale, v_scale, ring=False, window=0, **kw):
+    args = dict(DEC)
+    args.update(kw)
+    ones = np.ones(D)
+    return orc.attention_decode_fp8(q, kn, vn, kc, vc, lens, k_scale=k_scale, v_scale=v_scale,
+                                    ring=ring, window=window, gate=None, q_norm_w=ones,
+                                    k_norm_w=ones, **args)
+
+
+def test_decode_fp8_uniform_scores_average_the_dequantized_values():
+    """All keys zero (the appended one too: RMSNorm of 0 is 0), so every
+    visible key gets weight 1/L and the output is the mean of the stored
+    values, each code divided by v_scale; the new value 0.3 is stored as
+    E4M3(0.3 * 4) = 1.25, i.e. 0.3125."""
+    L = 5
+    q = np.random.default_rng(0).standard_normal((1, 4, D))
+    kc = np.zeros((1, 1, 8, D), dtype=np.uint8)
+    vc = np.zeros((1, 1, 8, D), dtype=np.uint8)
+    # slots 0..3: 1.0, 2.0, -1.0, 448 (codes 0x38, 0x40, 0xB8, 0x7E); slot 5 is not visible
+    for s, c in enumerate((0x38, 0x40, 0xB8, 0x7E)):
+        vc[0, 0, s] = c
+    vc[0, 0, 5] = 0x40
+    out, _, kca, vca = _dec(q, np.zeros((1, 1, D)), np.full((1, 1, D), 0.3), kc, vc, [L],
+                            k_scale=2.0, v_scale=4.0)
+    expect = ((1.0 + 2.0 - 1.0 + 448.0) / 4.0 + 0.3125) / L
+    assert np.allclose(out, expect, rtol=1e-14, atol=0)
+    assert np.all(vca[0, 0, L - 1] == 0x3A) and np.all(kca[0, 0, L - 1] == 0x00)
+    assert np.array_equal(np.delete(vca, L - 1, axis=2), np.delete(vc, L - 1, axis=2))
+
+
+def test_decode_fp8_two_keys_closed_form():
+    """q = 5 e_0 with unit norm weights and no rotation gives
+    q'_0 = 5 / sqrt(25/128 + eps); key 0 stores code 0x40 (= 2) in dim 0, key 1
+    zeros, so the scores are tau * q'_0 * 2 / k_scale and 0 and the output is
+    the two-way softmax mix of the stored values 1 / v_scale and -1 / v_scale."""
+    k_scale, v_scale = 8.0, 16.0
+    q = np.zeros((1, 2, D))
+    q[:, :, 0] = 5.0
+    kc = np.zeros((1, 1, 4, D), dtype=np.uint8)
+    kc[0, 0, 0, 0] = 0x40
+    vc = np.zeros((1, 1, 4, D), dtype=np.uint8)
+    vc[0, 0, 0] = 0x38
+    vc[0, 0, 1] = 0xB8
+    out, lse, _, _ = _dec(q, None, None, kc, vc, [2], k_scale, v_scale)
+    qp = 5.0 / np.sqrt(25.0 / D + 1e-6)
+    s0 = qp * 2.0 / k_scale / np.sqrt(D)
+    w0 = 1.0 / (1.0 + np.exp(-s0))
+    expect = (w0 - (1.0 - w0)) / v_scale
+    assert np.allclose(out, expect, rtol=1e-13, atol=0)
+    assert np.allclose(lse, np.log(np.exp(s0) + 1.0), rtol=1e-13)
+
+
+def test_decode_fp8_ring_overwrites_the_oldest_slot():
+    """Ring of 4 slots, length 6: the new token goes to slot 5 % 4 = 1,
+    replacing what was there, and the 4 slots are the visible keys.  With
+    zero keys the output is the mean of the 4 stored values."""
+    q = np.random.default_rng(1).standard_normal((1, 1, D))
+    kc = np.zeros((1, 1, 4, D), dtype=np.uint8)
+    vc = np.zeros((1, 1, 4, D), dtype=np.uint8)
+    for s, c in enumerate((0x38, 0x40, 0x48, 0x50)):   # 1, 2, 4, 8
+        vc[0, 0, s] = c
+    out, _, _, vca = _dec(q, np.zeros((1, 1, D)), np.full((1, 1, D), -0.5), kc, vc, [6],
+                          k_scale=1.0, v_scale=2.0, ring=True, window=4)
+    assert np.all(vca[0, 0, 1] == 0xB8)                  # -0.5 * 2 = -1
+    expect = (1.0 + -1.0 + 4.0 + 8.0) / 2.0 / 4
+    assert np.allclose(out, expect, rtol=1e-14, atol=0)
+
+
+def test_decode_fp8_is_decode_over_the_dequantized_cache():
+    """With a power-of-two scale and cache values on the E4M3 grid, the FP8
+    step and the bf16-cache oracle see the same keys and values, and the new
+    key is quantized from the normalised, rotated k_new."""
+    rng = np.random.default_rng(2)
+    B, Hq, Hkv, cap = 2, 8, 2, 40
+    kc = rng.integers(0, 0x70, (B, Hkv, cap, D)).astype(np.uint8) | \
+        (rng.integers(0, 2, (B, Hkv, cap, D)).astype(np.uint8) << 7)
+    vc = rng.integers(0, 0x70, (B, Hkv, cap, D)).astype(np.uint8)
+    q = rng.standard_normal((B, Hq, D))
+    kn = rng.standard_normal((B, Hkv, D))
+    vn = rng.standard_normal((B, Hkv, D))
+    gq, gk = 1.0 + 0.1 * rng.standard_normal(D), 1.0 + 0.1 * rng.standard_normal(D)
+    kw = dict(rope_dim=42, rope_theta=10000.0, rms_eps=1e-6, pos_offset=7)
+    lens = [13, 40]
+    o8, l8, kca, vca = orc.attention_decode_fp8(q, kn, vn, kc, vc, lens, k_scale=64.0,
+                                                v_scale=32.0, ring=False, window=0, gate=None,
+                                                q_norm_w=gq, k_norm_w=gk, **kw)
+    ob, lb, kafter = orc.attention_decode(q, None, None, orc.e4m3_decode(kca) / 64.0,
+                                          orc.e4m3_decode(vca) / 32.0, lens, ring=False,
+                                          window=0, gate=None, q_norm_w=gq, k_norm_w=gk, **kw)
+    assert np.array_equal(o8, ob) and np.array_equal(l8, lb)
+    # the appended key: the oracle's K' quantized with k_scale
+    _, _, kref = orc.attention_decode(q, kn, vn, orc.e4m3_decode(kc) / 64.0,
+                                      orc.e4m3_decode(vc) / 32.0, lens, ring=False, window=0,
+                                      gate=None, q_norm_w=gq, k_norm_w=gk, **kw)
+    for b, L in enumerate(lens):
+        assert np.array_equal(kca[b, :, L - 1], orc.quantize_e4m3(kref[b, :, L - 1], 64.0)[0])
+        assert np.array_equal(vca[b, :, L - 1], orc.quantize_e4m3(vn[b], 32.0)[0])
