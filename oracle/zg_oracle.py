@@ -39,6 +39,8 @@ __all__ = [
     "E4M3_MAX",
     "e4m3_decode",
     "quantize_e4m3",
+    "e4m3_row_scale",
+    "e4m3_rows",
     "attention_decode_fp8",
     "rms_norm",
     "rope_angles",
@@ -209,7 +211,7 @@ def attention_fwd(q, k, v, gate, q_norm_w, k_norm_w, *, window: int,
 def decode_group(q_group, k_new, v_new, k_cache, v_cache, seq_len: int, *,
                  ring: bool, window: int, gate_group, q_norm_w, k_norm_w,
                  rope_dim: int, rope_theta: float, rms_eps: float,
-                 softmax_scale: float = 0.0, pos_offset: int = 0):
+                 softmax_scale: float = 0.0, pos_offset: int = 0, q_map=None):
     """One decode step for the query heads of ONE KV head of ONE sequence.
 
     q_group [G,D] raw new-token queries; k_new, v_new [D] raw new key/value
@@ -222,7 +224,9 @@ def decode_group(q_group, k_new, v_new, k_cache, v_cache, seq_len: int, *,
 
     Returns (out [G,D], lse [G], k_appended [D] or None).  Reading: the
     cache holds K' (normalised and rotated at its own position) and decode is
-    exactly row L-1 of ``attention_fwd`` over the same keys.
+    exactly row L-1 of ``attention_fwd`` over the same keys.  ``q_map``, when
+    given, is applied to the normalised, rotated queries [G,D] before the
+    scores (the E4M3 variant quantizes them there).
     """
     q_group = np.asarray(q_group, dtype=np.float64)
     G, D = q_group.shape
@@ -245,6 +249,8 @@ def decode_group(q_group, k_new, v_new, k_cache, v_cache, seq_len: int, *,
         vv[-1] = np.asarray(v_new, dtype=np.float64)
     qn = rms_norm(q_group[None], q_norm_w, rms_eps)
     qn = apply_partial_rope(qn, np.array([p]), rope_dim, rope_theta)[0]  # [G,D]
+    if q_map is not None:
+        qn = q_map(qn)
     s = tau * (qn @ kk.T)                       # [G, keys]
     m = np.max(s, axis=1, keepdims=True)
     e = np.exp(s - m)
@@ -493,10 +499,31 @@ def quantize_e4m3(x: np.ndarray, scale: float):
     return codes.astype(np.uint8), np.where(neg, -q, q)
 
 
+def e4m3_row_scale(x: np.ndarray) -> np.ndarray:
+    """Per-row power-of-two scale for quantizing a tensor computed on the fly
+    (no amax history exists for it): s = 2^(8 - e) where amax = m 2^e with
+    m in [0.5, 1) (frexp; amax = 0 gives e = 0).  Then amax * s lies in
+    [128, 256), inside E4M3's range, and the scaling itself is exact.
+    Reading: the pages scale per tensor from an amax history; for queries
+    made inside the kernel the current amax of each head's row is used."""
+    amax = np.max(np.abs(np.asarray(x, dtype=np.float64)), axis=-1)
+    _, e = np.frexp(amax)
+    return np.exp2(8.0 - e)
+
+
+def e4m3_rows(x: np.ndarray) -> np.ndarray:
+    """Each row of x [G,D] quantized to E4M3 with its ``e4m3_row_scale``;
+    returns the values the codes stand for (decode(code) / s)."""
+    x = np.asarray(x, dtype=np.float64)
+    s = e4m3_row_scale(x)
+    return np.stack([quantize_e4m3(x[r], s[r])[1] / s[r] for r in range(x.shape[0])])
+
+
 def attention_decode_fp8(q, k_new, v_new, k_codes, v_codes, seq_lens, *, k_scale: float,
                          v_scale: float, ring: bool, window: int, gate, q_norm_w, k_norm_w,
                          rope_dim: int, rope_theta: float, rms_eps: float,
-                         softmax_scale: float = 0.0, pos_offset: int = 0):
+                         softmax_scale: float = 0.0, pos_offset: int = 0,
+                         quantize_q: bool = True):
     """Decode against a KV cache stored in E4M3 ([RB] 前置知识 › FP8 混合精度训练与
     TWEO for the format and per-tensor scaling; the cache-size row of [RB]'s
     structured-data table for why the cache is what decode streams).
@@ -506,7 +533,11 @@ def attention_decode_fp8(q, k_new, v_new, k_codes, v_codes, seq_lens, *, k_scale
     the new token's K' (step 1 of ``decode_group``, in fp64) and V are
     quantized with ``quantize_e4m3`` into their slot; the step is then
     ``decode_group`` over the dequantized cache, with the new token already
-    in it.  Returns (out [B,Hq,D], lse [B,Hq], k_codes_after, v_codes_after).
+    in it.  QK^T is an E4M3 matrix multiply: with ``quantize_q`` each
+    head's normalised, rotated query is quantized by ``e4m3_rows`` first
+    (products of E4M3 values are exact, so only the sum's rounding remains).
+    P V stays in the cache's value precision.  Returns (out [B,Hq,D],
+    lse [B,Hq], k_codes_after, v_codes_after).
     """
     q = np.asarray(q, dtype=np.float64)
     B, Hq, D = q.shape
@@ -533,7 +564,8 @@ def attention_decode_fp8(q, k_new, v_new, k_codes, v_codes, seq_lens, *, k_scale
                 e4m3_decode(vc[b, g]) / v_scale, L, ring=ring, window=window,
                 gate_group=None if gate is None else gate[b, hs], q_norm_w=q_norm_w,
                 k_norm_w=k_norm_w, rope_dim=rope_dim, rope_theta=rope_theta, rms_eps=rms_eps,
-                softmax_scale=softmax_scale, pos_offset=pos_offset)
+                softmax_scale=softmax_scale, pos_offset=pos_offset,
+                q_map=e4m3_rows if quantize_q else None)
             out[b, hs] = o
             lse[b, hs] = ls
     return out, lse, kc, vc

@@ -94,9 +94,12 @@ def test_decode_fp8_uniform_scores_average_the_dequantized_values():
 
 def test_decode_fp8_two_keys_closed_form():
     """q = 5 e_0 with unit norm weights and no rotation gives
-    q'_0 = 5 / sqrt(25/128 + eps); key 0 stores code 0x40 (= 2) in dim 0, key 1
-    zeros, so the scores are tau * q'_0 * 2 / k_scale and 0 and the output is
-    the two-way softmax mix of the stored values 1 / v_scale and -1 / v_scale."""
+    q'_0 = 5 / sqrt(25/128 + eps) = 11.31; key 0 stores code 0x40 (= 2) in dim
+    0, key 1 zeros, so the scores are tau * q'_0 * 2 / k_scale and 0 and the
+    output is the two-way softmax mix of the stored values 1 / v_scale and
+    -1 / v_scale.  With the query quantized: 11.31 = 0.707 * 2^4 gives the
+    scale 2^(8-4) = 16, and 16 * 11.31 = 181.0 rounds to the E4M3 value 176
+    (the neighbours in [128, 256) are 16 apart), so q'_0 enters as 11."""
     k_scale, v_scale = 8.0, 16.0
     q = np.zeros((1, 2, D))
     q[:, :, 0] = 5.0
@@ -105,13 +108,37 @@ def test_decode_fp8_two_keys_closed_form():
     vc = np.zeros((1, 1, 4, D), dtype=np.uint8)
     vc[0, 0, 0] = 0x38
     vc[0, 0, 1] = 0xB8
-    out, lse, _, _ = _dec(q, None, None, kc, vc, [2], k_scale, v_scale)
-    qp = 5.0 / np.sqrt(25.0 / D + 1e-6)
-    s0 = qp * 2.0 / k_scale / np.sqrt(D)
-    w0 = 1.0 / (1.0 + np.exp(-s0))
-    expect = (w0 - (1.0 - w0)) / v_scale
-    assert np.allclose(out, expect, rtol=1e-13, atol=0)
-    assert np.allclose(lse, np.log(np.exp(s0) + 1.0), rtol=1e-13)
+    for quantize_q, qp in ((False, 5.0 / np.sqrt(25.0 / D + 1e-6)), (True, 11.0)):
+        out, lse, _, _ = _dec(q, None, None, kc, vc, [2], k_scale, v_scale,
+                              quantize_q=quantize_q)
+        s0 = qp * 2.0 / k_scale / np.sqrt(D)
+        w0 = 1.0 / (1.0 + np.exp(-s0))
+        expect = (w0 - (1.0 - w0)) / v_scale
+        assert np.allclose(out, expect, rtol=1e-13, atol=0), quantize_q
+        assert np.allclose(lse, np.log(np.exp(s0) + 1.0), rtol=1e-13), quantize_q
+
+
+def test_e4m3_row_scale_and_rows():
+    """The row scale is the power of two that puts the row's amax in
+    [128, 256); a row whose values are on the E4M3 grid at that scale comes
+    back unchanged, and any row comes back within half an E4M3 quantum."""
+    assert orc.e4m3_row_scale(np.array([[1.0, -0.5]]))[0] == 128.0     # 1 = 0.5 * 2^1
+    assert orc.e4m3_row_scale(np.array([[0.75, 3.0]]))[0] == 64.0      # 3 = 0.75 * 2^2
+    assert orc.e4m3_row_scale(np.array([[-448.0]]))[0] == 2.0 ** -1    # 448 = 0.875 * 2^9
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((6, 128)) * np.exp2(rng.uniform(-8, 8, (6, 1)))
+    s = orc.e4m3_row_scale(x)
+    amax = np.abs(x).max(axis=1)
+    assert np.all((amax * s >= 128) & (amax * s < 256))
+    assert np.all(np.log2(s) == np.round(np.log2(s)))
+    grid = orc.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))       # the non-negative values
+    on = rng.choice(grid[grid <= 224], (3, 128)) * rng.choice([-1, 1], (3, 128))
+    on[:, 0] = 192.0                                                  # amax 192: scale 1
+    assert np.array_equal(orc.e4m3_rows(on), on)
+    y = orc.e4m3_rows(x)
+    xs = np.abs(x * s[:, None])
+    quantum = np.where(xs < 2.0**-6, 2.0**-9, np.exp2(np.floor(np.log2(np.maximum(xs, 2.0**-6))) - 3))
+    assert np.all(np.abs(y - x) * s[:, None] <= quantum / 2 + 1e-300)
 
 
 def test_decode_fp8_ring_overwrites_the_oldest_slot():
@@ -147,7 +174,7 @@ def test_decode_fp8_is_decode_over_the_dequantized_cache():
     lens = [13, 40]
     o8, l8, kca, vca = orc.attention_decode_fp8(q, kn, vn, kc, vc, lens, k_scale=64.0,
                                                 v_scale=32.0, ring=False, window=0, gate=None,
-                                                q_norm_w=gq, k_norm_w=gk, **kw)
+                                                q_norm_w=gq, k_norm_w=gk, quantize_q=False, **kw)
     ob, lb, kafter = orc.attention_decode(q, None, None, orc.e4m3_decode(kca) / 64.0,
                                           orc.e4m3_decode(vca) / 32.0, lens, ring=False,
                                           window=0, gate=None, q_norm_w=gq, k_norm_w=gk, **kw)
