@@ -54,12 +54,13 @@ static_assert(16 * (kD + 2 * kMaxRopeHalf) * 4 <= kVtBytes, "append scratch must
 // FUSED: the launch has one split per (b, kv head), so this workgroup owns
 // the whole key range: it appends the new token itself, before reading the
 // cache, and writes the normalised, gated output instead of a partial.
-// FP8: the cache holds E4M3 codes (one byte per element).  Each code is
-// widened to bf16 in registers, which is exact, so the MFMAs and the softmax
-// are those of the bf16 cache; the launch folds 1 / k_scale into the score
-// scale and the epilogue multiplies by 1 / v_scale.  The dims of Q' and K'
-// are fed to the MFMAs in another (common) order, so that a lane reads 32
-// consecutive bytes of a key row.
+// FP8: the cache holds E4M3 codes (one byte per element).  S^T = K' Q'^T
+// runs on the FP8 matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4): the key
+// codes as loaded (32 consecutive bytes of a key row per lane) against the
+// query rows quantized per head with a power-of-two scale.  The value codes
+// are widened to bf16 in registers, which is exact, for the bf16 PV MFMAs.
+// The launch folds 1 / k_scale into the score scale, each lane multiplies in
+// its head's 1 / s_q, and the epilogue multiplies by 1 / v_scale.
 template <bool PAGED, bool FUSED, bool FP8>
 __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[kVtBytes + kQsBytes + kQnBytes];
@@ -199,14 +200,45 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
                             : v * cs + qn[c * kD + d - p.rope_half] * sn;
       }
     }
-    qs[c * kQsStride + d] = __builtin_bit_cast(uint16_t, (__bf16)v);
+    if constexpr (FP8) reinterpret_cast<float*>(smem)[c * kD + d] = v;  // V^T area: free here
+    else qs[c * kQsStride + d] = __builtin_bit_cast(uint16_t, (__bf16)v);
   }
   __syncthreads();
   bf16x8 qf[4];
+  i32x8 qb;          // FP8: this lane's B operand, codes of dims 32kg..32kg+31 of head col
+  float qinv = 1.f;  // FP8: 1 / (that head's query scale)
+  if constexpr (FP8) {
+    // each head's row of Q' to E4M3 with the power-of-two scale 2^(8-e),
+    // amax = m 2^e (m in [0.5, 1), e >= -100): 16 threads per row, 8 dims each
+    const float* qr = reinterpret_cast<const float*>(smem);
+    const int c = tid >> 4, part = tid & 15;
+    float x8[8];
+    float am = 0.f;
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
-    qf[kk] = *reinterpret_cast<const bf16x8*>(qs + col * kQsStride +
-                                              (FP8 ? 32 * kg + 8 * kk : 32 * kk + 8 * kg));
+    for (int i = 0; i < 8; ++i) {
+      x8[i] = qr[c * kD + 8 * part + i];
+      am = fmaxf(am, fabsf(x8[i]));
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) am = fmaxf(am, __shfl_xor(am, o, 16));
+    int e;
+    frexpf(am, &e);
+    e = max(e, -100);
+    uint8_t* q8 = reinterpret_cast<uint8_t*>(qs);
+    st8(q8 + c * kD + 8 * part, pack_e4m3x8(x8, ldexpf(1.0f, 8 - e)));
+    if (part == 0) qn[c] = ldexpf(1.0f, e - 8);  // qn is dead after the rotation
+    __syncthreads();
+    const u32x4 lo = ld16(q8 + col * kD + 32 * kg), hi = ld16(q8 + col * kD + 32 * kg + 16);
+    qb = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    qinv = qn[col];
+  } else {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      qf[kk] = *reinterpret_cast<const bf16x8*>(qs + col * kQsStride + 32 * kk + 8 * kg);
+  }
+  // score scale in exp2 units of this lane's head
+  const float sl2 = FP8 ? p.scale_log2 * qinv : p.scale_log2;
 
   // ---- stream the split's keys.  Cache row of key `key` relative to the
   // cache base: a contiguous slab per (b, kv head), or the key's page slot
@@ -227,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const int nit = end > start ? (end - start + kKeysPerIter - 1) / kKeysPerIter : 0;
   const int mr = lane & 15;
   const int krel = 8 * (mr >> 2) + (mr & 3);  // + 4*blk: key of MFMA row mr
-  const float rescale_raw = kRescaleThreshold / p.scale_log2;
+  const float rescale_raw = kRescaleThreshold / sl2;
 
   // The raw cache bytes of the next kDepth slices are in flight while a
   // slice is processed, so that a wave keeps loads moving during its MFMAs
@@ -288,35 +320,43 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     const int base = start + it * kKeysPerIter + wvu * kKeysPerWave;  // wave-uniform
     bf16x8 kf[2][4];
     u32x4 vr[8];
+    f32x4 s[2];
+    if constexpr (FP8) {
+      // S^T = K' Q'^T on the FP8 matrix cores: the key codes as they came
+      // (row krel, bytes 32kg..32kg+31) against the query codes, one
+      // 16 x 16 x 128 product per 16 keys; block scales 1 (E8M0 127)
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        if constexpr (FP8) {
-          const u32x4& c = rk[d][blk][kk >> 1];
-          kf[blk][kk] = __builtin_bit_cast(
-              bf16x8, widen_e4m3x8(make_uint2(c[2 * (kk & 1)], c[2 * (kk & 1) + 1])));
-        } else {
-          kf[blk][kk] = __builtin_bit_cast(bf16x8, rk[d][blk][kk]);
-        }
+      for (int blk = 0; blk < 2; ++blk) {
+        const u32x4& lo = rk[d][blk][0];
+        const u32x4& hi = rk[d][blk][1];
+        const i32x8 ka = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        s[blk] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ka, qb, f32x4{}, 0, 0, 0, 127,
+                                                                  0, 127);
       }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if constexpr (FP8) vr[j] = widen_e4m3x8(rv8[d][j]);
-      else vr[j] = rv16[d][j];
+      for (int j = 0; j < 8; ++j) vr[j] = widen_e4m3x8(rv8[d][j]);
+    } else {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) kf[blk][kk] = __builtin_bit_cast(bf16x8, rk[d][blk][kk]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) vr[j] = rv16[d][j];
     }
     // the buffer's old contents are consumed before its refill is issued,
     // so the refill lands in the same registers (no copies at the loop end)
     __builtin_amdgcn_sched_barrier(0);
     load_slice(min(it + kDepth, nit - 1), d);
 
-    f32x4 s[2];
+    if constexpr (!FP8) {
 #pragma unroll
-    for (int blk = 0; blk < 2; ++blk) {
-      s[blk] = f32x4{};
+      for (int blk = 0; blk < 2; ++blk) {
+        s[blk] = f32x4{};
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[blk][kk], qf[kk], s[blk], 0, 0, 0);
+        for (int kk = 0; kk < 4; ++kk)
+          s[blk] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[blk][kk], qf[kk], s[blk], 0, 0, 0);
+      }
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -333,19 +373,19 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
     if (__builtin_amdgcn_ballot_w64(m_new > m_run + rescale_raw)) {
-      const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2((m_run - m_new) * p.scale_log2);
+      const float alpha = m_new == -INFINITY ? 1.0f : fast_exp2((m_run - m_new) * sl2);
 #pragma unroll
       for (int db = 0; db < 8; ++db) o[db] *= alpha;
       l_run *= alpha;
       m_run = m_new;
     }
-    const float neg_mc = m_run == -INFINITY ? 0.0f : -m_run * p.scale_log2;
+    const float neg_mc = m_run == -INFINITY ? 0.0f : -m_run * sl2;
     float pv[8];
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pv[4 * blk + e] = fast_exp2(__builtin_fmaf(s[blk][e], p.scale_log2, neg_mc));
+        pv[4 * blk + e] = fast_exp2(__builtin_fmaf(s[blk][e], sl2, neg_mc));
         l_run += pv[4 * blk + e];
       }
     }
@@ -375,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   l_run += __shfl_xor(l_run, 32, 64);
   __syncthreads();  // V^T tiles are dead; reuse them for red_o
   if (kg == 0) {
-    red_m[wv][col] = m_run == -INFINITY ? -INFINITY : m_run * p.scale_log2;
+    red_m[wv][col] = m_run == -INFINITY ? -INFINITY : m_run * sl2;
     red_l[wv][col] = l_run;
   }
   if (col < grp) {

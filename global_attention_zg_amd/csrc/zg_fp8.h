@@ -14,6 +14,9 @@ namespace zg {
 
 constexpr float kE4M3Max = 448.0f;
 
+// 32 bytes per lane: an A or B operand of the FP8 MFMAs (v_mfma_scale_*_f8f6f4)
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
 // Codes of x[0..7] * scale (product in fp32, clamped, then v_cvt_pk_fp8_f32,
 // which rounds to nearest even), bytes in element order.
 __device__ __forceinline__ uint2 pack_e4m3x8(const float* x, float scale) {

@@ -193,11 +193,15 @@ int zg_attn_decode_paged(const zg_attn_params* p,
  * with the product formed in fp32, clamped to [-448, 448] and rounded to
  * the nearest E4M3 value, ties to even (the codes zg_quantize_fp8 writes).
  * A cached key then stands for decode(code) / k_scale and a value for
- * decode(code) / v_scale, and the attention is zg_attn_decode's over those
- * values (up to fp32 rounding order): the kernel widens each code to bf16
- * without rounding, runs the bf16 MFMAs and the fp32 softmax, and applies
- * 1 / k_scale in the score scale and 1 / v_scale to the output.  A step
- * reads half the bytes of a bf16 cache.
+ * decode(code) / v_scale.  QK^T is an E4M3 product on the FP8 matrix cores:
+ * each query head's normalised, rotated row q' is quantized to E4M3 with the
+ * power-of-two scale s_q = 2^(8 - e), where amax|q'| = m 2^e, m in [0.5, 1)
+ * and e >= -100 (so amax * s_q lies in [128, 256)), and the scores are the
+ * fp32 sums of exact code products times 1 / (s_q k_scale).  The softmax is
+ * fp32; PV runs on the bf16 matrix cores with each value code widened to
+ * bf16 (exact: every E4M3 value is a bf16 value) and P rounded to bf16, and
+ * 1 / v_scale is applied to the output.  A step reads half the bytes of a
+ * bf16 cache.
  * Scales must be finite and > 0 (else ZG_ERR_INVALID). */
 
 /* zg_attn_decode with uint8 caches k_cache / v_cache [B,Hkv,cache_cap,D] of

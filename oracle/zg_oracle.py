@@ -502,13 +502,14 @@ def quantize_e4m3(x: np.ndarray, scale: float):
 def e4m3_row_scale(x: np.ndarray) -> np.ndarray:
     """Per-row power-of-two scale for quantizing a tensor computed on the fly
     (no amax history exists for it): s = 2^(8 - e) where amax = m 2^e with
-    m in [0.5, 1) (frexp; amax = 0 gives e = 0).  Then amax * s lies in
-    [128, 256), inside E4M3's range, and the scaling itself is exact.
-    Reading: the pages scale per tensor from an amax history; for queries
-    made inside the kernel the current amax of each head's row is used."""
+    m in [0.5, 1) (frexp; amax = 0 gives e = 0), e clamped to >= -100 so that
+    s stays finite in float32.  Then amax * s lies in [128, 256), inside
+    E4M3's range, and the scaling itself is exact.  Reading: the pages scale
+    per tensor from an amax history; for queries made inside the kernel the
+    current amax of each head's row is used."""
     amax = np.max(np.abs(np.asarray(x, dtype=np.float64)), axis=-1)
     _, e = np.frexp(amax)
-    return np.exp2(8.0 - e)
+    return np.exp2(8.0 - np.maximum(e, -100))
 
 
 def e4m3_rows(x: np.ndarray) -> np.ndarray:

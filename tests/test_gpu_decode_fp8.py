@@ -2,12 +2,16 @@
 zg_attn_decode_paged_fp8) against the fp64 oracle, through the C ABI.
 
 The oracle is attention_decode_fp8: decode over the dequantized cache after
-the new token's K' and V are quantized into their slot.  Outputs meet the
-same bf16 bar as the bf16 cache (the kernel's only extra step, widening a
-code to bf16, is exact).  Appended V codes are bit-exact (the same fp32
-product and rounding on both sides).  Appended K codes may differ by one
-code step where the kernel's fp32 K' and the oracle's fp64 K' straddle a
-rounding boundary; every other cache byte is unchanged."""
+the new token's K' and V are quantized into their slot, with each query
+head's row quantized to E4M3 for the QK^T product.  Outputs meet the same
+bf16 bar as the bf16 cache: E4M3 products are exact in fp32 and widening a
+value code to bf16 is exact, so the kernel differs from the oracle only by
+fp32 summation order, the bf16 P and output, and the rare query code that
+sits one step away (the kernel's fp32 q' against the oracle's fp64 q' on
+either side of a rounding boundary).  Appended V codes are bit-exact (the
+same fp32 product and rounding on both sides).  Appended K codes may differ
+by one code step for the same reason as query codes; every other cache byte
+is unchanged."""
 
 import sys
 
@@ -253,3 +257,33 @@ def test_decode_fp8_deterministic():
     a, _, _ = run_gpu(c, lens, 0, 0, num_splits=5)
     b, _, _ = run_gpu(c, lens, 0, 0, num_splits=5)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_decode_fp8_query_enters_quantized():
+    """The two-key closed form of the oracle's pins, on the GPU: q = 5 e_0
+    with unit norm weights and no rotation gives q'_0 = 11.31, which enters
+    QK^T as the E4M3 value 176 / 16 = 11.  Key 0 stores 1.0 in dim 0 (k_scale
+    1), key 1 zeros; values +1 and -1.  The output (2 sigma(tau * 11) - 1 =
+    0.4511) is 0.011 away from what an unquantized query gives (0.4621)."""
+    bd = _binding()
+    q = torch.zeros((1, 1, D), dtype=torch.bfloat16, device="cuda")
+    q[0, 0, 0] = 5.0
+    kc = torch.zeros((1, 1, 4, D), dtype=torch.uint8, device="cuda")
+    kc[0, 0, 0, 0] = 0x38
+    vc = torch.zeros_like(kc)
+    vc[0, 0, 0] = 0x38
+    vc[0, 0, 1] = 0xB8
+    ones = torch.ones(D, dtype=torch.float32, device="cuda")
+    sl = torch.tensor([2], dtype=torch.int32, device="cuda")
+    tau = 1.0 / np.sqrt(D)
+    expect = 2.0 / (1.0 + np.exp(-tau * 11.0)) - 1.0
+    unquantized = 2.0 / (1.0 + np.exp(-tau * 5.0 / np.sqrt(25.0 / D + 1e-6))) - 1.0
+    for ns in (1, 2):
+        out = torch.full_like(q, float("nan"))
+        bd.zg_attn_decode_fp8(q, None, None, kc, vc, sl, ring=0, window=0, k_scale=1.0,
+                              v_scale=1.0, gate=None, q_norm_w=ones, k_norm_w=ones, rope_dim=0,
+                              num_splits=ns, out=out)
+        torch.cuda.synchronize()
+        got = _f(out[0, 0])
+        assert np.all(np.abs(got - expect) < 2e-3), (ns, got[:4], expect)
+        assert np.all(np.abs(got - unquantized) > 8e-3)
