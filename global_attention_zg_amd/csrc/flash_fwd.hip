@@ -21,7 +21,8 @@
 //                   transposing LDS load ds_read_b64_tr_b16, B = P in registers)
 //
 // K' and V tiles go from global memory straight into LDS (global_load_lds,
-// no register staging) through a ring of three stages, row-major with
+// no register staging) through a ring (three tile stages, or four pairs of
+// tiles for the global layer), row-major with
 // 256-byte rows whose 16-byte chunks are XOR-swizzled by row: chunk ^ (row &
 // 15) for K', chunk ^ ((row & 3) << 2) for V.  With the 64-bank LDS every
 // MFMA operand read is then free of bank conflicts, and each read address is
@@ -36,7 +37,8 @@
 // accumulator (only when the running max grows by more than 2^8 in exp2
 // units).  In the global kernel the two waves that share a SIMD alternate
 // between an MFMA phase and a softmax phase, so that one wave's softmax
-// (VALU) runs under the other's matrix work.
+// (VALU) runs under the other's matrix work; each phase covers a pair of
+// tiles (64 keys), with one running-max update per pair.
 
 #include <type_traits>
 
@@ -61,16 +63,19 @@ template <bool BANDED> struct Cfg {
 constexpr int kBN = 32;                          // keys per KV tile (one MFMA block)
 constexpr int kRowBytes = kD * 2;                // 256-byte K'/V rows in LDS, 16-byte chunks XOR-swizzled
 constexpr int kTileBytes = kBN * kRowBytes;      // 8192 per K' or V stage
-// LDS ring of three stages per K' and V: copies fly two tiles ahead.  K'
-// stages come first, then the V stages.
+// LDS ring per K' and V, K' stages first, then the V stages.  Windowed
+// layers: three tile stages, copies fly two tiles ahead.  Global layers work
+// on pairs of tiles: four pair stages (eight tiles), copies fly two pairs
+// ahead (the fourth stage holds the pair the other wave of the SIMD may
+// still be reading).
 template <bool BANDED> struct Ring {
-  static constexpr int kStages = 3;
+  static constexpr int kStages = BANDED ? 3 : 8;
   static constexpr int kVOff = kStages * kTileBytes;
   static constexpr int kTilesBytes = 2 * kStages * kTileBytes;
 };
 constexpr int kQScratchBytes = Cfg<false>::kWaves * 32 * 65 * 4;  // query-prologue RoPE rows (reused)
 constexpr int kSmemGlobal =
-    Ring<false>::kTilesBytes > kQScratchBytes ? Ring<false>::kTilesBytes : kQScratchBytes;  // 66560
+    Ring<false>::kTilesBytes > kQScratchBytes ? Ring<false>::kTilesBytes : kQScratchBytes;  // 131072
 // Windowed layers also stage their query rows (8 KB per wave) behind the
 // tiles, and after the loop their fp32 output rows (16 KB per wave) for
 // coalesced stores.
@@ -365,9 +370,23 @@ __global__ __launch_bounds__(Cfg<BANDED>::kThreads, 2) void flash_fwd_kernel(Fla
   // tiles, and on a gated windowed layer the gate rows, are requested before
   // the query rows so their latencies overlap; the generic rotation needs LDS
   // first.
+  // Global layers: pair j holds tiles t_hi - 2j and t_hi - 2j - 1 in tile
+  // stages 2 (j % 4) and 2 (j % 4) + 1.  An odd tile count ends with tile
+  // -1: it is loaded from tile 0 (finite values) and masked out entirely.
+  const int np = (nt + 1) / 2;
+  auto gload_pair = [&](int j) {
+    const int ps = j & 3;
+    gload(t_hi - 2 * j, 2 * ps);
+    gload(max(t_hi - 2 * j - 1, 0), 2 * ps + 1);
+  };
   auto first_loads = [&] {
-    gload(t_hi, 0);
-    if (nt > 1) gload(t_hi - 1, 1);
+    if (BANDED) {
+      gload(t_hi, 0);
+      if (nt > 1) gload(t_hi - 1, 1);
+    } else {
+      gload_pair(0);
+      if (np > 1) gload_pair(1);
+    }
   };
   // Windowed layers move their query, gate and output rows in whole 256-byte
   // rows (16 lanes per row): each wave's 32 query rows go straight to LDS,
@@ -483,71 +502,100 @@ __global__ __launch_bounds__(Cfg<BANDED>::kThreads, 2) void flash_fwd_kernel(Fla
   if (BANDED && gate_pre) {
     if (nt > 1) sync_tiles<kCopies + 8>();
     else sync_tiles<8>();
-  } else {
+  } else if (BANDED) {
     if (nt > 1) sync_tiles<kCopies>();
+    else sync_tiles<0>();
+  } else {
+    // pair 0 (pair 1's copies may fly)
+    if (np > 1) sync_tiles<2 * kCopies>();
     else sync_tiles<0>();
   }
   if constexpr (BANDED) {
     for (int j = 0; j < nt; ++j) step(j, std::true_type{});
   } else {
-    // Global layers: the two waves on each SIMD (w and w + 4) take turns.
-    // Every wave runs the same sequence of phases separated by barriers:
-    // MFMA phase k (PV of tile k-1 while the K' operand reads of tile k fly,
-    // then QK' of tile k and the V operand reads of tile k) and softmax
-    // phase k (scores of tile k -> P).  Wave w + 4 passes one extra barrier
-    // first and wave w one extra at the end, so that one runs its MFMA
-    // phase while the other runs its softmax phase.
+    // Global layers: the two waves on each SIMD (w and w + 4) take turns,
+    // on pairs of 32-key tiles.  Every wave runs the same sequence of phases
+    // separated by barriers: softmax phase j (scores of pair j -> P) and
+    // MFMA phase j (PV of pair j and QK' of pair j + 1, interleaved so that
+    // each group of LDS operand reads flies under the previous eight
+    // MFMAs).  Wave w + 4 passes one extra barrier first and wave w one
+    // extra at the end, so that one runs its MFMA phase while the other runs
+    // its softmax phase.
     //
-    // Tile k+2 is copied into the stage of tile k-1 at the top of softmax
-    // phase k: every wave has finished reading tile k-1 by then (its reads
-    // end with the lgkmcnt(0) before the barrier closing softmax phase k-1).
-    // Barriers after an MFMA phase wait for every copy in flight (tile k+1),
-    // those after a softmax phase for all but the copies just issued, so
-    // tile k+1 has landed for every wave before the barrier that opens
-    // either wave's MFMA phase k+1.
+    // Pair j + 2 is copied into the stage of pair j - 2 at the top of softmax
+    // phase j: the other wave of the SIMD is then in MFMA phase j - 1, which
+    // reads pairs j - 1 and j only.  Barriers after an MFMA phase wait for
+    // every copy in flight (pair j + 2), those after a softmax phase for all
+    // but the copies just issued, so pair j + 1 has landed for every wave
+    // before the barrier that opens either wave's MFMA phase j.
     const bool second = wvu >= 4;
-    bf16x8 ka[8], va[8], pf[2];
-    f32x16 s;
-    auto qk_part = [&](int stg) {
-      qk_mfma(s, ka, qf);
+    bf16x8 ka[8], va[8], pf[4];
+    f32x16 sa, sb;
+    auto kstage = [&](int j, int u) { return smem + (2 * (j & 3) + u) * kTileBytes; };
+    auto vops = [&](int j, int u) {
       const lds_u8* vr[4];
 #pragma unroll
-      for (int bd = 0; bd < 4; ++bd) vr[bd] = vread0[bd] + stg * kTileBytes;
+      for (int bd = 0; bd < 4; ++bd) vr[bd] = vread0[bd] + (2 * (j & 3) + u) * kTileBytes;
       load_vops(va, vr);
     };
-    auto v_phase = [&](int k) {
-      const int t = t_hi - k;
-      if (t * kBN + kBN - 1 > wrow0) mask_blk(s, t * kBN, qm, lim, half);
-      const float neg_mc = softmax_rescale(st, blk_max(s), c, rescale_raw);
-      exp_blk(st, s, c, neg_mc, pf);
-      pin(pf[0]);
-      pin(pf[1]);
+    auto pv2 = [&](int t) {  // PV of one tile of the pair: P in pf[2t], pf[2t+1]
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int bd = 0; bd < 4; ++bd)
+          st.acc[bd] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[4 * kt + bd], pf[2 * t + kt], st.acc[bd], 0, 0, 0);
+      }
+    };
+    auto s_phase = [&](int j) {
+      const int ta = t_hi - 2 * j, tb = ta - 1;
+      if (ta * kBN + kBN - 1 > wrow0) mask_blk(sa, ta * kBN, qm, lim, half);
+      if (tb < 0 || tb * kBN + kBN - 1 > wrow0) mask_blk(sb, tb * kBN, qm, lim, half);
+      const float neg_mc = softmax_rescale(st, fmaxf(blk_max(sa), blk_max(sb)), c, rescale_raw);
+      bf16x8 p2[2];
+      exp_blk(st, sa, c, neg_mc, p2);
+      pf[0] = p2[0];
+      pf[1] = p2[1];
+      exp_blk(st, sb, c, neg_mc, p2);
+      pf[2] = p2[0];
+      pf[3] = p2[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pin(pf[i]);
       pin(st.l_run);
     };
     if (second) phase_barrier();
-    load_kops(ka, smem, kread_off);
-    qk_part(0);
+    // QK' of pair 0 and the V operands of its first tile
+    load_kops(ka, kstage(0, 0), kread_off);
+    qk_mfma(sa, ka, qf);
+    __builtin_amdgcn_sched_barrier(0);
+    load_kops(ka, kstage(0, 1), kread_off);
+    qk_mfma(sb, ka, qf);
+    vops(0, 0);
     phase_sync<0, false>();
-    int sk = 0;  // stage of tile k
-    for (int k = 0; k < nt; ++k) {
-      const int s1 = sk == 2 ? 0 : sk + 1;  // tile k+1
-      const int s2 = s1 == 2 ? 0 : s1 + 1;  // tile k+2 (held tile k-1)
-      if (k + 2 < nt) gload(t_hi - (k + 2), s2);
-      v_phase(k);
-      if (k + 2 < nt) phase_sync<kCopies, true>();
+    for (int j = 0; j < np; ++j) {
+      if (j + 2 < np) gload_pair(j + 2);
+      s_phase(j);
+      if (j + 2 < np) phase_sync<2 * kCopies, true>();
       else phase_sync<0, true>();
-      if (k + 1 < nt) {
-        load_kops(ka, smem + s1 * kTileBytes, kread_off);
-        pv_mfma(st, va, pf);
-        // keep the next V operand reads below the MFMAs that consume the
-        // current ones (otherwise both sets are live at once)
+      if (j + 1 < np) {
+        load_kops(ka, kstage(j + 1, 0), kread_off);
+        pv2(0);
         __builtin_amdgcn_sched_barrier(0);
-        qk_part(s1);
+        vops(j, 1);
+        qk_mfma(sa, ka, qf);
+        __builtin_amdgcn_sched_barrier(0);
+        load_kops(ka, kstage(j + 1, 1), kread_off);
+        pv2(1);
+        __builtin_amdgcn_sched_barrier(0);
+        vops(j + 1, 0);
+        qk_mfma(sb, ka, qf);
         phase_sync<0, false>();
       }
-      sk = s1;
     }
-    pv_mfma(st, va, pf);
+    pv2(0);
+    __builtin_amdgcn_sched_barrier(0);
+    vops(np - 1, 1);
+    pv2(1);
     if (!second) phase_barrier();
   }
 

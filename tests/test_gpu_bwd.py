@@ -46,7 +46,7 @@ def bwd_case(name, B, S, Hq, Hkv, gated):
     return c
 
 
-def run_gpu(c, window, gated=True, poison=True, **kw):
+def run_gpu(c, window, gated=True, poison=True, fwd_window=None, **kw):
     bd = _binding()
     q, k, v = (zc.to_dev(c[n], torch) for n in ("q", "k", "v"))
     g = zc.to_dev(c["gate"], torch) if gated else None
@@ -55,7 +55,8 @@ def run_gpu(c, window, gated=True, poison=True, **kw):
     gk = torch.from_numpy(c["gk"]).cuda()
     args = dict(KW)
     args.update(kw)
-    out, lse = bd.zg_attn_fwd(q, k, v, g, gq, gk, window=window, want_lse=True, **args)
+    out, lse = bd.zg_attn_fwd(q, k, v, g, gq, gk, want_lse=True,
+                              window=window if fwd_window is None else fwd_window, **args)
     bufs = {}
     if poison:
         bufs = dict(dq=torch.full_like(q, float("nan")), dk=torch.full_like(k, float("nan")),
@@ -108,11 +109,14 @@ def test_bwd_matches_oracle(B, S, Hq, Hkv, window, gated):
 
 
 def test_bwd_window_at_least_s_is_global_bitwise():
+    """The backward with window >= S gives the global backward's bits when
+    both are fed the same forward output and LSE (the global forward's)."""
     c = bwd_case("bwd_wide", 1, 300, 8, 2, False)
     a = run_gpu(c, 0, gated=False)
-    b = run_gpu(c, 300, gated=False)
-    for n in ("dq", "dk", "dv", "dq_norm_w", "dk_norm_w"):
-        assert torch.equal(a["raw"][n], b["raw"][n]), n
+    for W in (300, 301, 5000):
+        b = run_gpu(c, W, gated=False, fwd_window=0)
+        for n in ("dq", "dk", "dv", "dq_norm_w", "dk_norm_w"):
+            assert torch.equal(a["raw"][n], b["raw"][n]), (W, n)
 
 
 def test_bwd_is_deterministic():

@@ -161,13 +161,28 @@ def test_gate_plus_inf_is_bitwise_ungated():
     assert torch.all(z.float() == 0)
 
 
-def test_window_at_least_S_is_bitwise_global():
+def test_window_at_least_S_is_global():
+    """The windowed kernel with window >= S computes global attention.  The
+    global kernel takes one running max and one rescale vote per pair of
+    32-key tiles and the windowed kernel per tile, so P is rounded to bf16
+    against different maxima on some rows.  A bf16 P carries 2^-9 of
+    relative rounding, so an output that is a small sum of terms near 1
+    moves by a few 1e-3 in absolute terms (measured 1.8e-3, rel-RMS 1.3e-3,
+    LSE 1.6e-3).  Bounds: 2^-6 of the value + 4e-3 per element, 2e-3
+    rel-RMS, 5e-3 on the LSE; and each meets the oracle."""
     c = zc.fwd_case(108, 2, 333, 8, 2, gated=False)
     a = run_gpu(c, 0, gated=False)
+    o, l = orc.attention_fwd(zc.f64(c["q"]), zc.f64(c["k"]), zc.f64(c["v"]), None,
+                             c["gq"].astype(np.float64), c["gk"].astype(np.float64), window=0, **KW)
+    zc.compare(a["out"], o, "global")
+    ref = a["out"]
     for W in (333, 334, 5000):
         b = run_gpu(c, W, gated=False)
-        assert torch.equal(a["raw_out"].view(torch.int16), b["raw_out"].view(torch.int16))
-        assert np.array_equal(a["lse"], b["lse"])
+        zc.compare(b["out"], o, f"W={W}")
+        d = b["out"] - ref
+        assert np.all(np.abs(d) <= 2.0 ** -6 * np.abs(ref) + 4e-3), float(np.abs(d).max())
+        assert float(np.sqrt((d * d).sum() / (ref * ref).sum())) <= 2e-3
+        assert float(np.abs(b["lse"] - a["lse"]).max()) <= 5e-3
 
 
 def test_window_one_is_gated_value():
