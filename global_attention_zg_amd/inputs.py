@@ -94,17 +94,28 @@ def sign_magnitude_bytes(key, total: int, lo: int, hi: int, start: int = 0,
                          stop: int | None = None) -> np.ndarray:
     """Elements [start, stop) of a seeded uint8 tensor ``key`` of ``total``
     bytes: the low 7 bits uniform on [lo, hi) (0 <= lo < hi <= 128), the top
-    bit a fair coin.  Chunked and seeded like ``normal_bf16_bits``."""
+    bit a fair coin (one uniform draw x on [0, 2 (hi - lo)) per byte: the
+    magnitude is lo + x // 2 and the sign x % 2).  Chunked and seeded like
+    ``normal_bf16_bits``."""
     assert 0 <= lo < hi <= 128
     stop = total if stop is None else stop
     assert 0 <= start <= stop <= total
     res = np.empty(stop - start, dtype=np.uint8)
-    for c in range(start // CHUNK, (stop + CHUNK - 1) // CHUNK):
+
+    def work(c):
         base = c * CHUNK
         ln = min(CHUNK, total - base)
         g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([SEED_BASE, *key, c])))
-        mag = g.integers(lo, hi, ln, dtype=np.uint8)
-        sign = g.integers(0, 2, ln, dtype=np.uint8) << np.uint8(7)
+        x = g.integers(0, 2 * (hi - lo), ln, dtype=np.uint8)
+        b = (np.uint8(lo) + (x >> np.uint8(1))) | ((x & np.uint8(1)) << np.uint8(7))
         s0, s1 = max(start, base), min(stop, base + ln)
-        res[s0 - start:s1 - start] = (mag | sign)[s0 - base:s1 - base]
+        res[s0 - start:s1 - start] = b[s0 - base:s1 - base]
+
+    c0, c1 = start // CHUNK, (stop + CHUNK - 1) // CHUNK
+    if c1 - c0 <= 1:
+        for c in range(c0, c1):
+            work(c)
+    else:
+        with ThreadPoolExecutor(_threads()) as ex:
+            list(ex.map(work, range(c0, c1)))
     return res

@@ -287,3 +287,60 @@ def test_decode_fp8_query_enters_quantized():
         got = _f(out[0, 0])
         assert np.all(np.abs(got - expect) < 2e-3), (ns, got[:4], expect)
         assert np.all(np.abs(got - unquantized) > 8e-3)
+
+
+def _fill_codes(key, B, Hkv, cap, lo, hi):
+    """Seeded E4M3 cache [B,Hkv,cap,D] built on the device one sequence at a
+    time: magnitude codes in [lo, hi) with a random sign."""
+    t = torch.empty((B, Hkv, cap, D), dtype=torch.uint8, device="cuda")
+    per_b = Hkv * cap * D
+    for b in range(B):
+        t[b] = torch.from_numpy(inputs.sign_magnitude_bytes(key, B * per_b, lo, hi, b * per_b,
+                                                            (b + 1) * per_b)).reshape(
+            Hkv, cap, D).cuda()
+    return t
+
+
+def test_decode_fp8_256k_cache():
+    """B16, one new token at position 262144 against 262144 cached positions
+    in E4M3 (the bench's 256K step, automatic split count).  Codes have
+    magnitudes 2^-3..15 (exponent fields 4..10), so at scale 16 the cache
+    holds values in [2^-7, 0.94].  Checked against the oracle on sampled
+    (sequence, KV head) groups, and the appended slot's codes."""
+    bd = _binding()
+    B, Hq, Hkv, L = 16, 32, 8, 262145
+    tag, ks, vs = 311, 16.0, 16.0
+    kkey, vkey = (tag, 0, inputs.T_KCACHE), (tag, 0, inputs.T_VCACHE)
+    kc = _fill_codes(kkey, B, Hkv, L, 0x20, 0x58)
+    vc = _fill_codes(vkey, B, Hkv, L, 0x20, 0x58)
+    qb = zc.bits((tag, 0, inputs.T_Q), (B, Hq, D))
+    knb = zc.bits((tag, 0, inputs.T_KNEW), (B, Hkv, D))
+    vnb = zc.bits((tag, 0, inputs.T_VNEW), (B, Hkv, D))
+    gq = inputs.norm_weight((tag, 0, inputs.T_GQ), D)
+    gk = inputs.norm_weight((tag, 0, inputs.T_GK), D)
+    sl = torch.full((B,), L, dtype=torch.int32, device="cuda")
+    out = torch.full((B, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+    bd.zg_attn_decode_fp8(zc.to_dev(qb, torch), zc.to_dev(knb, torch), zc.to_dev(vnb, torch), kc,
+                          vc, sl, ring=0, window=0, k_scale=ks, v_scale=vs, gate=None,
+                          q_norm_w=torch.from_numpy(gq).cuda(),
+                          k_norm_w=torch.from_numpy(gk).cuda(), out=out, **KW)
+    torch.cuda.synchronize()
+    got = _f(out)
+    assert np.all(np.isfinite(got))
+    grp = Hq // Hkv
+    per = L * D
+    for b, g in ((0, 0), (7, 3), (15, 7)):
+        hs = slice(g * grp, (g + 1) * grp)
+        s0 = (b * Hkv + g) * per
+        kslab = inputs.sign_magnitude_bytes(kkey, B * Hkv * per, 0x20, 0x58, s0, s0 + per)
+        vslab = inputs.sign_magnitude_bytes(vkey, B * Hkv * per, 0x20, 0x58, s0, s0 + per)
+        o, _, kref, vref = orc.attention_decode_fp8(
+            zc.f64(qb[b:b + 1, hs]), zc.f64(knb[b:b + 1, g:g + 1]), zc.f64(vnb[b:b + 1, g:g + 1]),
+            kslab.reshape(1, 1, L, D), vslab.reshape(1, 1, L, D), [L], k_scale=ks, v_scale=vs,
+            ring=False, window=0, gate=None, q_norm_w=gq.astype(np.float64),
+            k_norm_w=gk.astype(np.float64), **KW)
+        zc.compare(got[b, hs], o[0], f"fp8 decode 256K b={b} g={g}")
+        assert np.array_equal(vc[b, g, L - 1].cpu().numpy(), vref[0, 0, L - 1])
+        kw = kc[b, g, L - 1].cpu().numpy().astype(np.int64)
+        kr = kref[0, 0, L - 1].astype(np.int64)
+        assert np.all((kw == kr) | ((kw >> 7 == kr >> 7) & (np.abs((kw & 0x7F) - (kr & 0x7F)) == 1)))
