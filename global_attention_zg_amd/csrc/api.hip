@@ -86,8 +86,8 @@ BwdLayout bwd_layout(const zg_attn_params* p) {
   l.dO = off;   off += align256(B * S * Hq * kD * 2);
   l.lse2 = off; off += align256(B * Hq * Spad * 4);
   l.dvec = off; off += align256(B * Hq * Spad * 4);
-  l.dqp = off;  off += align256(B * S * Hq * kD * 4);
-  l.dkp = off;  off += align256(B * S * Hkv * kD * 4);
+  l.dqp = off;  off += align256(B * S * Hq * kD * 2);
+  l.dkp = off;  off += align256(B * S * Hkv * kD * 2);
   l.part = off; off += align256((size_t)2 * zg::kBwdParts * kD * 4);
   l.total = off;
   return l;
@@ -318,8 +318,8 @@ int zg_attn_bwd(const zg_attn_params* p, const void* q, const void* k, const voi
                       : const_cast<uint16_t*>(static_cast<const uint16_t*>(dout));
   float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
   float* dvec = reinterpret_cast<float*>(ws + L.dvec);
-  float* dqp = reinterpret_cast<float*>(ws + L.dqp);
-  float* dkp = reinterpret_cast<float*>(ws + L.dkp);
+  uint16_t* dqp = reinterpret_cast<uint16_t*>(ws + L.dqp);
+  uint16_t* dkp = reinterpret_cast<uint16_t*>(ws + L.dkp);
   float* part_q = reinterpret_cast<float*>(ws + L.part);
   float* part_k = part_q + (size_t)zg::kBwdParts * kD;
   const int B = p->batch, S = p->seqlen, Hq = p->n_q_heads, Hkv = p->n_kv_heads;

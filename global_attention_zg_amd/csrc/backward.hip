@@ -287,15 +287,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
 
   // dq' = tau * dQ; register r of block bd -> dim 32bd + 8(r/4) + 4 half + r%4
   if (qok) {
-    float* dst = p.dqp + qrow * kD + 4 * half;
+    uint16_t* dst = p.dqp + qrow * kD + 4 * half;
 #pragma unroll
     for (int bd = 0; bd < 4; ++bd)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = acc[bd][4 * q4 + e] * p.scale;
-        *reinterpret_cast<f32x4*>(dst + 32 * bd + 8 * q4) = o;
+        const f32x16& a = acc[bd];
+        uint2 w;
+        w.x = pack_bf16x2(a[4 * q4] * p.scale, a[4 * q4 + 1] * p.scale);
+        w.y = pack_bf16x2(a[4 * q4 + 2] * p.scale, a[4 * q4 + 3] * p.scale);
+        *reinterpret_cast<uint2*>(dst + 32 * bd + 8 * q4) = w;
       }
   }
 }
@@ -471,16 +472,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
   // register r of block bd -> dim 32bd + 8(r/4) + 4 half + r%4 of key kj
   if (kok) {
     const long long krow = ((long long)b * p.S + kj) * p.Hkv + g;
-    float* dkd = p.dkp + krow * kD + 4 * half;
+    uint16_t* dkd = p.dkp + krow * kD + 4 * half;
     uint16_t* dvd = p.dv + krow * kD + 4 * half;
 #pragma unroll
     for (int bd = 0; bd < 4; ++bd)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = dk[bd][4 * q4 + e] * p.scale;
-        *reinterpret_cast<f32x4*>(dkd + 32 * bd + 8 * q4) = o;
+        uint2 k2;
+        k2.x = pack_bf16x2(dk[bd][4 * q4] * p.scale, dk[bd][4 * q4 + 1] * p.scale);
+        k2.y = pack_bf16x2(dk[bd][4 * q4 + 2] * p.scale, dk[bd][4 * q4 + 3] * p.scale);
+        *reinterpret_cast<uint2*>(dkd + 32 * bd + 8 * q4) = k2;
         uint2 w;
         w.x = pack_bf16x2(dvv[bd][4 * q4], dvv[bd][4 * q4 + 1]);
         w.y = pack_bf16x2(dvv[bd][4 * q4 + 2], dvv[bd][4 * q4 + 3]);
@@ -498,7 +499,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
 // A fixed grid of kBwdParts blocks strides over the rows.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void prologue_bwd_kernel(const uint16_t* __restrict__ x,
-                                                           const float* __restrict__ dyp,
+                                                           const uint16_t* __restrict__ dyp,
                                                            const float* __restrict__ w,
                                                            uint16_t* __restrict__ dx,
                                                            float* __restrict__ part, long long rows,
@@ -525,13 +526,7 @@ __global__ __launch_bounds__(256) void prologue_bwd_kernel(const uint16_t* __res
     float xv[8], dyv[8];
     if (ok) {
       unpack_bf16x8(ld16(x + row * kD + 8 * c16), xv);
-      const f32x4 a = *reinterpret_cast<const f32x4*>(dyp + row * kD + 8 * c16);
-      const f32x4 bq = *reinterpret_cast<const f32x4*>(dyp + row * kD + 8 * c16 + 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dyv[e] = a[e];
-        dyv[4 + e] = bq[e];
-      }
+      unpack_bf16x8(ld16(dyp + row * kD + 8 * c16), dyv);
     } else {
 #pragma unroll
       for (int e = 0; e < 8; ++e) xv[e] = dyv[e] = 0.f;
@@ -644,7 +639,7 @@ hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_prologue_bwd(const uint16_t* x, const float* dyp, const float* w, uint16_t* dx,
+hipError_t launch_prologue_bwd(const uint16_t* x, const uint16_t* dyp, const float* w, uint16_t* dx,
                                float* part, long long rows, int S, int heads, long long pos_offset,
                                int rope_half, float eps, const RopeTable& tab, hipStream_t stream) {
   hipLaunchKernelGGL(prologue_bwd_kernel, dim3(kBwdParts), dim3(256), 0, stream, x, dyp, w, dx, part,

@@ -143,8 +143,8 @@ struct BwdParams {
   const uint16_t* dO;   // bf16 [B,S,Hq,D]
   const float* lse2;    // fp32 [B,Hq,Spad]  LSE * log2(e); +inf for rows >= S
   const float* dvec;    // fp32 [B,Hq,Spad]  rowsum(dY * Y); 0 for rows >= S
-  float* dqp;           // fp32 [B,S,Hq,D]   dL/dQ'
-  float* dkp;           // fp32 [B,S,Hkv,D]  dL/dK'
+  uint16_t* dqp;        // bf16 [B,S,Hq,D]   dL/dQ'
+  uint16_t* dkp;        // bf16 [B,S,Hkv,D]  dL/dK'
   uint16_t* dv;         // bf16 [B,S,Hkv,D]
   int B, S, Spad, Hq, Hkv, window;
   float scale_log2;     // softmax scale * log2(e)
@@ -163,7 +163,7 @@ hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t stream);
 // dx = d(prologue)/dx^T dy' for rows of `heads` heads; partial weight
 // gradients go to part[kBwdParts][D], then dw = sum of the parts.
-hipError_t launch_prologue_bwd(const uint16_t* x, const float* dyp, const float* w, uint16_t* dx,
+hipError_t launch_prologue_bwd(const uint16_t* x, const uint16_t* dyp, const float* w, uint16_t* dx,
                                float* part, long long rows, int S, int heads, long long pos_offset,
                                int rope_half, float eps, const RopeTable& tab, hipStream_t stream);
 hipError_t launch_reduce_parts(const float* part, float* dw, hipStream_t stream);

@@ -279,7 +279,7 @@ int zg_linear_fp8(int M, int N, int K, const void* xq, const void* wq, float out
                   void* y, void* stream);
 
 /* Bytes of device workspace zg_attn_bwd needs (recomputed Q' and K', dO,
- * per-row LSE*log2(e) and rowsum(dY*Y), fp32 dL/dQ' and dL/dK', and the
+ * per-row LSE*log2(e) and rowsum(dY*Y), bf16 dL/dQ' and dL/dK', and the
  * partial sums of the two weight gradients); 0 for an invalid p. */
 size_t zg_attn_bwd_workspace_size(const zg_attn_params* p);
 

@@ -200,7 +200,7 @@ def test_bwd_workspace_size_formula(bd):
     a = lambda x: (x + 255) // 256 * 256  # noqa: E731
     spad = (S + 127) // 128 * 128
     want = (a(B * S * Hq * D * 2) + a(B * S * Hkv * D * 2) + a(B * S * Hq * D * 2)
-            + 2 * a(B * Hq * spad * 4) + a(B * S * Hq * D * 4) + a(B * S * Hkv * D * 4)
+            + 2 * a(B * Hq * spad * 4) + a(B * S * Hq * D * 2) + a(B * S * Hkv * D * 2)
             + a(2 * 512 * D * 4))
     assert bd.zg_attn_bwd_workspace_size(p) == want
     p.head_dim = 64
