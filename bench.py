@@ -138,6 +138,30 @@ def time_events(torch, fn, iters):
     return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e-3
 
 
+def time_stats(torch, fn, iters, flush=None):
+    """Median, min and max duration of fn() by HIP events on the current
+    stream. With `flush` (a device buffer larger than L2 plus the MALL), the
+    buffer is rewritten before every timed call, outside the events, so that
+    each call starts with cold caches."""
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for i, (a, b) in enumerate(evs):
+        if flush is not None:
+            flush.fill_(i & 0xFF)
+        a.record(st)
+        fn()
+        b.record(st)
+    torch.cuda.synchronize()
+    ts = np.array([a.elapsed_time(b) for a, b in evs]) * 1e-3
+    return float(np.median(ts)), float(ts.min()), float(ts.max())
+
+
+def flush_buffer(torch):
+    """512 MiB of device memory: twice the MALL, far more than the L2s."""
+    return torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+
 def flash_source_hash():
     h = hashlib.sha256()
     for path in FLASH_SRCS:
@@ -159,10 +183,58 @@ def read_traffic():
     return t.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline():
+def sclk_mhz():
+    """Current shader clock of GPU 0 as rocm-smi reports it, or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=20)
+        card = next(iter(json.loads(r.stdout).values()))
+        for k, v in card.items():
+            if "sclk" in k.lower() and "speed" in k.lower():
+                return float(str(v).strip("()").lower().replace("mhz", ""))
+    except (OSError, ValueError, StopIteration, subprocess.SubprocessError, AttributeError):
+        return None
+    return None
+
+
+def reference_peaks(torch, iters=20):
+    """Measured ceilings on this GPU beside the published ones: a plain 1 GiB
+    device copy (read + write bytes per second), the library bf16 GEMM behind
+    torch.mm on 8192^3, and the shader clock."""
+    log("reference peaks: 1 GiB copy, 8192^3 bf16 library GEMM")
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    t_copy = time_events(torch, lambda: dst.copy_(src), iters)
+    del src, dst
+    m = 8192
+    a = torch.randn((m, m), dtype=torch.bfloat16, device="cuda")
+    b = torch.randn((m, m), dtype=torch.bfloat16, device="cuda")
+    c = torch.empty((m, m), dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        torch.mm(a, b, out=c)
+    t_mm = time_events(torch, lambda: torch.mm(a, b, out=c), iters)
+    del a, b, c
+    torch.cuda.empty_cache()
+    return {"copy_gbs": round(2 * n / t_copy / 1e9, 1),
+            "copy_frac_of_spec": round(2 * n / t_copy / 1e9 / PEAK_HBM_GBS, 4),
+            "library_gemm_bf16_tflops": round(2.0 * m ** 3 / t_mm / 1e12, 1),
+            "library_gemm_frac_of_spec": round(2.0 * m ** 3 / t_mm / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "sclk_mhz_after": sclk_mhz(),
+            "spec": {"hbm_gbs": PEAK_HBM_GBS, "bf16_tflops": PEAK_BF16_TFLOPS,
+                     "sclk_mhz": 2400.0}}
+
+
+def cpu_baseline(gpu_rows=None):
     """The fp64 oracle timed on a bounded sample of the block: the first 4096
     query rows of one gated SWA layer and the first 8192 rows of the global
-    layer (all 32 query heads), with the same seeded inputs."""
+    layer (all 32 query heads), with the same seeded inputs.  Causal rows
+    depend only on the keys before them, so these prefix rows are also rows
+    of the full 262144-position layers: `gpu_rows` (layer -> the kernel's
+    output on those rows, from the timed run) is compared with them."""
     from global_attention_zg_amd import inputs
     from oracle import zg_oracle as orc
 
@@ -176,6 +248,7 @@ def cpu_baseline():
 
     flops = 0
     t_total = 0.0
+    parity = {}
     for layer, window, rows, gated in ((0, 128, 4096, True), (5, 0, 8192, False)):
         # the first `rows` positions of the layer's tensors are a prefix of the
         # full [1, S, H, D] tensors in the flat element order
@@ -186,9 +259,16 @@ def cpu_baseline():
         gq = inputs.norm_weight((4, layer, inputs.T_GQ), D).astype(np.float64)
         gk = inputs.norm_weight((4, layer, inputs.T_GK), D).astype(np.float64)
         t0 = time.perf_counter()
-        orc.attention_fwd(q, k, v, g, gq, gk, window=window, **KW)
+        ref, _ = orc.attention_fwd(q, k, v, g, gq, gk, window=window, **KW)
         t_total += time.perf_counter() - t0
         flops += 32 * inband_pairs(rows, window) * FLOP_PER_PAIR
+        if gpu_rows is not None and layer in gpu_rows:
+            d = gpu_rows[layer] - ref
+            parity["swa_layer0" if window else "global_layer5"] = {
+                "rows": f"0..{rows - 1}, all 32 heads",
+                "max_abs": float(np.abs(d).max()),
+                "rel_rms": float(np.sqrt((d * d).sum() / (ref * ref).sum())),
+                "bound": "max_abs <= 2e-2 and rel_rms <= 1e-2"}
     try:
         from threadpoolctl import threadpool_info
         threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
@@ -199,7 +279,7 @@ def cpu_baseline():
                 sample="first 4096 query rows of one gated SWA layer + first 8192 rows of the "
                        "global layer of the 256K block, all 32 query heads, fp64 numpy; "
                        f"{flops / 1e9:.1f} GFLOP in {t_total:.1f} s",
-                seconds=round(t_total, 2))
+                seconds=round(t_total, 2)), parity
 
 
 def main():
@@ -296,15 +376,19 @@ def main():
         "block_breakdown_ms": {"swa_layer": round(swa_t * 1e3, 3),
                                "global_layer": round(t_glob * 1e3, 3)},
     }
+    # the kernel's output on the rows the oracle sample covers
+    gpu_rows = {0: layers[0].out[:, :4096].float().cpu().numpy().astype(np.float64),
+                5: glob.out[:, :8192].float().cpu().numpy().astype(np.float64)}
     del layers, glob
     torch.cuda.empty_cache()
 
     if not args.no_components:
         result["components"] = run_components(torch, bd, None, 20)
+        result["reference_peaks"] = reference_peaks(torch)
 
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle, bounded sample)")
-        result["cpu_baseline"] = cpu_baseline()
+        result["cpu_baseline"], result["parity_vs_oracle"] = cpu_baseline(gpu_rows)
     result["host"] = {"cpu": platform.processor() or platform.machine(),
                       "affinity_cores": len(os.sched_getaffinity(0))}
     print(json.dumps(result), flush=True)
@@ -318,19 +402,26 @@ def run_components(torch, bd, only, iters):
         l2 = Layer(torch, bd, 2, 0, 4, 4096, 32, 8, 128, True)
         for _ in range(3):
             l2()
-        t = time_events(torch, l2, iters)
-        comps["swa_4k_b4"] = {"ms": round(t * 1e3, 4), "tflops": round(l2.flops / t / 1e12, 2),
+        fl = flush_buffer(torch)
+        t, t_lo, t_hi = time_stats(torch, l2, iters, flush=fl)
+        comps["swa_4k_b4"] = {"ms": round(t * 1e3, 4), "ms_min": round(t_lo * 1e3, 4),
+                              "ms_max": round(t_hi * 1e3, 4), "caches_flushed": True,
+                              "tflops": round(l2.flops / t / 1e12, 2),
                               "tokens_per_s": round(4 * 4096 / t, 1),
                               "hbm_gbs_alg": round(l2.alg_bytes / t / 1e9, 1),
                               "frac_hbm": round(l2.alg_bytes / t / 1e9 / PEAK_HBM_GBS, 4)}
-        del l2
+        t_warm = time_events(torch, l2, iters)
+        comps["swa_4k_b4"]["ms_mean_warm_caches"] = round(t_warm * 1e3, 4)
+        del l2, fl
     if only in (None, "global16k"):
         log("component: global S16384")
         l3 = Layer(torch, bd, 3, 0, 1, 16384, 32, 8, 0, False)
         for _ in range(2):
             l3()
-        t = time_events(torch, l3, max(1, iters // 2))
-        comps["global_16k"] = {"ms": round(t * 1e3, 4), "tflops": round(l3.flops / t / 1e12, 2),
+        t, t_lo, t_hi = time_stats(torch, l3, max(1, iters // 2))
+        comps["global_16k"] = {"ms": round(t * 1e3, 4), "ms_min": round(t_lo * 1e3, 4),
+                               "ms_max": round(t_hi * 1e3, 4),
+                               "tflops": round(l3.flops / t / 1e12, 2),
                                "tokens_per_s": round(16384 / t, 1),
                                "frac_mfma": round(l3.flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del l3
@@ -625,14 +716,19 @@ def decode_components(torch, bd, iters):
             bd.zg_attn_decode(q, kn, vn, kc, vc, sl, ring=ring, window=window, gate=g,
                               q_norm_w=gq, k_norm_w=gk, out=o, workspace=ws, **KW)
 
+        # the ring's 8.4 MB would stay in the caches between steps: flush
+        fl = flush_buffer(torch) if ring else None
+
         def record(name, fn, cap, elem_bytes=2):
             for _ in range(2):
                 fn()
-            t = time_events(torch, fn, iters)
+            t, t_lo, t_hi = time_stats(torch, fn, iters, flush=fl)
             keys = min(L, cap)
             alg = B * Hkv * keys * D * 2 * elem_bytes + (q.numel() * 2 + o.numel()) * 2
             flops = B * Hq * keys * FLOP_PER_PAIR
-            out[name] = {"ms": round(t * 1e3, 4), "tokens_per_s": round(B / t, 1),
+            out[name] = {"ms": round(t * 1e3, 4), "ms_min": round(t_lo * 1e3, 4),
+                         "ms_max": round(t_hi * 1e3, 4), "caches_flushed": fl is not None,
+                         "tokens_per_s": round(B / t, 1),
                          "hbm_gbs_alg": round(alg / t / 1e9, 1),
                          "frac_hbm": round(alg / t / 1e9 / PEAK_HBM_GBS, 4),
                          "tflops": round(flops / t / 1e12, 3),
@@ -686,7 +782,7 @@ def decode_components(torch, bd, iters):
         out[kind + "_fp8"]["max_abs_vs_bf16_cache"] = round(
             float((o8.float() - o.float()).abs().max()), 5)
         del kc8, vc8
-        del kc, vc
+        del kc, vc, fl
         torch.cuda.empty_cache()
     return out
 
