@@ -291,7 +291,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only",
                     choices=["swa4k", "global16k", "decode", "decode_block", "block_global", "bwd",
-                             "varlen", "proj", "variants"],
+                             "varlen", "proj", "variants", "block_swa"],
                     default=None, help="time one workload only (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="with --only: first run a plain 1 GiB device copy, the reference "
@@ -438,6 +438,15 @@ def run_components(torch, bd, only, iters):
         comps.update(varlen_components(torch, bd, max(1, iters // 2)))
     if only in (None, "bwd"):
         comps.update(bwd_components(torch, bd, max(1, iters // 2)))
+    if only == "block_swa":
+        log("gated SWA layer of the 256K block")
+        ls = Layer(torch, bd, 4, 0, 1, 262144, 32, 8, 128, True)
+        ls()
+        t = time_events(torch, ls, max(1, iters // 2))
+        comps["block_swa_256k"] = {"ms": round(t * 1e3, 4),
+                                   "hbm_gbs_alg": round(ls.alg_bytes / t / 1e9, 1),
+                                   "frac_hbm": round(ls.alg_bytes / t / 1e9 / PEAK_HBM_GBS, 4)}
+        del ls
     if only == "block_global":
         log("global layer of the 256K block")
         lg = Layer(torch, bd, 4, 5, 1, 262144, 32, 8, 0, False)

@@ -305,7 +305,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
 // dk' and dv: one 256-thread workgroup = (batch, kv head g, block of 128
 // keys), wave w owning keys 32w..32w+31 of the block.  The workgroup visits
 // every (query head of the group, 32-query tile) whose queries can see its
-// keys; per tile and wave, with this lane's key in column l % 32:
+// keys: query tiles from the last one down, the group's heads innermost.
+// Workgroups of one KV head that run at the same time (consecutive key
+// blocks, on one XCD) then read the same Q'/dO tiles at about the same time,
+// out of that XCD's L2.  Per tile and wave, with this lane's key in column
+// l % 32:
 //   S  = Q' K'^T  (A = Q' rows, ds_read_b128; B = K' in registers)
 //   dP = dO V^T   (A = dO rows; B = V rows of the block, both ds_read_b128)
 //   P = exp2(S c - lse2), dS = P (dP - Dr)
@@ -355,8 +359,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
     chk[j] = 16u * ((uint32_t)(lane & 15) ^ swz(lrow[j]));
   }
   auto gload = [&](int i, int stg) {
-    const int hh = i / nq;
-    const int q0 = (qt_lo + i % nq) * 32;
+    const int hh = i % grp;
+    const int q0 = (qt_lo + nq - 1 - i / grp) * 32;
     const int head = g * grp + hh;
     const long long base = ((long long)b * p.S + q0) * qstride + (long long)head * kD;
     const unsigned char* qb = (const unsigned char*)(p.qp + base);
@@ -419,7 +423,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
 
   for (int i = 0; i < ntile; ++i) {
     const int stg = i & 1;
-    const int q0 = (qt_lo + i % nq) * 32;
+    const int q0 = (qt_lo + nq - 1 - i / grp) * 32;
     const lds_u8* qt = smem + stg * kDkvStage;
     const lds_u8* ot = qt + kTileB;
     const lds_u8* lt = qt + 2 * kTileB;
