@@ -500,7 +500,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
 //   r = (mean(x^2) + eps)^-1/2
 //   dx = r (w * dx_hat) - x r^3 mean(w * dx_hat * x)
 //   dw += dx_hat * x * r              (per-block partials, summed later)
-// A fixed grid of kBwdParts blocks strides over the rows.
+// A fixed grid of kBwdParts blocks (eight per CU) strides over groups of 16
+// rows; each group's x and dy' rows are loaded one iteration ahead, and the
+// barriers wait for LDS only, so those loads stay in flight across them.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void prologue_bwd_kernel(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ dyp,
@@ -524,27 +526,43 @@ __global__ __launch_bounds__(256) void prologue_bwd_kernel(const uint16_t* __res
   }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const int R = 2 * rope_half;
+  if (rows == 0) {
+    if (threadIdx.x < kD) part[(long long)blockIdx.x * kD + threadIdx.x] = 0.f;
+    return;
+  }
+  // Rows past the end read row rows - 1 (always in bounds, no branch, so the
+  // next group's loads need no wait before this group's work) and store
+  // nothing; an in-range row reads no other slot's row or angles.
+  auto load = [&](long long rg, u32x4& xu, u32x4& du) {
+    const long long row = min(rg * 16 + slot, rows - 1);
+    xu = ld16(x + row * kD + 8 * c16);
+    du = ld16(dyp + row * kD + 8 * c16);
+  };
+  // this lane's rotary frequencies (angles t = c16 and c16 + 16; rope_half <= 32)
+  static_assert(kMaxRopeHalf <= 32, "two angles per lane");
+  const uint64_t fr0 = c16 < rope_half ? tab.frac[c16] : 0;
+  const uint64_t fr1 = c16 + 16 < rope_half ? tab.frac[c16 + 16] : 0;
+  u32x4 xu, du;
+  load(blockIdx.x, xu, du);
   for (long long rg = blockIdx.x; rg * 16 < rows; rg += gridDim.x) {  // uniform per block
     const long long row = rg * 16 + slot;
     const bool ok = row < rows;
     float xv[8], dyv[8];
-    if (ok) {
-      unpack_bf16x8(ld16(x + row * kD + 8 * c16), xv);
-      unpack_bf16x8(ld16(dyp + row * kD + 8 * c16), dyv);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) xv[e] = dyv[e] = 0.f;
-    }
+    unpack_bf16x8(xu, xv);
+    unpack_bf16x8(du, dyv);
+    load(rg + gridDim.x, xu, du);  // the next group's rows
     const long long pos = pos_offset + (row / heads) % S;
     if (R > 0) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) rowbuf[slot][8 * c16 + e] = dyv[e];
       // the block's first row of each position computes its angles, one per
       // lane t % 16, for all rows of that position
-      if ((int)(row % heads) == 0 || slot == 0)
-        for (int t = c16; t < rope_half; t += 16) rope_cos_sin(tab, t, pos, cs[slot][t], sn[slot][t]);
+      if ((int)(row % heads) == 0 || slot == 0) {
+        if (c16 < rope_half) rope_cos_sin_f(fr0, pos, cs[slot][c16], sn[slot][c16]);
+        if (c16 + 16 < rope_half) rope_cos_sin_f(fr1, pos, cs[slot][c16 + 16], sn[slot][c16 + 16]);
+      }
     }
-    __syncthreads();
+    lds_barrier();
     const int ref = slot - (int)min(row % heads, (long long)slot);
     float dh[8];
 #pragma unroll
@@ -583,7 +601,7 @@ __global__ __launch_bounds__(256) void prologue_bwd_kernel(const uint16_t* __res
       for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
       st16(dx + row * kD + 8 * c16, u);
     }
-    __syncthreads();  // rowbuf is rewritten by the next group
+    lds_barrier();  // rowbuf and the angle tables are rewritten by the next group
   }
   // sum the 16 row slots of the block
 #pragma unroll
@@ -597,14 +615,29 @@ __global__ __launch_bounds__(256) void prologue_bwd_kernel(const uint16_t* __res
   }
 }
 
-// dw[d] = sum over the kBwdParts partials (fixed order: deterministic).
-__global__ __launch_bounds__(kD) void reduce_parts_kernel(const float* __restrict__ part,
-                                                          float* __restrict__ dw) {
-  const int d = threadIdx.x;
+// dw[d] = sum over the kBwdParts partials in a fixed order (deterministic):
+// thread (chunk c, dim d) sums partials c*kChunk .. c*kChunk + kChunk - 1 in
+// order, then the eight chunk sums are added in order of c.
+constexpr int kReduceChunks = 8;
+__global__ __launch_bounds__(kReduceChunks * kD) void reduce_parts_kernel(const float* __restrict__ part,
+                                                                          float* __restrict__ dw) {
+  constexpr int kChunk = kBwdParts / kReduceChunks;
+  __shared__ float red[kReduceChunks][kD];
+  const int d = threadIdx.x % kD, c = threadIdx.x / kD;
+  const float* src = part + (long long)c * kChunk * kD + d;
   float s = 0.f;
-  for (int k = 0; k < kBwdParts; ++k) s += part[(long long)k * kD + d];
-  dw[d] = s;
+#pragma unroll 16
+  for (int k = 0; k < kChunk; ++k) s += src[(long long)k * kD];
+  red[c][d] = s;
+  __syncthreads();
+  if (c == 0) {
+    float t = red[0][d];
+#pragma unroll
+    for (int j = 1; j < kReduceChunks; ++j) t += red[j][d];
+    dw[d] = t;
+  }
 }
+static_assert(kBwdParts % kReduceChunks == 0, "partials split evenly over the chunks");
 
 }  // namespace
 
@@ -652,7 +685,7 @@ hipError_t launch_prologue_bwd(const uint16_t* x, const uint16_t* dyp, const flo
 }
 
 hipError_t launch_reduce_parts(const float* part, float* dw, hipStream_t stream) {
-  hipLaunchKernelGGL(reduce_parts_kernel, dim3(1), dim3(kD), 0, stream, part, dw);
+  hipLaunchKernelGGL(reduce_parts_kernel, dim3(1), dim3(kReduceChunks * kD), 0, stream, part, dw);
   return hipGetLastError();
 }
 

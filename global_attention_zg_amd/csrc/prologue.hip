@@ -22,6 +22,7 @@ namespace zg {
 namespace {
 
 constexpr int kRowsPerBlock = 16;
+constexpr long long kPrologueBlocks = 2048;
 
 __global__ __launch_bounds__(256) void k_prologue_kernel(const uint16_t* __restrict__ k,
                                                          const float* __restrict__ w,
@@ -34,40 +35,47 @@ __global__ __launch_bounds__(256) void k_prologue_kernel(const uint16_t* __restr
   __shared__ float cs[kRowsPerBlock][kMaxRopeHalf], sn[kRowsPerBlock][kMaxRopeHalf];
   const int lrow = threadIdx.x / 16;
   const int c16 = threadIdx.x % 16;
-  const long long row = (long long)blockIdx.x * kRowsPerBlock + lrow;
-  const bool ok = row < rows;
-  float x[8];
-  if (ok) {
-    unpack_bf16x8(ld16(k + row * kD + 8 * c16), x);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = 0.f;
-  }
-  // position of the row's token within its sequence
-  const long long tok = row / Hkv;
-  long long s;
-  if (cu_seqlens) {  // packed: the last sequence b with cu_seqlens[b] <= tok
-    int lo = 0, hi = nseq;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (cu_seqlens[mid] <= tok) lo = mid;
-      else hi = mid;
+  // Groups of 16 rows, strided over a fixed grid; each group's rows are
+  // loaded one iteration ahead.  Rows past the end read row rows - 1 (in
+  // bounds, no branch) and store nothing.
+  auto load = [&](long long rg) {
+    return ld16(k + min(rg * kRowsPerBlock + lrow, rows - 1) * kD + 8 * c16);
+  };
+  const RowConsts kc = row_consts(w, rope_half, tab, c16);
+  u32x4 xu = load(blockIdx.x);
+  for (long long rg = blockIdx.x; rg * kRowsPerBlock < rows; rg += gridDim.x) {  // uniform
+    const long long row = rg * kRowsPerBlock + lrow;
+    const bool ok = row < rows;
+    float x[8];
+    unpack_bf16x8(xu, x);
+    xu = load(rg + gridDim.x);
+    // position of the row's token within its sequence
+    const long long tok = row / Hkv;
+    long long s;
+    if (cu_seqlens) {  // packed: the last sequence b with cu_seqlens[b] <= tok
+      int lo = 0, hi = nseq;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cu_seqlens[mid] <= tok) lo = mid;
+        else hi = mid;
+      }
+      s = max(tok - (long long)cu_seqlens[lo], 0LL);
+    } else {
+      s = tok % S;
     }
-    s = max(tok - (long long)cu_seqlens[lo], 0LL);
-  } else {
-    s = tok % S;
-  }
-  // rows are (b, s, head): the first row of each position in the block
-  // computes the angles for all of them
-  const int hh = (int)(row % Hkv);
-  const int ref = lrow - min(hh, lrow);
-  norm_rope_row(x, c16, w, eps, rope_half, tab, pos_offset + s, xs[lrow], ref == lrow, cs[lrow],
-                sn[lrow], cs[ref], sn[ref]);
-  if (ok) {
-    u32x4 o;
+    // rows are (b, s, head): the first row of each position in the group
+    // computes the angles for all of them
+    const int hh = (int)(row % Hkv);
+    const int ref = lrow - min(hh, lrow);
+    norm_rope_row(x, c16, kc, eps, rope_half, pos_offset + s, xs[lrow], ref == lrow, cs[lrow],
+                  sn[lrow], cs[ref], sn[ref]);
+    if (ok) {
+      u32x4 o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-    st16(kout + row * kD + 8 * c16, o);
+      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+      st16(kout + row * kD + 8 * c16, o);
+    }
+    lds_barrier();  // xs and the angle tables are rewritten by the next group
   }
 }
 
@@ -159,8 +167,9 @@ hipError_t launch_k_prologue(const uint16_t* k, const float* w, uint16_t* kout, 
                              const RopeTable& tab, hipStream_t stream, const int* cu_seqlens,
                              int nseq) {
   if (rows == 0) return hipSuccess;
-  const long long blocks = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  // eight 256-thread blocks per CU stride over the groups of 16 rows
+  const long long groups = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  const long long blocks = groups < kPrologueBlocks ? groups : kPrologueBlocks;
   hipLaunchKernelGGL(k_prologue_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k, w,
                      kout, rows, S, Hkv, cu_seqlens, nseq, pos_offset, rope_half, eps, tab);
   return hipGetLastError();

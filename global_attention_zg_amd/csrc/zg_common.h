@@ -27,9 +27,7 @@ struct RopeTable {
   uint64_t frac[kMaxRopeHalf];
 };
 
-__device__ __forceinline__ void rope_cos_sin(const RopeTable& tab, int t, long long pos,
-                                             float& c, float& s) {
-  const uint64_t f = tab.frac[t];
+__device__ __forceinline__ void rope_cos_sin_f(uint64_t f, long long pos, float& c, float& s) {
   const uint64_t p = (uint64_t)pos;
   const uint32_t pl = (uint32_t)p, ph = (uint32_t)(p >> 32);
   const uint32_t fl = (uint32_t)f, fh = (uint32_t)(f >> 32);
@@ -39,6 +37,18 @@ __device__ __forceinline__ void rope_cos_sin(const RopeTable& tab, int t, long l
   // v_sin_f32 / v_cos_f32 take their argument in revolutions.
   s = __builtin_amdgcn_sinf(r);
   c = __builtin_amdgcn_cosf(r);
+}
+
+__device__ __forceinline__ void rope_cos_sin(const RopeTable& tab, int t, long long pos,
+                                             float& c, float& s) {
+  rope_cos_sin_f(tab.frac[t], pos, c, s);
+}
+
+// Workgroup barrier that waits for this wave's LDS operations only (the
+// release fence of __syncthreads() also waits for every global load in
+// flight, which would end any prefetch across the barrier).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -154,7 +154,7 @@ struct BwdParams {
 // Row padding of the LSE / D vectors (a multiple of every query block).
 constexpr int kBwdRowPad = 128;
 // Number of per-block partial sums of each RMSNorm weight gradient.
-constexpr int kBwdParts = 512;
+constexpr int kBwdParts = 2048;
 
 hipError_t launch_bwd_prep(const uint16_t* dy, const uint16_t* y, const uint16_t* gate,
                            const float* lse, uint16_t* dO, uint16_t* dgate, float* lse2,

@@ -11,17 +11,43 @@
 
 namespace zg {
 
+// The per-lane constants of the row code: the lane's 8 norm weights and the
+// frequencies of its rotary angles t = c16 and c16 + 16 (rope_half <= 32).
+// Kernels that loop over rows load them once, so that no global load sits
+// between a prefetch and its use inside the loop.
+struct RowConsts {
+  float wl[8];
+  uint64_t fr0, fr1;
+};
+static_assert(kMaxRopeHalf <= 32, "two rotary angles per lane");
+
+__device__ __forceinline__ RowConsts row_consts(const float* w, int rope_half, const RopeTable& tab,
+                                                int c16) {
+  RowConsts k;
+  const u32x4 w0 = ld16(w + 8 * c16);
+  const u32x4 w1 = ld16(w + 8 * c16 + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    k.wl[i] = __uint_as_float(w0[i]);
+    k.wl[4 + i] = __uint_as_float(w1[i]);
+  }
+  k.fr0 = c16 < rope_half ? tab.frac[c16] : 0;
+  k.fr1 = c16 + 16 < rope_half ? tab.frac[c16 + 16] : 0;
+  return k;
+}
+
 // Normalise + rotate one row held as 8 values per lane (lane c16 = 0..15 of
 // the row owns dims 8*c16 .. 8*c16+7).  `xs` is the row's LDS scratch.  The
 // rotary cosines / sines live in per-row LDS tables; rows at the same
 // position (the heads of one token) share them: the block's first row of
 // each position (`own` true) fills its table, one angle per lane t % 16, and
 // every row reads the table `cs_r` / `sn_r` of that first row.  Every thread
-// of the block calls this together (one barrier).
-__device__ __forceinline__ void norm_rope_row(float* x, int c16, const float* w, float eps,
-                                              int rope_half, const RopeTable& tab,
-                                              long long pos, float* xs, bool own, float* cs_w,
-                                              float* sn_w, const float* cs_r, const float* sn_r) {
+// of the block calls this together (one barrier, which waits for LDS only:
+// global loads in flight stay in flight).
+__device__ __forceinline__ void norm_rope_row(float* x, int c16, const RowConsts& k, float eps,
+                                              int rope_half, long long pos, float* xs, bool own,
+                                              float* cs_w, float* sn_w, const float* cs_r,
+                                              const float* sn_r) {
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ss += x[i] * x[i];
@@ -29,19 +55,16 @@ __device__ __forceinline__ void norm_rope_row(float* x, int c16, const float* w,
 #pragma unroll
   for (int o = 8; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 16);
   const float r = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
-  const u32x4 w0 = ld16(w + 8 * c16);
-  const u32x4 w1 = ld16(w + 8 * c16 + 4);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[i] *= r * __uint_as_float(w0[i]);
-    x[4 + i] *= r * __uint_as_float(w1[i]);
-  }
+  for (int i = 0; i < 8; ++i) x[i] *= r * k.wl[i];
   if (rope_half == 0) return;
 #pragma unroll
   for (int i = 0; i < 8; ++i) xs[8 * c16 + i] = x[i];
-  if (own)
-    for (int t = c16; t < rope_half; t += 16) rope_cos_sin(tab, t, pos, cs_w[t], sn_w[t]);
-  __syncthreads();
+  if (own) {
+    if (c16 < rope_half) rope_cos_sin_f(k.fr0, pos, cs_w[c16], sn_w[c16]);
+    if (c16 + 16 < rope_half) rope_cos_sin_f(k.fr1, pos, cs_w[c16 + 16], sn_w[c16 + 16]);
+  }
+  lds_barrier();
   const int R = 2 * rope_half;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -55,6 +78,15 @@ __device__ __forceinline__ void norm_rope_row(float* x, int c16, const float* w,
         x[i] = x[i] * c + xs[d - rope_half] * s;
     }
   }
+}
+
+// The same for a single row (decode): loads the lane constants itself.
+__device__ __forceinline__ void norm_rope_row(float* x, int c16, const float* w, float eps,
+                                              int rope_half, const RopeTable& tab,
+                                              long long pos, float* xs, bool own, float* cs_w,
+                                              float* sn_w, const float* cs_r, const float* sn_r) {
+  norm_rope_row(x, c16, row_consts(w, rope_half, tab, c16), eps, rope_half, pos, xs, own, cs_w,
+                sn_w, cs_r, sn_r);
 }
 
 }  // namespace zg

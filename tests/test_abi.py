@@ -201,7 +201,7 @@ def test_bwd_workspace_size_formula(bd):
     spad = (S + 127) // 128 * 128
     want = (a(B * S * Hq * D * 2) + a(B * S * Hkv * D * 2) + a(B * S * Hq * D * 2)
             + 2 * a(B * Hq * spad * 4) + a(B * S * Hq * D * 2) + a(B * S * Hkv * D * 2)
-            + a(2 * 512 * D * 4))
+            + a(2 * 2048 * D * 4))
     assert bd.zg_attn_bwd_workspace_size(p) == want
     p.head_dim = 64
     assert bd.zg_attn_bwd_workspace_size(p) == 0
