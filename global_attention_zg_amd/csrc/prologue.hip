@@ -8,9 +8,11 @@
 // remaining dims pass through.  The queries get the same treatment inside the
 // attention kernels, fused into their Q-tile loads.
 //
-// Layout: 16 lanes per row, 8 bf16 (16 bytes) per lane, 16 rows per
-// 256-thread block.  The row's normalised values go through LDS so that each
-// lane can read the partner dim of its rotary pairs.
+// Layout: 16 lanes per row, 8 bf16 (16 bytes) per lane, groups of 16 rows
+// per 256-thread block (the key prologue strides a fixed grid over the
+// groups; the decode append takes one group per block).  The row's
+// normalised values go through LDS so that each lane can read the partner
+// dim of its rotary pairs.
 
 #include "zg_common.h"
 #include "zg_fp8.h"
