@@ -332,9 +332,11 @@ int zg_attn_bwd(const zg_attn_params* p, const void* q, const void* k, const voi
                                      static_cast<const uint16_t*>(gate), lse, dO,
                                      static_cast<uint16_t*>(dgate), lse2, dvec, B, S, Spad, Hq, s);
   if (e != hipSuccess) return ZG_ERR_HIP;
-  e = zg::launch_k_prologue(static_cast<const uint16_t*>(q), q_norm_w, qp, (long long)B * S * Hq, S,
-                            Hq, p->pos_offset, rh, p->rms_eps, tab, s);
-  if (e != hipSuccess) return ZG_ERR_HIP;
+  if (!zg::bwd_dq_fuses_q(rh)) {  // else the dq' kernel forms Q' itself
+    e = zg::launch_k_prologue(static_cast<const uint16_t*>(q), q_norm_w, qp, (long long)B * S * Hq,
+                              S, Hq, p->pos_offset, rh, p->rms_eps, tab, s);
+    if (e != hipSuccess) return ZG_ERR_HIP;
+  }
   e = zg::launch_k_prologue(static_cast<const uint16_t*>(k), k_norm_w, kp, (long long)B * S * Hkv,
                             S, Hkv, p->pos_offset, rh, p->rms_eps, tab, s);
   if (e != hipSuccess) return ZG_ERR_HIP;
@@ -356,6 +358,12 @@ int zg_attn_bwd(const zg_attn_params* p, const void* q, const void* k, const voi
   bp.window = p->window;
   bp.scale_log2 = scale_log2(p);
   bp.scale = (float)(p->softmax_scale > 0.f ? (double)p->softmax_scale : 1.0 / sqrt((double)kD));
+  bp.q = static_cast<const uint16_t*>(q);
+  bp.q_norm_w = q_norm_w;
+  bp.eps = p->rms_eps;
+  bp.rope_half = rh;
+  bp.pos_offset = p->pos_offset;
+  bp.tab = tab;
   if (zg::launch_bwd_dq(bp, s) != hipSuccess) return ZG_ERR_HIP;
   if (zg::launch_bwd_dkv(bp, s) != hipSuccess) return ZG_ERR_HIP;
   e = zg::launch_prologue_bwd(static_cast<const uint16_t*>(q), dqp, q_norm_w,

@@ -151,6 +151,9 @@ struct DqGeo {
   int n_pos_blocks, hgroups, n_bhg;
 };
 
+// RH = rope_dim / 2 when Q' is formed here (21 or 0), -1 when it is read
+// from p.qp.
+template <int RH>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) {
   constexpr int NS = 3;
   constexpr int kVOff = NS * kTileB;
@@ -221,12 +224,59 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
   const long long qrow = ((long long)b * p.S + (qok ? qi : 0)) * p.Hq + head;
   bf16x8 qf[8], of[8];
   {
-    const uint16_t* qs = p.qp + qrow * kD + 64 * half;
     const uint16_t* os = p.dO + qrow * kD + 64 * half;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      qf[j] = __builtin_bit_cast(bf16x8, qok ? ld16(qs + 8 * j) : u32x4{0, 0, 0, 0});
+    for (int j = 0; j < 8; ++j)
       of[j] = __builtin_bit_cast(bf16x8, qok ? ld16(os + 8 * j) : u32x4{0, 0, 0, 0});
+    if constexpr (RH >= 0) {
+      // Q' of this lane's half row: RMSNorm (+ weight) and the rotary pairs
+      // (t, t + RH), with the same expressions in the same order as the
+      // forward's fused query prologue, so that these are the bits the
+      // forward multiplied.  Written to p.qp for the dk'/dv kernel.
+      const uint16_t* src = p.q + qrow * kD + 64 * half;
+      float x[64];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const u32x4 u = qok ? ld16(src + 8 * j) : u32x4{0, 0, 0, 0};
+        unpack_bf16x8(u, x + 8 * j);
+      }
+      float ss = 0.f;
+#pragma unroll
+      for (int d = 0; d < 64; ++d) ss += x[d] * x[d];
+      ss = pair_sum32(ss);
+      const float r = 1.0f / sqrtf(ss * (1.0f / kD) + p.eps);
+      const float* wsrc = p.q_norm_w + 64 * half;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const u32x4 w4 = ld16(wsrc + 4 * j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[4 * j + i] *= r * __uint_as_float(w4[i]);
+      }
+      if (RH > 0 && half == 0) {
+        const long long pos = p.pos_offset + qi;
+        float y[2 * (RH > 0 ? RH : 1)];
+#pragma unroll
+        for (int t = 0; t < RH; ++t) {
+          float cc, sn;
+          rope_cos_sin(p.tab, t, pos, cc, sn);
+          y[t] = x[t] * cc - x[t + RH] * sn;
+          y[t + RH] = x[t + RH] * cc + x[t] * sn;
+        }
+#pragma unroll
+        for (int d = 0; d < 2 * RH; ++d) x[d] = y[d];
+      }
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) qf[kk] = pack_bf16x8(x + 8 * kk);
+      if (qok) {
+        uint16_t* dst = const_cast<uint16_t*>(p.qp) + qrow * kD + 64 * half;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) st16(dst + 8 * j, __builtin_bit_cast(u32x4, qf[j]));
+      }
+    } else {
+      const uint16_t* qs = p.qp + qrow * kD + 64 * half;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        qf[j] = __builtin_bit_cast(bf16x8, qok ? ld16(qs + 8 * j) : u32x4{0, 0, 0, 0});
     }
   }
   const long long lrw = ((long long)b * p.Hq + head) * p.Spad + qi;  // qi < Spad
@@ -664,7 +714,12 @@ hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream) {
   geo.n_bhg = p.B * p.Hkv * geo.hgroups;
   const long long blocks = (long long)geo.n_pos_blocks * geo.n_bhg;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, geo);
+  if (!bwd_dq_fuses_q(p.rope_half))
+    hipLaunchKernelGGL(bwd_dq_kernel<-1>, dim3((unsigned)blocks), dim3(256), 0, stream, p, geo);
+  else if (p.rope_half == 21)
+    hipLaunchKernelGGL(bwd_dq_kernel<21>, dim3((unsigned)blocks), dim3(256), 0, stream, p, geo);
+  else
+    hipLaunchKernelGGL(bwd_dq_kernel<0>, dim3((unsigned)blocks), dim3(256), 0, stream, p, geo);
   return hipGetLastError();
 }
 

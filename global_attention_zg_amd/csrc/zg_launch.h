@@ -134,10 +134,11 @@ hipError_t launch_gemm_bf16_tn(GemmParams p, hipStream_t stream);
 hipError_t launch_quantize_fp8(const uint16_t* x, uint8_t* q, long long n, float scale,
                                hipStream_t stream);
 
-// Training backward.  Q' / K' are the normalised + rotated rows recomputed by
-// launch_k_prologue; dO = dY * sigmoid(G) (dY itself on an ungated layer).
+// Training backward.  K' is recomputed by launch_k_prologue; so is Q', except
+// where the dq' kernel forms it itself (bwd_dq_fuses_q) and writes it to qp
+// for the dk'/dv kernel.  dO = dY * sigmoid(G) (dY itself on an ungated layer).
 struct BwdParams {
-  const uint16_t* qp;   // bf16 [B,S,Hq,D]   Q'
+  const uint16_t* qp;   // bf16 [B,S,Hq,D]   Q' (written by the dq' kernel when it fuses Q')
   const uint16_t* kp;   // bf16 [B,S,Hkv,D]  K'
   const uint16_t* v;    // bf16 [B,S,Hkv,D]
   const uint16_t* dO;   // bf16 [B,S,Hq,D]
@@ -149,7 +150,18 @@ struct BwdParams {
   int B, S, Spad, Hq, Hkv, window;
   float scale_log2;     // softmax scale * log2(e)
   float scale;          // softmax scale
+  // for the dq' kernel's own Q' (bwd_dq_fuses_q): raw q and the prologue
+  const uint16_t* q;    // bf16 [B,S,Hq,D]
+  const float* q_norm_w;
+  float eps;
+  int rope_half;
+  long long pos_offset;
+  RopeTable tab;
 };
+
+// The dq' kernel forms Q' itself, with the forward's fused query prologue,
+// when the rotation runs in registers there (rope_dim 42 or 0).
+inline bool bwd_dq_fuses_q(int rope_half) { return rope_half == 21 || rope_half == 0; }
 
 // Row padding of the LSE / D vectors (a multiple of every query block).
 constexpr int kBwdRowPad = 128;
