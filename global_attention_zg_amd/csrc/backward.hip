@@ -17,7 +17,8 @@
 // Kernels:
 //   bwd_prep_kernel      dO, dG, Dr and LSE*log2(e) per query row
 //   bwd_dq_kernel        query-stationary: dq' for 32 rows per wave; K' and V
-//                        tiles stream through LDS as in the forward
+//                        tiles stream through LDS as in the forward; forms
+//                        Q' from q itself (rope_dim 42 or 0) and writes it
 //   bwd_dkv_kernel       key-stationary: dk' and dv for 32 keys per wave,
 //                        summed over the group's query heads; Q' and dO
 //                        tiles stream through LDS
