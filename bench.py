@@ -228,10 +228,15 @@ def reference_peaks(torch, iters=20):
                      "sclk_mhz": 2400.0}}
 
 
+# Oracle sample of the block (layer -> leading query rows), about 15 s of
+# fp64 work on 16 host cores: the global layer's cost grows with rows^2.
+SAMPLE_ROWS = {0: 8192, 5: 11584}
+
+
 def cpu_baseline(gpu_rows=None):
-    """The fp64 oracle timed on a bounded sample of the block: the first 4096
-    query rows of one gated SWA layer and the first 8192 rows of the global
-    layer (all 32 query heads), with the same seeded inputs.  Causal rows
+    """The fp64 oracle timed on a bounded sample of the block: the first
+    SAMPLE_ROWS query rows of one gated SWA layer and of the global layer
+    (all 32 query heads), with the same seeded inputs.  Causal rows
     depend only on the keys before them, so these prefix rows are also rows
     of the full 262144-position layers: `gpu_rows` (layer -> the kernel's
     output on those rows, from the timed run) is compared with them."""
@@ -249,7 +254,7 @@ def cpu_baseline(gpu_rows=None):
     flops = 0
     t_total = 0.0
     parity = {}
-    for layer, window, rows, gated in ((0, 128, 4096, True), (5, 0, 8192, False)):
+    for layer, window, rows, gated in ((0, 128, SAMPLE_ROWS[0], True), (5, 0, SAMPLE_ROWS[5], False)):
         # the first `rows` positions of the layer's tensors are a prefix of the
         # full [1, S, H, D] tensors in the flat element order
         q = f64((4, layer, inputs.T_Q), (1, rows, 32, D))
@@ -276,7 +281,8 @@ def cpu_baseline(gpu_rows=None):
         threads = len(os.sched_getaffinity(0))
     return dict(value=round(flops / t_total / 1e12, 6), unit="TFLOP/s", cores=int(threads),
                 kind="oracle",
-                sample="first 4096 query rows of one gated SWA layer + first 8192 rows of the "
+                sample=f"first {SAMPLE_ROWS[0]} query rows of one gated SWA layer + first "
+                       f"{SAMPLE_ROWS[5]} rows of the "
                        "global layer of the 256K block, all 32 query heads, fp64 numpy; "
                        f"{flops / 1e9:.1f} GFLOP in {t_total:.1f} s",
                 seconds=round(t_total, 2)), parity
@@ -377,8 +383,8 @@ def main():
                                "global_layer": round(t_glob * 1e3, 3)},
     }
     # the kernel's output on the rows the oracle sample covers
-    gpu_rows = {0: layers[0].out[:, :4096].float().cpu().numpy().astype(np.float64),
-                5: glob.out[:, :8192].float().cpu().numpy().astype(np.float64)}
+    gpu_rows = {l: (layers[l].out[:, :n].float().cpu().numpy().astype(np.float64))
+                for l, n in SAMPLE_ROWS.items()}
     del layers, glob
     torch.cuda.empty_cache()
 
