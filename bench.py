@@ -228,7 +228,7 @@ def reference_peaks(torch, iters=20):
                      "sclk_mhz": 2400.0}}
 
 
-# Oracle sample of the block (layer -> leading query rows), about 15 s of
+# Oracle sample of the block (layer -> leading query rows), about 13 s of
 # fp64 work on 16 host cores: the global layer's cost grows with rows^2.
 SAMPLE_ROWS = {0: 8192, 5: 11584}
 

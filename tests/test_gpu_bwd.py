@@ -178,3 +178,32 @@ def test_bwd_global_2k_layer():
     ref = run_oracle(c, 0, gated=False)
     errs = compare_grads(got, ref, "global2k")
     print(errs, file=sys.stderr)
+
+
+@pytest.mark.parametrize("rope_dim", [42, 30])
+def test_bwd_q_prime_matches_oracle_prologue(rope_dim):
+    """The Q' the backward uses (formed inside the dq' kernel at rope_dim 42,
+    recomputed by the key prologue kernel otherwise) is the oracle's RMSNorm +
+    partial RoPE of q to bf16 rounding.  Q' sits at the start of the
+    workspace (its first segment), rows [B,S,Hq,D]."""
+    bd = _binding()
+    B, S, Hq, Hkv, pos = 2, 150, 8, 2, 33
+    c = bwd_case("qprime", B, S, Hq, Hkv, gated=True)
+    q, k, v, g = (zc.to_dev(c[n], torch) for n in ("q", "k", "v", "gate"))
+    dy = zc.to_dev(c["dout"], torch)
+    gq = torch.from_numpy(c["gq"]).cuda()
+    gk = torch.from_numpy(c["gk"]).cuda()
+    args = dict(KW, rope_dim=rope_dim, pos_offset=pos)
+    out, lse = bd.zg_attn_fwd(q, k, v, g, gq, gk, want_lse=True, window=128, **args)
+    p = bd.make_params(B, S, Hq, Hkv, zc.D, 128, rope_dim, 10000.0, 1e-6, 0.0, pos)
+    ws = torch.zeros(bd.zg_attn_bwd_workspace_size(p), dtype=torch.uint8, device="cuda")
+    bd.zg_attn_bwd(q, k, v, g, gq, gk, out, lse, dy, window=128, workspace=ws, **args)
+    torch.cuda.synchronize()
+    n = B * S * Hq * zc.D
+    qp = ws[:2 * n].view(torch.bfloat16).float().cpu().numpy().astype(np.float64)
+    qp = qp.reshape(B, S, Hq, zc.D)
+    qn = orc.rms_norm(zc.f64(c["q"]), c["gq"].astype(np.float64), 1e-6)
+    ref = np.stack([orc.apply_partial_rope(qn[b], pos + np.arange(S), rope_dim, 10000.0)
+                    for b in range(B)])
+    d = np.abs(qp - ref)
+    assert np.all(d <= 2.0 ** -8 * np.abs(ref) + 1e-5), float(d.max())
