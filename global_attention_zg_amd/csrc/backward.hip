@@ -551,10 +551,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
 //   r = (mean(x^2) + eps)^-1/2
 //   dx = r (w * dx_hat) - x r^3 mean(w * dx_hat * x)
 //   dw += dx_hat * x * r              (per-block partials, summed later)
-// A fixed grid of kBwdParts blocks (eight per CU; at 87 VGPRs five are resident
-// at a time) strides over groups of 16
-// rows; each group's x and dy' rows are loaded one iteration ahead, and the
-// barriers wait for LDS only, so those loads stay in flight across them.
+// A fixed grid of kBwdParts blocks (eight per CU; at 87 VGPRs five are
+// resident at a time) strides over groups of 16 rows; each group's x and dy'
+// rows are loaded one iteration ahead, and the barriers wait for LDS only, so
+// those loads stay in flight across them.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void prologue_bwd_kernel(const uint16_t* __restrict__ x,
                                                            const uint16_t* __restrict__ dyp,
