@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libzgattn.so")
-SOURCES = ["prologue.hip", "flash_fwd.hip", "decode.hip", "backward.hip", "gemm.hip", "api.hip"]
+SOURCES = ["prologue.hip", "flash_fwd.hip", "flash_causal.hip", "decode.hip", "backward.hip", "gemm.hip", "api.hip"]
 ARCH = "gfx950"
 
 
@@ -35,6 +35,12 @@ CFLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC", "-Wall", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
+
+
+# Per-source extra flags.  The causal kernel keeps its output accumulators in
+# AGPRs through inline asm and wants every other MFMA result (the scores,
+# which the softmax reads) written straight to VGPRs.
+SOURCE_FLAGS = {"flash_causal.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
 
 
 def _run(cmd):
@@ -54,7 +60,8 @@ def build(verbose: bool = False, extra_flags=()) -> str:
 
     def one(src):
         obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        out = _run([cc, *CFLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
+        out = _run([cc, *CFLAGS, *SOURCE_FLAGS.get(src, []), *extra_flags, "-c",
+                    os.path.join(CSRC, src), "-o", obj])
         if verbose and out.strip():
             print(out)
         return obj

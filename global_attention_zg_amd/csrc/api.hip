@@ -129,6 +129,7 @@ static int fwd_impl(const zg_attn_params* p, const int* cu_seqlens, long long to
   fp.v = static_cast<const uint16_t*>(v);
   fp.gate = static_cast<const uint16_t*>(gate);
   fp.q_norm_w = q_norm_w;
+  fp.k_norm_w = k_norm_w;
   fp.out = static_cast<uint16_t*>(out);
   fp.lse = lse;
   fp.cu_seqlens = cu_seqlens;

@@ -1,0 +1,520 @@
+// Global (full causal) flash attention, forward.
+//
+// Page "ZGCM-1:面向数学与智能体搜索的全开源高效基础模型" (paper.rainbus.top),
+// section 前置知识 › 滑动窗口注意力(SWA)与混合注意力: the global layers
+// attend over the whole causal prefix; section 核心方法: GQA, 32 query heads
+// share 8 KV heads.  Section 技术新颖性: the quadratic cost of these layers is
+// what the hybrid's advantage at long context comes from, so this kernel is
+// where a long prefill spends its time.
+//
+// One wave per SIMD.  A workgroup of four waves serves one KV head g and 64
+// query positions: wave w is query head w of g's group at all 64 positions
+// (GQA packing: each K'/V tile copied into LDS feeds the four heads).  A wave
+// holds its 64 query rows as two halves of 32 rows, each with its own
+// accumulator (128 fp32 per lane in all), so that every K' and V operand it
+// reads from LDS feeds two MFMAs.
+//
+// Per 32-key tile the wave runs four slots; the MFMAs of each slot do not
+// depend on the VALU work placed beside them, so the matrix cores and the
+// vector ALUs of the SIMD work side by side:
+//   A: S0 = K'(j+1) Q0'^T           beside  softmax of half 1 on tile j -> P1
+//   B: O1 += V(j)^T P1^T             beside  softmax of half 0 on tile j+1 -> P0
+//   C: S1 = K'(j+1) Q1'^T           beside  the V(j+1) operand reads
+//   D: O0 += V(j+1)^T P0^T           beside  the K'(j+2) operand reads
+// A lazy rescale of an accumulator (the running max grew by more than 2^8 in
+// exp2 units) is applied at the next slot boundary, before that half's next
+// PV product; the row sum is rescaled at once.
+//
+// K'/V tiles go global -> LDS directly (global_load_lds_dwordx4) through a
+// ring of NS tile stages with the banded kernel's swizzled 256-byte rows;
+// copies fly NS - 2 tiles ahead, and one barrier per tile both publishes the
+// tile two ahead and frees the stage of the tile just read.  Tiles are
+// visited from the diagonal down; query blocks are launched longest-first.
+
+#include "zg_common.h"
+#include "zg_launch.h"
+#include "zg_lds.h"
+#include "zg_flash_tile.h"
+
+namespace zg {
+
+namespace {
+
+using namespace flash;
+
+constexpr int kCWaves = 4;
+constexpr int kCThreads = 64 * kCWaves;
+constexpr int kCRows = 64;       // query rows per wave (two halves of 32)
+constexpr int kCCopies = 4;      // a wave's global -> LDS copies per tile (2 KB of K', 2 KB of V)
+
+// Causal mask of one 32-key block for this lane's row: register r holds key
+// kblk + 4 h + 8 (r/4) + r%4, visible iff key <= qm, i.e. iff the immediate
+// 8 (r/4) + r%4 is at most thr = qm - kblk - 4 h.
+__device__ __forceinline__ void mask_causal(f32x16& s, int thr) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 8 * (r >> 2) + (r & 3) > thr ? -INFINITY : s[r];
+}
+
+// S^T = K' Q'^T + seed for one 32-key block: Q' carries the softmax scale
+// times log2(e) and the accumulator starts from minus the row's softmax
+// offset, so the result is the exp2 argument of P itself.
+__device__ __forceinline__ void qk_seeded(f32x16& s, const bf16x8 (&ka)[8], const bf16x8 (&qf)[8],
+                                          const f32x16& seed) {
+  s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], seed, 0, 0, 0);
+#pragma unroll
+  for (int kk = 1; kk < 8; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[kk], s, 0, 0, 0);
+}
+
+// Word w (0..7) of P: elements 2w, 2w+1 of P = exp2(s) packed to bf16
+// (word w of the PV B operand of k-step w/4), and their sum, from the
+// rounded values the MFMA multiplies, added to the row sum.
+__device__ __forceinline__ uint32_t p_word(const f32x16& s, int w, float& l_run) {
+  const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+  const uint32_t u = pack_bf16x2(fast_exp2(s[2 * w]), fast_exp2(s[2 * w + 1]));
+  l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u), one2, l_run, false);
+  return u;
+}
+
+// O^T += V^T P^T (the operand layout of load_vops and P) with the accumulator held
+// in AGPRs by the asm constraint, so that the register allocator never moves
+// it; the score MFMAs then write their results to VGPRs, where the softmax
+// reads them.  Back-to-back accumulation into the same registers needs no
+// wait states; a VALU read of the accumulator does (acc_settle).
+__device__ __forceinline__ void pv_agpr(f32x16 (&acc)[4], const bf16x8 (&va)[8],
+                                        const bf16x8 (&pf)[2]) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int bd = 0; bd < 4; ++bd)
+      asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[bd]) : "v"(va[4 * t + bd]), "v"(pf[t]));
+  }
+}
+
+// The i-th MFMA (k-step i/4, dim block i%4) of pv_agpr.
+__device__ __forceinline__ void pv_agpr_one(f32x16 (&acc)[4], const bf16x8 (&va)[8],
+                                            const bf16x8 (&pf)[2], int i) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc[i % 4]) : "v"(va[i]), "v"(pf[i / 4]));
+}
+
+// Wait states between the last accumulation and a VALU read of the
+// accumulator (more than the 18 an MFMA of 16 passes needs).
+__device__ __forceinline__ void acc_settle(f32x16 (&acc)[4]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
+}
+
+// RH: rope_dim / 2 when fixed at compile time (21 or 0), else -1.
+// NS: K'/V tile stages in LDS.
+template <int RH, bool PACKED, int NS>
+__global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams p, Geo geo) {
+  constexpr int kSmem = 2 * NS * kTileBytes;
+  constexpr int kVOff = NS * kTileBytes;
+  static_assert(kCWaves * 32 * 65 * 4 <= kSmem, "query RoPE rows must fit");
+  static_assert(NS >= 3, "copies fly NS - 2 tiles ahead");
+  __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kSmem];
+  lds_u8* smem = (lds_u8*)smem_raw;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int qcol = lane & 31;
+  const int half = lane >> 5;
+  const int grp = p.Hq / p.Hkv;
+
+  // ---- workgroup -> (position block, batch, kv head, head group)
+  const int bid = blockIdx.x;
+  const int bhg = bid % geo.n_bhg;
+  const int pb = geo.n_pos_blocks - 1 - bid / geo.n_bhg;  // longest causal rows first
+  const int hg = bhg % geo.hgroups;
+  const int bgi = bhg / geo.hgroups;
+  const int g = bgi % p.Hkv;
+  const int b = bgi / p.Hkv;
+  const int head = g * grp + hg * geo.heads_per_wg + (wv % geo.heads_per_wg);
+  const int i0w = pb * geo.pos_per_wg;
+  int S = p.S;
+  long long tok0 = (long long)b * p.S;
+  long long lse0 = (long long)b * p.Hq * p.S, lse_hs = p.S;
+  if constexpr (PACKED) {
+    const long long c0 = min(max((long long)p.cu_seqlens[b], 0LL), p.total);
+    const long long c1 = min(max((long long)p.cu_seqlens[b + 1], c0), p.total);
+    tok0 = c0;
+    S = (int)min(c1 - c0, (long long)p.S);
+    lse0 = tok0;
+    lse_hs = p.total;
+    if (i0w >= S) return;  // whole workgroup: past the end of a short sequence
+  }
+  // This wave's rows: half h is rows wrow0 + 32 h + (lane % 32).  Rows past
+  // the end are padding with row S-1's visibility.
+  const int wrow0 = i0w + (wv / geo.heads_per_wg) * kCRows;
+  int qi[2], qm[2];
+  bool qok[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    qi[h] = wrow0 + 32 * h + qcol;
+    qok[h] = qi[h] < S;
+    qm[h] = min(qi[h], S - 1);
+  }
+  const int hi = min(S, i0w + geo.pos_per_wg);  // keys < hi
+  const int t_hi = (hi - 1) / kBN;
+  const int nt = t_hi + 1;
+
+  // ---- K'/V staging: wave w fills the 1 KB blocks 2w, 2w + 1 (rows 4n ..
+  // 4n + 3) of each 8 KB tile; lane L writes physical chunk L % 16 of row
+  // 4n + L / 16 and so fetches the logical chunk the row's swizzle puts there.
+  const long long kvstride = (long long)p.Hkv * kD;
+  const uint16_t* kbase = p.kp + tok0 * kvstride + g * kD;
+  const uint16_t* vbase = p.v + tok0 * kvstride + g * kD;
+  uint32_t row_off[2], kchunk[2];
+  int lrow[2];
+  const uint32_t vchunk = 16u * ((lane & 15) ^ (((lane >> 4) & 3) << 2));
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    lrow[j] = 4 * (2 * wv + j) + (lane >> 4);
+    row_off[j] = (uint32_t)(lrow[j] * kvstride * 2);
+    kchunk[j] = 16u * ((lane & 15) ^ (lrow[j] & 15));
+  }
+  // tile t (0 <= t <= t_hi) -> stage stg; keys >= S (only in the top tile)
+  // load key S-1 and are masked out
+  auto gload = [&](int t, int stg) __attribute__((always_inline)) {
+    const unsigned char* kb = (const unsigned char*)(kbase + (long long)t * kBN * kvstride);
+    const unsigned char* vb = (const unsigned char*)(vbase + (long long)t * kBN * kvstride);
+    const uint32_t kl = lds_addr(smem + stg * kTileBytes + 2 * wv * 1024);
+    const uint32_t vl = kl + kVOff;
+    if (t * kBN + kBN <= S) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        dma16_s(kb, row_off[j] + kchunk[j], kl + j * 1024);
+        dma16_s(vb, row_off[j] + vchunk, vl + j * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t off = (uint32_t)((min(t * kBN + lrow[j], S - 1) - t * kBN) * kvstride * 2);
+        dma16_s(kb, off + kchunk[j], kl + j * 1024);
+        dma16_s(vb, off + vchunk, vl + j * 1024);
+      }
+    }
+  };
+  // visit index j -> tile t_hi - j; indices past the last tile copy tile 0
+  // (finite values, never used), which keeps the number of copies in flight
+  // the same on every iteration
+  auto gload_j = [&](int j, int stg) __attribute__((always_inline)) { gload(max(t_hi - j, 0), stg); };
+
+  // per-lane LDS read offsets: K' row q%32 at logical chunk 8h; V rows
+  // 4h + i/4 at dims 32bd + 16 (group parity) + 4 (i%4) for the transposing loads
+  const uint32_t kread_off = qcol * kRowBytes + ((uint32_t)((8 * half) ^ (qcol & 15)) << 4);
+  const int gi = lane & 15;
+  const int vq = gi >> 2;
+  const int vlow = 2 * ((lane >> 4) & 1) + ((gi & 3) >> 1);
+  const lds_u8* vread0[4];  // stage 0; stage k adds k * kTileBytes
+#pragma unroll
+  for (int bd = 0; bd < 4; ++bd) {
+    const int off = (4 * half + vq) * kRowBytes + (((bd ^ vq) << 2 | vlow) << 4) + 8 * (gi & 1);
+    vread0[bd] = smem + kVOff + off;
+  }
+
+  TileState st[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int bd = 0; bd < 4; ++bd) st[h].acc[bd] = f32x16{};
+    st[h].l_run = 0.f;
+  }
+
+  // ---- start-up: the ring is filled with the first NS tiles while the
+  // query rows are loaded and normalised + rotated (the generic rotation uses
+  // LDS rows first and fills the ring afterwards)
+  auto fill_ring = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int jj = 0; jj < NS; ++jj) gload_j(jj, jj);
+  };
+  if (RH >= 0) fill_ring();
+  // max |w_k| over the 128 key-norm weights (two per lane, then the wave)
+  float wk = fmaxf(fabsf(p.k_norm_w[2 * lane]), fabsf(p.k_norm_w[2 * lane + 1]));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) wk = fmaxf(wk, __shfl_xor(wk, o));
+  bf16x8 qf[2][8];
+  bool fast_ok = true;
+  // (the halves are fenced from each other so that the scheduler does not
+  // overlap their loads: the register peak of the prologue would otherwise
+  // push the loop's operands out to scratch)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    __builtin_amdgcn_sched_barrier(0);
+    float x[64];
+    const long long qrow = (tok0 + (qok[h] ? qi[h] : 0)) * p.Hq + head;
+    const uint16_t* src = p.q + qrow * kD + 64 * half;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      u32x4 u = qok[h] ? ld16(src + 8 * j) : u32x4{0, 0, 0, 0};
+      unpack_bf16x8(u, x + 8 * j);
+    }
+    float* qs = reinterpret_cast<float*>(smem_raw) + (wv * 32 + qcol) * 65;
+    q_prologue<RH>(x, half, p, p.pos_offset + qi[h], qs, qf[h]);
+    // Softmax offset.  q' is held pre-scaled by c = scale log2(e), so the
+    // scores come out in exp2 units.  Every score of this row is at most
+    //   U = |c q'| sqrt(D) max|w_k|   (RoPE keeps norms; the key RMSNorm
+    // bounds each normalised key by sqrt(D) before the weight), taken here
+    // over the bf16 c q' the products use and widened by 2^-6 for the bf16
+    // rounding of k' and the fp32 sums.  With P = exp2(s - U) every weight is
+    // at most 1.  The row's own key is visible, so its largest weight is at
+    // least exp2(s_ii - U); while that stays above 2^-100 the fixed offset
+    // loses nothing to underflow and no running max is needed.
+    float qq = 0.f, sii = 0.f;
+    const uint16_t* krow = p.kp + ((tok0 + qm[h]) * p.Hkv + g) * kD + 64 * half;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float qv[8], kv[8];
+      unpack_bf16x8(__builtin_bit_cast(u32x4, qf[h][j]), qv);
+      unpack_bf16x8(ld16(krow + 8 * j), kv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qq = __builtin_fmaf(qv[e], qv[e], qq);
+        sii = __builtin_fmaf(qv[e], kv[e], sii);
+      }
+    }
+    qq = pair_sum32(qq);
+    sii = pair_sum32(sii);
+    const float u = sqrtf(qq) * sqrtf((float)kD) * wk * (1.0f + 0.015625f);
+    st[h].m_run = u;
+    fast_ok = fast_ok && u - sii <= 100.0f;
+    // the query operands stay in accumulation registers for the whole
+    // kernel (the matrix cores read their A/B operands from either file),
+    // which leaves the vector registers to the loop's working set
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) asm volatile("; q' operand to AGPRs" : "=a"(qf[h][kk]) : "0"(qf[h][kk]));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Workgroup-uniform: if any row's largest weight could underflow, every
+  // wave first takes its rows' exact maxima (a pass of the score products
+  // alone) and uses those as the offsets instead.
+  const bool exact_max = __syncthreads_or(!fast_ok) != 0;
+  if (RH < 0) fill_ring();  // (the barrier above ended the prologue's LDS use)
+  sync_tiles<0>();
+
+  // a tile needs masking for half h if it reaches past the half's first row
+  auto masked = [&](int j, int h) __attribute__((always_inline)) { return (t_hi - j) * kBN + kBN - 1 > wrow0 + 32 * h; };
+  auto kst = [&](int stg) __attribute__((always_inline)) { return smem + stg * kTileBytes; };
+  bf16x8 ka[8], va[8], pf[2][2];
+  f32x16 s[2];
+  if (exact_max) {
+    float mx[2] = {-INFINITY, -INFINITY};
+    int stg = 0;
+    for (int j = 0; j < nt; ++j) {
+      // tile j has landed (the first NS before the loop; later tiles j + 1 ..
+      // j + NS - 1 may fly)
+      if (j > 0) sync_tiles<kCCopies * (NS - 1)>();
+      load_kops(ka, kst(stg), kread_off);
+      qk_mfma(s[0], ka, qf[0]);
+      qk_mfma(s[1], ka, qf[1]);
+      lds_barrier();  // every wave has read stage stg
+      gload_j(j + NS, stg);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (masked(j, h)) mask_causal(s[h], qm[h] - (t_hi - j) * kBN - 4 * half);
+        mx[h] = fmaxf(mx[h], blk_max(s[h]));
+      }
+      stg = stg + 1 == NS ? 0 : stg + 1;
+    }
+    sync_tiles<0>();
+    fill_ring();
+    sync_tiles<0>();
+#pragma unroll
+    for (int h = 0; h < 2; ++h) st[h].m_run = mx[h];
+  }
+  // m_run: the row's softmax offset (exp2 units); the score accumulators
+  // start from its negative
+  f32x16 seed[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) seed[h][r] = -st[h].m_run;
+  }
+
+  auto vops = [&](int stg) __attribute__((always_inline)) {
+    const lds_u8* vr[4];
+#pragma unroll
+    for (int bd = 0; bd < 4; ++bd) vr[bd] = vread0[bd] + stg * kTileBytes;
+    load_vops(va, vr);
+  };
+  auto mask = [&](int h, int j) __attribute__((always_inline)) {
+    if (masked(j, h)) mask_causal(s[h], qm[h] - (t_hi - j) * kBN - 4 * half);
+  };
+  // Half h's P, packed to bf16, and its row sums.  The results are consumed
+  // by an empty asm at the end of the slot, so that the compiler keeps this
+  // VALU work beside that slot's MFMAs instead of sinking it to the first use.
+  auto softmax = [&](int h) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      u32x4 u;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) u[w] = p_word(s[h], 4 * t + w, st[h].l_run);
+      pf[h][t] = __builtin_bit_cast(bf16x8, u);
+    }
+    pin(pf[h][0]);
+    pin(pf[h][1]);
+    pin(st[h].l_run);
+  };
+  // The PV MFMAs of half 1 beside half 0's P.  The scheduler cannot see the
+  // asm MFMAs' latency, so the order is fixed here, software-pipelined over
+  // the eight words of P: MFMA g goes with the exps of word g and the
+  // packing and row sum of word g - 1, so that no step waits on the one just
+  // before it and no two MFMAs are issued back to back.
+  auto pv1_sm0 = [&]() __attribute__((always_inline)) {
+    const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
+    float e[16];
+    u32x4 u[2];
+    auto word = [&](int w) __attribute__((always_inline)) {
+      // (bit-cast a scalar: a bit-cast of a vector element reads element 0)
+      const uint32_t uw = pack_bf16x2(e[2 * w], e[2 * w + 1]);
+      u[w / 4][w % 4] = uw;
+      st[0].l_run =
+          __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, uw), one2, st[0].l_run, false);
+    };
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      pv_agpr_one(st[1].acc, va, pf[1], g);
+      e[2 * g] = fast_exp2(s[0][2 * g]);
+      e[2 * g + 1] = fast_exp2(s[0][2 * g + 1]);
+      if (g > 0) word(g - 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    word(7);
+    pf[0][0] = __builtin_bit_cast(bf16x8, u[0]);
+    pf[0][1] = __builtin_bit_cast(bf16x8, u[1]);
+    pin(pf[0][0]);
+    pin(pf[0][1]);
+    pin(st[0].l_run);
+  };
+
+  // Per 32-key tile j the wave runs four slots; the MFMAs of each slot do not
+  // depend on the VALU work beside them:
+  //   A(j): S0 = K'(j+1) Q0'^T   | half 1's P of tile j
+  //   B(j): O1 += V(j) P1(j)     | half 0's P of tile j + 1
+  //   C(j): S1 = K'(j+1) Q1'^T   | the V(j+1) operand reads
+  //   D(j): O0 += V(j+1) P0(j+1) | the K'(j+2) operand reads
+  // The causal mask (only the first tiles of a wave need it) is applied
+  // under a wave-uniform branch at the slot boundary before a half's P, so
+  // that the slots themselves stay single blocks.
+
+  // ---- warm-up: both halves' scores of tile 0, half 0's P and PV
+  load_kops(ka, kst(0), kread_off);
+  qk_seeded(s[0], ka, qf[0], seed[0]);
+  qk_seeded(s[1], ka, qf[1], seed[1]);
+  mask(0, 0);
+  softmax(0);
+  vops(0);
+  load_kops(ka, kst(1 % NS), kread_off);  // tile 1 (or a copy of tile 0)
+  lds_barrier();                          // every wave has read tile 0
+  gload_j(NS, 0);
+  pv_agpr(st[0].acc, va, pf[0]);
+
+  // ---- main loop.  On entry to iteration j: S1 of tile j, ka = K'(j + 1),
+  // va = V(j), O0 through tile j, O1 through tile j - 1.
+  int sa = 1 % NS;  // stage of tile j + 1
+  for (int j = 0; j + 1 < nt; ++j) {
+    const int sb = sa + 1 == NS ? 0 : sa + 1;  // stage of tile j + 2
+    mask(1, j);
+    // A
+    __builtin_amdgcn_sched_barrier(0);
+    qk_seeded(s[0], ka, qf[0], seed[0]);
+    softmax(1);
+    __builtin_amdgcn_sched_barrier(0);
+    mask(0, j + 1);
+    // B
+    __builtin_amdgcn_sched_barrier(0);
+    pv1_sm0();
+    __builtin_amdgcn_sched_barrier(0);
+    // C
+    qk_seeded(s[1], ka, qf[1], seed[1]);
+    vops(sa);
+    __builtin_amdgcn_sched_barrier(0);
+    // tile j + 2 has landed for every wave, and no wave still reads tile
+    // j + 1's stage, which takes tile j + 1 + NS
+    sync_tiles<kCCopies * (NS - 2)>();
+    gload_j(j + 1 + NS, sa);
+    // D
+    __builtin_amdgcn_sched_barrier(0);
+    pv_agpr(st[0].acc, va, pf[0]);
+    load_kops(ka, kst(sb), kread_off);
+    __builtin_amdgcn_sched_barrier(0);
+    sa = sb;
+  }
+  // ---- tail: half 1 of the last tile
+  mask(1, nt - 1);
+  softmax(1);
+  pv_agpr(st[1].acc, va, pf[1]);
+  wait_vm<0>();  // the copies of tiles past the end
+
+  // ---- epilogue: normalise, gate (if any), store.  Register r of block bd,
+  // lane half h -> dim 32 bd + 8 (r/4) + 4 h + r%4: four runs of 4 dims.
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    acc_settle(st[h].acc);
+    const float l_tot = pair_sum32(st[h].l_run);
+    const float inv = 1.0f / l_tot;
+    if (p.lse && qok[h] && half == 0)
+      p.lse[lse0 + head * lse_hs + qi[h]] = (st[h].m_run + __log2f(l_tot)) * kLn2;
+    if (!qok[h]) continue;
+    const long long qrow = (tok0 + qi[h]) * p.Hq + head;
+    uint16_t* dst = p.out + qrow * kD + 4 * half;
+    const uint16_t* gsrc = p.gate ? p.gate + qrow * kD + 4 * half : nullptr;
+#pragma unroll
+    for (int bd = 0; bd < 4; ++bd) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = st[h].acc[bd][4 * q4 + e] * inv;
+        const int off = 32 * bd + 8 * q4;
+        if (gsrc) {
+          const uint2 gg = *reinterpret_cast<const uint2*>(gsrc + off);
+          o[0] *= sigmoidf_(bf_lo(gg.x));
+          o[1] *= sigmoidf_(bf_hi(gg.x));
+          o[2] *= sigmoidf_(bf_lo(gg.y));
+          o[3] *= sigmoidf_(bf_hi(gg.y));
+        }
+        uint2 w;
+        w.x = pack_bf16x2(o[0], o[1]);
+        w.y = pack_bf16x2(o[2], o[3]);
+        *reinterpret_cast<uint2*>(dst + off) = w;
+      }
+    }
+  }
+}
+
+constexpr int kCStages = 8;
+
+template <int RH, bool PACKED>
+void launch_causal(dim3 grid, hipStream_t stream, const FlashParams& p, const Geo& geo) {
+  hipLaunchKernelGGL((flash_causal_kernel<RH, PACKED, kCStages>), grid, dim3(kCThreads), 0, stream,
+                     p, geo);
+}
+
+}  // namespace
+
+hipError_t launch_flash_causal(const FlashParams& p, hipStream_t stream) {
+  if (p.B == 0 || p.S == 0) return hipSuccess;
+  const int grp = p.Hq / p.Hkv;
+  Geo geo;
+  geo.heads_per_wg = grp < kCWaves ? grp : kCWaves;
+  geo.hgroups = grp / geo.heads_per_wg;
+  geo.pos_per_wg = kCRows * kCWaves / geo.heads_per_wg;
+  geo.n_pos_blocks = (p.S + geo.pos_per_wg - 1) / geo.pos_per_wg;
+  geo.n_bhg = p.B * p.Hkv * geo.hgroups;
+  const long long blocks = (long long)geo.n_pos_blocks * geo.n_bhg;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks);
+  if (p.cu_seqlens) {
+    if (p.rope_half == 21) launch_causal<21, true>(grid, stream, p, geo);
+    else if (p.rope_half == 0) launch_causal<0, true>(grid, stream, p, geo);
+    else launch_causal<-1, true>(grid, stream, p, geo);
+  } else {
+    if (p.rope_half == 21) launch_causal<21, false>(grid, stream, p, geo);
+    else if (p.rope_half == 0) launch_causal<0, false>(grid, stream, p, geo);
+    else launch_causal<-1, false>(grid, stream, p, geo);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace zg

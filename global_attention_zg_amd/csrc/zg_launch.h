@@ -16,6 +16,7 @@ struct FlashParams {
   const uint16_t* v;     // bf16 [B,S,Hkv,D]
   const uint16_t* gate;  // bf16 [B,S,Hq,D] or null
   const float* q_norm_w; // fp32 [D]
+  const float* k_norm_w; // fp32 [D] (the causal kernel bounds its scores with it)
   uint16_t* out;         // bf16 [B,S,Hq,D]
   float* lse;            // fp32 [B,Hq,S], or [Hq,total] when packed; or null
   int B, S, Hq, Hkv, window, rope_half;
@@ -41,6 +42,8 @@ hipError_t launch_k_prologue(const uint16_t* k, const float* w, uint16_t* kout, 
                              const int* cu_seqlens = nullptr, int nseq = 0);
 
 hipError_t launch_flash_fwd(const FlashParams& p, hipStream_t stream);
+// The global (window 0) layer's kernel; launch_flash_fwd routes to it.
+hipError_t launch_flash_causal(const FlashParams& p, hipStream_t stream);
 
 // Where a sequence's cache rows live.  Contiguous: one slab [cap, D] per
 // (b, kv head).  Paged (block_table != null): token t of sequence b is slot
