@@ -21,6 +21,7 @@ ZG_ERR_INVALID = -1
 ZG_ERR_UNSUPPORTED = -2
 ZG_ERR_WORKSPACE = -3
 ZG_ERR_HIP = -4
+ZG_ERR_TOO_LARGE = -5
 
 
 class ZgAttnError(RuntimeError):
@@ -66,6 +67,8 @@ def _load():
     lib.zg_attn_decode_workspace_size.restype = sz
     lib.zg_attn_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, i, i, vp, vp, vp, vp, i, vp, sz, vp]
     lib.zg_attn_decode.restype = i
+    lib.zg_attn_decode_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, i, i, vp, vp, vp, vp, i, vp]
+    lib.zg_attn_decode_noalloc.restype = i
     lib.zg_attn_decode_paged.argtypes = [P, vp, vp, vp, vp, vp, i, vp, i, i, vp, vp, vp, vp, vp,
                                          i, vp, sz, vp]
     lib.zg_attn_decode_paged.restype = i
@@ -103,7 +106,8 @@ EXPORTED = ("zg_attn_fwd_workspace_size", "zg_attn_fwd", "zg_attn_fwd_varlen_wor
             "zg_attn_decode_workspace_size", "zg_attn_decode", "zg_attn_kv_write_pages",
             "zg_attn_decode_paged", "zg_attn_bwd_workspace_size", "zg_attn_bwd",
             "zg_linear", "zg_qkvg_proj", "zg_quantize_fp8", "zg_linear_fp8",
-            "zg_attn_decode_fp8", "zg_attn_decode_paged_fp8", "zg_attn_strerror")
+            "zg_attn_decode_fp8", "zg_attn_decode_paged_fp8", "zg_attn_decode_noalloc",
+            "zg_attn_strerror")
 
 
 def library_path() -> str:
@@ -261,6 +265,25 @@ def zg_attn_decode(q, k_new, v_new, k_cache, v_cache, seq_lens, *, ring, window,
                              _ptr(v_cache), _ptr(seq_lens), cap, int(ring), _ptr(gate),
                              _ptr(q_norm_w), _ptr(k_norm_w), _ptr(out), num_splits,
                              _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st)
+    return out
+
+
+def zg_attn_decode_noalloc(q, k_new, v_new, k_cache, v_cache, seq_lens, *, ring, window, gate,
+                           q_norm_w, k_norm_w, rope_dim=42, rope_theta=10000.0, rms_eps=1e-6,
+                           softmax_scale=0.0, pos_offset=0, num_splits=0, out=None, stream=None):
+    """zg_attn_decode with the split partials in the library's static scratch
+    (no workspace).  Returns out."""
+    B, Hq, D = q.shape
+    Hkv, cap = k_cache.shape[1], k_cache.shape[2]
+    p = make_params(B, 0, Hq, Hkv, D, window, rope_dim, rope_theta, rms_eps, softmax_scale,
+                    pos_offset)
+    if out is None:
+        out = torch.empty_like(q)
+    st = _lib.zg_attn_decode_noalloc(ctypes.byref(p), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                     _ptr(k_cache), _ptr(v_cache), _ptr(seq_lens), cap, int(ring),
+                                     _ptr(gate), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(out),
+                                     num_splits, _stream(stream))
     _check(st)
     return out
 

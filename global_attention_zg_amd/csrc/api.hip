@@ -7,6 +7,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/zg_attn.h"
 #include "zg_launch.h"
 
@@ -52,6 +54,31 @@ float scale_log2(const zg_attn_params* p) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? ZG_OK : ZG_ERR_HIP; }
+
+// The no-allocation decode's split partials: one array per GPU, held until
+// the process ends.  In host code `scratch` names a host-side stand-in, not
+// a device address; the address on each device comes from
+// hipGetSymbolAddress, looked up once per device with that device current,
+// and only that address is passed to kernels.
+constexpr size_t kNoallocScratchBytes = ZG_DECODE_NOALLOC_SCRATCH_BYTES;
+static __device__ __attribute__((aligned(256))) unsigned char scratch[kNoallocScratchBytes];
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address (looked up on first use).
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ZG_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return ZG_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ZG_OK;
+}
 
 size_t kprime_bytes(const zg_attn_params* p) {
   return (size_t)p->batch * (size_t)p->seqlen * (size_t)p->n_kv_heads * kD * 2;
@@ -246,6 +273,8 @@ const char* zg_attn_strerror(int status) {
     case ZG_ERR_UNSUPPORTED: return "unsupported configuration";
     case ZG_ERR_WORKSPACE: return "workspace missing or too small";
     case ZG_ERR_HIP: return "HIP launch or runtime error";
+    case ZG_ERR_TOO_LARGE:
+      return "the split partials exceed the no-allocation decode's static scratch";
     default: return "unknown status";
   }
 }
@@ -399,6 +428,26 @@ int zg_attn_decode(const zg_attn_params* p, const void* q, const void* k_new, co
   return decode_impl(p, q, k_new, v_new, k_cache, v_cache, seq_lens, cache_cap, ring, contiguous,
                      gate, q_norm_w, k_norm_w, out, num_splits, workspace, workspace_bytes,
                      stream);
+}
+
+int zg_attn_decode_noalloc(const zg_attn_params* p, const void* q, const void* k_new,
+                           const void* v_new, void* k_cache, void* v_cache, const int* seq_lens,
+                           int cache_cap, int ring, const void* gate, const float* q_norm_w,
+                           const float* k_norm_w, void* out, int num_splits, void* stream) {
+  if (ring != 0 && ring != 1) return ZG_ERR_INVALID;
+  const int st = check_params(p);
+  if (st != ZG_OK) return st;
+  if (cache_cap < 1 || num_splits < 0 || num_splits > 256) return ZG_ERR_INVALID;
+  if (p->batch == 0) return ZG_OK;
+  // the size check comes before any HIP call
+  if (zg_attn_decode_workspace_size(p, cache_cap, num_splits) > kNoallocScratchBytes)
+    return ZG_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  const int sst = noalloc_scratch(&ws);
+  if (sst != ZG_OK) return sst;
+  const zg::CacheMap contiguous{nullptr, 0, 0, 0};
+  return decode_impl(p, q, k_new, v_new, k_cache, v_cache, seq_lens, cache_cap, ring, contiguous,
+                     gate, q_norm_w, k_norm_w, out, num_splits, ws, kNoallocScratchBytes, stream);
 }
 
 int zg_attn_decode_paged(const zg_attn_params* p, const void* q, const void* k_new,

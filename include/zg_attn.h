@@ -49,6 +49,7 @@ extern "C" {
                                   rope_dim > head_dim/2, odd rope_dim, ...)    */
 #define ZG_ERR_WORKSPACE   -3  /* workspace missing or smaller than required   */
 #define ZG_ERR_HIP         -4  /* a HIP launch or runtime call failed          */
+#define ZG_ERR_TOO_LARGE   -5  /* more scratch than zg_attn_decode_noalloc holds */
 
 typedef struct zg_attn_params {
   int   batch;          /* B  (>= 0)                                            */
@@ -142,6 +143,29 @@ int zg_attn_decode(const zg_attn_params* p,
                    const float* q_norm_w, const float* k_norm_w,
                    void* out, int num_splits,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- decode without allocation ------------------------------------------
+ * For callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments and semantics as zg_attn_decode without the
+ * workspace, and for equal inputs and num_splits the same output and cache
+ * bits.  The split partials live in a static device array of
+ * ZG_DECODE_NOALLOC_SCRATCH_BYTES per GPU, which the library holds until the
+ * process ends; a call whose partials (zg_attn_decode_workspace_size) would
+ * not fit returns ZG_ERR_TOO_LARGE before any HIP call.  The array is that
+ * of the device current on the calling thread, which must be the stream's
+ * device; its address is looked up once per device, on the first call
+ * there.  All calls on one GPU share the array: calls that overlap in time
+ * on one GPU (two streams, or two threads) race and must be serialised by
+ * the caller.  Nothing is allocated; no result depends on the array's
+ * previous contents. */
+#define ZG_DECODE_NOALLOC_SCRATCH_BYTES (8u << 20)
+int zg_attn_decode_noalloc(const zg_attn_params* p,
+                           const void* q, const void* k_new, const void* v_new,
+                           void* k_cache, void* v_cache, const int* seq_lens,
+                           int cache_cap, int ring, const void* gate,
+                           const float* q_norm_w, const float* k_norm_w,
+                           void* out, int num_splits, void* stream);
 
 /* Paged KV cache (a serving layout for the global layers' cache, whose size
  * at 256K tokens the structured-data table of the ZGCM-1 page, row

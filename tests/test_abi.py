@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(bd):
 
 def test_strerror(bd):
     assert bd.zg_attn_strerror(0) == "ok"
-    for st in (-1, -2, -3, -4):
+    for st in (-1, -2, -3, -4, -5):
         assert bd.zg_attn_strerror(st) and bd.zg_attn_strerror(st) != "unknown status"
     assert bd.zg_attn_strerror(-99) == "unknown status"
 
@@ -146,6 +146,32 @@ def test_decode_rejects_bad_arguments(bd):
     assert _dec(bd, p0, 128, 1) == bd.ZG_OK
     pbad = bd.make_params(2, 0, 32, 8, 96, 128)
     assert _dec(bd, pbad, 128, 1, **ok) == bd.ZG_ERR_UNSUPPORTED
+
+
+def _dec_noalloc(bd, p, cap, ring, num_splits=0, **ptrs):
+    a = [ptrs.get(n) for n in ("q", "kn", "vn", "kc", "vc", "sl")]
+    return bd._lib.zg_attn_decode_noalloc(ctypes.byref(p), *a, cap, ring, ptrs.get("gate"),
+                                          ptrs.get("qw"), ptrs.get("kw"), ptrs.get("out"),
+                                          num_splits, None)
+
+
+def test_noalloc_decode_rejects_before_any_hip_call(bd):
+    """Every rejection, the size limit included, comes before the library
+    touches HIP (the scratch address lookup), so it holds on a host without a
+    GPU."""
+    ok = dict(q=FAKE, kc=FAKE, vc=FAKE, sl=FAKE, qw=FAKE, kw=FAKE, out=FAKE)
+    p = bd.make_params(2, 0, 32, 8, 128, 0)
+    assert _dec_noalloc(bd, p, 128, 2, **ok) == bd.ZG_ERR_INVALID
+    assert _dec_noalloc(bd, p, 0, 0, **ok) == bd.ZG_ERR_INVALID
+    assert _dec_noalloc(bd, p, 128, 0, num_splits=257, **ok) == bd.ZG_ERR_INVALID
+    assert _dec_noalloc(bd, bd.make_params(2, 0, 32, 8, 96, 0), 128, 0, **ok) == bd.ZG_ERR_UNSUPPORTED
+    assert _dec_noalloc(bd, bd.make_params(0, 0, 32, 8, 128, 0), 128, 0) == bd.ZG_OK
+    # the partials of 64 sequences x 32 heads x 64 splits (68 MB) exceed the array
+    big = bd.make_params(64, 0, 32, 8, 128, 0)
+    need = bd.zg_attn_decode_workspace_size(big, 1 << 20, 64)
+    assert need > (8 << 20)
+    assert _dec_noalloc(bd, big, 1 << 20, 0, num_splits=64, **ok) == bd.ZG_ERR_TOO_LARGE
+    assert "scratch" in bd.zg_attn_strerror(bd.ZG_ERR_TOO_LARGE)
 
 
 def _dec_fp8(bd, p, cap, ring, k_scale, v_scale, num_splits=0, **ptrs):
