@@ -385,7 +385,10 @@ int zg_attn_bwd(const zg_attn_params* p, const void* q, const void* k, const voi
   bp.Spad = Spad;
   bp.Hq = Hq;
   bp.Hkv = Hkv;
-  bp.window = p->window;
+  // a window of at least S sees every causal key; clamping keeps the key
+  // kernel's band arithmetic (last query of a key block = keys + window - 1)
+  // inside int for any window up to INT_MAX
+  bp.window = p->window > S ? S : p->window;
   bp.scale_log2 = scale_log2(p);
   bp.scale = (float)(p->softmax_scale > 0.f ? (double)p->softmax_scale : 1.0 / sqrt((double)kD));
   bp.q = static_cast<const uint16_t*>(q);

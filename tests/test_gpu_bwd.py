@@ -110,10 +110,11 @@ def test_bwd_matches_oracle(B, S, Hq, Hkv, window, gated):
 
 def test_bwd_window_at_least_s_is_global_bitwise():
     """The backward with window >= S gives the global backward's bits when
-    both are fed the same forward output and LSE (the global forward's)."""
+    both are fed the same forward output and LSE (the global forward's),
+    up to the largest window an int holds."""
     c = bwd_case("bwd_wide", 1, 300, 8, 2, False)
     a = run_gpu(c, 0, gated=False)
-    for W in (300, 301, 5000):
+    for W in (300, 301, 5000, 2 ** 31 - 1):
         b = run_gpu(c, W, gated=False, fwd_window=0)
         for n in ("dq", "dk", "dv", "dq_norm_w", "dk_norm_w"):
             assert torch.equal(a["raw"][n], b["raw"][n]), (W, n)
