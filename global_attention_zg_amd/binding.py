@@ -133,6 +133,54 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+class _Args:
+    """Checks of a call's tensor arguments before their pointers go to the
+    library: first each tensor's dtype, shape and layout as the C ABI
+    documents them, then (done()) that every one is on the same CUDA device.
+    Raises ValueError; None is accepted only where the C ABI takes NULL."""
+
+    def __init__(self):
+        self.seen = []
+
+    def req(self, t, name, dtype, shape=None, optional=False):
+        if t is None:
+            if optional:
+                return
+            raise ValueError(f"{name} is required")
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name} must be a torch.Tensor")
+        dts = dtype if isinstance(dtype, tuple) else (dtype,)
+        if t.dtype not in dts:
+            raise ValueError(f"{name} must be {' or '.join(str(d) for d in dts)}, got {t.dtype}")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        self.seen.append((t, name))
+
+    def done(self):
+        dev = None
+        for t, name in self.seen:
+            if not t.is_cuda:
+                raise ValueError(f"{name} must be on a CUDA device")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+BF16 = torch.bfloat16
+F32 = torch.float32
+I32 = torch.int32
+U8 = torch.uint8
+
+
+def _dims(t, name, n):
+    if not isinstance(t, torch.Tensor) or t.dim() != n:
+        raise ValueError(f"{name} must be a {n}-d tensor")
+    return tuple(t.shape)
+
+
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -147,8 +195,20 @@ def zg_attn_fwd(q, k, v, gate, q_norm_w, k_norm_w, *, window, rope_dim=42, rope_
                 want_lse=False, k_out=None, workspace=None, stream=None):
     """q [B,S,Hq,128], k/v [B,S,Hkv,128], gate [B,S,Hq,128] or None (bf16, CUDA);
     norm weights fp32 [128].  Returns (out, lse or None)."""
-    B, S, Hq, D = q.shape
-    Hkv = k.shape[2]
+    B, S, Hq, D = _dims(q, "q", 4)
+    Hkv = _dims(k, "k", 4)[2]
+    a = _Args()
+    a.req(q, "q", BF16)
+    a.req(k, "k", BF16, (B, S, Hkv, D))
+    a.req(v, "v", BF16, (B, S, Hkv, D))
+    a.req(gate, "gate", BF16, (B, S, Hq, D), optional=True)
+    a.req(q_norm_w, "q_norm_w", F32, (D,))
+    a.req(k_norm_w, "k_norm_w", F32, (D,))
+    a.req(out, "out", BF16, (B, S, Hq, D), optional=True)
+    a.req(lse, "lse", F32, (B, Hq, S), optional=True)
+    a.req(k_out, "k_out", BF16, (B, S, Hkv, D), optional=True)
+    a.req(workspace, "workspace", U8, None, optional=True)
+    a.done()
     p = make_params(B, S, Hq, Hkv, D, window, rope_dim, rope_theta, rms_eps, softmax_scale,
                     pos_offset)
     if out is None:
@@ -178,8 +238,21 @@ def zg_attn_fwd_varlen(q, k, v, gate, q_norm_w, k_norm_w, cu_seqlens, max_seqlen
                        workspace=None, stream=None):
     """Packed batch: q [T,Hq,128], k/v [T,Hkv,128], gate [T,Hq,128] or None;
     cu_seqlens int32 [B+1] on the device.  Returns (out, lse [Hq,T] or None)."""
-    T, Hq, D = q.shape
-    Hkv = k.shape[1]
+    T, Hq, D = _dims(q, "q", 3)
+    Hkv = _dims(k, "k", 3)[1]
+    a = _Args()
+    a.req(q, "q", BF16)
+    a.req(k, "k", BF16, (T, Hkv, D))
+    a.req(v, "v", BF16, (T, Hkv, D))
+    a.req(gate, "gate", BF16, (T, Hq, D), optional=True)
+    a.req(q_norm_w, "q_norm_w", F32, (D,))
+    a.req(k_norm_w, "k_norm_w", F32, (D,))
+    a.req(cu_seqlens, "cu_seqlens", I32, None)
+    a.req(out, "out", BF16, (T, Hq, D), optional=True)
+    a.req(lse, "lse", F32, (Hq, T), optional=True)
+    a.req(k_out, "k_out", BF16, (T, Hkv, D), optional=True)
+    a.req(workspace, "workspace", U8, None, optional=True)
+    a.done()
     B = cu_seqlens.numel() - 1
     p = make_params(B, max_seqlen, Hq, Hkv, D, window, rope_dim, rope_theta, rms_eps,
                     softmax_scale, pos_offset)
@@ -212,8 +285,26 @@ def zg_attn_bwd(q, k, v, gate, q_norm_w, k_norm_w, out, lse, dout, *, window, ro
     """Gradients of sum(dout * out) for out, lse = zg_attn_fwd(...) with the same
     inputs.  Returns a dict: dq, dk, dv, dgate (None when gate is None),
     dq_norm_w, dk_norm_w."""
-    B, S, Hq, D = q.shape
-    Hkv = k.shape[2]
+    B, S, Hq, D = _dims(q, "q", 4)
+    Hkv = _dims(k, "k", 4)[2]
+    a = _Args()
+    a.req(q, "q", BF16)
+    for t, n in ((k, "k"), (v, "v")):
+        a.req(t, n, BF16, (B, S, Hkv, D))
+    for t, n in ((out, "out"), (dout, "dout")):
+        a.req(t, n, BF16, (B, S, Hq, D))
+    a.req(gate, "gate", BF16, (B, S, Hq, D), optional=True)
+    a.req(q_norm_w, "q_norm_w", F32, (D,))
+    a.req(k_norm_w, "k_norm_w", F32, (D,))
+    a.req(lse, "lse", F32, (B, Hq, S))
+    a.req(dq, "dq", BF16, (B, S, Hq, D), optional=True)
+    a.req(dk, "dk", BF16, (B, S, Hkv, D), optional=True)
+    a.req(dv, "dv", BF16, (B, S, Hkv, D), optional=True)
+    a.req(dgate, "dgate", BF16, (B, S, Hq, D), optional=True)
+    a.req(dq_norm_w, "dq_norm_w", F32, (D,), optional=True)
+    a.req(dk_norm_w, "dk_norm_w", F32, (D,), optional=True)
+    a.req(workspace, "workspace", U8, None, optional=True)
+    a.done()
     p = make_params(B, S, Hq, Hkv, D, window, rope_dim, rope_theta, rms_eps, softmax_scale,
                     pos_offset)
     dq = torch.empty_like(q) if dq is None else dq
@@ -238,6 +329,32 @@ def zg_attn_bwd(q, k, v, gate, q_norm_w, k_norm_w, out, lse, dout, *, window, ro
             "dq_norm_w": dq_norm_w, "dk_norm_w": dk_norm_w}
 
 
+def _check_decode(q, k_new, v_new, caches, seq_lens, gate, q_norm_w, k_norm_w, out, Hkv,
+                  cache_dtype, block_table=None):
+    B, Hq, D = _dims(q, "q", 3)
+    a = _Args()
+    a.req(q, "q", BF16)
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        a.req(t, n, BF16, (B, Hkv, D), optional=True)
+    shape = tuple(caches[0].shape) if isinstance(caches[0], torch.Tensor) else None
+    for t, n in zip(caches, ("k_cache", "v_cache")):
+        a.req(t, n, cache_dtype, shape)
+    if shape is None or len(shape) != 4 or shape[1] != Hkv or shape[3] != D:
+        raise ValueError(f"caches must be [*, {Hkv}, *, {D}]")
+    if block_table is None and shape[0] != B:
+        raise ValueError(f"caches must hold {B} sequences, got {shape[0]}")
+    if block_table is not None:
+        a.req(block_table, "block_table", I32, None)
+        if block_table.dim() != 2 or block_table.shape[0] != B:
+            raise ValueError(f"block_table must be [{B}, max_pages]")
+    a.req(seq_lens, "seq_lens", I32, (B,))
+    a.req(gate, "gate", BF16, (B, Hq, D), optional=True)
+    a.req(q_norm_w, "q_norm_w", F32, (D,))
+    a.req(k_norm_w, "k_norm_w", F32, (D,))
+    a.req(out, "out", BF16, (B, Hq, D), optional=True)
+    return a
+
+
 def zg_attn_decode_num_splits(p: Params, cache_cap: int) -> int:
     return int(_lib.zg_attn_decode_num_splits(ctypes.byref(p), cache_cap))
 
@@ -251,6 +368,11 @@ def zg_attn_decode(q, k_new, v_new, k_cache, v_cache, seq_lens, *, ring, window,
                    pos_offset=0, num_splits=0, out=None, workspace=None, stream=None):
     """q [B,Hq,128]; k_new/v_new [B,Hkv,128] or None; caches [B,Hkv,cap,128]
     (updated in place); seq_lens int32 [B] on the device.  Returns out."""
+    _dims(k_cache, "k_cache", 4)
+    a = _check_decode(q, k_new, v_new, (k_cache, v_cache), seq_lens, gate, q_norm_w, k_norm_w, out,
+                  k_cache.shape[1], BF16)
+    a.req(workspace, "workspace", U8, None, optional=True)
+    a.done()
     B, Hq, D = q.shape
     Hkv, cap = k_cache.shape[1], k_cache.shape[2]
     p = make_params(B, 0, Hq, Hkv, D, window, rope_dim, rope_theta, rms_eps, softmax_scale,
@@ -274,6 +396,10 @@ def zg_attn_decode_noalloc(q, k_new, v_new, k_cache, v_cache, seq_lens, *, ring,
                            softmax_scale=0.0, pos_offset=0, num_splits=0, out=None, stream=None):
     """zg_attn_decode with the split partials in the library's static scratch
     (no workspace).  Returns out."""
+    _dims(k_cache, "k_cache", 4)
+    a = _check_decode(q, k_new, v_new, (k_cache, v_cache), seq_lens, gate, q_norm_w, k_norm_w, out,
+                  k_cache.shape[1], BF16)
+    a.done()
     B, Hq, D = q.shape
     Hkv, cap = k_cache.shape[1], k_cache.shape[2]
     p = make_params(B, 0, Hq, Hkv, D, window, rope_dim, rope_theta, rms_eps, softmax_scale,
@@ -292,7 +418,17 @@ def zg_attn_kv_write_pages(k_prime, v, k_pages, v_pages, block_table, *, stream=
     """k_prime / v [B,S,Hkv,128] (K' from zg_attn_fwd's k_out, and V) into the
     page pool k_pages / v_pages [num_pages,Hkv,page_size,128]; block_table
     int32 [B,max_pages] on the device."""
-    B, S, Hkv, D = k_prime.shape
+    B, S, Hkv, D = _dims(k_prime, "k_prime", 4)
+    a = _Args()
+    a.req(k_prime, "k_prime", BF16)
+    a.req(v, "v", BF16, (B, S, Hkv, D))
+    np_, _, ps, _ = _dims(k_pages, "k_pages", 4)
+    for t, n in ((k_pages, "k_pages"), (v_pages, "v_pages")):
+        a.req(t, n, BF16, (np_, Hkv, ps, D))
+    a.req(block_table, "block_table", I32, None)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be [{B}, max_pages]")
+    a.done()
     num_pages, _, page_size, _ = k_pages.shape
     p = make_params(B, S, Hkv, Hkv, D)
     st = _lib.zg_attn_kv_write_pages(ctypes.byref(p), _ptr(k_prime), _ptr(v), _ptr(k_pages),
@@ -307,6 +443,11 @@ def zg_attn_decode_paged(q, k_new, v_new, k_pages, v_pages, block_table, seq_len
                          workspace=None, stream=None):
     """zg_attn_decode over a page pool [num_pages,Hkv,page_size,128] with an
     int32 block table [B,max_pages].  Returns out."""
+    _dims(k_pages, "k_pages", 4)
+    a = _check_decode(q, k_new, v_new, (k_pages, v_pages), seq_lens, gate, q_norm_w, k_norm_w, out,
+                  k_pages.shape[1], BF16, block_table)
+    a.req(workspace, "workspace", U8, None, optional=True)
+    a.done()
     B, Hq, D = q.shape
     num_pages, Hkv, page_size, _ = k_pages.shape
     max_pages = block_table.shape[1]
@@ -335,6 +476,11 @@ def zg_attn_decode_fp8(q, k_new, v_new, k_cache, v_cache, seq_lens, *, ring, win
     """zg_attn_decode over an E4M3 cache: k_cache / v_cache uint8 [B,Hkv,cap,128]
     hold the codes of K' * k_scale and V * v_scale (updated in place).
     Returns out (bf16 [B,Hq,128])."""
+    _dims(k_cache, "k_cache", 4)
+    a = _check_decode(q, k_new, v_new, (k_cache, v_cache), seq_lens, gate, q_norm_w, k_norm_w, out,
+                  k_cache.shape[1], U8)
+    a.req(workspace, "workspace", U8, None, optional=True)
+    a.done()
     B, Hq, D = q.shape
     Hkv, cap = k_cache.shape[1], k_cache.shape[2]
     p = make_params(B, 0, Hq, Hkv, D, window, rope_dim, rope_theta, rms_eps, softmax_scale,
@@ -360,6 +506,11 @@ def zg_attn_decode_paged_fp8(q, k_new, v_new, k_pages, v_pages, block_table, seq
                              num_splits=0, out=None, workspace=None, stream=None):
     """zg_attn_decode_paged over E4M3 pages uint8 [num_pages,Hkv,page_size,128].
     Returns out."""
+    _dims(k_pages, "k_pages", 4)
+    a = _check_decode(q, k_new, v_new, (k_pages, v_pages), seq_lens, gate, q_norm_w, k_norm_w, out,
+                  k_pages.shape[1], U8, block_table)
+    a.req(workspace, "workspace", U8, None, optional=True)
+    a.done()
     B, Hq, D = q.shape
     num_pages, Hkv, page_size, _ = k_pages.shape
     max_pages = block_table.shape[1]
@@ -384,7 +535,12 @@ def zg_attn_decode_paged_fp8(q, k_new, v_new, k_pages, v_pages, block_table, seq
 
 def zg_linear(x, w, out=None, stream=None):
     """y = x w^T: x [M,K], w [N,K] bf16 on the device -> y [M,N] bf16."""
-    M, K = x.shape
+    M, K = _dims(x, "x", 2)
+    a = _Args()
+    a.req(x, "x", BF16)
+    a.req(w, "w", BF16, (_dims(w, "w", 2)[0], K))
+    a.req(out, "out", BF16, (M, w.shape[0]), optional=True)
+    a.done()
     N = w.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=x.dtype, device=x.device)
@@ -396,7 +552,15 @@ def zg_qkvg_proj(x, w, n_q_heads, n_kv_heads, gated, *, q=None, k=None, v=None, 
                  stream=None):
     """x [T,hidden] bf16, w [Nw,hidden] stacking W_q, W_k, W_v (and W_g when
     gated).  Returns (q [T,Hq,128], k [T,Hkv,128], v, gate or None)."""
-    T, hidden = x.shape
+    T, hidden = _dims(x, "x", 2)
+    a = _Args()
+    a.req(x, "x", BF16)
+    nw = (n_q_heads * (2 if gated else 1) + 2 * n_kv_heads) * 128
+    a.req(w, "w", BF16, (nw, hidden))
+    for t, n, h in ((q, "q", n_q_heads), (k, "k", n_kv_heads), (v, "v", n_kv_heads),
+                    (gate, "gate", n_q_heads)):
+        a.req(t, n, BF16, (T, h, 128), optional=True)
+    a.done()
     D = 128
     p = make_params(1, T, n_q_heads, n_kv_heads, D)
     dev = x.device
@@ -412,6 +576,10 @@ def zg_qkvg_proj(x, w, n_q_heads, n_kv_heads, gated, *, q=None, k=None, v=None, 
 
 def zg_quantize_fp8(x, scale, out=None, stream=None):
     """bf16 tensor -> uint8 tensor of E4M3 codes of x * scale (same shape)."""
+    a = _Args()
+    a.req(x, "x", BF16)
+    a.req(out, "out", U8, tuple(x.shape), optional=True)
+    a.done()
     if out is None:
         out = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
     _check(_lib.zg_quantize_fp8(x.numel(), _ptr(x), float(scale), _ptr(out), _stream(stream)))
@@ -420,7 +588,12 @@ def zg_quantize_fp8(x, scale, out=None, stream=None):
 
 def zg_linear_fp8(xq, wq, out_scale, out=None, stream=None):
     """E4M3 codes xq [M,K], wq [N,K] (uint8) -> y [M,N] bf16 = out_scale * xq . wq^T."""
-    M, K = xq.shape
+    M, K = _dims(xq, "xq", 2)
+    a = _Args()
+    a.req(xq, "xq", U8)
+    a.req(wq, "wq", U8, (_dims(wq, "wq", 2)[0], K))
+    a.req(out, "out", BF16, (M, wq.shape[0]), optional=True)
+    a.done()
     N = wq.shape[0]
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
