@@ -39,7 +39,7 @@ KW = dict(rope_dim=42, rope_theta=10000.0, rms_eps=1e-6)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flash_fwd_global_256k_traffic.json")
 # sources the flash kernel is compiled from (the traffic summary is keyed by their hash)
 FLASH_SRCS = [os.path.join(ROOT, "global_attention_zg_amd", "csrc", f)
-              for f in ("flash_fwd.hip", "zg_common.h", "zg_lds.h")]
+              for f in ("flash_causal.hip", "zg_flash_tile.h", "zg_common.h", "zg_lds.h")]
 
 
 def inband_pairs(S, W):
@@ -171,7 +171,7 @@ def flash_source_hash():
 
 
 def read_traffic():
-    """HBM bytes per launch of the global-layer flash kernel from the committed
+    """HBM bytes per launch of the global-layer causal kernel from the committed
     rocprofv3 counter summary, or None if it is missing or stale."""
     try:
         with open(TRAFFIC_FILE) as f:
@@ -228,64 +228,220 @@ def reference_peaks(torch, iters=20):
                      "sclk_mhz": 2400.0}}
 
 
-# Oracle sample of the block (layer -> leading query rows), about 13 s of
-# fp64 work on 16 host cores: the global layer's cost grows with rows^2.
-SAMPLE_ROWS = {0: 8192, 5: 11584}
+# The global layer's rows the oracle checks and times at 256K: the fixed rows
+# of the workload's plan plus 55 seeded ones.
+GLOBAL_ROWS_FIXED = [0, 1, 127, 128, 129, 4095, 65535, 131071, 262143]
+GLOBAL_ROWS_SEED = 262144
+
+
+def global_sample_rows(S=262144, extra=55, seed=GLOBAL_ROWS_SEED):
+    rng = np.random.default_rng(seed)
+    rows = set(r for r in GLOBAL_ROWS_FIXED if r < S)
+    while len(rows) < len(GLOBAL_ROWS_FIXED) + extra:
+        rows.add(int(rng.integers(0, S)))
+    return sorted(rows)
+
+
+# leading rows of one gated SWA layer of the 256K block in the oracle sample
+SWA_SAMPLE_ROWS = 8192
+
+
+def host_info():
+    """CPU model, cores this process may use, and the BLAS thread count."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas = None
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(),
+            "affinity_cores": len(os.sched_getaffinity(0)), "blas_threads": blas}
+
+
+def _f64_rows(key, S, H, rows):
+    """Rows `rows` of a seeded [1, S, H, D] bf16 tensor as float64 [1, len(rows), H, D]."""
+    from global_attention_zg_amd import inputs
+    from oracle import zg_oracle as orc
+    total, per = S * H * D, H * D
+    out = np.empty((1, len(rows), H, D))
+    for i, r in enumerate(rows):
+        bits = inputs.normal_bf16_bits(key, total, r * per, (r + 1) * per)
+        out[0, i] = orc.bf16_bits_to_f64(bits).reshape(H, D)
+    return out
+
+
+def _f64_prefix(key, S, H, n):
+    """The first n positions of a seeded [1, S, H, D] bf16 tensor, float64."""
+    from global_attention_zg_amd import inputs
+    from oracle import zg_oracle as orc
+    return orc.bf16_bits_to_f64(inputs.normal_bf16_bits(key, S * H * D, 0, n * H * D)).reshape(
+        1, n, H, D)
 
 
 def cpu_baseline(gpu_rows=None):
-    """The fp64 oracle timed on a bounded sample of the block: the first
-    SAMPLE_ROWS query rows of one gated SWA layer and of the global layer
-    (all 32 query heads), with the same seeded inputs.  Causal rows
-    depend only on the keys before them, so these prefix rows are also rows
-    of the full 262144-position layers: `gpu_rows` (layer -> the kernel's
-    output on those rows, from the timed run) is compared with them."""
+    """The fp64 oracle, as it stands, timed on the host on each workload:
+    in full where that takes a few seconds, otherwise on a stated sample whose
+    time is scaled to the whole workload by its share of the (query, key)
+    pairs (labelled extrapolated).  Inputs are the benchmark's own seeded
+    tensors.  Only the oracle calls are timed, not the input generation.
+
+    `gpu_rows` (name -> the timed run's output on the sampled rows) is
+    compared with the oracle's rows of the 256K block: causal rows depend only
+    on the keys before them, so rows of the full layers can be checked one by
+    one."""
     from global_attention_zg_amd import inputs
     from oracle import zg_oracle as orc
 
-    S_full = 262144
-
-    def f64(key, shape):
-        # prefix of the full [1, S_full, H, D] tensor, same seeded elements
-        total = S_full * int(np.prod(shape[2:]))
-        n = int(np.prod(shape))
-        return orc.bf16_bits_to_f64(inputs.normal_bf16_bits(key, total, 0, n)).reshape(shape)
-
-    flops = 0
-    t_total = 0.0
+    gq4 = lambda t, l: inputs.norm_weight((t, l, inputs.T_GQ), D).astype(np.float64)  # noqa: E731
+    gk4 = lambda t, l: inputs.norm_weight((t, l, inputs.T_GK), D).astype(np.float64)  # noqa: E731
+    per_cfg = {}
     parity = {}
-    for layer, window, rows, gated in ((0, 128, SAMPLE_ROWS[0], True), (5, 0, SAMPLE_ROWS[5], False)):
-        # the first `rows` positions of the layer's tensors are a prefix of the
-        # full [1, S, H, D] tensors in the flat element order
-        q = f64((4, layer, inputs.T_Q), (1, rows, 32, D))
-        k = f64((4, layer, inputs.T_K), (1, rows, 8, D))
-        v = f64((4, layer, inputs.T_V), (1, rows, 8, D))
-        g = f64((4, layer, inputs.T_GATE), (1, rows, 32, D)) if gated else None
-        gq = inputs.norm_weight((4, layer, inputs.T_GQ), D).astype(np.float64)
-        gk = inputs.norm_weight((4, layer, inputs.T_GK), D).astype(np.float64)
+
+    def timed(fn):
         t0 = time.perf_counter()
-        ref, _ = orc.attention_fwd(q, k, v, g, gq, gk, window=window, **KW)
-        t_total += time.perf_counter() - t0
-        flops += 32 * inband_pairs(rows, window) * FLOP_PER_PAIR
-        if gpu_rows is not None and layer in gpu_rows:
-            d = gpu_rows[layer] - ref
-            parity["swa_layer0" if window else "global_layer5"] = {
-                "rows": f"0..{rows - 1}, all 32 heads",
-                "max_abs": float(np.abs(d).max()),
-                "rel_rms": float(np.sqrt((d * d).sum() / (ref * ref).sum())),
-                "bound": "max_abs <= 2e-2 and rel_rms <= 1e-2"}
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    return dict(value=round(flops / t_total / 1e12, 6), unit="TFLOP/s", cores=int(threads),
-                kind="oracle",
-                sample=f"first {SAMPLE_ROWS[0]} query rows of one gated SWA layer + first "
-                       f"{SAMPLE_ROWS[5]} rows of the "
-                       "global layer of the 256K block, all 32 query heads, fp64 numpy; "
-                       f"{flops / 1e9:.1f} GFLOP in {t_total:.1f} s",
-                seconds=round(t_total, 2)), parity
+        r = fn()
+        return r, time.perf_counter() - t0
+
+    def record(name, flops_sample, t, flops_full, sample):
+        e = {"tflops": round(flops_sample / t / 1e12, 6), "seconds_sample": round(t, 3),
+             "sample": sample}
+        if flops_sample < flops_full:
+            e["seconds_full_extrapolated"] = round(t * flops_full / flops_sample, 2)
+            e["kind"] = "sampled, extrapolated by pair count"
+        else:
+            e["kind"] = "full"
+        per_cfg[name] = e
+
+    # tiny pair: B1 S512 4/1 heads, gated SWA and global on the same inputs, in full
+    from tests import zg_cases as zc
+    c = zc.fwd_case(1, 1, 512, 4, 1, gated=True)
+    args = [zc.f64(c[n]) for n in ("q", "k", "v", "gate")]
+    w = (c["gq"].astype(np.float64), c["gk"].astype(np.float64))
+    _, t1 = timed(lambda: orc.attention_fwd(*args, *w, window=128, **KW))
+    _, t2 = timed(lambda: orc.attention_fwd(*args[:3], None, *w, window=0, **KW))
+    fl = 4 * (inband_pairs(512, 128) + inband_pairs(512, 0)) * FLOP_PER_PAIR
+    record("tiny_pair_s512", fl, t1 + t2, fl, "both layers in full")
+
+    # gated SWA B4 S4096 32/8: one sequence in full (the four are alike)
+    S = 4096
+    q = _f64_prefix((2, 0, inputs.T_Q), 4 * S, 32, S)
+    k = _f64_prefix((2, 0, inputs.T_K), 4 * S, 8, S)
+    v = _f64_prefix((2, 0, inputs.T_V), 4 * S, 8, S)
+    g = _f64_prefix((2, 0, inputs.T_GATE), 4 * S, 32, S)
+    _, t = timed(lambda: orc.attention_fwd(q, k, v, g, gq4(2, 0), gk4(2, 0), window=128, **KW))
+    record("swa_4k_b4", 32 * inband_pairs(S, 128) * FLOP_PER_PAIR, t,
+           4 * 32 * inband_pairs(S, 128) * FLOP_PER_PAIR, "sequence 0 of 4 in full, all 32 heads")
+
+    # global S16384: 64 sampled rows, all 32 heads
+    S = 16384
+    rows = global_sample_rows(S, 55, S)
+    q = _f64_rows((3, 0, inputs.T_Q), S, 32, rows)
+    k = _f64_prefix((3, 0, inputs.T_K), S, 8, S)
+    v = _f64_prefix((3, 0, inputs.T_V), S, 8, S)
+    qfull = np.zeros((1, S, 32, D))
+    qfull[0, rows] = q[0]
+    _, t = timed(lambda: orc.attention_fwd(qfull, k, v, None, gq4(3, 0), gk4(3, 0), window=0,
+                                           rows=rows, **KW))
+    record("global_16k", 32 * sum(r + 1 for r in rows) * FLOP_PER_PAIR, t,
+           32 * inband_pairs(S, 0) * FLOP_PER_PAIR, f"{len(rows)} sampled rows, all 32 heads")
+    del q, k, v, qfull
+
+    # the 256K block: one gated SWA layer's first SWA_SAMPLE_ROWS rows (x5 layers)
+    # and the global layer's 64 sampled rows
+    S = 262144
+    n = SWA_SAMPLE_ROWS
+    q = _f64_prefix((4, 0, inputs.T_Q), S, 32, n)
+    k = _f64_prefix((4, 0, inputs.T_K), S, 8, n)
+    v = _f64_prefix((4, 0, inputs.T_V), S, 8, n)
+    g = _f64_prefix((4, 0, inputs.T_GATE), S, 32, n)
+    (ref_swa, _), t_swa = timed(lambda: orc.attention_fwd(q, k, v, g, gq4(4, 0), gk4(4, 0),
+                                                          window=128, **KW))
+    del q, k, v, g
+    rows = global_sample_rows(S)
+    qs = _f64_rows((4, 5, inputs.T_Q), S, 32, rows)
+    k = _f64_prefix((4, 5, inputs.T_K), S, 8, S)
+    v = _f64_prefix((4, 5, inputs.T_V), S, 8, S)
+
+    # q with only the sampled rows written: the oracle reads just those rows
+    # (np.zeros maps untouched pages lazily, so this holds 64 rows of memory)
+    qfull = np.zeros((1, S, 32, D))
+    qfull[0, rows] = qs[0]
+    (ref_glob, _), t_glob = timed(lambda: orc.attention_fwd(qfull, k, v, None, gq4(4, 5),
+                                                            gk4(4, 5), window=0, rows=rows,
+                                                            **KW))
+    del k, v, qfull
+    fl_swa = 32 * inband_pairs(n, 128) * FLOP_PER_PAIR
+    fl_glob = 32 * sum(r + 1 for r in rows) * FLOP_PER_PAIR
+    full_block = (5 * 32 * inband_pairs(S, 128) + 32 * inband_pairs(S, 0)) * FLOP_PER_PAIR
+    # the block time: five SWA layers scaled from the prefix, the global layer from the rows
+    t_block = 5 * t_swa * inband_pairs(S, 128) / inband_pairs(n, 128) + \
+        t_glob * 32 * inband_pairs(S, 0) * FLOP_PER_PAIR / fl_glob
+    per_cfg["block_256k"] = {
+        "tflops": round((fl_swa + fl_glob) / (t_swa + t_glob) / 1e12, 6),
+        "seconds_sample": round(t_swa + t_glob, 3),
+        "seconds_full_extrapolated": round(t_block, 1),
+        "kind": "sampled, extrapolated by pair count",
+        "sample": f"first {n} rows of one gated SWA layer (x5 layers) and {len(rows)} sampled "
+                  "rows of the global layer, all 32 heads"}
+    if gpu_rows is not None:
+        for name, ref, what in (("swa_layer0", ref_swa, f"rows 0..{n - 1}"),
+                                ("global_layer5", ref_glob,
+                                 f"{len(rows)} rows: {GLOBAL_ROWS_FIXED} + 55 seeded")):
+            d = gpu_rows[name] - ref
+            parity[name] = {"rows": what + ", all 32 heads", "max_abs": float(np.abs(d).max()),
+                            "rel_rms": float(np.sqrt((d * d).sum() / (ref * ref).sum())),
+                            "bound": "max_abs <= 2e-2 and rel_rms <= 1e-2"}
+
+    # decode at 256K, B16: two (sequence, KV head) groups of the global cache
+    # (of 128), and the SWA ring in full
+    B, Hq, Hkv, L = 16, 32, 8, 262145
+    grp = Hq // Hkv
+    tq = 0.0
+    for b, gi in ((0, 0), (15, 7)):
+        def slab(t):
+            per = L * D
+            s0 = (b * Hkv + gi) * per
+            return orc.bf16_bits_to_f64(inputs.normal_bf16_bits((5, 0, t), B * Hkv * per, s0,
+                                                                s0 + per)).reshape(L, D)
+        kc, vc = slab(inputs.T_KCACHE), slab(inputs.T_VCACHE)
+        qg = orc.bf16_bits_to_f64(zc.bits((5, 0, inputs.T_Q), (B, Hq, D))[b, gi * grp:(gi + 1) * grp])
+        kn = orc.bf16_bits_to_f64(zc.bits((5, 0, inputs.T_KNEW), (B, Hkv, D))[b, gi])
+        vn = orc.bf16_bits_to_f64(zc.bits((5, 0, inputs.T_VNEW), (B, Hkv, D))[b, gi])
+        _, t = timed(lambda: orc.decode_group(qg, kn, vn, kc, vc, L, ring=False, window=0,
+                                              gate_group=None, q_norm_w=gq4(5, 0),
+                                              k_norm_w=gk4(5, 0), **KW))
+        tq += t
+    record("decode_global_256k", 2 * grp * L * FLOP_PER_PAIR, tq, B * Hq * L * FLOP_PER_PAIR,
+           "2 of the 128 (sequence, KV head) groups, 262145 keys each")
+    qb = zc.bits((5, 1, inputs.T_Q), (B, Hq, D))
+    kcb = zc.bits((5, 1, inputs.T_KCACHE), (B, Hkv, 128, D))
+    vcb = zc.bits((5, 1, inputs.T_VCACHE), (B, Hkv, 128, D))
+    knb = zc.bits((5, 1, inputs.T_KNEW), (B, Hkv, D))
+    vnb = zc.bits((5, 1, inputs.T_VNEW), (B, Hkv, D))
+    gb = zc.bits((5, 1, inputs.T_GATE), (B, Hq, D))
+    _, t = timed(lambda: orc.attention_decode(zc.f64(qb), zc.f64(knb), zc.f64(vnb), zc.f64(kcb),
+                                              zc.f64(vcb), [L] * B, ring=True, window=128,
+                                              gate=zc.f64(gb), q_norm_w=gq4(5, 1),
+                                              k_norm_w=gk4(5, 1), **KW))
+    fl = B * Hq * 128 * FLOP_PER_PAIR
+    record("decode_swa_ring", fl, t, fl, "all 16 sequences, ring of 128")
+
+    info = host_info()
+    head = per_cfg["block_256k"]
+    return dict(value=head["tflops"], unit="TFLOP/s", cores=info["blas_threads"] or
+                info["affinity_cores"], kind="oracle",
+                sample=head["sample"] + f"; fp64 numpy, {head['seconds_sample']} s on the host",
+                seconds=head["seconds_sample"],
+                block_seconds_full_extrapolated=head["seconds_full_extrapolated"],
+                per_config=per_cfg, host=info), parity
 
 
 def main():
@@ -304,7 +460,7 @@ def main():
                          "for scaling the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
@@ -375,7 +531,7 @@ def main():
                    "layers": "5 gated SWA (W=128) + 1 global causal", "q_heads": Hq,
                    "kv_heads": Hkv, "head_dim": D, "rope_dim": 42, "parallelism": "none"},
         "tokens_per_s": round(B * S / t_step, 1),
-        "roofline": {"bound": "mfma", "kernel": "flash_fwd_kernel (global causal, S=262144)",
+        "roofline": {"bound": "mfma", "kernel": "flash_causal_kernel (global causal, S=262144)",
                      "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
@@ -383,8 +539,10 @@ def main():
                                "global_layer": round(t_glob * 1e3, 3)},
     }
     # the kernel's output on the rows the oracle sample covers
-    gpu_rows = {l: (layers[l].out[:, :n].float().cpu().numpy().astype(np.float64))
-                for l, n in SAMPLE_ROWS.items()}
+    grow = torch.tensor(global_sample_rows(S), dtype=torch.long, device="cuda")
+    gpu_rows = {"swa_layer0": layers[0].out[:, :SWA_SAMPLE_ROWS].float().cpu().numpy().astype(
+                    np.float64),
+                "global_layer5": layers[5].out[:, grow].float().cpu().numpy().astype(np.float64)}
     del layers, glob
     torch.cuda.empty_cache()
 
@@ -395,8 +553,7 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle, bounded sample)")
         result["cpu_baseline"], result["parity_vs_oracle"] = cpu_baseline(gpu_rows)
-    result["host"] = {"cpu": platform.processor() or platform.machine(),
-                      "affinity_cores": len(os.sched_getaffinity(0))}
+    result["host"] = host_info()
     print(json.dumps(result), flush=True)
 
 
@@ -565,6 +722,8 @@ def variant_components(torch, bd, iters):
                                               arms[name]["ms_32_layers"], 3)
     out["interleave_arms_64k"] = {"swa_layer_ms": round(times["swa"] * 1e3, 4),
                                   "global_layer_ms": round(times["global"] * 1e3, 4),
+                                  "composed": "each arm's ms_32_layers is the layer counts times "
+                                              "the two measured layer times, not a timed run",
                                   "arms": arms}
     for W in (64, 256, 512, 1024):
         log(f"component: swa W{W} B4 S4096")
