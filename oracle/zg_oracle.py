@@ -346,7 +346,8 @@ def rms_norm_bwd(x: np.ndarray, gamma: np.ndarray, eps: float, dxhat: np.ndarray
 
 def attention_bwd(q, k, v, gate, q_norm_w, k_norm_w, dout, *, window: int,
                   rope_dim: int, rope_theta: float, rms_eps: float,
-                  softmax_scale: float = 0.0, pos_offset: int = 0, chunk: int = 1024):
+                  softmax_scale: float = 0.0, pos_offset: int = 0, chunk: int = 1024,
+                  rows=None, keys=None):
     """Gradients of L = sum(dout * Y) for the layer Y = attention_fwd(...)[0].
 
     Returns a dict with dq, dk, dv (shapes of q, k, v), dgate (shape of gate,
@@ -356,6 +357,15 @@ def attention_bwd(q, k, v, gate, q_norm_w, k_norm_w, dout, *, window: int,
         dV_g += P^T dO;  dP = dO V^T;  Dr = rowsum(dO * O)
         dS = P * (dP - Dr);  dq' = tau dS K';  dk'_g += tau dS^T Q'
     then back through RoPE (rope_bwd) and RMSNorm (rms_norm_bwd).
+
+    Sampling (for layers too long to differentiate whole): ``rows`` (sorted
+    query indices) and/or ``keys`` (sorted key indices) select what is
+    returned: dq and dgate at ``rows`` ([B,len(rows),...]), dk and dv at
+    ``keys``.  The same per-row steps run, on ``rows`` plus every row that
+    sees one of ``keys``; a selected key's gradient sums over exactly the rows
+    that see it, so every returned value is the full computation's up to the
+    order of the fp64 sums.  The norm-weight gradients sum over all rows and
+    are None when sampling.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -367,10 +377,23 @@ def attention_bwd(q, k, v, gate, q_norm_w, k_norm_w, dout, *, window: int,
     grp = Hq // Hkv
     tau = softmax_scale if softmax_scale > 0 else 1.0 / math.sqrt(D)
     pos = pos_offset + np.arange(S, dtype=np.int64)
-    dq = np.zeros_like(q)
-    dk = np.zeros_like(k)
-    dv = np.zeros_like(v)
-    dgate = None if gate is None else np.zeros(np.shape(gate), dtype=np.float64)
+    sampled = rows is not None or keys is not None
+    rsel = np.arange(S) if rows is None else np.asarray(rows, dtype=np.int64)
+    ksel = np.arange(S) if keys is None else np.asarray(keys, dtype=np.int64)
+    # the query rows to run: the selected ones and every row that sees a
+    # selected key (rows i with 0 <= i - j < window, or i >= j when global)
+    need = np.zeros(S, dtype=bool)
+    need[rsel] = True
+    if keys is not None:
+        for j in ksel:
+            need[j:S if window == 0 else min(S, j + window)] = True
+    else:
+        need[:] = True
+    run_rows = np.nonzero(need)[0]
+    dq = np.zeros((B, len(rsel), Hq, D))
+    dk = np.zeros((B, len(ksel), Hkv, D))
+    dv = np.zeros((B, len(ksel), Hkv, D))
+    dgate = None if gate is None else np.zeros((B, len(rsel), Hq, D))
     dwq = np.zeros(D)
     dwk = np.zeros(D)
     for b in range(B):
@@ -378,9 +401,11 @@ def attention_bwd(q, k, v, gate, q_norm_w, k_norm_w, dout, *, window: int,
         kp = apply_partial_rope(rms_norm(k[b], k_norm_w, rms_eps), pos, rope_dim, rope_theta)
         dqp = np.zeros_like(qp)
         dkp = np.zeros_like(kp)
-        for c0 in range(0, S, chunk):
-            ridx = np.arange(c0, min(S, c0 + chunk))
-            lo = 0 if window == 0 else max(0, c0 - window + 1)
+        dvb = np.zeros_like(v[b])
+        dgb = None if gate is None else np.zeros((S, Hq, D))
+        for c0 in range(0, len(run_rows), chunk):
+            ridx = run_rows[c0:c0 + chunk]
+            lo = 0 if window == 0 else max(0, int(ridx[0]) - window + 1)
             hi = int(ridx[-1]) + 1
             jj = np.arange(lo, hi)
             mask = visible(ridx[:, None], jj[None, :], window)
@@ -397,23 +422,26 @@ def attention_bwd(q, k, v, gate, q_norm_w, k_norm_w, dout, *, window: int,
                     if gate is not None:
                         sg = _sigmoid(np.asarray(gate[b, ridx, h, :], dtype=np.float64))
                         do = dy * sg
-                        dgate[b, ridx, h, :] = dy * o * sg * (1.0 - sg)
+                        dgb[ridx, h, :] = dy * o * sg * (1.0 - sg)
                     else:
                         do = dy
-                    dv[b, lo:hi, g, :] += P.T @ do
+                    dvb[lo:hi, g, :] += P.T @ do
                     dP = do @ vg.T
                     dr = np.sum(do * o, axis=1, keepdims=True)
                     dS = P * (dP - dr)
                     dqp[ridx, h, :] += tau * (dS @ kg)
                     dkp[lo:hi, g, :] += tau * (dS.T @ qp[ridx, h, :])
-        dqh = rope_bwd(dqp, pos, rope_dim, rope_theta)
-        dkh = rope_bwd(dkp, pos, rope_dim, rope_theta)
-        dq[b], gq = rms_norm_bwd(q[b], q_norm_w, rms_eps, dqh)
-        dk[b], gk = rms_norm_bwd(k[b], k_norm_w, rms_eps, dkh)
+        dqh = rope_bwd(dqp[rsel], pos[rsel], rope_dim, rope_theta)
+        dkh = rope_bwd(dkp[ksel], pos[ksel], rope_dim, rope_theta)
+        dq[b], gq = rms_norm_bwd(q[b, rsel], q_norm_w, rms_eps, dqh)
+        dk[b], gk = rms_norm_bwd(k[b, ksel], k_norm_w, rms_eps, dkh)
+        dv[b] = dvb[ksel]
+        if dgate is not None:
+            dgate[b] = dgb[rsel]
         dwq += gq
         dwk += gk
     return {"dq": dq, "dk": dk, "dv": dv, "dgate": dgate,
-            "dq_norm_w": dwq, "dk_norm_w": dwk}
+            "dq_norm_w": None if sampled else dwq, "dk_norm_w": None if sampled else dwk}
 
 
 # ---------------------------------------------------------------------------

@@ -136,3 +136,25 @@ def test_backward_chunking_changes_nothing():
     b = orc.attention_bwd(q, k, v, g, wq, wk, dy, window=5, chunk=4, **KW)
     for key in a:
         np.testing.assert_allclose(a[key], b[key], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("window", [0, 5])
+@pytest.mark.parametrize("gated", [True, False])
+def test_backward_sampling_matches_full(window, gated):
+    """rows / keys select entries of the full result: the same values (up to
+    the order of the fp64 sums), and the row set grows to every row that sees
+    a selected key (a key seen only by unselected rows is still right)."""
+    q, k, v, g, wq, wk, dy = _case(11, B=2, S=29, gated=gated)
+    full = orc.attention_bwd(q, k, v, g, wq, wk, dy, window=window, chunk=6, **KW)
+    rows = np.array([0, 3, 17, 28])
+    keys = np.array([1, 2, 20, 27])
+    for kw in (dict(rows=rows, keys=keys), dict(rows=rows), dict(keys=keys)):
+        s = orc.attention_bwd(q, k, v, g, wq, wk, dy, window=window, chunk=3, **kw, **KW)
+        r = kw.get("rows", np.arange(29))
+        c = kw.get("keys", np.arange(29))
+        np.testing.assert_allclose(s["dq"], full["dq"][:, r], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(s["dk"], full["dk"][:, c], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(s["dv"], full["dv"][:, c], rtol=1e-12, atol=1e-12)
+        if gated:
+            np.testing.assert_allclose(s["dgate"], full["dgate"][:, r], rtol=1e-12, atol=1e-12)
+        assert s["dq_norm_w"] is None and s["dk_norm_w"] is None

@@ -141,6 +141,29 @@ def test_e4m3_row_scale_and_rows():
     assert np.all(np.abs(y - x) * s[:, None] <= quantum / 2 + 1e-300)
 
 
+def test_e4m3_row_scale_clamp():
+    """The exponent clamp: rows with amax >= 2^-101 keep amax * s in
+    [128, 256); below that the scale stops at 2^108, which float32 still
+    holds (2^108 < its largest finite value, 2^128 (1 - 2^-24)), where the
+    unclamped 2^(8 - e) would overflow to inf for amax < 2^-120.  Such a row
+    is then far below E4M3's smallest step (2^-9) and quantizes to zeros of
+    its own signs; an all-zero row takes s = 2^8 (frexp(0) = (0, 0))."""
+    f32max = float(np.finfo(np.float32).max)
+    for e in (-99, -100):
+        a = 0.75 * 2.0 ** e                      # = 0.75 2^e, frexp exponent e
+        s = orc.e4m3_row_scale(np.array([[a, -a / 3]]))[0]
+        assert s == 2.0 ** (8 - e) and 128 <= a * s < 256
+    for e in (-101, -121, -140, -1074):
+        a = 0.5 * 2.0 ** e if e > -1074 else 2.0 ** -1074
+        s = orc.e4m3_row_scale(np.array([[a]]))[0]
+        assert s == 2.0 ** 108 and s <= f32max and np.isfinite(np.float32(s))
+    assert orc.e4m3_row_scale(np.zeros((1, 4)))[0] == 256.0
+    tiny = np.array([[2.0 ** -123, -2.0 ** -124, 3 * 2.0 ** -125, 0.0]])
+    y = orc.e4m3_rows(tiny)
+    assert np.all(y == 0.0)
+    assert list(np.signbit(y[0])) == [False, True, False, False]
+
+
 def test_decode_fp8_ring_overwrites_the_oldest_slot():
     """Ring of 4 slots, length 6: the new token goes to slot 5 % 4 = 1,
     replacing what was there, and the 4 slots are the visible keys.  With
