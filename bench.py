@@ -230,18 +230,6 @@ def reference_peaks(torch, iters=20):
 
 # The global layer's rows the oracle checks and times at 256K: the fixed rows
 # of the workload's plan plus 55 seeded ones.
-GLOBAL_ROWS_FIXED = [0, 1, 127, 128, 129, 4095, 65535, 131071, 262143]
-GLOBAL_ROWS_SEED = 262144
-
-
-def global_sample_rows(S=262144, extra=55, seed=GLOBAL_ROWS_SEED):
-    rng = np.random.default_rng(seed)
-    rows = set(r for r in GLOBAL_ROWS_FIXED if r < S)
-    while len(rows) < len(GLOBAL_ROWS_FIXED) + extra:
-        rows.add(int(rng.integers(0, S)))
-    return sorted(rows)
-
-
 # leading rows of one gated SWA layer of the 256K block in the oracle sample
 SWA_SAMPLE_ROWS = 8192
 
@@ -342,7 +330,7 @@ def cpu_baseline(gpu_rows=None):
 
     # global S16384: 64 sampled rows, all 32 heads
     S = 16384
-    rows = global_sample_rows(S, 55, S)
+    rows = inputs.global_sample_rows(S, 55, S)
     q = _f64_rows((3, 0, inputs.T_Q), S, 32, rows)
     k = _f64_prefix((3, 0, inputs.T_K), S, 8, S)
     v = _f64_prefix((3, 0, inputs.T_V), S, 8, S)
@@ -365,7 +353,7 @@ def cpu_baseline(gpu_rows=None):
     (ref_swa, _), t_swa = timed(lambda: orc.attention_fwd(q, k, v, g, gq4(4, 0), gk4(4, 0),
                                                           window=128, **KW))
     del q, k, v, g
-    rows = global_sample_rows(S)
+    rows = inputs.global_sample_rows(S)
     qs = _f64_rows((4, 5, inputs.T_Q), S, 32, rows)
     k = _f64_prefix((4, 5, inputs.T_K), S, 8, S)
     v = _f64_prefix((4, 5, inputs.T_V), S, 8, S)
@@ -394,7 +382,7 @@ def cpu_baseline(gpu_rows=None):
     if gpu_rows is not None:
         for name, ref, what in (("swa_layer0", ref_swa, f"rows 0..{n - 1}"),
                                 ("global_layer5", ref_glob,
-                                 f"{len(rows)} rows: {GLOBAL_ROWS_FIXED} + 55 seeded")):
+                                 f"{len(rows)} rows: {list(inputs.GLOBAL_ROWS_FIXED)} + 55 seeded")):
             d = gpu_rows[name] - ref
             parity[name] = {"rows": what + ", all 32 heads", "max_abs": float(np.abs(d).max()),
                             "rel_rms": float(np.sqrt((d * d).sum() / (ref * ref).sum())),
@@ -539,7 +527,8 @@ def main():
                                "global_layer": round(t_glob * 1e3, 3)},
     }
     # the kernel's output on the rows the oracle sample covers
-    grow = torch.tensor(global_sample_rows(S), dtype=torch.long, device="cuda")
+    from global_attention_zg_amd import inputs
+    grow = torch.tensor(inputs.global_sample_rows(S), dtype=torch.long, device="cuda")
     gpu_rows = {"swa_layer0": layers[0].out[:, :SWA_SAMPLE_ROWS].float().cpu().numpy().astype(
                     np.float64),
                 "global_layer5": layers[5].out[:, grow].float().cpu().numpy().astype(np.float64)}

@@ -119,3 +119,22 @@ def sign_magnitude_bytes(key, total: int, lo: int, hi: int, start: int = 0,
         with ThreadPoolExecutor(_threads()) as ex:
             list(ex.map(work, range(c0, c1)))
     return res
+
+
+# Query rows at which a long global layer is compared with the oracle (which
+# cannot afford every row of a 256K layer): the first rows, both sides of the
+# first tile and 128-row boundaries, the powers of two, the last row, and
+# seeded uniform rows up to 64 in all.
+GLOBAL_ROWS_FIXED = (0, 1, 127, 128, 129, 4095, 65535, 131071, 262143)
+GLOBAL_ROWS_SEED = 262144
+
+
+def global_sample_rows(S: int = 262144, extra: int = 55, seed: int = GLOBAL_ROWS_SEED) -> list:
+    rng = np.random.default_rng(seed)
+    rows = set(r for r in GLOBAL_ROWS_FIXED if r < S)
+    if S - 1 not in rows:
+        rows.add(S - 1)
+    n = min(S, len(rows) + extra)
+    while len(rows) < n:
+        rows.add(int(rng.integers(0, S)))
+    return sorted(rows)

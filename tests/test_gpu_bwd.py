@@ -181,6 +181,33 @@ def test_bwd_global_2k_layer():
     print(errs, file=sys.stderr)
 
 
+def test_bwd_global_16k_layer_sampled():
+    """The global layer the benchmark's backward times (B1 S16384, 32/8
+    heads): dq at 62 sampled rows (the first rows, tile and power-of-two
+    boundaries, the last row, seeded rows) and dk, dv at 24 keys among the
+    last 512 positions, against the oracle's sampled backward (which runs
+    every row that sees those keys).  Every key at once through an identity:
+    the rows of P sum to 1, so the sum of dV over a kv head's keys is the sum
+    of dO over its group's rows and heads; that sum is held to the same bar."""
+    S = 16384
+    c = bwd_case("bwd_g16k", 1, S, 32, 8, False)
+    got = run_gpu(c, 0, gated=False, poison=False)
+    rows = inputs.global_sample_rows(S, 55, S + 1)
+    rng = np.random.default_rng(S)
+    keys = {S - 512, S - 300, S - 129, S - 128, S - 33, S - 32, S - 2, S - 1}
+    while len(keys) < 24:
+        keys.add(int(rng.integers(S - 512, S)))
+    keys = sorted(keys)
+    ref = orc.attention_bwd(zc.f64(c["q"]), zc.f64(c["k"]), zc.f64(c["v"]), None, c["gq"], c["gk"],
+                            zc.f64(c["dout"]), window=0, rows=rows, keys=keys, **KW)
+    errs = {"dq": zc.compare_grad(got["dq"][:, rows], ref["dq"], "g16k:dq"),
+            "dk": zc.compare_grad(got["dk"][:, keys], ref["dk"], "g16k:dk"),
+            "dv": zc.compare_grad(got["dv"][:, keys], ref["dv"], "g16k:dv")}
+    dsum = zc.f64(c["dout"])[0].reshape(S, 8, 4, zc.D).sum(axis=(0, 2))   # [Hkv, D]
+    errs["sum dv"] = zc.compare_grad(got["dv"][0].sum(axis=0), dsum, "g16k: sum of dv")
+    print(errs, file=sys.stderr)
+
+
 @pytest.mark.parametrize("rope_dim", [42, 30])
 def test_bwd_q_prime_matches_oracle_prologue(rope_dim):
     """The Q' the backward uses (formed inside the dq' kernel at rope_dim 42,

@@ -100,6 +100,22 @@ def test_decode_parity(ring, window, cap, lens, num_splits):
                            zc.to_dev(c["vn"], torch)[b].view(torch.int16).cpu())
 
 
+def test_decode_theta_1e7_at_256k_positions():
+    """The 10M RoPE base of the 256K stage, new tokens at positions near
+    262144 (pos_offset 261000 + lengths up to 1145): output and the appended
+    K' rows."""
+    lens = [1, 900, 1145]
+    c = dec_case(206, len(lens), 8, 2, 1200)
+    kw = dict(rope_theta=1e7, pos_offset=261000)
+    out, kc, _ = run_gpu(c, lens, 0, 0, **kw)
+    o, _, kafter = run_oracle(c, lens, 0, 0, **kw)
+    zc.compare(_f(out), o, "decode theta=1e7")
+    for b, L in enumerate(lens):
+        got = _f(kc[b, :, L - 1])
+        ref = kafter[b, :, L - 1]
+        assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-5)
+
+
 @pytest.mark.parametrize("grp", [1, 2, 4, 8])
 def test_decode_group_sizes(grp):
     lens = [7, 333]

@@ -169,6 +169,21 @@ def test_decode_fp8_no_new_token_and_theta_options():
         assert np.array_equal(vc.cpu().numpy(), c["vc"])
 
 
+def test_decode_fp8_tiny_query_scale_clamp():
+    """Query-norm weights of 2^-125 make every head's q' row amax about
+    2^-123: the row scale's exponent clamp holds the scale at 2^108 (the
+    unclamped 2^131 is inf in fp32), so every query code is zero, all scores
+    vanish and each head averages the visible values."""
+    lens = [1, 77, 300]
+    c = fp8_case(307, 3, 8, 2, 300)
+    c["gq"] = np.full(D, 2.0 ** -125, dtype=np.float32)
+    out, _, _ = run_gpu(c, lens, 0, 0)
+    o, _, _, _ = run_oracle(c, lens, 0, 0)
+    got = _f(out)
+    assert np.all(np.isfinite(got))
+    zc.compare(got, o, "fp8 decode tiny query")
+
+
 def test_decode_fp8_every_code_widens_exactly():
     """One key takes all the weight (its stored K is 448 in every dim and
     q' = 1 in every dim, so every other score is more than 5000 below it):

@@ -115,12 +115,20 @@ def test_fwd_tiny_pair_config():
         check_lse(g["lse"], l, f"tiny W={window}")
 
 
-def test_fwd_large_position_offset():
+@pytest.mark.parametrize("theta", [10000.0, 1e7])
+def test_fwd_large_position_offset(theta):
+    """Positions 262000 .. 262199, at the 10K base and at the 10M base the
+    pages use for the 256K stage: outputs, LSE and the rotated keys."""
     c = zc.fwd_case(104, 1, 200, 8, 2, gated=True)
     for window in (128, 0):
-        g = run_gpu(c, window, pos_offset=262000)
-        o, l = run_oracle(c, window, pos_offset=262000)
-        zc.compare(g["out"], o, "pos_offset")
+        g = run_gpu(c, window, pos_offset=262000, rope_theta=theta, k_out=True)
+        o, l = run_oracle(c, window, pos_offset=262000, rope_theta=theta)
+        zc.compare(g["out"], o, f"pos_offset theta={theta} W={window}")
+        check_lse(g["lse"], l, f"pos_offset theta={theta} W={window}")
+    kn = orc.rms_norm(zc.f64(c["k"]), c["gk"].astype(np.float64), 1e-6)
+    ref = orc.apply_partial_rope(kn[0], 262000 + np.arange(200), 42, theta)
+    d = np.abs(g["k_out"][0] - ref)
+    assert np.all(d <= 2.0 ** -8 * np.abs(ref) + 1e-5), float(d.max())
 
 
 def test_fwd_theta_and_scale_options():
