@@ -42,6 +42,7 @@ __all__ = [
     "e4m3_row_scale",
     "e4m3_rows",
     "attention_decode_fp8",
+    "attention_fwd_fp8",
     "rms_norm",
     "rope_angles",
     "apply_partial_rope",
@@ -145,7 +146,7 @@ def _sigmoid(g: np.ndarray) -> np.ndarray:
 def attention_fwd(q, k, v, gate, q_norm_w, k_norm_w, *, window: int,
                   rope_dim: int, rope_theta: float, rms_eps: float,
                   softmax_scale: float = 0.0, pos_offset: int = 0,
-                  rows=None, chunk: int = 1024):
+                  rows=None, chunk: int = 1024, q_map=None, k_map=None):
     """Prefill / training forward of one attention layer, in float64.
 
     Shapes: q [B,S,Hq,D], k and v [B,S,Hkv,D], gate [B,S,Hq,D] or None,
@@ -159,6 +160,10 @@ def attention_fwd(q, k, v, gate, q_norm_w, k_norm_w, *, window: int,
     elementwise (reading of the gate whose formula the page lost: the local
     attention output is multiplied by a sigmoid gate of the output's shape).
     LSE is the natural-log log-sum-exp of the scaled scores.
+
+    ``q_map`` / ``k_map``, when given, are applied to the normalised, rotated
+    query rows [r,Hq,D] / key rows [keys,Hkv,D] before the scores (the E4M3
+    variant quantizes them there).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -178,11 +183,15 @@ def attention_fwd(q, k, v, gate, q_norm_w, k_norm_w, *, window: int,
         kmax = int(rows.max()) + 1 if nr else 0
         kn = rms_norm(k[b, :kmax], k_norm_w, rms_eps)
         kn = apply_partial_rope(kn, pos[:kmax], rope_dim, rope_theta)
+        if k_map is not None:
+            kn = k_map(kn)
         vb = v[b, :kmax]
         for c0 in range(0, nr, chunk):
             ridx = rows[c0:c0 + chunk]
             qn = rms_norm(q[b, ridx], q_norm_w, rms_eps)
             qn = apply_partial_rope(qn, pos[ridx], rope_dim, rope_theta)
+            if q_map is not None:
+                qn = q_map(qn)
             lo = 0 if window == 0 else max(0, int(ridx.min()) - window + 1)
             hi = int(ridx.max()) + 1
             jj = np.arange(lo, hi)
@@ -503,14 +512,15 @@ def e4m3_decode(codes: np.ndarray) -> np.ndarray:
 
 
 def quantize_e4m3(x: np.ndarray, scale: float):
-    """E4M3 codes and values of x * scale.
+    """E4M3 codes and values of x * scale (scale a number, or an array that
+    broadcasts against x).
 
     Reading: the product is formed in float32 (the precision of the kernel
     that takes the decision), then clamped to [-448, 448] and rounded to the
     nearest E4M3 value with ties to even; the sign of a value that rounds to
     zero is kept (negative zero).  Returns (codes uint8, values float64).
     """
-    v = (np.asarray(x, dtype=np.float32) * np.float32(scale)).astype(np.float64)
+    v = (np.asarray(x, dtype=np.float32) * np.asarray(scale, dtype=np.float32)).astype(np.float64)
     v = np.clip(v, -E4M3_MAX, E4M3_MAX)
     neg = np.signbit(v)
     a = np.abs(v)
@@ -544,8 +554,8 @@ def e4m3_rows(x: np.ndarray) -> np.ndarray:
     """Each row of x [G,D] quantized to E4M3 with its ``e4m3_row_scale``;
     returns the values the codes stand for (decode(code) / s)."""
     x = np.asarray(x, dtype=np.float64)
-    s = e4m3_row_scale(x)
-    return np.stack([quantize_e4m3(x[r], s[r])[1] / s[r] for r in range(x.shape[0])])
+    s = e4m3_row_scale(x)[:, None]
+    return quantize_e4m3(x, s)[1] / s
 
 
 def attention_decode_fp8(q, k_new, v_new, k_codes, v_codes, seq_lens, *, k_scale: float,
@@ -598,6 +608,37 @@ def attention_decode_fp8(q, k_new, v_new, k_codes, v_codes, seq_lens, *, k_scale
             out[b, hs] = o
             lse[b, hs] = ls
     return out, lse, kc, vc
+
+
+def attention_fwd_fp8(q, k, v, gate, q_norm_w, k_norm_w, *, k_scale: float, window: int,
+                      rope_dim: int, rope_theta: float, rms_eps: float,
+                      softmax_scale: float = 0.0, pos_offset: int = 0, rows=None,
+                      chunk: int = 1024):
+    """Prefill / training forward with QK^T as an E4M3 matrix multiply ([RB]
+    前置知识 › FP8 混合精度训练与 TWEO: forward matmuls in E4M3 with
+    power-of-two scales; [SB] ⚙️ 训练系统: hybrid FP8 training).
+
+    Reading, the same as the E4M3 decode's: the normalised, rotated keys K'
+    (in fp64) are quantized with the caller's per-tensor ``k_scale``
+    (``quantize_e4m3``: the product formed in float32, clamped to +-448,
+    rounded to nearest even) and enter as code / k_scale; each query head's
+    normalised, rotated row q' is quantized with its own power-of-two scale
+    (``e4m3_rows``).  The scores tau q~' . k~' are then exact up to the
+    summation (E4M3 products are exact), and the softmax, P V (V as given, in
+    bf16) and the gate are those of ``attention_fwd``.  Returns (out, lse) as
+    ``attention_fwd`` does.
+    """
+    def k_map(kn):
+        return quantize_e4m3(kn, k_scale)[1] / k_scale
+
+    def q_map(qn):
+        r, h, d = qn.shape
+        return e4m3_rows(qn.reshape(r * h, d)).reshape(r, h, d)
+
+    return attention_fwd(q, k, v, gate, q_norm_w, k_norm_w, window=window, rope_dim=rope_dim,
+                         rope_theta=rope_theta, rms_eps=rms_eps, softmax_scale=softmax_scale,
+                         pos_offset=pos_offset, rows=rows, chunk=chunk, q_map=q_map,
+                         k_map=k_map)
 
 
 # ---------------------------------------------------------------------------

@@ -209,3 +209,81 @@ def test_decode_fp8_is_decode_over_the_dequantized_cache():
     for b, L in enumerate(lens):
         assert np.array_equal(kca[b, :, L - 1], orc.quantize_e4m3(kref[b, :, L - 1], 64.0)[0])
         assert np.array_equal(vca[b, :, L - 1], orc.quantize_e4m3(vn[b], 32.0)[0])
+
+
+# ---------------------------------------------------------------------------
+# E4M3 prefill forward (attention_fwd_fp8)
+# ---------------------------------------------------------------------------
+FWD = dict(rope_dim=0, rope_theta=10000.0, rms_eps=0.0)
+
+
+def test_fwd_fp8_on_grid_inputs_equal_the_bf16_forward():
+    """Rows of +-1 have RMS 1, so with eps 0 and no rotation q' = +-w_q and
+    k' = +-w_k exactly; with weights in {0.5, 1, 1.5, 2} every q' row sits on
+    the E4M3 grid at its own scale (amax 2: scale 64) and every k' on the grid
+    at k_scale 16, so quantization changes nothing and the E4M3 forward is
+    the plain forward."""
+    rng = np.random.default_rng(21)
+    B, S, Hq, Hkv = 1, 37, 4, 2
+    q = rng.choice([-1.0, 1.0], (B, S, Hq, D))
+    k = rng.choice([-1.0, 1.0], (B, S, Hkv, D))
+    v = rng.standard_normal((B, S, Hkv, D))
+    g = rng.standard_normal((B, S, Hq, D))
+    wq = rng.choice([0.5, 1.0, 1.5, 2.0], D)
+    wk = rng.choice([0.5, 1.0, 1.5, 2.0], D)
+    wq[0] = wk[0] = 2.0
+    for W in (0, 5):
+        o8, l8 = orc.attention_fwd_fp8(q, k, v, g, wq, wk, k_scale=16.0, window=W, **FWD)
+        o, l = orc.attention_fwd(q, k, v, g, wq, wk, window=W, **FWD)
+        assert np.array_equal(o8, o) and np.array_equal(l8, l)
+
+
+def test_fwd_fp8_two_tokens_closed_form():
+    """q_0 = q_1 = k_0 = 5 e_0 and k_1 = 5 e_1, unit weights, eps 1e-6, no
+    rotation: q'_0 = k'_0 = 5 / sqrt(25/128 + 1e-6) = 11.31.  The query row
+    scale is 2^(8-4) = 16 and 181.0 rounds to 176, so q~'_0 = 11; at
+    k_scale 3 the key gives 33.94, which rounds to 32 (the E4M3 values in
+    [32, 64) are 4 apart), so k~'_0 = 32/3.  Row 0 sees only key 0 (output
+    v_0, LSE s = tau 11 (32/3)); row 1 mixes v_0 (score s) and v_1 (score 0)."""
+    q = np.zeros((1, 2, 1, D))
+    q[..., 0] = 5.0
+    k = np.zeros((1, 2, 1, D))
+    k[0, 0, 0, 0] = 5.0
+    k[0, 1, 0, 1] = 5.0
+    v = np.random.default_rng(22).standard_normal((1, 2, 1, D))
+    ones = np.ones(D)
+    kw = dict(FWD, rms_eps=1e-6)
+    o, lse = orc.attention_fwd_fp8(q, k, v, None, ones, ones, k_scale=3.0, window=0, **kw)
+    s = 11.0 * (32.0 / 3.0) / np.sqrt(D)
+    w0 = 1.0 / (1.0 + np.exp(-s))
+    assert np.allclose(o[0, 0, 0], v[0, 0, 0], rtol=1e-14, atol=1e-15)
+    assert np.allclose(o[0, 1, 0], w0 * v[0, 0, 0] + (1 - w0) * v[0, 1, 0], rtol=1e-13, atol=1e-15)
+    assert np.allclose(lse[0, 0], [s, np.log(np.exp(s) + 1.0)], rtol=1e-13)
+
+
+def test_fwd_fp8_within_the_quantization_bound():
+    """Random layer: each E4M3 value is within 2^-4 (relative) of what it
+    encodes, so |s~ - s| <= tau sum_d |q'_d k'_d| (2 * 2^-4 + 2^-8) for every
+    pair, and the LSE (1-Lipschitz in the max norm of a row's scores) moves
+    by at most the row's largest such bound.  q' and k' for the bound come
+    from the oracle's own norm and rotation."""
+    rng = np.random.default_rng(23)
+    B, S, Hq, Hkv = 1, 50, 4, 2
+    q = rng.standard_normal((B, S, Hq, D))
+    k = rng.standard_normal((B, S, Hkv, D))
+    v = rng.standard_normal((B, S, Hkv, D))
+    wq = 1 + 0.2 * rng.standard_normal(D)
+    wk = 1 + 0.2 * rng.standard_normal(D)
+    kw = dict(rope_dim=42, rope_theta=1e4, rms_eps=1e-6)
+    _, l8 = orc.attention_fwd_fp8(q, k, v, None, wq, wk, k_scale=16.0, window=0, **kw)
+    _, l = orc.attention_fwd(q, k, v, None, wq, wk, window=0, **kw)
+    pos = np.arange(S)
+    qp = orc.apply_partial_rope(orc.rms_norm(q[0], wq, 1e-6), pos, 42, 1e4)
+    kp = orc.apply_partial_rope(orc.rms_norm(k[0], wk, 1e-6), pos, 42, 1e4)
+    rel = 2 * 2.0 ** -4 + 2.0 ** -8
+    for h in range(Hq):
+        bound = np.abs(qp[:, h]) @ np.abs(kp[:, h // 2]).T * rel / np.sqrt(D)  # [S, S]
+        bound = np.where(np.tril(np.ones((S, S), dtype=bool)), bound, 0.0).max(axis=1)
+        d = np.abs(l8[0, h] - l[0, h])
+        assert np.all(d <= bound + 1e-12)
+        assert np.any(d > 0)      # the quantization is there
