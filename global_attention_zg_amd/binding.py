@@ -61,6 +61,11 @@ def _load():
     lib.zg_attn_fwd_varlen_workspace_size.restype = sz
     lib.zg_attn_fwd_varlen.argtypes = [P, vp, ll, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.zg_attn_fwd_varlen.restype = i
+    lib.zg_attn_fwd_fp8_workspace_size.argtypes = [P]
+    lib.zg_attn_fwd_fp8_workspace_size.restype = sz
+    lib.zg_attn_fwd_fp8.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp, sz,
+                                    vp]
+    lib.zg_attn_fwd_fp8.restype = i
     lib.zg_attn_decode_num_splits.argtypes = [P, i]
     lib.zg_attn_decode_num_splits.restype = i
     lib.zg_attn_decode_workspace_size.argtypes = [P, i, i]
@@ -107,7 +112,7 @@ EXPORTED = ("zg_attn_fwd_workspace_size", "zg_attn_fwd", "zg_attn_fwd_varlen_wor
             "zg_attn_decode_paged", "zg_attn_bwd_workspace_size", "zg_attn_bwd",
             "zg_linear", "zg_qkvg_proj", "zg_quantize_fp8", "zg_linear_fp8",
             "zg_attn_decode_fp8", "zg_attn_decode_paged_fp8", "zg_attn_decode_noalloc",
-            "zg_attn_strerror")
+            "zg_attn_fwd_fp8_workspace_size", "zg_attn_fwd_fp8", "zg_attn_strerror")
 
 
 def library_path() -> str:
@@ -224,6 +229,50 @@ def zg_attn_fwd(q, k, v, gate, q_norm_w, k_norm_w, *, window, rope_dim=42, rope_
     st = _lib.zg_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(q_norm_w),
                           _ptr(k_norm_w), _ptr(out), _ptr(lse), _ptr(k_out),
                           _ptr(workspace) if k_out is None else None, ws_bytes, _stream(stream))
+    _check(st)
+    return out, lse
+
+
+def zg_attn_fwd_fp8_workspace_size(p: Params) -> int:
+    return int(_lib.zg_attn_fwd_fp8_workspace_size(ctypes.byref(p)))
+
+
+def zg_attn_fwd_fp8(q, k, v, gate, q_norm_w, k_norm_w, *, k_scale, window=0, rope_dim=42,
+                    rope_theta=10000.0, rms_eps=1e-6, softmax_scale=0.0, pos_offset=0, out=None,
+                    lse=None, want_lse=False, k_out=None, workspace=None, stream=None):
+    """The E4M3 forward of a global layer: arguments as zg_attn_fwd, plus the
+    per-tensor k_scale; k_out (optional) receives the uint8 K' codes
+    [B,S,Hkv,128].  Returns (out, lse or None)."""
+    B, S, Hq, D = _dims(q, "q", 4)
+    Hkv = _dims(k, "k", 4)[2]
+    a = _Args()
+    a.req(q, "q", BF16)
+    a.req(k, "k", BF16, (B, S, Hkv, D))
+    a.req(v, "v", BF16, (B, S, Hkv, D))
+    a.req(gate, "gate", BF16, (B, S, Hq, D), optional=True)
+    a.req(q_norm_w, "q_norm_w", F32, (D,))
+    a.req(k_norm_w, "k_norm_w", F32, (D,))
+    a.req(out, "out", BF16, (B, S, Hq, D), optional=True)
+    a.req(lse, "lse", F32, (B, Hq, S), optional=True)
+    a.req(k_out, "k_out", U8, (B, S, Hkv, D), optional=True)
+    a.req(workspace, "workspace", U8, None, optional=True)
+    a.done()
+    p = make_params(B, S, Hq, Hkv, D, window, rope_dim, rope_theta, rms_eps, softmax_scale,
+                    pos_offset)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    ws_bytes = 0
+    if k_out is None:
+        ws_bytes = zg_attn_fwd_fp8_workspace_size(p)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    st = _lib.zg_attn_fwd_fp8(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
+                              _ptr(q_norm_w), _ptr(k_norm_w), float(k_scale), _ptr(out),
+                              _ptr(lse), _ptr(k_out), _ptr(workspace) if k_out is None else None,
+                              ws_bytes, _stream(stream))
     _check(st)
     return out, lse
 

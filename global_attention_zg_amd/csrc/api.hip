@@ -174,6 +174,57 @@ static int fwd_impl(const zg_attn_params* p, const int* cu_seqlens, long long to
   return hip_status(zg::launch_flash_fwd(fp, s));
 }
 
+// The E4M3 forward of a global layer (fixed-length batches).
+static int fwd_fp8_impl(const zg_attn_params* p, const void* q, const void* k, const void* v,
+                        const void* gate, const float* q_norm_w, const float* k_norm_w,
+                        float k_scale, void* out, float* lse, void* k_out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  if (!(isfinite(k_scale) && k_scale > 0.f)) return ZG_ERR_INVALID;
+  if (p->window > 0 && p->window < p->seqlen) return ZG_ERR_UNSUPPORTED;
+  if ((long long)p->seqlen * p->n_q_heads > 0x7fffffffLL) return ZG_ERR_UNSUPPORTED;
+  if (p->batch == 0 || p->seqlen == 0) return ZG_OK;
+  if (!q || !k || !v || !q_norm_w || !k_norm_w || !out) return ZG_ERR_INVALID;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(q_norm_w) ||
+      !aligned16(k_norm_w) || !aligned16(out) || (gate && !aligned16(gate)) ||
+      (k_out && !aligned16(k_out)) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
+    return ZG_ERR_INVALID;
+  void* kp = k_out;
+  if (!kp) {
+    if (!workspace || workspace_bytes < kprime_bytes(p) / 2) return ZG_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return ZG_ERR_INVALID;
+    kp = workspace;
+  }
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const zg::RopeTable tab = make_rope_table(p);
+  hipError_t e = zg::launch_k_prologue_fp8(
+      static_cast<const uint16_t*>(k), k_norm_w, static_cast<uint8_t*>(kp), k_scale,
+      (long long)p->batch * p->seqlen * p->n_kv_heads, p->seqlen, p->n_kv_heads, p->pos_offset,
+      p->rope_dim / 2, p->rms_eps, tab, s);
+  if (e != hipSuccess) return ZG_ERR_HIP;
+  zg::FlashParams fp{};
+  fp.q = static_cast<const uint16_t*>(q);
+  fp.kp8 = static_cast<const uint8_t*>(kp);
+  fp.k_scale = k_scale;
+  fp.v = static_cast<const uint16_t*>(v);
+  fp.gate = static_cast<const uint16_t*>(gate);
+  fp.q_norm_w = q_norm_w;
+  fp.k_norm_w = k_norm_w;
+  fp.out = static_cast<uint16_t*>(out);
+  fp.lse = lse;
+  fp.total = (long long)p->batch * p->seqlen;
+  fp.B = p->batch;
+  fp.S = p->seqlen;
+  fp.Hq = p->n_q_heads;
+  fp.Hkv = p->n_kv_heads;
+  fp.window = 0;
+  fp.rope_half = p->rope_dim / 2;
+  fp.scale_log2 = scale_log2(p);
+  fp.eps = p->rms_eps;
+  fp.pos_offset = p->pos_offset;
+  fp.tab = tab;
+  return hip_status(zg::launch_flash_causal(fp, s));
+}
+
 // Shared body of the contiguous and the paged decode.
 static int decode_impl(const zg_attn_params* p, const void* q, const void* k_new,
                        const void* v_new, void* k_cache, void* v_cache, const int* seq_lens,
@@ -310,6 +361,21 @@ int zg_attn_fwd_varlen(const zg_attn_params* p, const int* cu_seqlens, long long
   if (p->batch == 0 || p->seqlen == 0 || total_tokens == 0) return ZG_OK;
   return fwd_impl(p, cu_seqlens, total_tokens, q, k, v, gate, q_norm_w, k_norm_w, out, lse,
                   k_out, workspace, workspace_bytes, stream);
+}
+
+size_t zg_attn_fwd_fp8_workspace_size(const zg_attn_params* p) {
+  if (check_params(p) != ZG_OK) return 0;
+  return kprime_bytes(p) / 2;
+}
+
+int zg_attn_fwd_fp8(const zg_attn_params* p, const void* q, const void* k, const void* v,
+                    const void* gate, const float* q_norm_w, const float* k_norm_w,
+                    float k_scale, void* out, float* lse, void* k_out, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  int st = check_params(p);
+  if (st != ZG_OK) return st;
+  return fwd_fp8_impl(p, q, k, v, gate, q_norm_w, k_norm_w, k_scale, out, lse, k_out, workspace,
+                      workspace_bytes, stream);
 }
 
 size_t zg_attn_bwd_workspace_size(const zg_attn_params* p) {

@@ -30,8 +30,20 @@
 // copies fly NS - 2 tiles ahead, and one barrier per tile both publishes the
 // tile two ahead and frees the stage of the tile just read.  Tiles are
 // visited from the diagonal down; query blocks are launched longest-first.
+//
+// The E4M3 variant (page "ZGCM-1:面向数学与智能体搜索的全开源高效基础模型",
+// section 前置知识 › FP8 混合精度训练与 TWEO: forward matrix multiplies in
+// E4M3 with power-of-two scaling) runs S = K' Q'^T on the FP8 matrix cores
+// (v_mfma_scale_f32_32x32x64_f8f6f4, two per 32-key block and 32 query rows):
+// K' arrives as E4M3 codes of K' * k_scale (128-byte LDS rows), each query
+// row is quantized with its own power-of-two scale in the prologue, and the
+// softmax multiplies the code products by c / (query scale * k_scale) in the
+// same FMA that subtracts the row's offset.  P V stays in bf16.
+
+#include <type_traits>
 
 #include "zg_common.h"
+#include "zg_fp8.h"
 #include "zg_launch.h"
 #include "zg_lds.h"
 #include "zg_flash_tile.h"
@@ -45,7 +57,6 @@ using namespace flash;
 constexpr int kCWaves = 4;
 constexpr int kCThreads = 64 * kCWaves;
 constexpr int kCRows = 64;       // query rows per wave (two halves of 32)
-constexpr int kCCopies = 4;      // a wave's global -> LDS copies per tile (2 KB of K', 2 KB of V)
 
 // Causal mask of one 32-key block for this lane's row: register r holds key
 // kblk + 4 h + 8 (r/4) + r%4, visible iff key <= qm, i.e. iff the immediate
@@ -65,12 +76,12 @@ __device__ __forceinline__ void qk_seeded(f32x16& s, const bf16x8 (&ka)[8], cons
   for (int kk = 1; kk < 8; ++kk) s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kk], qf[kk], s, 0, 0, 0);
 }
 
-// Word w (0..7) of P: elements 2w, 2w+1 of P = exp2(s) packed to bf16
-// (word w of the PV B operand of k-step w/4), and their sum, from the
-// rounded values the MFMA multiplies, added to the row sum.
-__device__ __forceinline__ uint32_t p_word(const f32x16& s, int w, float& l_run) {
+// A word of P: two elements exp2(a0), exp2(a1) packed to bf16 (a word of
+// the PV B operand), and their sum, from the rounded values the MFMA
+// multiplies, added to the row sum.
+__device__ __forceinline__ uint32_t p_word(float a0, float a1, float& l_run) {
   const bf16x2 one2 = {(__bf16)1.0f, (__bf16)1.0f};
-  const uint32_t u = pack_bf16x2(fast_exp2(s[2 * w]), fast_exp2(s[2 * w + 1]));
+  const uint32_t u = pack_bf16x2(fast_exp2(a0), fast_exp2(a1));
   l_run = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, u), one2, l_run, false);
   return u;
 }
@@ -103,12 +114,34 @@ __device__ __forceinline__ void acc_settle(f32x16 (&acc)[4]) {
                : "+a"(acc[0]), "+a"(acc[1]), "+a"(acc[2]), "+a"(acc[3]));
 }
 
+// S^T = K' Q'^T of one 32-key block on the FP8 matrix cores: operand m holds
+// dims 64 h + 32 m .. + 31 (h = lane / 32) as E4M3 codes, the same dims for
+// the key row (A) and the query row (B), so the products pair up whatever
+// order the unit sums them in.  The block scales are 1: the result is the sum
+// of the code products.
+__device__ __forceinline__ void qk_fp8(f32x16& s, const i32x8 (&ka)[2], const i32x8 (&qf)[2]) {
+  s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[0], qf[0], f32x16{}, 0, 0, 0, 127, 0, 127);
+  s = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ka[1], qf[1], s, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ i32x8 join_i32x8(const u32x4& lo, const u32x4& hi) {
+  return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+               (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+}
+
 // RH: rope_dim / 2 when fixed at compile time (21 or 0), else -1.
-// NS: K'/V tile stages in LDS.
-template <int RH, bool PACKED, int NS>
+// NS: K'/V tile stages in LDS.  FP8: the E4M3 variant.
+template <int RH, bool PACKED, int NS, bool FP8>
 __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams p, Geo geo) {
-  constexpr int kSmem = 2 * NS * kTileBytes;
-  constexpr int kVOff = NS * kTileBytes;
+  constexpr int kKRow = FP8 ? kD : kRowBytes;  // bytes per K' row in LDS
+  constexpr int kKTile = kBN * kKRow;
+  constexpr int kSmem = NS * (kKTile + kTileBytes);
+  constexpr int kVOff = NS * kKTile;
+  // a wave's global -> LDS copies per tile: 2 KB of V and 2 KB (bf16) or
+  // 1 KB (E4M3) of K'
+  constexpr int kCopies = FP8 ? 3 : 4;
+  constexpr int kKOps = FP8 ? 2 : 8;  // score-product operands per 32 rows
+  using QOp = typename std::conditional<FP8, i32x8, bf16x8>::type;
   static_assert(kCWaves * 32 * 65 * 4 <= kSmem, "query RoPE rows must fit");
   static_assert(NS >= 3, "copies fly NS - 2 tiles ahead");
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kSmem];
@@ -161,9 +194,17 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
   // ---- K'/V staging: wave w fills the 1 KB blocks 2w, 2w + 1 (rows 4n ..
   // 4n + 3) of each 8 KB tile; lane L writes physical chunk L % 16 of row
   // 4n + L / 16 and so fetches the logical chunk the row's swizzle puts there.
-  const long long kvstride = (long long)p.Hkv * kD;
-  const uint16_t* kbase = p.kp + tok0 * kvstride + g * kD;
+  // E4M3 K' (4 KB tiles of 128-byte rows, chunks swizzled by row % 8): wave w
+  // fills rows 8w .. 8w + 7, lane L physical chunk L % 8 of row 8w + L / 8.
+  const long long kvstride = (long long)p.Hkv * kD;  // elements per token
+  constexpr int kKEB = FP8 ? 1 : 2;                  // bytes per K' element
+  const unsigned char* kbase =
+      FP8 ? p.kp8 + tok0 * kvstride + g * kD
+          : reinterpret_cast<const unsigned char*>(p.kp + tok0 * kvstride + g * kD);
   const uint16_t* vbase = p.v + tok0 * kvstride + g * kD;
+  const int krow8 = 8 * wv + (lane >> 3);
+  const uint32_t krow8_off = (uint32_t)(krow8 * kvstride);
+  const uint32_t kchunk8 = 16u * ((lane & 7) ^ (krow8 & 7));
   uint32_t row_off[2], kchunk[2];
   int lrow[2];
   const uint32_t vchunk = 16u * ((lane & 15) ^ (((lane >> 4) & 3) << 2));
@@ -176,21 +217,24 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
   // tile t (0 <= t <= t_hi) -> stage stg; keys >= S (only in the top tile)
   // load key S-1 and are masked out
   auto gload = [&](int t, int stg) __attribute__((always_inline)) {
-    const unsigned char* kb = (const unsigned char*)(kbase + (long long)t * kBN * kvstride);
+    const unsigned char* kb = kbase + (long long)t * kBN * kvstride * kKEB;
     const unsigned char* vb = (const unsigned char*)(vbase + (long long)t * kBN * kvstride);
-    const uint32_t kl = lds_addr(smem + stg * kTileBytes + 2 * wv * 1024);
-    const uint32_t vl = kl + kVOff;
+    const uint32_t kl = lds_addr(smem + stg * kKTile + (FP8 ? 1 : 2) * wv * 1024);
+    const uint32_t vl = lds_addr(smem + kVOff + stg * kTileBytes + 2 * wv * 1024);
     if (t * kBN + kBN <= S) {
+      if constexpr (FP8) dma16_s(kb, krow8_off + kchunk8, kl);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        dma16_s(kb, row_off[j] + kchunk[j], kl + j * 1024);
+        if constexpr (!FP8) dma16_s(kb, row_off[j] + kchunk[j], kl + j * 1024);
         dma16_s(vb, row_off[j] + vchunk, vl + j * 1024);
       }
     } else {
+      if constexpr (FP8)
+        dma16_s(kb, (uint32_t)((min(t * kBN + krow8, S - 1) - t * kBN) * kvstride) + kchunk8, kl);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const uint32_t off = (uint32_t)((min(t * kBN + lrow[j], S - 1) - t * kBN) * kvstride * 2);
-        dma16_s(kb, off + kchunk[j], kl + j * 1024);
+        if constexpr (!FP8) dma16_s(kb, off + kchunk[j], kl + j * 1024);
         dma16_s(vb, off + vchunk, vl + j * 1024);
       }
     }
@@ -200,9 +244,12 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
   // the same on every iteration
   auto gload_j = [&](int j, int stg) __attribute__((always_inline)) { gload(max(t_hi - j, 0), stg); };
 
-  // per-lane LDS read offsets: K' row q%32 at logical chunk 8h; V rows
-  // 4h + i/4 at dims 32bd + 16 (group parity) + 4 (i%4) for the transposing loads
-  const uint32_t kread_off = qcol * kRowBytes + ((uint32_t)((8 * half) ^ (qcol & 15)) << 4);
+  // per-lane LDS read offsets: K' row q%32 at logical chunk 8h (E4M3: 4h);
+  // V rows 4h + i/4 at dims 32bd + 16 (group parity) + 4 (i%4) for the
+  // transposing loads
+  const uint32_t kread_off =
+      FP8 ? qcol * kKRow + ((uint32_t)((4 * half) ^ (qcol & 7)) << 4)
+          : qcol * kRowBytes + ((uint32_t)((8 * half) ^ (qcol & 15)) << 4);
   const int gi = lane & 15;
   const int vq = gi >> 2;
   const int vlow = 2 * ((lane >> 4) & 1) + ((gi & 3) >> 1);
@@ -233,7 +280,8 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
   float wk = fmaxf(fabsf(p.k_norm_w[2 * lane]), fabsf(p.k_norm_w[2 * lane + 1]));
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) wk = fmaxf(wk, __shfl_xor(wk, o));
-  bf16x8 qf[2][8];
+  QOp qf[2][kKOps];
+  float fsc[2] = {1.f, 1.f};  // E4M3: exp2 units per unit of code product, per half
   bool fast_ok = true;
   // (the halves are fenced from each other so that the scheduler does not
   // overlap their loads: the register peak of the prologue would otherwise
@@ -250,7 +298,50 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
       unpack_bf16x8(u, x + 8 * j);
     }
     float* qs = reinterpret_cast<float*>(smem_raw) + (wv * 32 + qcol) * 65;
-    q_prologue<RH>(x, half, p, p.pos_offset + qi[h], qs, qf[h]);
+    float qq = 0.f, sii = 0.f, u;
+    if constexpr (FP8) {
+      // E4M3 query row: q' with the power-of-two scale 2^(8-e) that puts its
+      // amax = m 2^e (m in [0.5, 1), e clamped to >= -100) in [128, 256)
+      q_norm_rope<RH>(x, half, p, p.pos_offset + qi[h], qs);
+      float am = 0.f;
+#pragma unroll
+      for (int d = 0; d < 64; ++d) am = fmaxf(am, fabsf(x[d]));
+      am = pair_max32(am);
+      int e;
+      frexpf(am, &e);
+      e = max(e, -100);
+      uint2 c8[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c8[j] = pack_e4m3x8(x + 8 * j, ldexpf(1.0f, 8 - e));
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        qf[h][m] = join_i32x8(u32x4{c8[4 * m].x, c8[4 * m].y, c8[4 * m + 1].x, c8[4 * m + 1].y},
+                              u32x4{c8[4 * m + 2].x, c8[4 * m + 2].y, c8[4 * m + 3].x, c8[4 * m + 3].y});
+      fsc[h] = p.scale_log2 * ldexpf(1.0f / p.k_scale, e - 8);
+      // |codes| of the row and its product with the row's own key's codes
+      const unsigned char* krow = p.kp8 + ((tok0 + qm[h]) * p.Hkv + g) * kD + 64 * half;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float qv[8], kv[8];
+        unpack_bf16x8(widen_e4m3x8(c8[j]), qv);
+        unpack_bf16x8(widen_e4m3x8(ld8(krow + 8 * j)), kv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          qq = __builtin_fmaf(qv[i], qv[i], qq);
+          sii = __builtin_fmaf(qv[i], kv[i], sii);
+        }
+      }
+      qq = pair_sum32(qq);
+      sii = pair_sum32(sii) * fsc[h];
+      // Softmax offset (exp2 units): every score is at most fsc |q codes|
+      // |k codes| by Cauchy-Schwarz, and a key row's codes have norm at most
+      // k_scale |k'| (1 + 2^-4) + 2^-10 sqrt(D) (relative rounding 2^-4 of
+      // normal values, 2^-10 absolute below them; clamping only shrinks
+      // them), with |k'| <= sqrt(D) max|w_k|; 2^-8 covers the fp32 sums.
+      const float kc_norm = (p.k_scale * wk * 1.0625f + 0.0009765625f) * sqrtf((float)kD);
+      u = fsc[h] * sqrtf(qq) * kc_norm * (1.0f + 0.00390625f);
+    } else {
+      q_prologue<RH>(x, half, p, p.pos_offset + qi[h], qs, qf[h]);
     // Softmax offset.  q' is held pre-scaled by c = scale log2(e), so the
     // scores come out in exp2 units.  Every score of this row is at most
     //   U = |c q'| sqrt(D) max|w_k|   (RoPE keeps norms; the key RMSNorm
@@ -260,29 +351,29 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
     // at most 1.  The row's own key is visible, so its largest weight is at
     // least exp2(s_ii - U); while that stays above 2^-100 the fixed offset
     // loses nothing to underflow and no running max is needed.
-    float qq = 0.f, sii = 0.f;
-    const uint16_t* krow = p.kp + ((tok0 + qm[h]) * p.Hkv + g) * kD + 64 * half;
+      const uint16_t* krow = p.kp + ((tok0 + qm[h]) * p.Hkv + g) * kD + 64 * half;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float qv[8], kv[8];
-      unpack_bf16x8(__builtin_bit_cast(u32x4, qf[h][j]), qv);
-      unpack_bf16x8(ld16(krow + 8 * j), kv);
+      for (int j = 0; j < 8; ++j) {
+        float qv[8], kv[8];
+        unpack_bf16x8(__builtin_bit_cast(u32x4, qf[h][j]), qv);
+        unpack_bf16x8(ld16(krow + 8 * j), kv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qq = __builtin_fmaf(qv[e], qv[e], qq);
-        sii = __builtin_fmaf(qv[e], kv[e], sii);
+        for (int e = 0; e < 8; ++e) {
+          qq = __builtin_fmaf(qv[e], qv[e], qq);
+          sii = __builtin_fmaf(qv[e], kv[e], sii);
+        }
       }
+      qq = pair_sum32(qq);
+      sii = pair_sum32(sii);
+      u = sqrtf(qq) * sqrtf((float)kD) * wk * (1.0f + 0.015625f);
     }
-    qq = pair_sum32(qq);
-    sii = pair_sum32(sii);
-    const float u = sqrtf(qq) * sqrtf((float)kD) * wk * (1.0f + 0.015625f);
     st[h].m_run = u;
     fast_ok = fast_ok && u - sii <= 100.0f;
     // the query operands stay in accumulation registers for the whole
     // kernel (the matrix cores read their A/B operands from either file),
     // which leaves the vector registers to the loop's working set
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) asm volatile("; q' operand to AGPRs" : "=a"(qf[h][kk]) : "0"(qf[h][kk]));
+    for (int kk = 0; kk < kKOps; ++kk) asm volatile("; q' operand to AGPRs" : "=a"(qf[h][kk]) : "0"(qf[h][kk]));
     __builtin_amdgcn_sched_barrier(0);
   }
   // Workgroup-uniform: if any row's largest weight could underflow, every
@@ -294,19 +385,34 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
 
   // a tile needs masking for half h if it reaches past the half's first row
   auto masked = [&](int j, int h) __attribute__((always_inline)) { return (t_hi - j) * kBN + kBN - 1 > wrow0 + 32 * h; };
-  auto kst = [&](int stg) __attribute__((always_inline)) { return smem + stg * kTileBytes; };
-  bf16x8 ka[8], va[8], pf[2][2];
+  QOp ka[kKOps];
+  bf16x8 va[8], pf[2][2];
   f32x16 s[2];
+  // this lane's K' operands of the tile in stage stg
+  auto kops = [&](int stg) __attribute__((always_inline)) {
+    const lds_u8* kt = smem + stg * kKTile;
+    if constexpr (FP8) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+        ka[m] = join_i32x8(__builtin_bit_cast(u32x4, lds_read_b128(kt + (kread_off ^ ((2u * m) << 4)))),
+                           __builtin_bit_cast(u32x4, lds_read_b128(kt + (kread_off ^ ((2u * m + 1) << 4)))));
+    } else {
+      load_kops(ka, kt, kread_off);
+    }
+  };
   if (exact_max) {
     float mx[2] = {-INFINITY, -INFINITY};
     int stg = 0;
     for (int j = 0; j < nt; ++j) {
       // tile j has landed (the first NS before the loop; later tiles j + 1 ..
       // j + NS - 1 may fly)
-      if (j > 0) sync_tiles<kCCopies * (NS - 1)>();
-      load_kops(ka, kst(stg), kread_off);
-      qk_mfma(s[0], ka, qf[0]);
-      qk_mfma(s[1], ka, qf[1]);
+      if (j > 0) sync_tiles<kCopies * (NS - 1)>();
+      kops(stg);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if constexpr (FP8) qk_fp8(s[h], ka, qf[h]);
+        else qk_mfma(s[h], ka, qf[h]);
+      }
       lds_barrier();  // every wave has read stage stg
       gload_j(j + NS, stg);
 #pragma unroll
@@ -320,16 +426,26 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
     fill_ring();
     sync_tiles<0>();
 #pragma unroll
-    for (int h = 0; h < 2; ++h) st[h].m_run = mx[h];
+    for (int h = 0; h < 2; ++h) st[h].m_run = FP8 ? mx[h] * fsc[h] : mx[h];
   }
   // m_run: the row's softmax offset (exp2 units); the score accumulators
-  // start from its negative
+  // start from its negative (E4M3: the softmax's FMA subtracts it)
   f32x16 seed[2];
+  float nu[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
+    nu[h] = -st[h].m_run;
 #pragma unroll
     for (int r = 0; r < 16; ++r) seed[h][r] = -st[h].m_run;
   }
+  // the exp2 argument of score r of half h
+  auto arg = [&](int h, int r) __attribute__((always_inline)) {
+    return FP8 ? __builtin_fmaf(s[h][r], fsc[h], nu[h]) : s[h][r];
+  };
+  auto qk = [&](int h) __attribute__((always_inline)) {
+    if constexpr (FP8) qk_fp8(s[h], ka, qf[h]);
+    else qk_seeded(s[h], ka, qf[h], seed[h]);
+  };
 
   auto vops = [&](int stg) __attribute__((always_inline)) {
     const lds_u8* vr[4];
@@ -348,7 +464,8 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
     for (int t = 0; t < 2; ++t) {
       u32x4 u;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) u[w] = p_word(s[h], 4 * t + w, st[h].l_run);
+      for (int w = 0; w < 4; ++w)
+        u[w] = p_word(arg(h, 8 * t + 2 * w), arg(h, 8 * t + 2 * w + 1), st[h].l_run);
       pf[h][t] = __builtin_bit_cast(bf16x8, u);
     }
     pin(pf[h][0]);
@@ -374,8 +491,8 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
       pv_agpr_one(st[1].acc, va, pf[1], g);
-      e[2 * g] = fast_exp2(s[0][2 * g]);
-      e[2 * g + 1] = fast_exp2(s[0][2 * g + 1]);
+      e[2 * g] = fast_exp2(arg(0, 2 * g));
+      e[2 * g + 1] = fast_exp2(arg(0, 2 * g + 1));
       if (g > 0) word(g - 1);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -398,13 +515,13 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
   // that the slots themselves stay single blocks.
 
   // ---- warm-up: both halves' scores of tile 0, half 0's P and PV
-  load_kops(ka, kst(0), kread_off);
-  qk_seeded(s[0], ka, qf[0], seed[0]);
-  qk_seeded(s[1], ka, qf[1], seed[1]);
+  kops(0);
+  qk(0);
+  qk(1);
   mask(0, 0);
   softmax(0);
   vops(0);
-  load_kops(ka, kst(1 % NS), kread_off);  // tile 1 (or a copy of tile 0)
+  kops(1 % NS);  // tile 1 (or a copy of tile 0)
   lds_barrier();                          // every wave has read tile 0
   gload_j(NS, 0);
   pv_agpr(st[0].acc, va, pf[0]);
@@ -417,7 +534,7 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
     mask(1, j);
     // A
     __builtin_amdgcn_sched_barrier(0);
-    qk_seeded(s[0], ka, qf[0], seed[0]);
+    qk(0);
     softmax(1);
     __builtin_amdgcn_sched_barrier(0);
     mask(0, j + 1);
@@ -426,17 +543,17 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
     pv1_sm0();
     __builtin_amdgcn_sched_barrier(0);
     // C
-    qk_seeded(s[1], ka, qf[1], seed[1]);
+    qk(1);
     vops(sa);
     __builtin_amdgcn_sched_barrier(0);
     // tile j + 2 has landed for every wave, and no wave still reads tile
     // j + 1's stage, which takes tile j + 1 + NS
-    sync_tiles<kCCopies * (NS - 2)>();
+    sync_tiles<kCopies * (NS - 2)>();
     gload_j(j + 1 + NS, sa);
     // D
     __builtin_amdgcn_sched_barrier(0);
     pv_agpr(st[0].acc, va, pf[0]);
-    load_kops(ka, kst(sb), kread_off);
+    kops(sb);
     __builtin_amdgcn_sched_barrier(0);
     sa = sb;
   }
@@ -485,10 +602,10 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
 
 constexpr int kCStages = 8;
 
-template <int RH, bool PACKED>
+template <int RH, bool PACKED, bool FP8 = false>
 void launch_causal(dim3 grid, hipStream_t stream, const FlashParams& p, const Geo& geo) {
-  hipLaunchKernelGGL((flash_causal_kernel<RH, PACKED, kCStages>), grid, dim3(kCThreads), 0, stream,
-                     p, geo);
+  hipLaunchKernelGGL((flash_causal_kernel<RH, PACKED, kCStages, FP8>), grid, dim3(kCThreads), 0,
+                     stream, p, geo);
 }
 
 }  // namespace
@@ -505,7 +622,12 @@ hipError_t launch_flash_causal(const FlashParams& p, hipStream_t stream) {
   const long long blocks = (long long)geo.n_pos_blocks * geo.n_bhg;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks);
-  if (p.cu_seqlens) {
+  if (p.kp8) {  // the E4M3 variant: fixed-length batches
+    if (p.cu_seqlens) return hipErrorInvalidValue;
+    if (p.rope_half == 21) launch_causal<21, false, true>(grid, stream, p, geo);
+    else if (p.rope_half == 0) launch_causal<0, false, true>(grid, stream, p, geo);
+    else launch_causal<-1, false, true>(grid, stream, p, geo);
+  } else if (p.cu_seqlens) {
     if (p.rope_half == 21) launch_causal<21, true>(grid, stream, p, geo);
     else if (p.rope_half == 0) launch_causal<0, true>(grid, stream, p, geo);
     else launch_causal<-1, true>(grid, stream, p, geo);

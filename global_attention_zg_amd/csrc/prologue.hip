@@ -26,13 +26,17 @@ namespace {
 constexpr int kRowsPerBlock = 16;
 constexpr long long kPrologueBlocks = 2048;
 
+// FP8: kout receives the E4M3 codes of K' * k_scale (one byte per element)
+// instead of bf16 K'.
+template <bool FP8>
 __global__ __launch_bounds__(256) void k_prologue_kernel(const uint16_t* __restrict__ k,
                                                          const float* __restrict__ w,
-                                                         uint16_t* __restrict__ kout,
+                                                         void* __restrict__ kout,
                                                          long long rows, int S, int Hkv,
                                                          const int* __restrict__ cu_seqlens,
                                                          int nseq, long long pos_offset,
-                                                         int rope_half, float eps, RopeTable tab) {
+                                                         int rope_half, float eps, RopeTable tab,
+                                                         float k_scale) {
   __shared__ float xs[kRowsPerBlock][kD];
   __shared__ float cs[kRowsPerBlock][kMaxRopeHalf], sn[kRowsPerBlock][kMaxRopeHalf];
   const int lrow = threadIdx.x / 16;
@@ -72,10 +76,14 @@ __global__ __launch_bounds__(256) void k_prologue_kernel(const uint16_t* __restr
     norm_rope_row(x, c16, kc, eps, rope_half, pos_offset + s, xs[lrow], ref == lrow, cs[lrow],
                   sn[lrow], cs[ref], sn[ref]);
     if (ok) {
-      u32x4 o;
+      if constexpr (FP8) {
+        st8(static_cast<uint8_t*>(kout) + row * kD + 8 * c16, pack_e4m3x8(x, k_scale));
+      } else {
+        u32x4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
-      st16(kout + row * kD + 8 * c16, o);
+        for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+        st16(static_cast<uint16_t*>(kout) + row * kD + 8 * c16, o);
+      }
     }
     lds_barrier();  // xs and the angle tables are rewritten by the next group
   }
@@ -164,16 +172,31 @@ __global__ __launch_bounds__(256) void kv_write_pages_kernel(const uint16_t* __r
 
 }  // namespace
 
+static long long prologue_blocks(long long rows) {
+  // eight 256-thread blocks per CU stride over the groups of 16 rows
+  const long long groups = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
+  return groups < kPrologueBlocks ? groups : kPrologueBlocks;
+}
+
 hipError_t launch_k_prologue(const uint16_t* k, const float* w, uint16_t* kout, long long rows,
                              int S, int Hkv, long long pos_offset, int rope_half, float eps,
                              const RopeTable& tab, hipStream_t stream, const int* cu_seqlens,
                              int nseq) {
   if (rows == 0) return hipSuccess;
-  // eight 256-thread blocks per CU stride over the groups of 16 rows
-  const long long groups = (rows + kRowsPerBlock - 1) / kRowsPerBlock;
-  const long long blocks = groups < kPrologueBlocks ? groups : kPrologueBlocks;
-  hipLaunchKernelGGL(k_prologue_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, k, w,
-                     kout, rows, S, Hkv, cu_seqlens, nseq, pos_offset, rope_half, eps, tab);
+  hipLaunchKernelGGL(k_prologue_kernel<false>, dim3((unsigned)prologue_blocks(rows)), dim3(256), 0,
+                     stream, k, w, (void*)kout, rows, S, Hkv, cu_seqlens, nseq, pos_offset,
+                     rope_half, eps, tab, 1.0f);
+  return hipGetLastError();
+}
+
+hipError_t launch_k_prologue_fp8(const uint16_t* k, const float* w, uint8_t* kout, float k_scale,
+                                 long long rows, int S, int Hkv, long long pos_offset,
+                                 int rope_half, float eps, const RopeTable& tab,
+                                 hipStream_t stream, const int* cu_seqlens, int nseq) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_prologue_kernel<true>, dim3((unsigned)prologue_blocks(rows)), dim3(256), 0,
+                     stream, k, w, (void*)kout, rows, S, Hkv, cu_seqlens, nseq, pos_offset,
+                     rope_half, eps, tab, k_scale);
   return hipGetLastError();
 }
 

@@ -144,18 +144,16 @@ __device__ __forceinline__ void load_vops(bf16x8 (&va)[8], const lds_u8* const (
   }
 }
 
-// Query prologue of one lane: x holds dims 64 half .. 64 half + 63 of its
-// raw query row.  RMSNorm over the 128 dims (both lane halves), the weight,
-// then the partial rotation at position pos (rotary pairs (t, t + R/2), all
-// inside lane half 0), and the result times c = softmax scale * log2(e),
-// packed as the 8 k-steps of the score products' B operand: the products
-// then come out in exp2 units.  RH: rope_dim / 2 when fixed at compile time
-// (21 or 0: the rotation stays in registers); -1 for any other even
-// rope_dim <= 64, which rotates through qs, a private LDS row of 64 floats
-// of this lane.
+// Query normalisation of one lane: x holds dims 64 half .. 64 half + 63 of
+// its raw query row.  RMSNorm over the 128 dims (both lane halves), the
+// weight, then the partial rotation at position pos (rotary pairs (t, t +
+// R/2), all inside lane half 0); x then holds those dims of q'.  RH:
+// rope_dim / 2 when fixed at compile time (21 or 0: the rotation stays in
+// registers); -1 for any other even rope_dim <= 64, which rotates through
+// qs, a private LDS row of 64 floats of this lane.
 template <int RH>
-__device__ __forceinline__ void q_prologue(float (&x)[64], int half, const FlashParams& p,
-                                           long long pos, float* qs, bf16x8 (&qf)[8]) {
+__device__ __forceinline__ void q_norm_rope(float (&x)[64], int half, const FlashParams& p,
+                                            long long pos, float* qs) {
   float ss = 0.f;
 #pragma unroll
   for (int d = 0; d < 64; ++d) ss += x[d] * x[d];
@@ -196,6 +194,15 @@ __device__ __forceinline__ void q_prologue(float (&x)[64], int half, const Flash
 #pragma unroll
     for (int d = 0; d < 64; ++d) x[d] = qs[d];
   }
+}
+
+// The query prologue of the bf16 kernels: q' times c = softmax scale *
+// log2(e), packed as the 8 k-steps of the score products' B operand (the
+// products then come out in exp2 units).
+template <int RH>
+__device__ __forceinline__ void q_prologue(float (&x)[64], int half, const FlashParams& p,
+                                           long long pos, float* qs, bf16x8 (&qf)[8]) {
+  q_norm_rope<RH>(x, half, p, pos, qs);
 #pragma unroll
   for (int d = 0; d < 64; ++d) x[d] *= p.scale_log2;
 #pragma unroll

@@ -13,6 +13,10 @@ namespace zg {
 struct FlashParams {
   const uint16_t* q;     // bf16 [B,S,Hq,D] raw queries
   const uint16_t* kp;    // bf16 [B,S,Hkv,D] normalised + rotated keys
+  // E4M3 variant (kp8 != null, global layers): the keys as E4M3 codes of
+  // K' * k_scale [B,S,Hkv,D], one byte each; kp is then unused
+  const uint8_t* kp8;
+  float k_scale;
   const uint16_t* v;     // bf16 [B,S,Hkv,D]
   const uint16_t* gate;  // bf16 [B,S,Hq,D] or null
   const float* q_norm_w; // fp32 [D]
@@ -40,6 +44,14 @@ hipError_t launch_k_prologue(const uint16_t* k, const float* w, uint16_t* kout, 
                              int S, int Hkv, long long pos_offset, int rope_half, float eps,
                              const RopeTable& tab, hipStream_t stream,
                              const int* cu_seqlens = nullptr, int nseq = 0);
+
+// The same with K' written as the E4M3 codes of K' * k_scale (one byte per
+// element: product in fp32, clamped to +-448, rounded to nearest even).
+hipError_t launch_k_prologue_fp8(const uint16_t* k, const float* w, uint8_t* kout, float k_scale,
+                                 long long rows, int S, int Hkv, long long pos_offset,
+                                 int rope_half, float eps, const RopeTable& tab,
+                                 hipStream_t stream, const int* cu_seqlens = nullptr,
+                                 int nseq = 0);
 
 hipError_t launch_flash_fwd(const FlashParams& p, hipStream_t stream);
 // The global (window 0) layer's kernel; launch_flash_fwd routes to it.

@@ -252,6 +252,31 @@ int zg_attn_decode_paged_fp8(const zg_attn_params* p,
                              void* out, int num_splits,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- FP8 (E4M3) prefill -------------------------------------------------------
+ * The same page and section (E4M3 forward matrix multiplies with per-tensor
+ * scaling).  The forward of a global layer (window 0, or a window >= seqlen)
+ * with S = K' Q'^T on the FP8 matrix cores: the key prologue writes K' as
+ * the E4M3 codes of K' * k_scale (fp32 product, clamp to +-448, round to
+ * nearest even; k_scale is the caller's per-tensor scale, finite and > 0),
+ * each query head's row q' is quantized with its own power-of-two scale
+ * exactly as in zg_attn_decode_fp8, and the scores are the fp32 sums of the
+ * exact code products times softmax_scale / (s_q k_scale).  The softmax is
+ * fp32 and P V runs on the bf16 matrix cores with V as given, as in
+ * zg_attn_fwd.  K' * k_scale should stay well inside +-448: |K'| is at most
+ * sqrt(head_dim) max|k_norm_w| per element, so k_scale <= 448 / (11.4
+ * max|k_norm_w|) never clamps.
+ *
+ * Arguments as for zg_attn_fwd, except: k_scale; k_out, when not NULL,
+ * receives the uint8 codes [B,S,Hkv,D] (else the workspace holds them, of
+ * zg_attn_fwd_fp8_workspace_size bytes).  A window in (0, seqlen) returns
+ * ZG_ERR_UNSUPPORTED: windowed layers are bound by HBM bytes, which an E4M3
+ * score product does not reduce. */
+size_t zg_attn_fwd_fp8_workspace_size(const zg_attn_params* p);
+int zg_attn_fwd_fp8(const zg_attn_params* p, const void* q, const void* k, const void* v,
+                    const void* gate, const float* q_norm_w, const float* k_norm_w,
+                    float k_scale, void* out, float* lse, void* k_out,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- The projections on either side of the attention ----------------------
  * Page "ZGCM-1:面向数学与智能体搜索的全开源高效基础模型", section 核心方法, and
  * page "7B 打 235B？…", section 🏗️ 架构: hidden size 4096 feeding 32 query
