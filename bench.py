@@ -31,12 +31,20 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0  # dense FP8 MFMA, MI355X spec
+# The E4M3 attention runs Q K^T (half the flops) at the FP8 rate and P V (the
+# other half) at the bf16 rate: at both peaks a layer takes F/2 / 5000 +
+# F/2 / 2500 = F / 3333.3 s per TFLOP F.
+PEAK_MIXED_FP8_TFLOPS = round(2.0 / (1.0 / PEAK_FP8_TFLOPS + 1.0 / PEAK_BF16_TFLOPS), 1)
+# the E4M3 forward's per-tensor K' scale: the keys' RMSNorm bounds |K'| by
+# sqrt(128) max|w_k| (about 15 for the benchmark's weights), so 16 stays
+# inside E4M3's 448
+FP8_K_SCALE = 16.0
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 FLOP_PER_PAIR = 4 * 128     # QK^T and PV, 2 flop per MAC, head dim 128
 BWD_FLOP_PER_PAIR = 10 * 128  # backward: S, dP, dV, dK, dQ products (algorithmic count)
 D = 128
 KW = dict(rope_dim=42, rope_theta=10000.0, rms_eps=1e-6)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flash_fwd_global_256k_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flash_causal_global_256k_traffic.json")
 # sources the flash kernel is compiled from (the traffic summary is keyed by their hash)
 FLASH_SRCS = [os.path.join(ROOT, "global_attention_zg_amd", "csrc", f)
               for f in ("flash_causal.hip", "zg_flash_tile.h", "zg_common.h", "zg_lds.h")]
@@ -73,9 +81,10 @@ def norm_w(torch, key):
 class Layer:
     """Device-resident inputs, outputs and workspace of one forward layer."""
 
-    def __init__(self, torch, bd, tag, layer, B, S, Hq, Hkv, window, gated):
+    def __init__(self, torch, bd, tag, layer, B, S, Hq, Hkv, window, gated, k_scale=None):
         from global_attention_zg_amd import inputs
         self.window = window
+        self.k_scale = k_scale  # set: the E4M3 forward with this per-tensor K' scale
         self.q = dev_tensor(torch, (tag, layer, inputs.T_Q), (B, S, Hq, D))
         self.k = dev_tensor(torch, (tag, layer, inputs.T_K), (B, S, Hkv, D))
         self.v = dev_tensor(torch, (tag, layer, inputs.T_V), (B, S, Hkv, D))
@@ -84,15 +93,21 @@ class Layer:
         self.gk = norm_w(torch, (tag, layer, inputs.T_GK))
         self.out = torch.empty_like(self.q)
         p = bd.make_params(B, S, Hq, Hkv, D, window)
-        self.ws = torch.empty(bd.zg_attn_fwd_workspace_size(p), dtype=torch.uint8, device="cuda")
+        ws = bd.zg_attn_fwd_fp8_workspace_size(p) if k_scale else bd.zg_attn_fwd_workspace_size(p)
+        self.ws = torch.empty(ws, dtype=torch.uint8, device="cuda")
         self.bd = bd
         self.flops = B * Hq * inband_pairs(S, window) * FLOP_PER_PAIR
         self.alg_bytes = (self.q.numel() + self.k.numel() + self.v.numel() + self.out.numel()
                           + (self.g.numel() if gated else 0)) * 2
 
     def __call__(self):
-        self.bd.zg_attn_fwd(self.q, self.k, self.v, self.g, self.gq, self.gk, window=self.window,
-                            out=self.out, workspace=self.ws, **KW)
+        if self.k_scale:
+            self.bd.zg_attn_fwd_fp8(self.q, self.k, self.v, self.g, self.gq, self.gk,
+                                    k_scale=self.k_scale, window=self.window, out=self.out,
+                                    workspace=self.ws, **KW)
+        else:
+            self.bd.zg_attn_fwd(self.q, self.k, self.v, self.g, self.gq, self.gk,
+                                window=self.window, out=self.out, workspace=self.ws, **KW)
 
 
 class BwdLayer:
@@ -178,7 +193,7 @@ def read_traffic():
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("flash_fwd_sha256_16") != flash_source_hash():
+    if t.get("source_sha256_16") != flash_source_hash():
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -441,7 +456,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only",
                     choices=["swa4k", "global16k", "decode", "decode_block", "block_global", "bwd",
-                             "varlen", "proj", "variants", "block_swa"],
+                             "varlen", "proj", "variants", "block_swa", "block_global_fp8"],
                     default=None, help="time one workload only (for profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="with --only: first run a plain 1 GiB device copy, the reference "
@@ -577,6 +592,21 @@ def run_components(torch, bd, only, iters):
                                "tokens_per_s": round(16384 / t, 1),
                                "frac_mfma": round(l3.flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
         del l3
+        # the E4M3 variant on the same inputs: half the flops (Q K^T) at the
+        # FP8 peak, half (P V) at the bf16 peak
+        l8 = Layer(torch, bd, 3, 0, 1, 16384, 32, 8, 0, False, k_scale=FP8_K_SCALE)
+        for _ in range(2):
+            l8()
+        t8, t8_lo, t8_hi = time_stats(torch, l8, max(1, iters // 2))
+        comps["global_16k_fp8"] = {"ms": round(t8 * 1e3, 4), "ms_min": round(t8_lo * 1e3, 4),
+                                   "ms_max": round(t8_hi * 1e3, 4), "k_scale": FP8_K_SCALE,
+                                   "tflops": round(l8.flops / t8 / 1e12, 2),
+                                   "tokens_per_s": round(16384 / t8, 1),
+                                   "peak_mixed_tflops": PEAK_MIXED_FP8_TFLOPS,
+                                   "frac_mixed_peak": round(l8.flops / t8 / 1e12 /
+                                                            PEAK_MIXED_FP8_TFLOPS, 4),
+                                   "speedup_vs_bf16": round(t / t8, 3)}
+        del l8
     torch.cuda.empty_cache()
     if only in (None, "decode"):
         comps.update(decode_components(torch, bd, max(1, iters // 2)))
@@ -599,6 +629,16 @@ def run_components(torch, bd, only, iters):
                                    "hbm_gbs_alg": round(ls.alg_bytes / t / 1e9, 1),
                                    "frac_hbm": round(ls.alg_bytes / t / 1e9 / PEAK_HBM_GBS, 4)}
         del ls
+    if only == "block_global_fp8":
+        log("global layer of the 256K block, E4M3 scores")
+        lg = Layer(torch, bd, 4, 5, 1, 262144, 32, 8, 0, False, k_scale=FP8_K_SCALE)
+        lg()
+        t = time_events(torch, lg, max(1, iters // 2))
+        comps["block_global_256k_fp8"] = {"ms": round(t * 1e3, 3),
+                                          "tflops": round(lg.flops / t / 1e12, 2),
+                                          "frac_mixed_peak": round(lg.flops / t / 1e12 /
+                                                                   PEAK_MIXED_FP8_TFLOPS, 4)}
+        del lg
     if only == "block_global":
         log("global layer of the 256K block")
         lg = Layer(torch, bd, 4, 5, 1, 262144, 32, 8, 0, False)
