@@ -141,6 +141,7 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
   // 1 KB (E4M3) of K'
   constexpr int kCopies = FP8 ? 3 : 4;
   constexpr int kKOps = FP8 ? 2 : 8;  // score-product operands per 32 rows
+  constexpr int kQkMfma = kKOps;      // score MFMAs per 32 rows and 32 keys
   using QOp = typename std::conditional<FP8, i32x8, bf16x8>::type;
   static_assert(kCWaves * 32 * 65 * 4 <= kSmem, "query RoPE rows must fit");
   static_assert(NS >= 3, "copies fly NS - 2 tiles ahead");
@@ -194,8 +195,10 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
   // ---- K'/V staging: wave w fills the 1 KB blocks 2w, 2w + 1 (rows 4n ..
   // 4n + 3) of each 8 KB tile; lane L writes physical chunk L % 16 of row
   // 4n + L / 16 and so fetches the logical chunk the row's swizzle puts there.
-  // E4M3 K' (4 KB tiles of 128-byte rows, chunks swizzled by row % 8): wave w
-  // fills rows 8w .. 8w + 7, lane L physical chunk L % 8 of row 8w + L / 8.
+  // E4M3 K' (4 KB tiles of 128-byte rows; chunk c of row r at physical chunk
+  // c ^ ((r / 2) % 8), so that the 16 rows one 16-lane read group touches
+  // cover all 64 banks): wave w fills rows 8w .. 8w + 7, lane L physical
+  // chunk L % 8 of row 8w + L / 8.
   const long long kvstride = (long long)p.Hkv * kD;  // elements per token
   constexpr int kKEB = FP8 ? 1 : 2;                  // bytes per K' element
   const unsigned char* kbase =
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
   const uint16_t* vbase = p.v + tok0 * kvstride + g * kD;
   const int krow8 = 8 * wv + (lane >> 3);
   const uint32_t krow8_off = (uint32_t)(krow8 * kvstride);
-  const uint32_t kchunk8 = 16u * ((lane & 7) ^ (krow8 & 7));
+  const uint32_t kchunk8 = 16u * ((lane & 7) ^ ((krow8 >> 1) & 7));
   uint32_t row_off[2], kchunk[2];
   int lrow[2];
   const uint32_t vchunk = 16u * ((lane & 15) ^ (((lane >> 4) & 3) << 2));
@@ -248,7 +251,7 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
   // V rows 4h + i/4 at dims 32bd + 16 (group parity) + 4 (i%4) for the
   // transposing loads
   const uint32_t kread_off =
-      FP8 ? qcol * kKRow + ((uint32_t)((4 * half) ^ (qcol & 7)) << 4)
+      FP8 ? qcol * kKRow + ((uint32_t)((4 * half) ^ ((qcol >> 1) & 7)) << 4)
           : qcol * kRowBytes + ((uint32_t)((8 * half) ^ (qcol & 15)) << 4);
   const int gi = lane & 15;
   const int vq = gi >> 2;
@@ -545,6 +548,13 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
     // C
     qk(1);
     vops(sa);
+    // one score MFMA, then its share of the sixteen V reads (so that the
+    // reads spread under the products instead of queueing at the barrier)
+#pragma unroll
+    for (int gg = 0; gg < kQkMfma; ++gg) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 16 / kQkMfma, 0);  // LDS reads
+    }
     __builtin_amdgcn_sched_barrier(0);
     // tile j + 2 has landed for every wave, and no wave still reads tile
     // j + 1's stage, which takes tile j + 1 + NS
