@@ -715,11 +715,47 @@ def decode_block_components(torch, bd, iters):
         t_graph = time_events(torch, graph.replay, iters)
         keys = 16 * 8 * (L + 5 * 128)
         alg = keys * D * 2 * 2
+        # the same step as one launch (zg_attn_decode_block), eager and graphed
+        blk = [dict(q=l.q, k_new=l.kn, v_new=l.vn, k_cache=l.kc, v_cache=l.vc, gate=l.g,
+                    q_norm_w=l.gq, k_norm_w=l.gk, out=torch.empty_like(l.q), ring=l.ring,
+                    window=l.window) for l in layers]
+        arr, _ = bd._block_layers(blk, layers[0].sl)
+        p = bd.make_params(16, 0, 32, 8, D, 0, **KW)
+        ws = torch.zeros(bd.zg_attn_decode_block_workspace_size(p, arr), dtype=torch.uint8,
+                         device="cuda")
+
+        def fused():
+            bd.zg_attn_decode_block(blk, layers[0].sl, workspace=ws, **KW)
+
+        for _ in range(2):
+            fused()
+        torch.cuda.synchronize()
+        # (the one-launch step splits the global layer differently, so its
+        # outputs differ from the per-layer calls' by rounding only)
+        fused_diff = max(float((a.float() - d["out"].float()).abs().max().item())
+                         for a, d in zip(ref, blk))
+        t_fused = time_events(torch, fused, iters)
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fused()
+        torch.cuda.current_stream().wait_stream(side)
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2):
+            fused()
+        g2.replay()
+        torch.cuda.synchronize()
+        t_fused_graph = time_events(torch, g2.replay, iters)
         out[kind] = {"ms_eager": round(t_eager * 1e3, 4), "ms_graph": round(t_graph * 1e3, 4),
                      "tokens_per_s_graph": round(16 / t_graph, 1),
                      "hbm_gbs_alg_graph": round(alg / t_graph / 1e9, 1),
-                     "graph_equals_eager": bool(same)}
-        del graph, layers
+                     "graph_equals_eager": bool(same),
+                     "one_launch": {"ms_eager": round(t_fused * 1e3, 4),
+                                    "ms_graph": round(t_fused_graph * 1e3, 4),
+                                    "tokens_per_s_graph": round(16 / t_fused_graph, 1),
+                                    "hbm_gbs_alg_graph": round(alg / t_fused_graph / 1e9, 1),
+                                    "max_abs_vs_per_layer_calls": round(fused_diff, 6),
+                                    "splits_global": bd.zg_attn_decode_block_num_splits(p, L)}}
+        del graph, g2, layers, blk
         torch.cuda.empty_cache()
     return out
 

@@ -46,6 +46,16 @@ class Params(ctypes.Structure):
     ]
 
 
+class DecodeLayer(ctypes.Structure):
+    """One layer of a block decode step (zg_decode_layer)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("q", "k_new", "v_new", "k_cache", "v_cache",
+                                                "gate", "q_norm_w", "k_norm_w", "out")] + \
+               [("cache_cap", ctypes.c_int), ("ring", ctypes.c_int), ("window", ctypes.c_int)]
+
+
+DECODE_BLOCK_MAX_LAYERS = 6
+
+
 def _load():
     if not os.path.exists(_LIB_PATH):
         raise ImportError(f"{_LIB_PATH} is not built; run global_attention_zg_amd.build")
@@ -74,6 +84,13 @@ def _load():
     lib.zg_attn_decode.restype = i
     lib.zg_attn_decode_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, i, i, vp, vp, vp, vp, i, vp]
     lib.zg_attn_decode_noalloc.restype = i
+    LP = ctypes.POINTER(DecodeLayer)
+    lib.zg_attn_decode_block_num_splits.argtypes = [P, i]
+    lib.zg_attn_decode_block_num_splits.restype = i
+    lib.zg_attn_decode_block_workspace_size.argtypes = [P, i, LP]
+    lib.zg_attn_decode_block_workspace_size.restype = sz
+    lib.zg_attn_decode_block.argtypes = [P, i, LP, vp, vp, sz, vp]
+    lib.zg_attn_decode_block.restype = i
     lib.zg_attn_decode_paged.argtypes = [P, vp, vp, vp, vp, vp, i, vp, i, i, vp, vp, vp, vp, vp,
                                          i, vp, sz, vp]
     lib.zg_attn_decode_paged.restype = i
@@ -112,7 +129,9 @@ EXPORTED = ("zg_attn_fwd_workspace_size", "zg_attn_fwd", "zg_attn_fwd_varlen_wor
             "zg_attn_decode_paged", "zg_attn_bwd_workspace_size", "zg_attn_bwd",
             "zg_linear", "zg_qkvg_proj", "zg_quantize_fp8", "zg_linear_fp8",
             "zg_attn_decode_fp8", "zg_attn_decode_paged_fp8", "zg_attn_decode_noalloc",
-            "zg_attn_fwd_fp8_workspace_size", "zg_attn_fwd_fp8", "zg_attn_strerror")
+            "zg_attn_fwd_fp8_workspace_size", "zg_attn_fwd_fp8",
+            "zg_attn_decode_block_num_splits", "zg_attn_decode_block_workspace_size",
+            "zg_attn_decode_block", "zg_attn_strerror")
 
 
 def library_path() -> str:
@@ -438,6 +457,70 @@ def zg_attn_decode(q, k_new, v_new, k_cache, v_cache, seq_lens, *, ring, window,
                              _ptr(workspace), ws_bytes, _stream(stream))
     _check(st)
     return out
+
+
+def _block_layers(layers, seq_lens):
+    """Check every layer's tensors (as zg_attn_decode does, all layers with
+    the same batch, heads and device) and build the zg_decode_layer array."""
+    if not 1 <= len(layers) <= DECODE_BLOCK_MAX_LAYERS:
+        raise ValueError(f"1 to {DECODE_BLOCK_MAX_LAYERS} layers")
+    arr = (DecodeLayer * len(layers))()
+    first = None
+    a_all = _Args()
+    for i, L in enumerate(layers):
+        q, kc = L["q"], L["k_cache"]
+        _dims(kc, f"layers[{i}].k_cache", 4)
+        a = _check_decode(q, L.get("k_new"), L.get("v_new"), (kc, L["v_cache"]), seq_lens,
+                          L.get("gate"), L["q_norm_w"], L["k_norm_w"], L.get("out"), kc.shape[1],
+                          BF16)
+        a.done()
+        a_all.seen.extend(a.seen)
+        dims = (q.shape[0], q.shape[1], kc.shape[1])
+        if first is None:
+            first = dims
+        elif dims != first:
+            raise ValueError(f"layers[{i}] has (B, Hq, Hkv) {dims}, layer 0 {first}")
+        if L.get("out") is None:
+            L["out"] = torch.empty_like(q)
+        arr[i] = DecodeLayer(q.data_ptr(), None if L.get("k_new") is None else L["k_new"].data_ptr(),
+                             None if L.get("v_new") is None else L["v_new"].data_ptr(),
+                             kc.data_ptr(), L["v_cache"].data_ptr(),
+                             None if L.get("gate") is None else L["gate"].data_ptr(),
+                             L["q_norm_w"].data_ptr(), L["k_norm_w"].data_ptr(), L["out"].data_ptr(),
+                             kc.shape[2], int(L["ring"]), int(L["window"]))
+    a_all.done()
+    return arr, first
+
+
+def zg_attn_decode_block_num_splits(p: Params, cache_cap: int) -> int:
+    return int(_lib.zg_attn_decode_block_num_splits(ctypes.byref(p), cache_cap))
+
+
+def zg_attn_decode_block_workspace_size(p: Params, arr) -> int:
+    return int(_lib.zg_attn_decode_block_workspace_size(ctypes.byref(p), len(arr), arr))
+
+
+def zg_attn_decode_block(layers, seq_lens, *, rope_dim=42, rope_theta=10000.0, rms_eps=1e-6,
+                         softmax_scale=0.0, pos_offset=0, workspace=None, stream=None):
+    """One decode step of up to 6 layers in one launch.  layers: dicts with
+    q, k_new, v_new (or None), k_cache, v_cache, gate (or None), q_norm_w,
+    k_norm_w, ring, window and optionally out (else allocated and stored in
+    the dict).  The workspace (uint8) must be zero-filled before its first
+    step; a new one is.  Returns the list of outputs."""
+    arr, (B, Hq, Hkv) = _block_layers(layers, seq_lens)
+    p = make_params(B, 0, Hq, Hkv, 128, 0, rope_dim, rope_theta, rms_eps, softmax_scale,
+                    pos_offset)
+    nbytes = zg_attn_decode_block_workspace_size(p, arr)
+    if workspace is None:
+        workspace = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=layers[0]["q"].device)
+    else:
+        a = _Args()
+        a.req(workspace, "workspace", U8, None)
+        a.done()
+    st = _lib.zg_attn_decode_block(ctypes.byref(p), len(arr), arr, _ptr(seq_lens), _ptr(workspace),
+                                   workspace.numel(), _stream(stream))
+    _check(st)
+    return [L["out"] for L in layers]
 
 
 def zg_attn_decode_noalloc(q, k_new, v_new, k_cache, v_cache, seq_lens, *, ring, window, gate,

@@ -300,6 +300,61 @@ static int decode_impl(const zg_attn_params* p, const void* q, const void* k_new
   return hip_status(zg::launch_decode(dp, s));
 }
 
+static_assert(zg::kMaxBlockLayers == ZG_DECODE_BLOCK_MAX_LAYERS, "block layer limit");
+
+// Workspace of a block decode step: the ticket words of every layer with
+// several splits (one uint32 per (b, kv head)), then those layers' partials
+// ([B,Hq,ns,D] fp32 followed by [B,Hq,ns,2]), in 256-byte aligned segments.
+struct BlockLayout {
+  int ns[zg::kMaxBlockLayers];
+  size_t tickets[zg::kMaxBlockLayers];
+  size_t part[zg::kMaxBlockLayers];
+  size_t total;
+};
+
+// Splits of one layer in a block decode step: enough that the layer alone
+// has a workgroup per CU (256), each split at least 256 keys.  The block's
+// other layers fill the remaining slots, so fewer, longer splits than a
+// one-layer decode's (auto_splits) pay less per-workgroup overhead.
+static int block_splits(const zg_attn_params* p, int cache_cap) {
+  const long long pairs = (long long)p->batch * p->n_kv_heads;
+  if (pairs <= 0) return 1;
+  long long s = (256 + pairs - 1) / pairs;
+  const long long by_len = (cache_cap + 255) / 256;
+  if (s > by_len) s = by_len;
+  if (s < 1) s = 1;
+  if (s > 64) s = 64;
+  return (int)s;
+}
+
+static int block_layout(const zg_attn_params* p, int n_layers, const zg_decode_layer* layers,
+                        BlockLayout& lay) {
+  int st = check_params(p);
+  if (st != ZG_OK) return st;
+  if (n_layers < 1 || n_layers > ZG_DECODE_BLOCK_MAX_LAYERS || !layers) return ZG_ERR_INVALID;
+  size_t off = 0;
+  for (int l = 0; l < n_layers; ++l) {
+    const zg_decode_layer& L = layers[l];
+    if (L.cache_cap < 1 || (L.ring != 0 && L.ring != 1) || L.window < 0) return ZG_ERR_INVALID;
+    if (L.ring && L.window != L.cache_cap) return ZG_ERR_INVALID;
+    lay.ns[l] = block_splits(p, L.cache_cap);
+    lay.tickets[l] = 0;
+    if (lay.ns[l] > 1) {
+      lay.tickets[l] = off;
+      off += align256((size_t)p->batch * p->n_kv_heads * sizeof(unsigned));
+    }
+  }
+  for (int l = 0; l < n_layers; ++l) {
+    lay.part[l] = 0;
+    if (lay.ns[l] > 1) {
+      lay.part[l] = off;
+      off += align256((size_t)p->batch * p->n_q_heads * lay.ns[l] * (kD + 2) * sizeof(float));
+    }
+  }
+  lay.total = off;
+  return ZG_OK;
+}
+
 // Page-pool arguments: page_size a power of two in [32, 65536], a table of
 // max_pages >= 1 entries per sequence, at least one page, and a slot count
 // (max_pages * page_size) that fits an int.
@@ -497,6 +552,89 @@ int zg_attn_decode(const zg_attn_params* p, const void* q, const void* k_new, co
   return decode_impl(p, q, k_new, v_new, k_cache, v_cache, seq_lens, cache_cap, ring, contiguous,
                      gate, q_norm_w, k_norm_w, out, num_splits, workspace, workspace_bytes,
                      stream);
+}
+
+int zg_attn_decode_block_num_splits(const zg_attn_params* p, int cache_cap) {
+  if (check_params(p) != ZG_OK || cache_cap < 1) return 0;
+  return block_splits(p, cache_cap);
+}
+
+size_t zg_attn_decode_block_workspace_size(const zg_attn_params* p, int n_layers,
+                                           const zg_decode_layer* layers) {
+  BlockLayout lay;
+  if (block_layout(p, n_layers, layers, lay) != ZG_OK) return 0;
+  return lay.total > 256 ? lay.total : 256;
+}
+
+int zg_attn_decode_block(const zg_attn_params* p, int n_layers, const zg_decode_layer* layers,
+                         const int* seq_lens, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  BlockLayout lay;
+  int st = block_layout(p, n_layers, layers, lay);
+  if (st != ZG_OK) return st;
+  if (p->batch == 0) return ZG_OK;
+  if (!seq_lens || (reinterpret_cast<uintptr_t>(seq_lens) & 3u)) return ZG_ERR_INVALID;
+  for (int l = 0; l < n_layers; ++l) {
+    const zg_decode_layer& L = layers[l];
+    if ((L.k_new == nullptr) != (L.v_new == nullptr)) return ZG_ERR_INVALID;
+    if (!L.q || !L.k_cache || !L.v_cache || !L.q_norm_w || !L.k_norm_w || !L.out)
+      return ZG_ERR_INVALID;
+    if (!aligned16(L.q) || !aligned16(L.k_cache) || !aligned16(L.v_cache) ||
+        !aligned16(L.q_norm_w) || !aligned16(L.k_norm_w) || !aligned16(L.out) ||
+        (L.gate && !aligned16(L.gate)) || (L.k_new && (!aligned16(L.k_new) || !aligned16(L.v_new))))
+      return ZG_ERR_INVALID;
+  }
+  if (lay.total > 0) {
+    if (!workspace || workspace_bytes < lay.total) return ZG_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return ZG_ERR_INVALID;
+  }
+  const zg::RopeTable tab = make_rope_table(p);
+  zg::DecodeBlockParams bp{};
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  long long wg = 0;
+  int slot = 0;
+  // layers with several splits (the long ones) are launched first
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int l = 0; l < n_layers; ++l) {
+      if ((lay.ns[l] > 1) != (pass == 0)) continue;
+      const zg_decode_layer& L = layers[l];
+      zg::DecodeParams& dp = bp.layer[slot];
+      dp.q = static_cast<const uint16_t*>(L.q);
+      dp.k_new = static_cast<const uint16_t*>(L.k_new);
+      dp.v_new = static_cast<const uint16_t*>(L.v_new);
+      dp.k_norm_w = L.k_norm_w;
+      dp.k_cache = static_cast<const uint16_t*>(L.k_cache);
+      dp.v_cache = static_cast<const uint16_t*>(L.v_cache);
+      dp.seq_lens = seq_lens;
+      dp.q_norm_w = L.q_norm_w;
+      dp.gate = static_cast<const uint16_t*>(L.gate);
+      dp.out = static_cast<uint16_t*>(L.out);
+      dp.B = p->batch;
+      dp.Hq = p->n_q_heads;
+      dp.Hkv = p->n_kv_heads;
+      dp.cap = L.cache_cap;
+      dp.ring = L.ring;
+      dp.window = L.window;
+      dp.nsplit = lay.ns[l];
+      dp.rope_half = p->rope_dim / 2;
+      dp.scale_log2 = scale_log2(p);
+      dp.eps = p->rms_eps;
+      dp.pos_offset = p->pos_offset;
+      dp.map = zg::CacheMap{nullptr, 0, 0, 0};
+      dp.tab = tab;
+      if (lay.ns[l] > 1) {
+        dp.tickets = reinterpret_cast<unsigned*>(ws + lay.tickets[l]);
+        dp.part_o = reinterpret_cast<float*>(ws + lay.part[l]);
+        dp.part_ml = dp.part_o + (size_t)p->batch * p->n_q_heads * lay.ns[l] * kD;
+      }
+      bp.wg0[slot] = (int)wg;
+      wg += (long long)p->batch * p->n_kv_heads * lay.ns[l];
+      if (wg > 0x7fffffffLL) return ZG_ERR_UNSUPPORTED;
+      ++slot;
+    }
+  }
+  bp.n_layers = n_layers;
+  return hip_status(zg::launch_decode_block(bp, (int)wg, reinterpret_cast<hipStream_t>(stream)));
 }
 
 int zg_attn_decode_noalloc(const zg_attn_params* p, const void* q, const void* k_new,

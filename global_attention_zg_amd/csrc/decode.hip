@@ -51,9 +51,33 @@ constexpr int kRedOBytes = kWaves * kMaxGroup * kD * 4;       // 16384 (inside t
 static_assert(kRedOBytes <= kVtBytes, "reduction area must fit in the V^T area");
 static_assert(16 * (kD + 2 * kMaxRopeHalf) * 4 <= kVtBytes, "append scratch must fit in the V^T area");
 
+// Device-coherent fp32 store and load (agent-scope atomics: write-through,
+// and a read of the coherent copy), for data that one workgroup of a launch
+// hands to another.
+__device__ __forceinline__ void store_coherent(float* q, float v) {
+  __hip_atomic_store(q, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* q) {
+  return __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The workgroup's shared memory (one instance per kernel).
+struct DecodeLds {
+  __attribute__((aligned(16))) unsigned char smem[kVtBytes + kQsBytes + kQnBytes];
+  float red_m[kWaves][16];
+  float red_l[kWaves][16];
+  int last;
+};
+
 // FUSED: the launch has one split per (b, kv head), so this workgroup owns
 // the whole key range: it appends the new token itself, before reading the
 // cache, and writes the normalised, gated output instead of a partial.
+// BLOCK: the workgroup belongs to a launch that decodes a whole block of
+// layers (decode_block_kernel).  A layer with several splits then needs no
+// other launch: the split whose key range holds the new token's slot appends
+// the token before reading the cache, and the last split of each (b, kv
+// head) to finish merges all of its splits' partials (a ticket counter per
+// (b, kv head), left at zero again for the next step).
 // FP8: the cache holds E4M3 codes (one byte per element).  S^T = K' Q'^T
 // runs on the FP8 matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4): the key
 // codes as loaded (32 consecutive bytes of a key row per lane) against the
@@ -61,11 +85,11 @@ static_assert(16 * (kD + 2 * kMaxRopeHalf) * 4 <= kVtBytes, "append scratch must
 // are widened to bf16 in registers, which is exact, for the bf16 PV MFMAs.
 // The launch folds 1 / k_scale into the score scale, each lane multiplies in
 // its head's 1 / s_q, and the epilogue multiplies by 1 / v_scale.
-template <bool PAGED, bool FUSED, bool FP8>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kVtBytes + kQsBytes + kQnBytes];
-  __shared__ float red_m[kWaves][16];
-  __shared__ float red_l[kWaves][16];
+template <bool PAGED, bool FUSED, bool FP8, bool BLOCK>
+__device__ __forceinline__ void decode_split_body(const DecodeParams& p, int bid, DecodeLds& lds) {
+  unsigned char* smem = lds.smem;
+  auto& red_m = lds.red_m;
+  auto& red_l = lds.red_l;
   uint16_t* vt_all = reinterpret_cast<uint16_t*>(smem);
   uint16_t* qs = reinterpret_cast<uint16_t*>(smem + kVtBytes);
   float* qn = reinterpret_cast<float*>(smem + kVtBytes + kQsBytes);
@@ -78,8 +102,8 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
   const int kg = lane >> 4;   // 0..3
   const int grp = p.Hq / p.Hkv;
 
-  const int split = blockIdx.x % p.nsplit;
-  const int bg = blockIdx.x / p.nsplit;
+  const int split = bid % p.nsplit;
+  const int bg = bid / p.nsplit;
   const int g = bg % p.Hkv;
   const int b = bg / p.Hkv;
 
@@ -118,8 +142,16 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
             (uint32_t)p.gate[((long long)b * p.Hq + g * grp) * kD + idx] << 16);
     }
   }
+  // the workgroup that appends the new token (workgroup-uniform)
+  bool append = false;
   if constexpr (FUSED) {
-    if (p.k_new) {
+    append = p.k_new != nullptr;
+  } else if constexpr (BLOCK) {
+    const int slot_new = p.ring ? (L - 1) % p.cap : L - 1;
+    append = p.k_new != nullptr && start <= slot_new && slot_new < end;
+  }
+  if constexpr (FUSED || BLOCK) {
+    if (append) {
       // the new key, normalised and rotated by the same row code as the
       // append kernel, and the new value, into slot len-1 (or its ring
       // slot); 16 lanes per row, only the first row is real.  The V^T area
@@ -451,13 +483,86 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
       p.out[oi] = __builtin_bit_cast(uint16_t, (__bf16)o);
     } else {
       const long long pi = ((long long)b * p.Hq + g * grp + c) * p.nsplit + split;
-      p.part_o[pi * kD + d] = acc;
-      if (d == 0) {
-        p.part_ml[2 * pi] = M;
-        p.part_ml[2 * pi + 1] = lsum;
+      if constexpr (BLOCK) {  // device-coherent stores (see the merge below)
+        store_coherent(p.part_o + pi * kD + d, acc);
+        if (d == 0) {
+          store_coherent(p.part_ml + 2 * pi, M);
+          store_coherent(p.part_ml + 2 * pi + 1, lsum);
+        }
+      } else {
+        p.part_o[pi * kD + d] = acc;
+        if (d == 0) {
+          p.part_ml[2 * pi] = M;
+          p.part_ml[2 * pi + 1] = lsum;
+        }
       }
     }
   }
+  if constexpr (BLOCK && !FUSED) {
+    // Publish the partial and take a ticket; the last split of this (b, kv
+    // head) merges.  The splits run on every XCD, each with its own L2, so
+    // the partials cross workgroups only through device-coherent accesses:
+    // they are stored write-through (agent-scope atomic stores), every
+    // thread waits for its stores to complete before the barrier, and only
+    // then does thread 0 take the ticket; the merging workgroup reads them
+    // with device-coherent loads.  No plain data crosses workgroups, so no
+    // L2 writeback or invalidate (a device-scope fence) is needed: those
+    // cost about a microsecond each, and a step has a thousand workgroups.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+      unsigned* t = p.tickets + (long long)b * p.Hkv + g;
+      const unsigned done = atomicAdd(t, 1u) + 1u;
+      const int last = done == (unsigned)p.nsplit;
+      if (last) atomicExch(t, 0u);
+      lds.last = last;
+    }
+    __syncthreads();
+    if (lds.last) {
+      // the arithmetic of decode_merge_kernel, element by element
+      for (int idx = tid; idx < grp * kD; idx += kThreads) {
+        const int c = idx / kD, d = idx % kD;
+        const long long bh = (long long)b * p.Hq + g * grp + c;
+        const float* ml = p.part_ml + bh * p.nsplit * 2;
+        const float* po = p.part_o + bh * p.nsplit * kD;
+        float M = -INFINITY;
+        for (int s2 = 0; s2 < p.nsplit; ++s2) M = fmaxf(M, load_coherent(ml + 2 * s2));
+        float a = 0.f, lsum = 0.f;
+        for (int s2 = 0; s2 < p.nsplit; ++s2) {
+          const float ms = load_coherent(ml + 2 * s2);
+          const float f = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
+          lsum += f * load_coherent(ml + 2 * s2 + 1);
+          a += f * load_coherent(po + (long long)s2 * kD + d);
+        }
+        const float inv = 1.0f / lsum;
+        float o = a * inv;
+        if (p.gate) o *= sigmoidf_(__uint_as_float((uint32_t)p.gate[bh * kD + d] << 16));
+        p.out[bh * kD + d] = __builtin_bit_cast(uint16_t, (__bf16)o);
+      }
+    }
+  }
+}
+
+template <bool PAGED, bool FUSED, bool FP8>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
+  __shared__ DecodeLds lds;
+  decode_split_body<PAGED, FUSED, FP8, false>(p, blockIdx.x, lds);
+}
+
+// One decode step of a block of layers in a single launch: workgroups
+// [wg0[l], wg0[l + 1]) are layer l's (b, kv head, split) workgroups, bf16
+// contiguous caches.  Each layer's parameters are read in place from the
+// kernel arguments.
+__global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockParams bp) {
+  __shared__ DecodeLds lds;
+  const int bid = blockIdx.x;
+  int l = 0;
+#pragma unroll
+  for (int i = 1; i < kMaxBlockLayers; ++i)
+    if (i < bp.n_layers && bid >= bp.wg0[i]) l = i;
+  const DecodeParams& p = bp.layer[l];
+  if (p.nsplit == 1) decode_split_body<false, true, false, true>(p, bid - bp.wg0[l], lds);
+  else decode_split_body<false, false, false, true>(p, bid - bp.wg0[l], lds);
 }
 
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
@@ -499,6 +604,12 @@ void launch_split(const DecodeParams& p, bool paged, dim3 grid, dim3 block, hipS
 }
 
 }  // namespace
+
+hipError_t launch_decode_block(const DecodeBlockParams& bp, int total_wgs, hipStream_t stream) {
+  if (total_wgs <= 0) return hipSuccess;
+  hipLaunchKernelGGL(decode_block_kernel, dim3((unsigned)total_wgs), dim3(kThreads), 0, stream, bp);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (p.B == 0) return hipSuccess;

@@ -117,9 +117,24 @@ struct DecodeParams {
   // launch folds 1 / k_scale into scale_log2; v_inv = 1 / v_scale.
   float k_scale, v_scale, v_inv;
   int fp8;
+  // block launch (launch_decode_block), several splits: one ticket counter
+  // per (b, kv head)
+  unsigned* tickets;
 };
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
+
+// A decode step of several layers in one launch (bf16 contiguous caches):
+// each layer's full parameters (its split count, workspace segments and, for
+// several splits, its tickets: one counter per (b, kv head), zero between
+// steps), and the first workgroup of each layer (ascending).
+constexpr int kMaxBlockLayers = 6;
+struct DecodeBlockParams {
+  DecodeParams layer[kMaxBlockLayers];
+  int wg0[kMaxBlockLayers];
+  int n_layers;
+};
+hipError_t launch_decode_block(const DecodeBlockParams& bp, int total_wgs, hipStream_t stream);
 
 
 // Projections: C = A B^T with A [M, K] and B [N, K] bf16 row major (row

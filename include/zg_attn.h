@@ -207,6 +207,57 @@ int zg_attn_decode_paged(const zg_attn_params* p,
                          void* out, int num_splits,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- One decode step of a block of layers ------------------------------------
+ * Page "ZGCM-1:面向数学与智能体搜索的全开源高效基础模型", section 前置知识 ›
+ * 滑动窗口注意力(SWA)与混合注意力 (the model repeats a block of five gated
+ * sliding-window layers and one global layer) and the structured-data
+ * table, row "256K 上下文推理 KV 缓存" (decode streams the caches).  One
+ * launch appends the new token and attends for every layer of such a block:
+ * layer l gives the same result as zg_attn_decode with p->window set to
+ * layers[l].window, its tensors, the same seq_lens and num_splits =
+ * zg_attn_decode_block_num_splits(p, layers[l].cache_cap), bit for bit,
+ * including the appended cache rows.  A layer with several splits merges
+ * them inside the launch: the last of its workgroups for each (sequence, kv
+ * head) to finish combines the partials.
+ *
+ * bf16 contiguous caches only.  Layers must not share caches or outputs.
+ * p->window is ignored (each layer brings its own); every other field of p
+ * applies to all layers.  The workspace's ticket words must be zero before
+ * the first step (fill a new workspace with zeros); each step leaves them
+ * zero again, so the same workspace serves every later step, including
+ * replays of a captured graph.  Steps that overlap on one workspace race. */
+#define ZG_DECODE_BLOCK_MAX_LAYERS 6
+typedef struct zg_decode_layer {
+  const void* q;         /* bf16 [B,Hq,D] raw new-token queries */
+  const void* k_new;     /* bf16 [B,Hkv,D] raw new key, or NULL (with v_new NULL) */
+  const void* v_new;     /* bf16 [B,Hkv,D] */
+  void* k_cache;         /* bf16 [B,Hkv,cache_cap,D], updated in place */
+  void* v_cache;         /* bf16 [B,Hkv,cache_cap,D], updated in place */
+  const void* gate;      /* bf16 [B,Hq,D] or NULL */
+  const float* q_norm_w; /* fp32 [D] */
+  const float* k_norm_w; /* fp32 [D] */
+  void* out;             /* bf16 [B,Hq,D] */
+  int cache_cap;         /* >= 1 */
+  int ring;              /* 1: ring of cache_cap slots (then window == cache_cap) */
+  int window;            /* 0 global, else the band */
+} zg_decode_layer;
+
+/* The split count zg_attn_decode_block uses for a layer of this cache
+ * capacity (enough splits for one workgroup per CU from that layer alone,
+ * at least 256 keys each); 0 if p is invalid or cache_cap < 1. */
+int zg_attn_decode_block_num_splits(const zg_attn_params* p, int cache_cap);
+
+/* Bytes of workspace for zg_attn_decode_block (at least 256); 0 if the
+ * arguments are invalid.  The workspace itself must be 256-byte aligned. */
+size_t zg_attn_decode_block_workspace_size(const zg_attn_params* p, int n_layers,
+                                           const zg_decode_layer* layers);
+/* 1 <= n_layers <= ZG_DECODE_BLOCK_MAX_LAYERS; seq_lens int32 [B] on the
+ * device (clamped as in zg_attn_decode).  Errors as zg_attn_decode's, all
+ * reported before the launch. */
+int zg_attn_decode_block(const zg_attn_params* p, int n_layers, const zg_decode_layer* layers,
+                         const int* seq_lens, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
 /* ---- FP8 (E4M3) KV cache ----------------------------------------------------
  * Page "ZGCM-1:面向数学与智能体搜索的全开源高效基础模型", section 前置知识 ›
  * FP8 混合精度训练与 TWEO: E4M3 with per-tensor scaling factors is the
