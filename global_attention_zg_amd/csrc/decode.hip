@@ -544,7 +544,7 @@ __device__ __forceinline__ void decode_split_body(const DecodeParams& p, int bid
 }
 
 template <bool PAGED, bool FUSED, bool FP8>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(DecodeParams p) {
   __shared__ DecodeLds lds;
   decode_split_body<PAGED, FUSED, FP8, false>(p, blockIdx.x, lds);
 }
@@ -553,7 +553,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecodeParams p) 
 // [wg0[l], wg0[l + 1]) are layer l's (b, kv head, split) workgroups, bf16
 // contiguous caches.  Each layer's parameters are read in place from the
 // kernel arguments.
-__global__ __launch_bounds__(kThreads) void decode_block_kernel(DecodeBlockParams bp) {
+__global__ __launch_bounds__(kThreads, 2) void decode_block_kernel(DecodeBlockParams bp) {
   __shared__ DecodeLds lds;
   const int bid = blockIdx.x;
   int l = 0;
