@@ -130,8 +130,11 @@ __device__ __forceinline__ i32x8 join_i32x8(const u32x4& lo, const u32x4& hi) {
 }
 
 // RH: rope_dim / 2 when fixed at compile time (21 or 0), else -1.
-// NS: K'/V tile stages in LDS.  FP8: the E4M3 variant.
-template <int RH, bool PACKED, int NS, bool FP8>
+// NS: K'/V tile stages in LDS.  FP8: the E4M3 variant.  ILV: the V operand
+// reads are interleaved with the second half's score MFMAs (2-4% faster up
+// to 64K keys; at 256K no faster, and the changed pace of the workgroups
+// triples their L2 misses, so long sequences run without it).
+template <int RH, bool PACKED, int NS, bool FP8, bool ILV>
 __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams p, Geo geo) {
   constexpr int kKRow = FP8 ? kD : kRowBytes;  // bytes per K' row in LDS
   constexpr int kKTile = kBN * kKRow;
@@ -550,10 +553,12 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
     vops(sa);
     // one score MFMA, then its share of the sixteen V reads (so that the
     // reads spread under the products instead of queueing at the barrier)
+    if constexpr (ILV) {
 #pragma unroll
-    for (int gg = 0; gg < kQkMfma; ++gg) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 16 / kQkMfma, 0);  // LDS reads
+      for (int gg = 0; gg < kQkMfma; ++gg) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 16 / kQkMfma, 0);  // LDS reads
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     // tile j + 2 has landed for every wave, and no wave still reads tile
@@ -612,10 +617,13 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
 
 constexpr int kCStages = 8;
 
-template <int RH, bool PACKED, bool FP8 = false>
+// Sequences up to this length use the interleaved schedule (ILV).
+constexpr int kIlvMaxS = 65536;
+
+template <int RH, bool PACKED, bool FP8 = false, bool ILV = true>
 void launch_causal(dim3 grid, hipStream_t stream, const FlashParams& p, const Geo& geo) {
-  hipLaunchKernelGGL((flash_causal_kernel<RH, PACKED, kCStages, FP8>), grid, dim3(kCThreads), 0,
-                     stream, p, geo);
+  hipLaunchKernelGGL((flash_causal_kernel<RH, PACKED, kCStages, FP8, ILV>), grid, dim3(kCThreads),
+                     0, stream, p, geo);
 }
 
 }  // namespace
@@ -632,9 +640,11 @@ hipError_t launch_flash_causal(const FlashParams& p, hipStream_t stream) {
   const long long blocks = (long long)geo.n_pos_blocks * geo.n_bhg;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks);
+  const bool ilv = p.S <= kIlvMaxS;
   if (p.kp8) {  // the E4M3 variant: fixed-length batches
     if (p.cu_seqlens) return hipErrorInvalidValue;
-    if (p.rope_half == 21) launch_causal<21, false, true>(grid, stream, p, geo);
+    if (p.rope_half == 21 && !ilv) launch_causal<21, false, true, false>(grid, stream, p, geo);
+    else if (p.rope_half == 21) launch_causal<21, false, true>(grid, stream, p, geo);
     else if (p.rope_half == 0) launch_causal<0, false, true>(grid, stream, p, geo);
     else launch_causal<-1, false, true>(grid, stream, p, geo);
   } else if (p.cu_seqlens) {
@@ -642,7 +652,8 @@ hipError_t launch_flash_causal(const FlashParams& p, hipStream_t stream) {
     else if (p.rope_half == 0) launch_causal<0, true>(grid, stream, p, geo);
     else launch_causal<-1, true>(grid, stream, p, geo);
   } else {
-    if (p.rope_half == 21) launch_causal<21, false>(grid, stream, p, geo);
+    if (p.rope_half == 21 && !ilv) launch_causal<21, false, false, false>(grid, stream, p, geo);
+    else if (p.rope_half == 21) launch_causal<21, false>(grid, stream, p, geo);
     else if (p.rope_half == 0) launch_causal<0, false>(grid, stream, p, geo);
     else launch_causal<-1, false>(grid, stream, p, geo);
   }

@@ -6,6 +6,7 @@ import sys
 import numpy as np
 import pytest
 
+from global_attention_zg_amd import inputs
 from oracle import zg_oracle as orc
 from tests import zg_cases as zc
 
@@ -304,3 +305,16 @@ def test_global_exact_max_fallback(Hq, Hkv):
     ref_out, ref_lse = run_oracle(c, 0, gated=False)
     zc.compare(got["out"], ref_out, f"exact-max path {Hq}/{Hkv}")
     check_lse(got["lse"], ref_lse, f"exact-max path {Hq}/{Hkv}")
+
+
+def test_global_long_sequence_schedule():
+    """Past 65536 keys the global kernel runs its other instruction schedule
+    (the V reads not interleaved with the score products); S = 70001, 8/2
+    heads, sampled rows against the oracle."""
+    S = 70001
+    c = zc.fwd_case(180, 1, S, 8, 2, gated=False)
+    g = run_gpu(c, 0, gated=False)
+    rows = inputs.global_sample_rows(S, 20, S)
+    o, l = run_oracle(c, 0, gated=False, rows=rows)
+    zc.compare(g["out"][:, rows], o, "global S=70001")
+    check_lse(g["lse"][:, :, rows], l, "global S=70001")

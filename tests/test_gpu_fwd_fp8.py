@@ -186,3 +186,15 @@ def test_fwd_fp8_global_16k_sampled_rows():
     zc.compare(g["out"][:, rows], o, "fp8 global 16K")
     check_lse(g["lse"][:, :, rows], l, "fp8 global 16K")
     check_codes(g["codes"], oracle_codes(c, 16.0))
+
+
+def test_fwd_fp8_long_sequence_schedule():
+    """The E4M3 kernel past 65536 keys (the non-interleaved schedule):
+    S = 70001, 8/2 heads, sampled rows against the oracle."""
+    S = 70001
+    c = zc.fwd_case(409, 1, S, 8, 2, gated=False)
+    g = run_gpu(c, 16.0)
+    rows = inputs.global_sample_rows(S, 20, S)
+    o, l = run_oracle(c, 16.0, rows=rows)
+    zc.compare(g["out"][:, rows], o, "fp8 global S=70001")
+    check_lse(g["lse"][:, :, rows], l, "fp8 global S=70001")
