@@ -246,7 +246,7 @@ def reference_peaks(torch, iters=20):
 # The global layer's rows the oracle checks and times at 256K: the fixed rows
 # of the workload's plan plus 55 seeded ones.
 # leading rows of one gated SWA layer of the 256K block in the oracle sample
-SWA_SAMPLE_ROWS = 8192
+SWA_SAMPLE_ROWS = 32768
 
 
 def host_info():
