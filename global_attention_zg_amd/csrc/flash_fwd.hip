@@ -54,19 +54,26 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kBlocksPerWave = 2;  // 1 KB blocks of each tile a wave copies
 constexpr int kCopies = 4;         // its K' + V copies per tile
 // LDS ring per K' and V, K' stages first, then the V stages: three tile
-// stages, copies fly two tiles ahead.  Behind the tiles the query rows are
-// staged (8 KB per wave), and after the loop the fp32 output rows (16 KB per
-// wave) for coalesced stores.
+// stages, copies fly two tiles ahead; 48 KB in all, so that three
+// workgroups fit a CU.  Before the loop the query rows (8 KB per wave) are
+// staged in the stages tiles 1 and 2 will use: waves 0, 1 in K' stages 1, 2,
+// waves 2, 3 in V stages 1, 2.  After the loop the fp32 output rows are
+// staged in two halves of 64 dims (8 KB per wave per half) for coalesced
+// stores.
 constexpr int NS = 3;
 constexpr int kVOff = NS * kTileBytes;
-constexpr int kQRegion = 2 * NS * kTileBytes;
-constexpr int kSmemBanded = kQRegion + kWaves * 32 * kRowBytes;  // 81920
-static_assert(kWaves * 32 * 128 * 4 <= kSmemBanded, "output staging must fit");
+constexpr int kSmemBanded = 2 * NS * kTileBytes;  // 49152
+constexpr int kOutHalfBytes = 32 * 64 * 4;        // a wave's 32 rows x 64 fp32
+static_assert(kWaves * kOutHalfBytes <= kSmemBanded, "output staging must fit");
+// this wave's query-row staging area (8 KB)
+__device__ __forceinline__ int q_stage_off(int w) {
+  return w < 2 ? (1 + w) * kTileBytes : kVOff + (w - 1) * kTileBytes;
+}
 
 // RH: rope_dim / 2 when known at compile time (0 or 21: the rotation runs in
 // registers), -1 for any other rope_dim (rotation through LDS).
 template <int RH, bool PACKED>
-__global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(FlashParams p, Geo geo) {
+__global__ __launch_bounds__(kThreads, 3) void flash_fwd_kernel(FlashParams p, Geo geo) {
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[kSmemBanded];
   lds_u8* smem = (lds_u8*)smem_raw;  // generic -> LDS address space
 
@@ -206,48 +213,33 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(FlashParams p, G
     stg = stg == NS - 1 ? 0 : stg + 1;
   };
 
-  // Start-up: the first two K'/V tiles and, on a gated layer, the gate rows
-  // are requested before the query rows are read, so their latencies overlap.
-  auto first_loads = [&] {
-    gload(t_hi, 0);
-    if (nt > 1) gload(t_hi - 1, 1);
-  };
-  // The query, gate and output rows move in whole 256-byte rows (16 lanes
-  // per row): each wave's 32 query rows go straight to LDS, and lane L
-  // prefetches 8 gate values of row 4k + L/16 (k = 0..7) in the layout of
-  // the coalesced output stores.
+  // Start-up: the query rows and the first K'/V tile are requested together,
+  // so their latencies overlap; tile 1 follows once every wave has read its
+  // query rows out of tile 1's stage.  The query, gate and output rows move
+  // in whole rows: each wave's 32 query rows go straight to LDS (16 lanes per
+  // 256-byte row); after the loop lane L loads 8 gate values of row
+  // 8k + L/8 (k = 0..3), dims 64 r + 8 (L%8) (r = 0, 1), the layout of the
+  // coalesced output stores (held from the start they would cost 32
+  // registers, which three workgroups per CU do not leave).
   const int wrow0 = i0w + (wv / geo.heads_per_wg) * 32;  // this wave's first query row
   const bool gate_pre = p.gate != nullptr;
+  const int qoff = q_stage_off(wvu);
   u32x4 gco[8];
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     const int row = 4 * n + (lane >> 4);
     const long long qr = (tok0 + min(wrow0 + row, S - 1)) * p.Hq + head;
-    dma16(p.q + qr * kD + 8 * ((lane & 15) ^ (row & 15)),
-          lds_addr(smem + kQRegion + wvu * 32 * kRowBytes + n * 1024));
+    dma16(p.q + qr * kD + 8 * ((lane & 15) ^ (row & 15)), lds_addr(smem + qoff + n * 1024));
   }
-  first_loads();
-  if (gate_pre) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const long long gr = (tok0 + min(wrow0 + 4 * k + (lane >> 4), S - 1)) * p.Hq + head;
-      gco[k] = ld16(p.gate + gr * kD + 8 * (lane & 15));
-    }
-  }
+  gload(t_hi, 0);
   // ---- fused query prologue: RMSNorm (+ weight), partial RoPE, -> bf16 B operand
   {
     float x[64];
     // this wave's 32 query rows arrived in LDS (row q%32, chunks swizzled by
-    // row); wait for them: the loads issued after them (4 per tile, 8 of
+    // row); wait for them: the loads issued after them (tile 0's 4, 8 of
     // gate) may still fly
-    if (nt > 1) {
-      if (gate_pre) wait_vm<16>();
-      else wait_vm<8>();
-    } else {
-      if (gate_pre) wait_vm<12>();
-      else wait_vm<4>();
-    }
-    const lds_u8* qr = smem + kQRegion + wv * 32 * kRowBytes + qcol * kRowBytes;
+    wait_vm<4>();
+    const lds_u8* qr = smem + qoff + qcol * kRowBytes;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const bf16x8 v = lds_read_b128(qr + (((8 * half + j) ^ (qcol & 15)) << 4));
@@ -256,19 +248,27 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(FlashParams p, G
     // (the generic rotation goes through a private LDS row per lane, in the
     // wave's own query rows' region, which it has already read, behind the
     // tiles in flight)
-    float* qs = reinterpret_cast<float*>(smem_raw + kQRegion + wv * 32 * kRowBytes) + qcol * 64;
+    float* qs = reinterpret_cast<float*>(smem_raw + qoff) + qcol * 64;
     q_prologue<RH>(x, half, p, p.pos_offset + qi, qs, qf);
   }
-  // tile 0 must have landed (loads issued after it: tile 1's copies, and on
-  // gated layers the eight gate rows)
-  if (gate_pre) {
-    if (nt > 1) sync_tiles<kCopies + 8>();
-    else sync_tiles<8>();
-  } else {
-    if (nt > 1) sync_tiles<kCopies>();
-    else sync_tiles<0>();
-  }
+  // every wave has read its query rows: tile 1 may take its stage
+  lds_barrier();
+  if (nt > 1) gload(t_hi - 1, 1);
+  // tile 0 must have landed (tile 1's copies may fly)
+  if (nt > 1) sync_tiles<kCopies>();
+  else sync_tiles<0>();
   for (int j = 0; j < nt; ++j) step(j, std::true_type{});
+  // the gate rows, in the layout of the coalesced output stores
+  if (gate_pre) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const long long gr = (tok0 + min(wrow0 + 8 * k + (lane >> 3), S - 1)) * p.Hq + head;
+        gco[4 * r + k] = ld16(p.gate + gr * kD + 64 * r + 8 * (lane & 7));
+      }
+    }
+  }
 
   // ---- epilogue: normalise, gate, store (register r of block bd, lane half
   // h -> dim 32 bd + 8 (r/4) + 4 h + r%4: four runs of 4 dims per block)
@@ -276,35 +276,39 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(FlashParams p, G
   const float inv = 1.0f / l_tot;
   if (p.lse && qok && half == 0)
     p.lse[lse0 + head * lse_hs + qi] = (st.m_run * c + __log2f(l_tot)) * kLn2;
-  {
-    // fp32 rows to LDS (the tiles are dead: every wave passed the last
-    // barrier), 16-byte chunk c of row q at chunk c ^ q; then row-coalesced
-    // gate and store, lane L handling dims 8(L%16).. of row 4k + L/16.
-    lds_u8* orow = smem + wv * 32 * 512;
 #pragma unroll
-    for (int bd = 0; bd < 4; ++bd) {
+  for (int r = 0; r < 2; ++r) {
+    // dims 64 r .. 64 r + 63 of the fp32 rows to LDS (the tiles are dead:
+    // every wave passed the last barrier; each wave uses its own 8 KB, in
+    // program order, so no barrier is needed between the halves): 16-byte
+    // chunk c of row q at chunk c ^ (q % 16); then row-coalesced gate and
+    // store, lane L handling dims 64 r + 8 (L%8).. of row 8k + L/8.
+    lds_u8* orow = smem + wv * kOutHalfBytes;
+#pragma unroll
+    for (int bh = 0; bh < 2; ++bh) {
+      const int bd = 2 * r + bh;
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         f32x4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[e] = st.acc[bd][4 * q4 + e] * inv;
-        const int ch = 8 * bd + 2 * q4 + half;
+        const int ch = 8 * bh + 2 * q4 + half;
         *reinterpret_cast<__attribute__((address_space(3))) f32x4*>(
-            orow + qcol * 512 + ((ch ^ qcol) << 4)) = o;
+            orow + qcol * 256 + ((ch ^ (qcol & 15)) << 4)) = o;
       }
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int row = 4 * k + (lane >> 4);
-      const int ch0 = 2 * (lane & 15);
+    for (int k = 0; k < 4; ++k) {
+      const int row = 8 * k + (lane >> 3);
+      const int ch0 = 2 * (lane & 7);
       const f32x4 a = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-          orow + row * 512 + ((ch0 ^ row) << 4));
+          orow + row * 256 + ((ch0 ^ (row & 15)) << 4));
       const f32x4 a2 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-          orow + row * 512 + (((ch0 + 1) ^ row) << 4));
+          orow + row * 256 + (((ch0 + 1) ^ (row & 15)) << 4));
       float o[8] = {a[0], a[1], a[2], a[3], a2[0], a2[1], a2[2], a2[3]};
       if (gate_pre) {
         float gv[8];
-        unpack_bf16x8(gco[k], gv);
+        unpack_bf16x8(gco[4 * r + k], gv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) o[e] *= sigmoidf_(gv[e]);
       }
@@ -313,7 +317,7 @@ __global__ __launch_bounds__(kThreads, 2) void flash_fwd_kernel(FlashParams p, G
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
-        st16(p.out + orw * kD + 8 * (lane & 15), w);
+        st16(p.out + orw * kD + 64 * r + 8 * (lane & 7), w);
       }
     }
   }
