@@ -42,19 +42,20 @@ __global__ __launch_bounds__(256) void k_prologue_kernel(const uint16_t* __restr
   const int lrow = threadIdx.x / 16;
   const int c16 = threadIdx.x % 16;
   // Groups of 16 rows, strided over a fixed grid; each group's rows are
-  // loaded one iteration ahead.  Rows past the end read row rows - 1 (in
-  // bounds, no branch) and store nothing.
+  // loaded two groups ahead (the loop is unrolled by two, so each of the two
+  // buffers is refilled in place as soon as it is consumed).  Rows past the
+  // end read row rows - 1 (in bounds, no branch) and store nothing.
   auto load = [&](long long rg) {
     return ld16(k + min(rg * kRowsPerBlock + lrow, rows - 1) * kD + 8 * c16);
   };
   const RowConsts kc = row_consts(w, rope_half, tab, c16);
-  u32x4 xu = load(blockIdx.x);
-  for (long long rg = blockIdx.x; rg * kRowsPerBlock < rows; rg += gridDim.x) {  // uniform
+  const long long G = gridDim.x;
+  auto body = [&](long long rg, u32x4& xu) __attribute__((always_inline)) {
     const long long row = rg * kRowsPerBlock + lrow;
     const bool ok = row < rows;
     float x[8];
     unpack_bf16x8(xu, x);
-    xu = load(rg + gridDim.x);
+    xu = load(rg + 2 * G);
     // position of the row's token within its sequence
     const long long tok = row / Hkv;
     long long s;
@@ -86,6 +87,12 @@ __global__ __launch_bounds__(256) void k_prologue_kernel(const uint16_t* __restr
       }
     }
     lds_barrier();  // xs and the angle tables are rewritten by the next group
+  };
+  u32x4 xa = load(blockIdx.x);
+  u32x4 xb = load(blockIdx.x + G);
+  for (long long rg = blockIdx.x; rg * kRowsPerBlock < rows; rg += 2 * G) {  // uniform
+    body(rg, xa);
+    if ((rg + G) * kRowsPerBlock < rows) body(rg + G, xb);
   }
 }
 
