@@ -333,15 +333,15 @@ def cpu_baseline(gpu_rows=None):
     fl = 4 * (inband_pairs(512, 128) + inband_pairs(512, 0)) * FLOP_PER_PAIR
     record("tiny_pair_s512", fl, t1 + t2, fl, "both layers in full")
 
-    # gated SWA B4 S4096 32/8: one sequence in full (the four are alike)
+    # gated SWA B4 S4096 32/8, in full
     S = 4096
-    q = _f64_prefix((2, 0, inputs.T_Q), 4 * S, 32, S)
-    k = _f64_prefix((2, 0, inputs.T_K), 4 * S, 8, S)
-    v = _f64_prefix((2, 0, inputs.T_V), 4 * S, 8, S)
-    g = _f64_prefix((2, 0, inputs.T_GATE), 4 * S, 32, S)
+    q = _f64_prefix((2, 0, inputs.T_Q), 4 * S, 32, 4 * S).reshape(4, S, 32, D)
+    k = _f64_prefix((2, 0, inputs.T_K), 4 * S, 8, 4 * S).reshape(4, S, 8, D)
+    v = _f64_prefix((2, 0, inputs.T_V), 4 * S, 8, 4 * S).reshape(4, S, 8, D)
+    g = _f64_prefix((2, 0, inputs.T_GATE), 4 * S, 32, 4 * S).reshape(4, S, 32, D)
     _, t = timed(lambda: orc.attention_fwd(q, k, v, g, gq4(2, 0), gk4(2, 0), window=128, **KW))
-    record("swa_4k_b4", 32 * inband_pairs(S, 128) * FLOP_PER_PAIR, t,
-           4 * 32 * inband_pairs(S, 128) * FLOP_PER_PAIR, "sequence 0 of 4 in full, all 32 heads")
+    fl = 4 * 32 * inband_pairs(S, 128) * FLOP_PER_PAIR
+    record("swa_4k_b4", fl, t, fl, "all 4 sequences in full, all 32 heads")
 
     # global S16384: 64 sampled rows, all 32 heads
     S = 16384
@@ -403,12 +403,13 @@ def cpu_baseline(gpu_rows=None):
                             "rel_rms": float(np.sqrt((d * d).sum() / (ref * ref).sum())),
                             "bound": "max_abs <= 2e-2 and rel_rms <= 1e-2"}
 
-    # decode at 256K, B16: two (sequence, KV head) groups of the global cache
-    # (of 128), and the SWA ring in full
+    # decode at 256K, B16: one (sequence, KV head) group of the global cache
+    # per sequence (16 of 128), and the SWA ring in full
     B, Hq, Hkv, L = 16, 32, 8, 262145
     grp = Hq // Hkv
     tq = 0.0
-    for b, gi in ((0, 0), (15, 7)):
+    pairs = [(b, b % Hkv) for b in range(B)]
+    for b, gi in pairs:
         def slab(t):
             per = L * D
             s0 = (b * Hkv + gi) * per
@@ -422,8 +423,9 @@ def cpu_baseline(gpu_rows=None):
                                               gate_group=None, q_norm_w=gq4(5, 0),
                                               k_norm_w=gk4(5, 0), **KW))
         tq += t
-    record("decode_global_256k", 2 * grp * L * FLOP_PER_PAIR, tq, B * Hq * L * FLOP_PER_PAIR,
-           "2 of the 128 (sequence, KV head) groups, 262145 keys each")
+    record("decode_global_256k", len(pairs) * grp * L * FLOP_PER_PAIR, tq,
+           B * Hq * L * FLOP_PER_PAIR,
+           f"{len(pairs)} of the 128 (sequence, KV head) groups, one per sequence, 262145 keys each")
     qb = zc.bits((5, 1, inputs.T_Q), (B, Hq, D))
     kcb = zc.bits((5, 1, inputs.T_KCACHE), (B, Hkv, 128, D))
     vcb = zc.bits((5, 1, inputs.T_VCACHE), (B, Hkv, 128, D))
