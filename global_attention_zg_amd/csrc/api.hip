@@ -97,7 +97,7 @@ int auto_splits(const zg_attn_params* p, int cache_cap) {
 
 // Backward workspace: 256-byte aligned segments, in this order.
 struct BwdLayout {
-  size_t qp, kp, dO, lse2, dvec, dqp, dkp, part, total;
+  size_t qp, kp, dO, lse2, dvec, part_q, part_k, red, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -113,9 +113,11 @@ BwdLayout bwd_layout(const zg_attn_params* p) {
   l.dO = off;   off += align256(B * S * Hq * kD * 2);
   l.lse2 = off; off += align256(B * Hq * Spad * 4);
   l.dvec = off; off += align256(B * Hq * Spad * 4);
-  l.dqp = off;  off += align256(B * S * Hq * kD * 2);
-  l.dkp = off;  off += align256(B * S * Hkv * kD * 2);
-  l.part = off; off += align256((size_t)2 * zg::kBwdParts * kD * 4);
+  l.part_q = off;
+  off += align256((size_t)zg::bwd_dq_blocks((int)B, (int)S, (int)Hq, (int)Hkv) * kD * 4);
+  l.part_k = off;
+  off += align256((size_t)zg::bwd_dkv_blocks((int)B, (int)S, (int)Hkv) * kD * 4);
+  l.red = off;  off += align256((size_t)2 * zg::kBwdRedChunks * kD * 4);
   l.total = off;
   return l;
 }
@@ -469,10 +471,6 @@ int zg_attn_bwd(const zg_attn_params* p, const void* q, const void* k, const voi
                       : const_cast<uint16_t*>(static_cast<const uint16_t*>(dout));
   float* lse2 = reinterpret_cast<float*>(ws + L.lse2);
   float* dvec = reinterpret_cast<float*>(ws + L.dvec);
-  uint16_t* dqp = reinterpret_cast<uint16_t*>(ws + L.dqp);
-  uint16_t* dkp = reinterpret_cast<uint16_t*>(ws + L.dkp);
-  float* part_q = reinterpret_cast<float*>(ws + L.part);
-  float* part_k = part_q + (size_t)zg::kBwdParts * kD;
   const int B = p->batch, S = p->seqlen, Hq = p->n_q_heads, Hkv = p->n_kv_heads;
   const int Spad = (S + zg::kBwdRowPad - 1) / zg::kBwdRowPad * zg::kBwdRowPad;
   const zg::RopeTable tab = make_rope_table(p);
@@ -498,8 +496,10 @@ int zg_attn_bwd(const zg_attn_params* p, const void* q, const void* k, const voi
   bp.dO = dO;
   bp.lse2 = lse2;
   bp.dvec = dvec;
-  bp.dqp = dqp;
-  bp.dkp = dkp;
+  bp.dq = static_cast<uint16_t*>(dq);
+  bp.dk = static_cast<uint16_t*>(dk);
+  bp.part_q = reinterpret_cast<float*>(ws + L.part_q);
+  bp.part_k = reinterpret_cast<float*>(ws + L.part_k);
   bp.dv = static_cast<uint16_t*>(dv);
   bp.B = B;
   bp.S = S;
@@ -513,23 +513,17 @@ int zg_attn_bwd(const zg_attn_params* p, const void* q, const void* k, const voi
   bp.scale_log2 = scale_log2(p);
   bp.scale = (float)(p->softmax_scale > 0.f ? (double)p->softmax_scale : 1.0 / sqrt((double)kD));
   bp.q = static_cast<const uint16_t*>(q);
+  bp.k = static_cast<const uint16_t*>(k);
   bp.q_norm_w = q_norm_w;
+  bp.k_norm_w = k_norm_w;
   bp.eps = p->rms_eps;
   bp.rope_half = rh;
   bp.pos_offset = p->pos_offset;
   bp.tab = tab;
   if (zg::launch_bwd_dq(bp, s) != hipSuccess) return ZG_ERR_HIP;
   if (zg::launch_bwd_dkv(bp, s) != hipSuccess) return ZG_ERR_HIP;
-  e = zg::launch_prologue_bwd(static_cast<const uint16_t*>(q), dqp, q_norm_w,
-                              static_cast<uint16_t*>(dq), part_q, (long long)B * S * Hq, S, Hq,
-                              p->pos_offset, rh, p->rms_eps, tab, s);
-  if (e != hipSuccess) return ZG_ERR_HIP;
-  e = zg::launch_prologue_bwd(static_cast<const uint16_t*>(k), dkp, k_norm_w,
-                              static_cast<uint16_t*>(dk), part_k, (long long)B * S * Hkv, S, Hkv,
-                              p->pos_offset, rh, p->rms_eps, tab, s);
-  if (e != hipSuccess) return ZG_ERR_HIP;
-  if (zg::launch_reduce_parts(part_q, dq_norm_w, s) != hipSuccess) return ZG_ERR_HIP;
-  return hip_status(zg::launch_reduce_parts(part_k, dk_norm_w, s));
+  return hip_status(zg::launch_reduce_parts(bp, reinterpret_cast<float*>(ws + L.red), dq_norm_w,
+                                              dk_norm_w, s));
 }
 
 int zg_attn_decode_num_splits(const zg_attn_params* p, int cache_cap) {

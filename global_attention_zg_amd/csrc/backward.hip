@@ -18,12 +18,13 @@
 //   bwd_prep_kernel      dO, dG, Dr and LSE*log2(e) per query row
 //   bwd_dq_kernel        query-stationary: dq' for 32 rows per wave; K' and V
 //                        tiles stream through LDS as in the forward; forms
-//                        Q' from q itself (rope_dim 42 or 0) and writes it
+//                        Q' from q itself (rope_dim 42 or 0) and writes it;
+//                        then back through RoPE and RMSNorm to dq
 //   bwd_dkv_kernel       key-stationary: dk' and dv for 32 keys per wave,
 //                        summed over the group's query heads; Q' and dO
-//                        tiles stream through LDS
-//   prologue_bwd_kernel  RoPE transpose + RMSNorm backward per row, and
-//                        per-block partial sums of the weight gradient
+//                        tiles stream through LDS; then dk' back to dk
+//   reduce_*_kernel      the norm-weight gradients from one partial sum per
+//                        workgroup of the two kernels above, in a fixed order
 // Splitting dq' from dk'/dv (each kernel recomputes P) avoids atomics.
 //
 // Tiles in LDS are 32 rows of 256 bytes whose 16-byte chunks are permuted by
@@ -72,6 +73,175 @@ __device__ __forceinline__ TrOffsets tr_offsets(int lane) {
 __device__ __forceinline__ bf16x8 tr_operand(const lds_u8* tile, const TrOffsets& o, int bd, int t) {
   const lds_u8* p0 = tile + o.off[bd] + t * 16 * kRowB;
   return lds_read_tr2(p0, p0 + o.delta);
+}
+
+// ---------------------------------------------------------------------------
+// Back through RoPE and RMSNorm, for the 32 rows one wave owns (one head,
+// consecutive positions pos0, pos0 + 1, ...), 16 lanes per row and 8 dims per
+// lane, four rows per pass:
+//   dx_hat = R(-phi) dy'               (transpose of the rotary pairs)
+//   r = (mean(x^2) + eps)^-1/2
+//   dx = r (w * dx_hat) - x r^3 mean(w * dx_hat * x)
+//   acc += dx_hat * x * r              (this lane's dims of the dw partial)
+// dy' (bf16) sits in the wave's LDS rows `dyl` (256 bytes each, 16-byte
+// chunks at logical ^ swz(row)); a row's rotary angles pass through `ang`
+// (4 rows x 64 floats), where lane t of the row computes angles t and t + 16.
+// Rows at or past nrows read row nrows - 1 and store nothing.  Only this
+// wave touches `dyl` and `ang`.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+__device__ __forceinline__ void row_bwd_wave(const lds_u8* dyl, lds_u8* ang, const uint16_t* x,
+                                             uint16_t* dx, long long rstride, int nrows,
+                                             long long pos0, const float* __restrict__ w,
+                                             int rope_half, float eps, const RopeTable& tab,
+                                             float acc[8]) {
+  const int lane = threadIdx.x & 63, slot = lane >> 4, c16 = lane & 15;
+  float wl[8];
+  {
+    const f32x4 w0 = *reinterpret_cast<const f32x4*>(w + 8 * c16);
+    const f32x4 w1 = *reinterpret_cast<const f32x4*>(w + 8 * c16 + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      wl[e] = w0[e];
+      wl[4 + e] = w1[e];
+    }
+  }
+  const int R = 2 * rope_half;
+  static_assert(kMaxRopeHalf <= 32, "two angles per lane");
+  const uint64_t fr0 = c16 < rope_half ? tab.frac[c16] : 0;
+  const uint64_t fr1 = c16 + 16 < rope_half ? tab.frac[c16 + 16] : 0;
+  u32x4 xu[8];
+#pragma unroll
+  for (int n = 0; n < 8; ++n)
+    xu[n] = ld16(x + (long long)min(4 * n + slot, nrows - 1) * rstride + 8 * c16);
+  lds_f32* cs = reinterpret_cast<lds_f32*>(ang) + 64 * slot;
+  lds_f32* sn = cs + 32;
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const int row = 4 * n + slot;
+    const lds_u8* rp = dyl + row * kRowB;
+    float xv[8], dyv[8];
+    unpack_bf16x8(xu[n], xv);
+    unpack_bf16x8(__builtin_bit_cast(u32x4, lds_read_b128(rp + ((c16 ^ swz(row)) << 4))), dyv);
+    float dh[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) dh[e] = dyv[e];
+    if (R > 0) {
+      const long long pos = pos0 + row;
+      float c0, s0, c1, s1;
+      if (c16 < rope_half) {
+        rope_cos_sin_f(fr0, pos, c0, s0);
+        cs[c16] = c0;
+        sn[c16] = s0;
+      }
+      if (c16 + 16 < rope_half) {
+        rope_cos_sin_f(fr1, pos, c1, s1);
+        cs[c16 + 16] = c1;
+        sn[c16 + 16] = s1;
+      }
+      wave_lds_sync();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 8 * c16 + e;
+        if (d < R) {
+          const int t = d < rope_half ? d : d - rope_half;
+          const int dp = d < rope_half ? d + rope_half : d - rope_half;  // rotary partner
+          const float pv = __uint_as_float(
+              (uint32_t)*reinterpret_cast<const lds_u16*>(rp + (((uint32_t)(dp >> 3) ^ swz(row)) << 4) +
+                                                          2 * (dp & 7))
+              << 16);
+          const float c = cs[t], sg = sn[t];
+          if (d < rope_half) dh[e] = dyv[e] * c + pv * sg;
+          else dh[e] = dyv[e] * c - pv * sg;
+        }
+      }
+      wave_lds_sync();  // the next pass rewrites the angles
+    }
+    float ss = 0.f, dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ss += xv[e] * xv[e];
+      dot += wl[e] * dh[e] * xv[e];
+    }
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) {
+      ss += __shfl_xor(ss, m, 16);
+      dot += __shfl_xor(dot, m, 16);
+    }
+    const float r = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
+    const float k3 = r * r * r * dot * (1.0f / kD);
+    if (row < nrows) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        o[e] = r * wl[e] * dh[e] - xv[e] * k3;
+        acc[e] += dh[e] * xv[e] * r;
+      }
+      u32x4 u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
+      st16(dx + (long long)row * rstride + 8 * c16, u);
+    }
+  }
+}
+
+// Epilogue shared by the dq' and dk'/dv kernels, after their last barrier
+// (every tile read, no copy in flight, so all of the LDS is free): the
+// wave's 32 x 128 gradient accumulators (register r of block bd = dim
+// 32 bd + 8 (r/4) + 4 half + r%4 of row l%32), times `scale` and rounded to
+// bf16, go to its LDS rows; row_bwd_wave takes them to dx; the workgroup's
+// partial sum of dw goes to row part_row of part (numbered by the rows the
+// workgroup covers, not by launch order, so that the sum's order does not
+// depend on the schedule).  LDS: 8 KB of rows and 1 KB of
+// angles per wave, then 4 x 512 bytes for the partials (38 KB in all).
+constexpr int kEpiRows = 0, kEpiAng = 4 * kTileB, kEpiRed = kEpiAng + 4 * 1024;
+constexpr int kEpiBytes = kEpiRed + 4 * kD * 4;
+
+__device__ __forceinline__ void grad_rows_epilogue(lds_u8* smem, const f32x16 (&a)[4], float scale,
+                                                   const uint16_t* x, uint16_t* dx,
+                                                   long long rstride, int nrows, long long pos0,
+                                                   const float* __restrict__ w, int rope_half,
+                                                   float eps, const RopeTable& tab,
+                                                   float* __restrict__ part, long long part_row) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wvu = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qcol = lane & 31, half = lane >> 5;
+  lds_u8* rows = smem + kEpiRows + wvu * kTileB;
+#pragma unroll
+  for (int bd = 0; bd < 4; ++bd)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      u32x2 v;
+      v[0] = pack_bf16x2(a[bd][4 * q4] * scale, a[bd][4 * q4 + 1] * scale);
+      v[1] = pack_bf16x2(a[bd][4 * q4 + 2] * scale, a[bd][4 * q4 + 3] * scale);
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+          rows + qcol * kRowB + (((uint32_t)(4 * bd + q4) ^ swz(qcol)) << 4) + 8 * half) = v;
+    }
+  wave_lds_sync();
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (nrows > 0)
+    row_bwd_wave(rows, smem + kEpiAng + wvu * 1024, x, dx, rstride, nrows, pos0, w, rope_half, eps,
+                 tab, acc);
+  // the wave's four row slots, then the four waves in order
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    acc[e] += __shfl_xor(acc[e], 16);
+    acc[e] += __shfl_xor(acc[e], 32);
+  }
+  lds_f32* red = reinterpret_cast<lds_f32*>(smem + kEpiRed);
+  if (lane < 16) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wvu * kD + 8 * lane + e] = acc[e];
+  }
+  lds_barrier();
+  if (tid < kD)
+    part[part_row * kD + tid] =
+        ((red[tid] + red[kD + tid]) + red[2 * kD + tid]) + red[3 * kD + tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -146,12 +316,6 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 //   dQ^T += K'^T dS^T (A = K'^T by transposing reads; B = dS^T as bf16)
 // K'/V tiles come through a three-stage ring of untracked copies.
 // ---------------------------------------------------------------------------
-struct DqGeo {
-  int hpw;  // query heads per workgroup
-  int ppw;  // query positions per workgroup
-  int n_pos_blocks, hgroups, n_bhg;
-};
-
 // RH = rope_dim / 2 when Q' is formed here (21 or 0), -1 when it is read
 // from p.qp.
 template <int RH>
@@ -336,20 +500,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
     stg = stg == 2 ? 0 : stg + 1;
   }
 
-  // dq' = tau * dQ; register r of block bd -> dim 32bd + 8(r/4) + 4 half + r%4
-  if (qok) {
-    uint16_t* dst = p.dqp + qrow * kD + 4 * half;
-#pragma unroll
-    for (int bd = 0; bd < 4; ++bd)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x16& a = acc[bd];
-        uint2 w;
-        w.x = pack_bf16x2(a[4 * q4] * p.scale, a[4 * q4 + 1] * p.scale);
-        w.y = pack_bf16x2(a[4 * q4 + 2] * p.scale, a[4 * q4 + 3] * p.scale);
-        *reinterpret_cast<uint2*>(dst + 32 * bd + 8 * q4) = w;
-      }
-  }
+  // dq' = tau * dQ, then back through RoPE and RMSNorm to dq
+  static_assert(kEpiBytes <= 2 * NS * kTileB, "the epilogue fits the tile ring");
+  grad_rows_epilogue(smem, acc, p.scale, p.q + (((long long)b * p.S + wrow0) * p.Hq + head) * kD,
+                     p.dq + (((long long)b * p.S + wrow0) * p.Hq + head) * kD,
+                     (long long)p.Hq * kD, min(32, p.S - wrow0), p.pos_offset + wrow0, p.q_norm_w,
+                     p.rope_half, p.eps, p.tab, p.part_q, (long long)pb * geo.n_bhg + bhg);
 }
 
 // ---------------------------------------------------------------------------
@@ -527,169 +683,70 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
   // register r of block bd -> dim 32bd + 8(r/4) + 4 half + r%4 of key kj
   if (kok) {
     const long long krow = ((long long)b * p.S + kj) * p.Hkv + g;
-    uint16_t* dkd = p.dkp + krow * kD + 4 * half;
     uint16_t* dvd = p.dv + krow * kD + 4 * half;
 #pragma unroll
     for (int bd = 0; bd < 4; ++bd)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        uint2 k2;
-        k2.x = pack_bf16x2(dk[bd][4 * q4] * p.scale, dk[bd][4 * q4 + 1] * p.scale);
-        k2.y = pack_bf16x2(dk[bd][4 * q4 + 2] * p.scale, dk[bd][4 * q4 + 3] * p.scale);
-        *reinterpret_cast<uint2*>(dkd + 32 * bd + 8 * q4) = k2;
         uint2 w;
         w.x = pack_bf16x2(dvv[bd][4 * q4], dvv[bd][4 * q4 + 1]);
         w.y = pack_bf16x2(dvv[bd][4 * q4 + 2], dvv[bd][4 * q4 + 3]);
         *reinterpret_cast<uint2*>(dvd + 32 * bd + 8 * q4) = w;
       }
   }
+  // dk' = tau * dK, then back through RoPE and RMSNorm to dk
+  static_assert(kEpiBytes <= 2 * kDkvStage + 4 * kTileB, "the epilogue fits the LDS");
+  const int r0 = kb0 + 32 * wvu;
+  grad_rows_epilogue(smem, dk, p.scale, p.k + (((long long)b * p.S + r0) * p.Hkv + g) * kD,
+                     p.dk + (((long long)b * p.S + r0) * p.Hkv + g) * kD, (long long)p.Hkv * kD,
+                     min(32, p.S - r0), p.pos_offset + r0, p.k_norm_w, p.rope_half, p.eps, p.tab,
+                     p.part_k, bid);
 }
 
 // ---------------------------------------------------------------------------
-// Back through RoPE and RMSNorm, per row of `heads` heads (16 lanes x 8 dims):
-//   dx_hat = R(-phi) dy'               (transpose of the rotary pairs)
-//   r = (mean(x^2) + eps)^-1/2
-//   dx = r (w * dx_hat) - x r^3 mean(w * dx_hat * x)
-//   dw += dx_hat * x * r              (per-block partials, summed later)
-// A fixed grid of kBwdParts blocks (eight per CU; at 87 VGPRs five are
-// resident at a time) strides over groups of 16 rows; each group's x and dy'
-// rows are loaded one iteration ahead, and the barriers wait for LDS only, so
-// those loads stay in flight across them.
+// Norm-weight gradients: dw = the sum of one gradient's n partials (the
+// workgroups of the dq' kernel for q, of the dk'/dv kernel for k) in a fixed
+// order, so that every run gives the same bits.  reduce_chunks_kernel:
+// block (j, which) sums rows j*ch .. j*ch + ch - 1 in order
+// (ch = ceil(n / kBwdRedChunks)); reduce_final_kernel adds the chunk sums of
+// gradient `which` in order (eight runs of 32, then the eight in order).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void prologue_bwd_kernel(const uint16_t* __restrict__ x,
-                                                           const uint16_t* __restrict__ dyp,
-                                                           const float* __restrict__ w,
-                                                           uint16_t* __restrict__ dx,
-                                                           float* __restrict__ part, long long rows,
-                                                           int S, int heads, long long pos_offset,
-                                                           int rope_half, float eps, RopeTable tab) {
-  __shared__ float rowbuf[16][kD + 4];
-  __shared__ float cs[16][kMaxRopeHalf], sn[16][kMaxRopeHalf];
-  const int slot = threadIdx.x >> 4, c16 = threadIdx.x & 15;
-  float wl[8];
-  {
-    const f32x4 w0 = *reinterpret_cast<const f32x4*>(w + 8 * c16);
-    const f32x4 w1 = *reinterpret_cast<const f32x4*>(w + 8 * c16 + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      wl[e] = w0[e];
-      wl[4 + e] = w1[e];
-    }
-  }
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const int R = 2 * rope_half;
-  if (rows == 0) {
-    if (threadIdx.x < kD) part[(long long)blockIdx.x * kD + threadIdx.x] = 0.f;
-    return;
-  }
-  // Rows past the end read row rows - 1 (always in bounds, no branch, so the
-  // next group's loads need no wait before this group's work) and store
-  // nothing; an in-range row reads no other slot's row or angles.
-  auto load = [&](long long rg, u32x4& xu, u32x4& du) {
-    const long long row = min(rg * 16 + slot, rows - 1);
-    xu = ld16(x + row * kD + 8 * c16);
-    du = ld16(dyp + row * kD + 8 * c16);
-  };
-  // this lane's rotary frequencies (angles t = c16 and c16 + 16; rope_half <= 32)
-  static_assert(kMaxRopeHalf <= 32, "two angles per lane");
-  const uint64_t fr0 = c16 < rope_half ? tab.frac[c16] : 0;
-  const uint64_t fr1 = c16 + 16 < rope_half ? tab.frac[c16 + 16] : 0;
-  u32x4 xu, du;
-  load(blockIdx.x, xu, du);
-  for (long long rg = blockIdx.x; rg * 16 < rows; rg += gridDim.x) {  // uniform per block
-    const long long row = rg * 16 + slot;
-    const bool ok = row < rows;
-    float xv[8], dyv[8];
-    unpack_bf16x8(xu, xv);
-    unpack_bf16x8(du, dyv);
-    load(rg + gridDim.x, xu, du);  // the next group's rows
-    const long long pos = pos_offset + (row / heads) % S;
-    if (R > 0) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) rowbuf[slot][8 * c16 + e] = dyv[e];
-      // the block's first row of each position computes its angles, one per
-      // lane t % 16, for all rows of that position
-      if ((int)(row % heads) == 0 || slot == 0) {
-        if (c16 < rope_half) rope_cos_sin_f(fr0, pos, cs[slot][c16], sn[slot][c16]);
-        if (c16 + 16 < rope_half) rope_cos_sin_f(fr1, pos, cs[slot][c16 + 16], sn[slot][c16 + 16]);
-      }
-    }
-    lds_barrier();
-    const int ref = slot - (int)min(row % heads, (long long)slot);
-    float dh[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * c16 + e;
-      dh[e] = dyv[e];
-      if (d < R) {
-        const int t = d < rope_half ? d : d - rope_half;
-        const float c = cs[ref][t], s = sn[ref][t];
-        if (d < rope_half) dh[e] = dyv[e] * c + rowbuf[slot][d + rope_half] * s;
-        else dh[e] = dyv[e] * c - rowbuf[slot][d - rope_half] * s;
-      }
-    }
-    float ss = 0.f, dot = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      ss += xv[e] * xv[e];
-      dot += wl[e] * dh[e] * xv[e];
-    }
-#pragma unroll
-    for (int m = 8; m >= 1; m >>= 1) {
-      ss += __shfl_xor(ss, m, 16);
-      dot += __shfl_xor(dot, m, 16);
-    }
-    const float r = 1.0f / sqrtf(ss * (1.0f / kD) + eps);
-    const float k3 = r * r * r * dot * (1.0f / kD);
-    if (ok) {
-      float o[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        o[e] = r * wl[e] * dh[e] - xv[e] * k3;
-        acc[e] += dh[e] * xv[e] * r;
-      }
-      u32x4 u;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
-      st16(dx + row * kD + 8 * c16, u);
-    }
-    lds_barrier();  // rowbuf and the angle tables are rewritten by the next group
-  }
-  // sum the 16 row slots of the block
-#pragma unroll
-  for (int e = 0; e < 8; ++e) rowbuf[slot][8 * c16 + e] = acc[e];
-  __syncthreads();
-  if (threadIdx.x < kD) {
-    float s = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) s += rowbuf[k][threadIdx.x];
-    part[(long long)blockIdx.x * kD + threadIdx.x] = s;
-  }
-}
-
-// dw[d] = sum over the kBwdParts partials in a fixed order (deterministic):
-// thread (chunk c, dim d) sums partials c*kChunk .. c*kChunk + kChunk - 1 in
-// order, then the eight chunk sums are added in order of c.
-constexpr int kReduceChunks = 8;
-__global__ __launch_bounds__(kReduceChunks * kD) void reduce_parts_kernel(const float* __restrict__ part,
-                                                                          float* __restrict__ dw) {
-  constexpr int kChunk = kBwdParts / kReduceChunks;
-  __shared__ float red[kReduceChunks][kD];
-  const int d = threadIdx.x % kD, c = threadIdx.x / kD;
-  const float* src = part + (long long)c * kChunk * kD + d;
+__global__ __launch_bounds__(kD) void reduce_chunks_kernel(const float* __restrict__ part_q,
+                                                           long long nq,
+                                                           const float* __restrict__ part_k,
+                                                           long long nk, float* __restrict__ red) {
+  const int which = blockIdx.y, j = blockIdx.x, d = threadIdx.x;
+  const float* part = which ? part_k : part_q;
+  const long long n = which ? nk : nq;
+  const long long ch = (n + kBwdRedChunks - 1) / kBwdRedChunks;
+  const long long r0 = j * ch, r1 = min(n, r0 + ch);
   float s = 0.f;
-#pragma unroll 16
-  for (int k = 0; k < kChunk; ++k) s += src[(long long)k * kD];
-  red[c][d] = s;
+  for (long long r = r0; r < r1; ++r) s += part[r * kD + d];
+  red[((long long)which * kBwdRedChunks + j) * kD + d] = s;
+}
+
+constexpr int kRedRuns = 8;
+static_assert(kBwdRedChunks % kRedRuns == 0, "chunk sums split evenly over the runs");
+__global__ __launch_bounds__(kRedRuns * kD) void reduce_final_kernel(const float* __restrict__ red,
+                                                                     float* __restrict__ dwq,
+                                                                     float* __restrict__ dwk) {
+  constexpr int kRun = kBwdRedChunks / kRedRuns;
+  __shared__ float runs[kRedRuns][kD];
+  const int which = blockIdx.x;
+  const int d = threadIdx.x % kD, c = threadIdx.x / kD;
+  const float* src = red + ((long long)which * kBwdRedChunks + c * kRun) * kD + d;
+  float s = 0.f;
+#pragma unroll 8
+  for (int k = 0; k < kRun; ++k) s += src[k * kD];
+  runs[c][d] = s;
   __syncthreads();
   if (c == 0) {
-    float t = red[0][d];
+    float t = runs[0][d];
 #pragma unroll
-    for (int j = 1; j < kReduceChunks; ++j) t += red[j][d];
-    dw[d] = t;
+    for (int j = 1; j < kRedRuns; ++j) t += runs[j][d];
+    (which ? dwk : dwq)[d] = t;
   }
 }
-static_assert(kBwdParts % kReduceChunks == 0, "partials split evenly over the chunks");
 
 }  // namespace
 
@@ -707,13 +764,7 @@ hipError_t launch_bwd_prep(const uint16_t* dy, const uint16_t* y, const uint16_t
 
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream) {
   if (p.B == 0 || p.S == 0) return hipSuccess;
-  const int grp = p.Hq / p.Hkv;
-  DqGeo geo;
-  geo.hpw = grp < 4 ? grp : 4;
-  geo.hgroups = grp / geo.hpw;
-  geo.ppw = 128 / geo.hpw;
-  geo.n_pos_blocks = (p.S + geo.ppw - 1) / geo.ppw;
-  geo.n_bhg = p.B * p.Hkv * geo.hgroups;
+  const DqGeo geo = bwd_dq_geo(p.B, p.S, p.Hq, p.Hkv);
   const long long blocks = (long long)geo.n_pos_blocks * geo.n_bhg;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   if (!bwd_dq_fuses_q(p.rope_half))
@@ -727,22 +778,20 @@ hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream) {
 
 hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t stream) {
   if (p.B == 0 || p.S == 0) return hipSuccess;
-  const long long blocks = (long long)((p.S + 127) / 128) * p.B * p.Hkv;
+  const long long blocks = bwd_dkv_blocks(p.B, p.S, p.Hkv);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_prologue_bwd(const uint16_t* x, const uint16_t* dyp, const float* w, uint16_t* dx,
-                               float* part, long long rows, int S, int heads, long long pos_offset,
-                               int rope_half, float eps, const RopeTable& tab, hipStream_t stream) {
-  hipLaunchKernelGGL(prologue_bwd_kernel, dim3(kBwdParts), dim3(256), 0, stream, x, dyp, w, dx, part,
-                     rows, S, heads, pos_offset, rope_half, eps, tab);
-  return hipGetLastError();
-}
-
-hipError_t launch_reduce_parts(const float* part, float* dw, hipStream_t stream) {
-  hipLaunchKernelGGL(reduce_parts_kernel, dim3(1), dim3(kReduceChunks * kD), 0, stream, part, dw);
+hipError_t launch_reduce_parts(const BwdParams& p, float* red, float* dwq, float* dwk,
+                               hipStream_t stream) {
+  hipLaunchKernelGGL(reduce_chunks_kernel, dim3(kBwdRedChunks, 2), dim3(kD), 0, stream, p.part_q,
+                     bwd_dq_blocks(p.B, p.S, p.Hq, p.Hkv), p.part_k,
+                     bwd_dkv_blocks(p.B, p.S, p.Hkv), red);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(reduce_final_kernel, dim3(2), dim3(kRedRuns * kD), 0, stream, red, dwq, dwk);
   return hipGetLastError();
 }
 

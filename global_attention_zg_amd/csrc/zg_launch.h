@@ -167,6 +167,9 @@ hipError_t launch_quantize_fp8(const uint16_t* x, uint8_t* q, long long n, float
 // Training backward.  K' is recomputed by launch_k_prologue; so is Q', except
 // where the dq' kernel forms it itself (bwd_dq_fuses_q) and writes it to qp
 // for the dk'/dv kernel.  dO = dY * sigmoid(G) (dY itself on an ungated layer).
+// The dq' and dk'/dv kernels finish with the RoPE / RMSNorm backward of their
+// rows: they write dq and dk, and one partial sum of the norm-weight gradient
+// per workgroup (part_q, part_k), which launch_reduce_parts adds up.
 struct BwdParams {
   const uint16_t* qp;   // bf16 [B,S,Hq,D]   Q' (written by the dq' kernel when it fuses Q')
   const uint16_t* kp;   // bf16 [B,S,Hkv,D]  K'
@@ -174,15 +177,18 @@ struct BwdParams {
   const uint16_t* dO;   // bf16 [B,S,Hq,D]
   const float* lse2;    // fp32 [B,Hq,Spad]  LSE * log2(e); +inf for rows >= S
   const float* dvec;    // fp32 [B,Hq,Spad]  rowsum(dY * Y); 0 for rows >= S
-  uint16_t* dqp;        // bf16 [B,S,Hq,D]   dL/dQ'
-  uint16_t* dkp;        // bf16 [B,S,Hkv,D]  dL/dK'
+  uint16_t* dq;         // bf16 [B,S,Hq,D]
+  uint16_t* dk;         // bf16 [B,S,Hkv,D]
   uint16_t* dv;         // bf16 [B,S,Hkv,D]
+  float* part_q;        // fp32 [bwd_dq_blocks][D]   partial d(q_norm_w)
+  float* part_k;        // fp32 [bwd_dkv_blocks][D]  partial d(k_norm_w)
   int B, S, Spad, Hq, Hkv, window;
   float scale_log2;     // softmax scale * log2(e)
   float scale;          // softmax scale
-  // for the dq' kernel's own Q' (bwd_dq_fuses_q): raw q and the prologue
-  const uint16_t* q;    // bf16 [B,S,Hq,D]
+  const uint16_t* q;    // bf16 [B,S,Hq,D]   raw q (the dq' kernel's Q' and RMSNorm backward)
+  const uint16_t* k;    // bf16 [B,S,Hkv,D]  raw k (the dk' RMSNorm backward)
   const float* q_norm_w;
+  const float* k_norm_w;
   float eps;
   int rope_half;
   long long pos_offset;
@@ -195,19 +201,44 @@ inline bool bwd_dq_fuses_q(int rope_half) { return rope_half == 21 || rope_half 
 
 // Row padding of the LSE / D vectors (a multiple of every query block).
 constexpr int kBwdRowPad = 128;
-// Number of per-block partial sums of each RMSNorm weight gradient.
-constexpr int kBwdParts = 2048;
+
+// Grid of the dq' kernel: a workgroup is (batch, kv head, group of hpw query
+// heads, ppw positions), hpw * ppw = 128 rows.
+struct DqGeo {
+  int hpw;  // query heads per workgroup
+  int ppw;  // query positions per workgroup
+  int n_pos_blocks, hgroups, n_bhg;
+};
+inline DqGeo bwd_dq_geo(int B, int S, int Hq, int Hkv) {
+  const int grp = Hq / Hkv;
+  DqGeo geo;
+  geo.hpw = grp < 4 ? grp : 4;
+  geo.hgroups = grp / geo.hpw;
+  geo.ppw = 128 / geo.hpw;
+  geo.n_pos_blocks = (S + geo.ppw - 1) / geo.ppw;
+  geo.n_bhg = B * Hkv * geo.hgroups;
+  return geo;
+}
+inline long long bwd_dq_blocks(int B, int S, int Hq, int Hkv) {
+  const DqGeo g = bwd_dq_geo(B, S, Hq, Hkv);
+  return (long long)g.n_pos_blocks * g.n_bhg;
+}
+// The dk'/dv kernel: a workgroup is (batch, kv head, 128 keys).
+inline long long bwd_dkv_blocks(int B, int S, int Hkv) {
+  return (long long)((S + 127) / 128) * B * Hkv;
+}
+// First stage of the weight-gradient sum: this many fixed chunks of partials
+// per gradient, summed in order, then the chunk sums in order.
+constexpr int kBwdRedChunks = 256;
 
 hipError_t launch_bwd_prep(const uint16_t* dy, const uint16_t* y, const uint16_t* gate,
                            const float* lse, uint16_t* dO, uint16_t* dgate, float* lse2,
                            float* dvec, int B, int S, int Spad, int Hq, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t stream);
-// dx = d(prologue)/dx^T dy' for rows of `heads` heads; partial weight
-// gradients go to part[kBwdParts][D], then dw = sum of the parts.
-hipError_t launch_prologue_bwd(const uint16_t* x, const uint16_t* dyp, const float* w, uint16_t* dx,
-                               float* part, long long rows, int S, int heads, long long pos_offset,
-                               int rope_half, float eps, const RopeTable& tab, hipStream_t stream);
-hipError_t launch_reduce_parts(const float* part, float* dw, hipStream_t stream);
+// d(q_norm_w) and d(k_norm_w) from the kernels' partials, in a fixed order;
+// red: fp32 [2][kBwdRedChunks][D] scratch.
+hipError_t launch_reduce_parts(const BwdParams& p, float* red, float* dwq, float* dwk,
+                               hipStream_t stream);
 
 }  // namespace zg

@@ -379,8 +379,9 @@ int zg_linear_fp8(int M, int N, int K, const void* xq, const void* wq, float out
                   void* y, void* stream);
 
 /* Bytes of device workspace zg_attn_bwd needs (recomputed Q' and K', dO,
- * per-row LSE*log2(e) and rowsum(dY*Y), bf16 dL/dQ' and dL/dK', and the
- * partial sums of the two weight gradients); 0 for an invalid p. */
+ * per-row LSE*log2(e) and rowsum(dY*Y), one partial sum of a weight
+ * gradient per workgroup of the two attention-gradient kernels, and 256
+ * chunk sums of each); 0 for an invalid p. */
 size_t zg_attn_bwd_workspace_size(const zg_attn_params* p);
 
 /* Training backward of one attention layer: the gradients of

@@ -225,9 +225,13 @@ def test_bwd_workspace_size_formula(bd):
     p = bd.make_params(B, S, Hq, Hkv, D, 128)
     a = lambda x: (x + 255) // 256 * 256  # noqa: E731
     spad = (S + 127) // 128 * 128
+    grp = Hq // Hkv
+    hpw = min(grp, 4)                                     # query heads per dq' workgroup
+    n_dq = -(-S // (128 // hpw)) * B * Hkv * (grp // hpw)  # dq' workgroups
+    n_dkv = -(-S // 128) * B * Hkv                         # dk'/dv workgroups
     want = (a(B * S * Hq * D * 2) + a(B * S * Hkv * D * 2) + a(B * S * Hq * D * 2)
-            + 2 * a(B * Hq * spad * 4) + a(B * S * Hq * D * 2) + a(B * S * Hkv * D * 2)
-            + a(2 * 2048 * D * 4))
+            + 2 * a(B * Hq * spad * 4) + a(n_dq * D * 4) + a(n_dkv * D * 4)
+            + a(2 * 256 * D * 4))
     assert bd.zg_attn_bwd_workspace_size(p) == want
     p.head_dim = 64
     assert bd.zg_attn_bwd_workspace_size(p) == 0
