@@ -448,6 +448,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
   const float lse_l = p.lse2[lrw];
   const float d_l = p.dvec[lrw];
   const float c = p.scale_log2;
+  // The loop reads these registers; have their loads land here.  Otherwise
+  // the compiler, which does not see the tile copies, waits for its loads
+  // inside the loop with a vmcnt that also drains the copies just issued.
+  pin(lse_l);
+  pin(d_l);
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    pin(qf[kk]);
+    pin(of[kk]);
+  }
 
   const uint32_t bread = (uint32_t)qcol * kRowB + (((uint32_t)(8 * half) ^ swz(qcol)) << 4);
   const TrOffsets tro = tr_offsets(lane);
@@ -613,6 +623,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
     for (int j = 0; j < 8; ++j)
       kf[j] = __builtin_bit_cast(bf16x8, kok ? ld16(ks + 8 * j) : u32x4{0, 0, 0, 0});
   }
+  // the K' loads land here, not inside the loop (see the dq' kernel)
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pin(kf[j]);
   const lds_u8* vblk = smem + kDkvV + wvu * kTileB;  // this wave's V rows
   const float c = p.scale_log2;
   const uint32_t bread = (uint32_t)qcol * kRowB + (((uint32_t)(8 * half) ^ swz(qcol)) << 4);

@@ -220,9 +220,10 @@ def _bwd(bd, p, **ptrs):
     return bd._lib.zg_attn_bwd(ctypes.byref(p), *args, ptrs.get("ws_bytes", 0), None)
 
 
-def test_bwd_workspace_size_formula(bd):
+@pytest.mark.parametrize("window", [128, 0, 300, 299])
+def test_bwd_workspace_size_formula(bd, window):
     B, S, Hq, Hkv, D = 2, 300, 32, 8, 128
-    p = bd.make_params(B, S, Hq, Hkv, D, 128)
+    p = bd.make_params(B, S, Hq, Hkv, D, window)
     a = lambda x: (x + 255) // 256 * 256  # noqa: E731
     spad = (S + 127) // 128 * 128
     grp = Hq // Hkv
