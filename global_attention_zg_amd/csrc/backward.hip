@@ -382,82 +382,124 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
       }
     }
   };
-  gload(t_hi, 0);
-  if (nt > 1) gload(t_hi - 1, 1);
-
   // ---- this lane's query row: Q' and dO as B operands, lse2 and Dr
   const long long qrow = ((long long)b * p.S + (qok ? qi : 0)) * p.Hq + head;
+  const long long lrw = ((long long)b * p.Hq + head) * p.Spad + qi;  // qi < Spad
+  const float lse_l = p.lse2[lrw];
+  const float d_l = p.dvec[lrw];
+  // The loop reads the registers loaded here; pin_row() has their loads land
+  // before it (and before the tile copies that follow them are issued).
+  // Otherwise the compiler, which does not see the tile copies, waits for
+  // its loads inside the loop with a vmcnt that also drains the copies just
+  // issued.
   bf16x8 qf[8], of[8];
-  {
+  auto pin_row = [&]() __attribute__((always_inline)) {
+    pin(lse_l);
+    pin(d_l);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      pin(qf[kk]);
+      pin(of[kk]);
+    }
+  };
+  if constexpr (RH >= 0) {
+    // Start-up as in the forward: tile 0 and the wave's 32 query rows are
+    // requested together, the rows straight into LDS (16 lanes per 256-byte
+    // row, in the stages tiles 1 and 2 will use: K' stages 1, 2 for waves 0,
+    // 1, V stages 1, 2 for waves 2, 3), the dO half rows into registers.
+    // Q' goes back out through the same LDS rows, row-coalesced; tile 1 is
+    // requested once every wave is done with them.
+    gload(t_hi, 0);
+    lds_u8* qrows = smem + (wvu < 2 ? (1 + wvu) * kTileB : kVOff + (wvu - 1) * kTileB);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int row = 4 * n + (lane >> 4);
+      const long long qr = ((long long)b * p.S + min(wrow0 + row, p.S - 1)) * p.Hq + head;
+      dma16(p.q + qr * kD + 8 * ((uint32_t)(lane & 15) ^ swz(row)), lds_addr(qrows + n * 1024));
+    }
+    {
+      const uint16_t* os = p.dO + qrow * kD + 64 * half;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        of[j] = __builtin_bit_cast(bf16x8, qok ? ld16(os + 8 * j) : u32x4{0, 0, 0, 0});
+    }
+    // Q' of this lane's half row: RMSNorm (+ weight) and the rotary pairs
+    // (t, t + RH), with the same expressions in the same order as the
+    // forward's fused query prologue, so that these are the bits the forward
+    // multiplied.  Written to p.qp for the dk'/dv kernel.
+    wait_vm<8>();  // the query rows (the dO loads after them may fly)
+    const lds_u8* qr = qrows + qcol * kRowB;
+    float x[64];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bf16x8 v = lds_read_b128(qr + (((uint32_t)(8 * half + j) ^ swz(qcol)) << 4));
+      unpack_bf16x8(__builtin_bit_cast(u32x4, v), x + 8 * j);
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int d = 0; d < 64; ++d) ss += x[d] * x[d];
+    ss = pair_sum32(ss);
+    const float r = 1.0f / sqrtf(ss * (1.0f / kD) + p.eps);
+    const float* wsrc = p.q_norm_w + 64 * half;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const u32x4 w4 = ld16(wsrc + 4 * j);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[4 * j + i] *= r * __uint_as_float(w4[i]);
+    }
+    if (RH > 0 && half == 0) {
+      const long long pos = p.pos_offset + qi;
+      float y[2 * (RH > 0 ? RH : 1)];
+#pragma unroll
+      for (int t = 0; t < RH; ++t) {
+        float cc, sn;
+        rope_cos_sin(p.tab, t, pos, cc, sn);
+        y[t] = x[t] * cc - x[t + RH] * sn;
+        y[t + RH] = x[t + RH] * cc + x[t] * sn;
+      }
+#pragma unroll
+      for (int d = 0; d < 2 * RH; ++d) x[d] = y[d];
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qf[kk] = pack_bf16x8(x + 8 * kk);
+    // Q' over the query half rows in LDS (each lane rewrites what it read),
+    // then out row-coalesced: lane L stores the chunk it would have copied
+    lds_u8* qw = qrows + qcol * kRowB;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(
+          qw + (((uint32_t)(8 * half + j) ^ swz(qcol)) << 4)) = qf[j];
+    wave_lds_sync();
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+      const int row = 4 * n + (lane >> 4);
+      if (wrow0 + row < p.S) {
+        const u32x4 v = __builtin_bit_cast(
+            u32x4, lds_read_b128(qrows + row * kRowB + ((uint32_t)(lane & 15) << 4)));
+        uint16_t* dst = const_cast<uint16_t*>(p.qp) +
+                        (((long long)b * p.S + wrow0 + row) * p.Hq + head) * kD +
+                        8 * ((uint32_t)(lane & 15) ^ swz(row));
+        st16(dst, v);
+      }
+    }
+    pin_row();
+    // every wave is done with its query rows: tile 1 may take their stage
+    lds_barrier();
+    if (nt > 1) gload(t_hi - 1, 1);
+  } else {
     const uint16_t* os = p.dO + qrow * kD + 64 * half;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       of[j] = __builtin_bit_cast(bf16x8, qok ? ld16(os + 8 * j) : u32x4{0, 0, 0, 0});
-    if constexpr (RH >= 0) {
-      // Q' of this lane's half row: RMSNorm (+ weight) and the rotary pairs
-      // (t, t + RH), with the same expressions in the same order as the
-      // forward's fused query prologue, so that these are the bits the
-      // forward multiplied.  Written to p.qp for the dk'/dv kernel.
-      const uint16_t* src = p.q + qrow * kD + 64 * half;
-      float x[64];
+    const uint16_t* qs = p.qp + qrow * kD + 64 * half;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const u32x4 u = qok ? ld16(src + 8 * j) : u32x4{0, 0, 0, 0};
-        unpack_bf16x8(u, x + 8 * j);
-      }
-      float ss = 0.f;
-#pragma unroll
-      for (int d = 0; d < 64; ++d) ss += x[d] * x[d];
-      ss = pair_sum32(ss);
-      const float r = 1.0f / sqrtf(ss * (1.0f / kD) + p.eps);
-      const float* wsrc = p.q_norm_w + 64 * half;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const u32x4 w4 = ld16(wsrc + 4 * j);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) x[4 * j + i] *= r * __uint_as_float(w4[i]);
-      }
-      if (RH > 0 && half == 0) {
-        const long long pos = p.pos_offset + qi;
-        float y[2 * (RH > 0 ? RH : 1)];
-#pragma unroll
-        for (int t = 0; t < RH; ++t) {
-          float cc, sn;
-          rope_cos_sin(p.tab, t, pos, cc, sn);
-          y[t] = x[t] * cc - x[t + RH] * sn;
-          y[t + RH] = x[t + RH] * cc + x[t] * sn;
-        }
-#pragma unroll
-        for (int d = 0; d < 2 * RH; ++d) x[d] = y[d];
-      }
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) qf[kk] = pack_bf16x8(x + 8 * kk);
-      if (qok) {
-        uint16_t* dst = const_cast<uint16_t*>(p.qp) + qrow * kD + 64 * half;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) st16(dst + 8 * j, __builtin_bit_cast(u32x4, qf[j]));
-      }
-    } else {
-      const uint16_t* qs = p.qp + qrow * kD + 64 * half;
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        qf[j] = __builtin_bit_cast(bf16x8, qok ? ld16(qs + 8 * j) : u32x4{0, 0, 0, 0});
-    }
+    for (int j = 0; j < 8; ++j)
+      qf[j] = __builtin_bit_cast(bf16x8, qok ? ld16(qs + 8 * j) : u32x4{0, 0, 0, 0});
+    pin_row();
+    gload(t_hi, 0);
+    if (nt > 1) gload(t_hi - 1, 1);
   }
-  const long long lrw = ((long long)b * p.Hq + head) * p.Spad + qi;  // qi < Spad
-  const float lse_l = p.lse2[lrw];
-  const float d_l = p.dvec[lrw];
   const float c = p.scale_log2;
-  // The loop reads these registers; have their loads land here.  Otherwise
-  // the compiler, which does not see the tile copies, waits for its loads
-  // inside the loop with a vmcnt that also drains the copies just issued.
-  pin(lse_l);
-  pin(d_l);
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    pin(qf[kk]);
-    pin(of[kk]);
-  }
 
   const uint32_t bread = (uint32_t)qcol * kRowB + (((uint32_t)(8 * half) ^ swz(qcol)) << 4);
   const TrOffsets tro = tr_offsets(lane);
