@@ -518,34 +518,41 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
     if (issue) gload(t - 2, stg == 0 ? 2 : stg - 1);
     const lds_u8* kt = smem + stg * kTileB;
     const lds_u8* vt = kt + kVOff;
-    f32x16 sT = f32x16{}, dpT = f32x16{};
+    // With fewer than four heads per workgroup its waves hold different
+    // query rows; a wave that sees none of the tile's keys (its rows lie
+    // wholly before the tile or a band past it) has only zero products
+    // to add and skips them.
+    const bool active = t * 32 <= wrow0 + 31 && wrow0 - (t * 32 + 31) < lim;
+    if (active) {
+      f32x16 sT = f32x16{}, dpT = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      sT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(kt + (bread ^ (uint32_t)(kk << 4))),
-                                                   qf[kk], sT, 0, 0, 0);
+      for (int kk = 0; kk < 8; ++kk)
+        sT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(kt + (bread ^ (uint32_t)(kk << 4))),
+                                                     qf[kk], sT, 0, 0, 0);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      dpT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(vt + (bread ^ (uint32_t)(kk << 4))),
-                                                    of[kk], dpT, 0, 0, 0);
-    // register r: key t*32 + 8(r/4) + 4 half + r%4 of this lane's query
-    const bool masked = banded || t * 32 + 31 > wrow0;
-    float ds[16];
+      for (int kk = 0; kk < 8; ++kk)
+        dpT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(vt + (bread ^ (uint32_t)(kk << 4))),
+                                                      of[kk], dpT, 0, 0, 0);
+      // register r: key t*32 + 8(r/4) + 4 half + r%4 of this lane's query
+      const bool masked = banded || t * 32 + 31 > wrow0;
+      float ds[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float pr = fast_exp2(__builtin_fmaf(sT[r], c, -lse_l));
-      if (masked) {
-        const int dq = qi - (t * 32 + 8 * (r >> 2) + 4 * half + (r & 3));
-        pr = (unsigned)dq < (unsigned)lim ? pr : 0.f;
+      for (int r = 0; r < 16; ++r) {
+        float pr = fast_exp2(__builtin_fmaf(sT[r], c, -lse_l));
+        if (masked) {
+          const int dq = qi - (t * 32 + 8 * (r >> 2) + 4 * half + (r & 3));
+          pr = (unsigned)dq < (unsigned)lim ? pr : 0.f;
+        }
+        ds[r] = pr * (dpT[r] - d_l);
       }
-      ds[r] = pr * (dpT[r] - d_l);
+      const bf16x8 dsf0 = pack_bf16x8(ds), dsf1 = pack_bf16x8(ds + 8);
+#pragma unroll
+      for (int bd = 0; bd < 4; ++bd)
+        acc[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(kt, tro, bd, 0), dsf0, acc[bd], 0, 0, 0);
+#pragma unroll
+      for (int bd = 0; bd < 4; ++bd)
+        acc[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(kt, tro, bd, 1), dsf1, acc[bd], 0, 0, 0);
     }
-    const bf16x8 dsf0 = pack_bf16x8(ds), dsf1 = pack_bf16x8(ds + 8);
-#pragma unroll
-    for (int bd = 0; bd < 4; ++bd)
-      acc[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(kt, tro, bd, 0), dsf0, acc[bd], 0, 0, 0);
-#pragma unroll
-    for (int bd = 0; bd < 4; ++bd)
-      acc[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(kt, tro, bd, 1), dsf1, acc[bd], 0, 0, 0);
     // tile j+1 must have landed; tile j+2's four copies may still fly
     if (issue) sync_tiles<4>();
     else sync_tiles<0>();
@@ -683,51 +690,59 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
   if (ntile > 1) sync_tiles<5>();
   else sync_tiles<0>();
 
+  const int kw = kb0 + 32 * wvu;  // the wave's first key
   for (int i = 0; i < ntile; ++i) {
     const int stg = i & 1;
     const int q0 = (qt_lo + nq - 1 - i / grp) * 32;
     const lds_u8* qt = smem + stg * kDkvStage;
     const lds_u8* ot = qt + kTileB;
     const lds_u8* lt = qt + 2 * kTileB;
-    f32x16 s = f32x16{}, dp = f32x16{};
+    // A wave whose 32 keys see none of the tile's 32 queries (on a band, a
+    // third of the visits: the block's visits span its 128 keys' band) has
+    // only zero products to add; it skips them and leaves its SIMD to the
+    // other workgroup, but still takes part in the copies and barriers.
+    const bool active = q0 + 31 >= kw && q0 - (kw + 31) < lim;
+    if (active) {
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(qt + (bread ^ (uint32_t)(kk << 4))),
-                                                  kf[kk], s, 0, 0, 0);
+      for (int kk = 0; kk < 8; ++kk)
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(qt + (bread ^ (uint32_t)(kk << 4))),
+                                                    kf[kk], s, 0, 0, 0);
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk)
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(ot + (bread ^ (uint32_t)(kk << 4))),
-                                                   lds_read_b128(vblk + (bread ^ (uint32_t)(kk << 4))),
-                                                   dp, 0, 0, 0);
-    // register r: query q0 + 8(r/4) + 4 half + r%4, key kj
-    float pr[16], ds[16];
+      for (int kk = 0; kk < 8; ++kk)
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(ot + (bread ^ (uint32_t)(kk << 4))),
+                                                     lds_read_b128(vblk + (bread ^ (uint32_t)(kk << 4))),
+                                                     dp, 0, 0, 0);
+      // register r: query q0 + 8(r/4) + 4 half + r%4, key kj
+      float pr[16], ds[16];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const f32x4 l4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-          lt + 4 * (8 * m + 4 * half));
-      const f32x4 d4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-          lt + 128 + 4 * (8 * m + 4 * half));
+      for (int m = 0; m < 4; ++m) {
+        const f32x4 l4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+            lt + 4 * (8 * m + 4 * half));
+        const f32x4 d4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+            lt + 128 + 4 * (8 * m + 4 * half));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * m + e;
-        const int dq = q0 + 8 * m + 4 * half + e - kj;
-        float x = fast_exp2(__builtin_fmaf(s[r], c, -l4[e]));
-        x = (unsigned)dq < (unsigned)lim ? x : 0.f;
-        pr[r] = x;
-        ds[r] = x * (dp[r] - d4[e]);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * m + e;
+          const int dq = q0 + 8 * m + 4 * half + e - kj;
+          float x = fast_exp2(__builtin_fmaf(s[r], c, -l4[e]));
+          x = (unsigned)dq < (unsigned)lim ? x : 0.f;
+          pr[r] = x;
+          ds[r] = x * (dp[r] - d4[e]);
+        }
       }
-    }
-    const bf16x8 pf0 = pack_bf16x8(pr), pf1 = pack_bf16x8(pr + 8);
-    const bf16x8 df0 = pack_bf16x8(ds), df1 = pack_bf16x8(ds + 8);
+      const bf16x8 pf0 = pack_bf16x8(pr), pf1 = pack_bf16x8(pr + 8);
+      const bf16x8 df0 = pack_bf16x8(ds), df1 = pack_bf16x8(ds + 8);
 #pragma unroll
-    for (int bd = 0; bd < 4; ++bd) {
-      dvv[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(ot, tro, bd, 0), pf0, dvv[bd], 0, 0, 0);
-      dk[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(qt, tro, bd, 0), df0, dk[bd], 0, 0, 0);
-    }
+      for (int bd = 0; bd < 4; ++bd) {
+        dvv[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(ot, tro, bd, 0), pf0, dvv[bd], 0, 0, 0);
+        dk[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(qt, tro, bd, 0), df0, dk[bd], 0, 0, 0);
+      }
 #pragma unroll
-    for (int bd = 0; bd < 4; ++bd) {
-      dvv[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(ot, tro, bd, 1), pf1, dvv[bd], 0, 0, 0);
-      dk[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(qt, tro, bd, 1), df1, dk[bd], 0, 0, 0);
+      for (int bd = 0; bd < 4; ++bd) {
+        dvv[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(ot, tro, bd, 1), pf1, dvv[bd], 0, 0, 0);
+        dk[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(qt, tro, bd, 1), df1, dk[bd], 0, 0, 0);
+      }
     }
     // tile i+1 has landed and every wave is done with tile i; then tile i+2
     // goes into tile i's stage
