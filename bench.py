@@ -140,8 +140,27 @@ class BwdLayer:
                             window=f.window, workspace=self.ws, **self.grads, **KW)
 
 
+WARM_S = 0.1
+
+
+def warm_up(torch, fn, seconds=WARM_S):
+    """Run fn back to back, in batches of 8 between synchronisations, for
+    about `seconds`: the timed calls that follow then run at the clock of
+    sustained work.  After an idle spell the GPU takes ~15 calls of a 2 ms
+    kernel to come back up to speed, which a few warm-up calls would leave
+    inside the timed region."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+
+
 def time_events(torch, fn, iters):
-    """Average duration of fn() on the current stream, by HIP events."""
+    """Average duration of fn() on the current stream, by HIP events, after
+    warm_up."""
+    warm_up(torch, fn)
     st = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(iters)]
@@ -157,7 +176,8 @@ def time_stats(torch, fn, iters, flush=None):
     """Median, min and max duration of fn() by HIP events on the current
     stream. With `flush` (a device buffer larger than L2 plus the MALL), the
     buffer is rewritten before every timed call, outside the events, so that
-    each call starts with cold caches."""
+    each call starts with cold caches.  warm_up runs first."""
+    warm_up(torch, fn)
     st = torch.cuda.current_stream()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(iters)]
