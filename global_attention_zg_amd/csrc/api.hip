@@ -476,19 +476,29 @@ int zg_attn_bwd(const zg_attn_params* p, const void* q, const void* k, const voi
   const zg::RopeTable tab = make_rope_table(p);
   const int rh = p->rope_dim / 2;
 
+  // K' is recomputed in the prep launch
+  zg::KPrimeJob kj{};
+  kj.k = static_cast<const uint16_t*>(k);
+  kj.w = k_norm_w;
+  kj.kout = kp;
+  kj.rows = (long long)B * S * Hkv;
+  kj.S = S;
+  kj.Hkv = Hkv;
+  kj.pos_offset = p->pos_offset;
+  kj.rope_half = rh;
+  kj.eps = p->rms_eps;
+  kj.tab = tab;
   hipError_t e = zg::launch_bwd_prep(static_cast<const uint16_t*>(dout),
                                      static_cast<const uint16_t*>(out),
                                      static_cast<const uint16_t*>(gate), lse, dO,
-                                     static_cast<uint16_t*>(dgate), lse2, dvec, B, S, Spad, Hq, s);
+                                     static_cast<uint16_t*>(dgate), lse2, dvec, B, S, Spad, Hq, kj,
+                                     s);
   if (e != hipSuccess) return ZG_ERR_HIP;
   if (!zg::bwd_dq_fuses_q(rh)) {  // else the dq' kernel forms Q' itself
     e = zg::launch_k_prologue(static_cast<const uint16_t*>(q), q_norm_w, qp, (long long)B * S * Hq,
                               S, Hq, p->pos_offset, rh, p->rms_eps, tab, s);
     if (e != hipSuccess) return ZG_ERR_HIP;
   }
-  e = zg::launch_k_prologue(static_cast<const uint16_t*>(k), k_norm_w, kp, (long long)B * S * Hkv,
-                            S, Hkv, p->pos_offset, rh, p->rms_eps, tab, s);
-  if (e != hipSuccess) return ZG_ERR_HIP;
   zg::BwdParams bp{};
   bp.qp = qp;
   bp.kp = kp;

@@ -37,6 +37,7 @@
 #include "zg_common.h"
 #include "zg_launch.h"
 #include "zg_lds.h"
+#include "zg_norm_rope.h"
 
 namespace zg {
 
@@ -249,6 +250,9 @@ __device__ __forceinline__ void grad_rows_epilogue(lds_u8* smem, const f32x16 (&
 // lse2 = LSE*log2(e).  Rows are enumerated over (b, h, s < Spad); rows past S
 // get lse2 = +inf and Dr = 0, so that they contribute P = 0 downstream.
 // 16 lanes per row, 8 dims each.
+// The same launch recomputes K' (the first kp.blocks blocks, 16 key rows
+// each, with the key prologue's row code and so its bits): both passes are
+// bound by HBM, and the small K' pass alone would run well below it.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restrict__ dy,
                                                        const uint16_t* __restrict__ y,
@@ -258,8 +262,29 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
                                                        uint16_t* __restrict__ dgate,
                                                        float* __restrict__ lse2,
                                                        float* __restrict__ dvec, int B, int S,
-                                                       int Spad, int Hq) {
-  const long long row = (long long)blockIdx.x * 16 + (threadIdx.x >> 4);
+                                                       int Spad, int Hq, KPrimeJob kp) {
+  if ((long long)blockIdx.x < kp.blocks) {
+    // K' of key rows 16 b .. 16 b + 15 (rows are (batch, position, kv head))
+    __shared__ float xs[16][kD];
+    __shared__ float cs[16][kMaxRopeHalf], sn[16][kMaxRopeHalf];
+    const int lrow = threadIdx.x / 16, c16 = threadIdx.x % 16;
+    const long long row = (long long)blockIdx.x * 16 + lrow;
+    float x[8];
+    unpack_bf16x8(ld16(kp.k + min(row, kp.rows - 1) * kD + 8 * c16), x);
+    const RowConsts kc = row_consts(kp.w, kp.rope_half, kp.tab, c16);
+    const long long s = (row / kp.Hkv) % kp.S;
+    const int ref = lrow - (int)min(row % kp.Hkv, (long long)lrow);
+    norm_rope_row(x, c16, kc, kp.eps, kp.rope_half, kp.pos_offset + s, xs[lrow], ref == lrow,
+                  cs[lrow], sn[lrow], cs[ref], sn[ref]);
+    if (row < kp.rows) {
+      u32x4 o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+      st16(kp.kout + row * kD + 8 * c16, o);
+    }
+    return;
+  }
+  const long long row = ((long long)blockIdx.x - kp.blocks) * 16 + (threadIdx.x >> 4);
   const int c16 = threadIdx.x & 15;
   if (row >= (long long)B * Hq * Spad) return;  // whole 16-lane groups leave together
   const int s = (int)(row % Spad);
@@ -822,13 +847,15 @@ __global__ __launch_bounds__(kRedRuns * kD) void reduce_final_kernel(const float
 
 hipError_t launch_bwd_prep(const uint16_t* dy, const uint16_t* y, const uint16_t* gate,
                            const float* lse, uint16_t* dO, uint16_t* dgate, float* lse2,
-                           float* dvec, int B, int S, int Spad, int Hq, hipStream_t stream) {
+                           float* dvec, int B, int S, int Spad, int Hq, KPrimeJob kp,
+                           hipStream_t stream) {
   const long long rows = (long long)B * Hq * Spad;
-  if (rows == 0) return hipSuccess;
-  const long long blocks = (rows + 15) / 16;
+  kp.blocks = (kp.rows + 15) / 16;
+  const long long blocks = kp.blocks + (rows + 15) / 16;
+  if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, dy, y, gate, lse,
-                     dO, dgate, lse2, dvec, B, S, Spad, Hq);
+                     dO, dgate, lse2, dvec, B, S, Spad, Hq, kp);
   return hipGetLastError();
 }
 

@@ -231,9 +231,25 @@ inline long long bwd_dkv_blocks(int B, int S, int Hkv) {
 // per gradient, summed in order, then the chunk sums in order.
 constexpr int kBwdRedChunks = 256;
 
+// K' recomputed inside the prep launch: rows = B * S * Hkv key rows of k
+// (token-major, heads innermost) through RMSNorm (weight w) + partial RoPE
+// into kout, with the key prologue's row code.  blocks is set by the launch.
+struct KPrimeJob {
+  const uint16_t* k;
+  const float* w;
+  uint16_t* kout;
+  long long rows;
+  int S, Hkv;
+  long long pos_offset;
+  int rope_half;
+  float eps;
+  RopeTable tab;
+  long long blocks;
+};
 hipError_t launch_bwd_prep(const uint16_t* dy, const uint16_t* y, const uint16_t* gate,
                            const float* lse, uint16_t* dO, uint16_t* dgate, float* lse2,
-                           float* dvec, int B, int S, int Spad, int Hq, hipStream_t stream);
+                           float* dvec, int B, int S, int Spad, int Hq, KPrimeJob kp,
+                           hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream);
 hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t stream);
 // d(q_norm_w) and d(k_norm_w) from the kernels' partials, in a fixed order;
