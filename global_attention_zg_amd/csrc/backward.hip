@@ -558,18 +558,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
       for (int kk = 0; kk < 8; ++kk)
         dpT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(vt + (bread ^ (uint32_t)(kk << 4))),
                                                       of[kk], dpT, 0, 0, 0);
-      // register r: key t*32 + 8(r/4) + 4 half + r%4 of this lane's query
-      const bool masked = banded || t * 32 + 31 > wrow0;
+      // register r: key t*32 + 8(r/4) + 4 half + r%4 of this lane's query.
+      // Only a tile that reaches past the wave's first query or below its
+      // last query's band needs the mask (a wave-uniform branch).
+      const bool masked = t * 32 + 31 > wrow0 || wrow0 + 31 - t * 32 >= lim;
       float ds[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = fast_exp2(__builtin_fmaf(sT[r], c, -lse_l));
-        if (masked) {
+      for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(__builtin_fmaf(sT[r], c, -lse_l));
+      if (masked) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
           const int dq = qi - (t * 32 + 8 * (r >> 2) + 4 * half + (r & 3));
-          pr = (unsigned)dq < (unsigned)lim ? pr : 0.f;
+          ds[r] = (unsigned)dq < (unsigned)lim ? ds[r] : 0.f;
         }
-        ds[r] = pr * (dpT[r] - d_l);
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ds[r] = ds[r] * (dpT[r] - d_l);  // P (dP - Dr)
       const bf16x8 dsf0 = pack_bf16x8(ds), dsf1 = pack_bf16x8(ds + 8);
 #pragma unroll
       for (int bd = 0; bd < 4; ++bd)
