@@ -617,6 +617,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
 constexpr int kDkvStage = 2 * kTileB + 256;  // Q', dO, lse2[32], Dr[32]
 constexpr int kDkvV = 2 * kDkvStage;         // V rows of the key block, 4 x 8 KB
 
+// BANDED: 0 < window < S.  A global layer (window 0, or at least S) masks
+// only the visits at the diagonal, under a wave-uniform branch; a band masks
+// every element (most of its visits cross an edge of the band).
+template <bool BANDED>
 __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) unsigned char smem_raw[2 * kDkvStage + 4 * kTileB];
   lds_u8* smem = (lds_u8*)smem_raw;
@@ -625,8 +629,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
   const int wvu = __builtin_amdgcn_readfirstlane(wv);
   const int qcol = lane & 31, half = lane >> 5;
   const int grp = p.Hq / p.Hkv;
-  const bool banded = p.window > 0;
-  const int lim = banded ? p.window : 0x7fffffff;
+  const bool banded = BANDED;
+  const int lim = BANDED ? p.window : 0x7fffffff;
 
   const int bid = blockIdx.x;
   const int bg = bid % (p.B * p.Hkv);
@@ -753,11 +757,25 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * m + e;
-          const int dq = q0 + 8 * m + 4 * half + e - kj;
           float x = fast_exp2(__builtin_fmaf(s[r], c, -l4[e]));
-          x = (unsigned)dq < (unsigned)lim ? x : 0.f;
+          if constexpr (BANDED) {
+            const int dq = q0 + 8 * m + 4 * half + e - kj;
+            x = (unsigned)dq < (unsigned)lim ? x : 0.f;
+          }
           pr[r] = x;
           ds[r] = x * (dp[r] - d4[e]);
+        }
+      }
+      if constexpr (!BANDED) {
+        // causal: only a visit whose queries reach below the wave's last key
+        if (q0 < kw + 31) {
+          const int dq0 = q0 + 4 * half - kj;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool ok = dq0 + 8 * (r >> 2) + (r & 3) >= 0;
+            pr[r] = ok ? pr[r] : 0.f;
+            ds[r] = ok ? ds[r] : 0.f;
+          }
         }
       }
       const bf16x8 pf0 = pack_bf16x8(pr), pf1 = pack_bf16x8(pr + 8);
@@ -881,7 +899,10 @@ hipError_t launch_bwd_dkv(const BwdParams& p, hipStream_t stream) {
   if (p.B == 0 || p.S == 0) return hipSuccess;
   const long long blocks = bwd_dkv_blocks(p.B, p.S, p.Hkv);
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(bwd_dkv_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  if (p.window > 0 && p.window < p.S)
+    hipLaunchKernelGGL(bwd_dkv_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(bwd_dkv_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
