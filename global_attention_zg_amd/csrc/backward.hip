@@ -34,6 +34,8 @@
 // rows 4n..4n+3 of a transposing read get values that differ in bits 2-3,
 // so ds_read_b64_tr_b16 of two adjacent chunks per row is conflict-free too.
 
+#include <type_traits>
+
 #include "zg_common.h"
 #include "zg_launch.h"
 #include "zg_lds.h"
@@ -724,8 +726,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
   else sync_tiles<0>();
 
   const int kw = kb0 + 32 * wvu;  // the wave's first key
-  for (int i = 0; i < ntile; ++i) {
-    const int stg = i & 1;
+  // Visit i in stage stg; the stage is a compile-time constant (the loop
+  // below runs visits in pairs), so that every LDS address in the visit is a
+  // per-lane base plus an immediate.
+  auto visit = [&](int i, auto stg_tag) __attribute__((always_inline)) {
+    constexpr int stg = decltype(stg_tag)::value;
     const int q0 = (qt_lo + nq - 1 - i / grp) * 32;
     const lds_u8* qt = smem + stg * kDkvStage;
     const lds_u8* ot = qt + kTileB;
@@ -795,6 +800,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
     // goes into tile i's stage
     sync_tiles<0>();
     if (i + 2 < ntile) gload(i + 2, stg);
+  };
+  for (int i = 0; i < ntile; i += 2) {
+    visit(i, std::integral_constant<int, 0>{});
+    if (i + 1 < ntile) visit(i + 1, std::integral_constant<int, 1>{});
   }
 
   // register r of block bd -> dim 32bd + 8(r/4) + 4 half + r%4 of key kj
