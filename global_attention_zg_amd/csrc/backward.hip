@@ -538,8 +538,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
   if (nt > 1) sync_tiles<4>();
   else sync_tiles<0>();
 
-  int stg = 0;
-  for (int j = 0; j < nt; ++j) {
+  // Tile j in stage j % 3; the stage is a compile-time constant (the loop
+  // below runs tiles in threes), so that every LDS address in the step is a
+  // per-lane base plus an immediate.
+  auto step = [&](int j, auto stg_tag) __attribute__((always_inline)) {
+    constexpr int stg = decltype(stg_tag)::value;
     const int t = t_hi - j;
     const bool issue = j + 2 < nt;
     if (issue) gload(t - 2, stg == 0 ? 2 : stg - 1);
@@ -587,7 +590,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
     // tile j+1 must have landed; tile j+2's four copies may still fly
     if (issue) sync_tiles<4>();
     else sync_tiles<0>();
-    stg = stg == 2 ? 0 : stg + 1;
+  };
+  for (int j = 0; j < nt; j += 3) {
+    step(j, std::integral_constant<int, 0>{});
+    if (j + 1 < nt) step(j + 1, std::integral_constant<int, 1>{});
+    if (j + 2 < nt) step(j + 2, std::integral_constant<int, 2>{});
   }
 
   // dq' = tau * dQ, then back through RoPE and RMSNorm to dq
