@@ -494,9 +494,10 @@ int zg_attn_bwd(const zg_attn_params* p, const void* q, const void* k, const voi
                                      static_cast<uint16_t*>(dgate), lse2, dvec, B, S, Spad, Hq, kj,
                                      s);
   if (e != hipSuccess) return ZG_ERR_HIP;
-  if (!zg::bwd_dq_fuses_q(rh)) {  // else the dq' kernel forms Q' itself
+  if (!zg::bwd_dq_fuses_q(rh)) {  // else the dq' kernel forms Q' * c itself
     e = zg::launch_k_prologue(static_cast<const uint16_t*>(q), q_norm_w, qp, (long long)B * S * Hq,
-                              S, Hq, p->pos_offset, rh, p->rms_eps, tab, s);
+                              S, Hq, p->pos_offset, rh, p->rms_eps, tab, s, nullptr, 0,
+                              scale_log2(p));
     if (e != hipSuccess) return ZG_ERR_HIP;
   }
   zg::BwdParams bp{};
@@ -504,7 +505,7 @@ int zg_attn_bwd(const zg_attn_params* p, const void* q, const void* k, const voi
   bp.kp = kp;
   bp.v = static_cast<const uint16_t*>(v);
   bp.dO = dO;
-  bp.lse2 = lse2;
+  bp.nlse2 = lse2;
   bp.dvec = dvec;
   bp.dq = static_cast<uint16_t*>(dq);
   bp.dk = static_cast<uint16_t*>(dk);

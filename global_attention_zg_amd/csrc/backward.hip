@@ -249,8 +249,10 @@ __device__ __forceinline__ void grad_rows_epilogue(lds_u8* smem, const f32x16 (&
 
 // ---------------------------------------------------------------------------
 // Per query row (b, s, h): Dr = sum dY*Y, dO = dY*sig(G), dG = dY*Y*(1-sig(G)),
-// lse2 = LSE*log2(e).  Rows are enumerated over (b, h, s < Spad); rows past S
-// get lse2 = +inf and Dr = 0, so that they contribute P = 0 downstream.
+// nlse2 = -LSE*log2(e) (the seed of the score products, whose result is
+// then the exp2 argument of P itself).  Rows are enumerated over
+// (b, h, s < Spad); rows past S get nlse2 = -inf and Dr = 0, so that they
+// contribute P = 0 downstream.
 // 16 lanes per row, 8 dims each.
 // The same launch recomputes K' (the first kp.blocks blocks, 16 key rows
 // each, with the key prologue's row code and so its bits): both passes are
@@ -262,7 +264,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
                                                        const float* __restrict__ lse,
                                                        uint16_t* __restrict__ dO,
                                                        uint16_t* __restrict__ dgate,
-                                                       float* __restrict__ lse2,
+                                                       float* __restrict__ nlse2,
                                                        float* __restrict__ dvec, int B, int S,
                                                        int Spad, int Hq, KPrimeJob kp) {
   if ((long long)blockIdx.x < kp.blocks) {
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
   const long long bh = row / Spad;
   if (s >= S) {
     if (c16 == 0) {
-      lse2[row] = INFINITY;
+      nlse2[row] = -INFINITY;
       dvec[row] = 0.f;
     }
     return;
@@ -328,7 +330,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
     st16(dgate + off, w1);
   }
   if (c16 == 0) {
-    lse2[row] = lse[bh * S + s] * kLog2e;
+    nlse2[row] = -(lse[bh * S + s] * kLog2e);
     dvec[row] = d;
   }
 }
@@ -339,7 +341,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const uint16_t* __restric
 // 32-key tile and wave:
 //   S^T  = K' Q'^T   (A = K' rows, ds_read_b128; B = Q' in registers)
 //   dP^T = V dO^T    (A = V rows, ds_read_b128; B = dO in registers)
-//   P^T = exp2(S^T c - lse2), dS^T = P^T (dP^T - Dr)
+//   P^T = exp2(S^T c - lse2), dS^T = P^T (dP^T - Dr), with S^T c - lse2 the
+//   score product itself: its B operand is Q' c (rounded to bf16 as the
+//   forward rounds it) and its accumulator starts at -lse2
 //   dQ^T += K'^T dS^T (A = K'^T by transposing reads; B = dS^T as bf16)
 // K'/V tiles come through a three-stage ring of untracked copies.
 // ---------------------------------------------------------------------------
@@ -409,10 +413,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
       }
     }
   };
-  // ---- this lane's query row: Q' and dO as B operands, lse2 and Dr
+  // ---- this lane's query row: Q' c and dO as B operands, -lse2 and Dr
   const long long qrow = ((long long)b * p.S + (qok ? qi : 0)) * p.Hq + head;
   const long long lrw = ((long long)b * p.Hq + head) * p.Spad + qi;  // qi < Spad
-  const float lse_l = p.lse2[lrw];
+  const float nl_l = p.nlse2[lrw];
   const float d_l = p.dvec[lrw];
   // The loop reads the registers loaded here; pin_row() has their loads land
   // before it (and before the tile copies that follow them are issued).
@@ -421,7 +425,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
   // issued.
   bf16x8 qf[8], of[8];
   auto pin_row = [&]() __attribute__((always_inline)) {
-    pin(lse_l);
+    pin(nl_l);
     pin(d_l);
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
@@ -487,10 +491,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
 #pragma unroll
       for (int d = 0; d < 2 * RH; ++d) x[d] = y[d];
     }
+    // the score operand: Q' times c, rounded as the forward rounds it
+#pragma unroll
+    for (int d = 0; d < 64; ++d) x[d] *= p.scale_log2;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) qf[kk] = pack_bf16x8(x + 8 * kk);
-    // Q' over the query half rows in LDS (each lane rewrites what it read),
-    // then out row-coalesced: lane L stores the chunk it would have copied
+    // Q' c over the query half rows in LDS (each lane rewrites what it
+    // read), then out row-coalesced for the dk'/dv kernel: lane L stores the
+    // chunk it would have copied
     lds_u8* qw = qrows + qcol * kRowB;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -518,6 +526,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       of[j] = __builtin_bit_cast(bf16x8, qok ? ld16(os + 8 * j) : u32x4{0, 0, 0, 0});
+    // the score operand Q' * c, formed by the key prologue
     const uint16_t* qs = p.qp + qrow * kD + 64 * half;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
@@ -526,7 +535,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
     gload(t_hi, 0);
     if (nt > 1) gload(t_hi - 1, 1);
   }
-  const float c = p.scale_log2;
 
   const uint32_t bread = (uint32_t)qcol * kRowB + (((uint32_t)(8 * half) ^ swz(qcol)) << 4);
   const TrOffsets tro = tr_offsets(lane);
@@ -554,7 +562,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
     // to add and skips them.
     const bool active = t * 32 <= wrow0 + 31 && wrow0 - (t * 32 + 31) < lim;
     if (active) {
-      f32x16 sT = f32x16{}, dpT = f32x16{};
+      f32x16 sT, dpT = f32x16{};
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sT[r] = nl_l;  // every register is this lane's query
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
         sT = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(kt + (bread ^ (uint32_t)(kk << 4))),
@@ -569,7 +579,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
       const bool masked = t * 32 + 31 > wrow0 || wrow0 + 31 - t * 32 >= lim;
       float ds[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(__builtin_fmaf(sT[r], c, -lse_l));
+      for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(sT[r]);
       if (masked) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -616,14 +626,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
 // l % 32:
 //   S  = Q' K'^T  (A = Q' rows, ds_read_b128; B = K' in registers)
 //   dP = dO V^T   (A = dO rows; B = V rows of the block, both ds_read_b128)
-//   P = exp2(S c - lse2), dS = P (dP - Dr)
+//   P = exp2(S c - lse2), dS = P (dP - Dr), with S c - lse2 the score
+//   product itself: A = Q' c (the dq' kernel writes it, rounded as the
+//   forward rounds it), its accumulator starting at -lse2 of the tile's rows;
+//   dK then accumulates (Q' c)^T dS and takes tau / c at the end
 //   dV^T += dO^T P, dK^T += Q'^T dS  (A by transposing reads; B = P, dS)
 // The block's V rows sit in LDS for the whole kernel (keeping them in
 // registers would leave room for one wave per SIMD only); Q'/dO tiles and
 // the tile's lse2 / Dr come through a two-stage ring of untracked copies
 // (five per wave and tile).
 // ---------------------------------------------------------------------------
-constexpr int kDkvStage = 2 * kTileB + 256;  // Q', dO, lse2[32], Dr[32]
+constexpr int kDkvStage = 2 * kTileB + 256;  // Q', dO, nlse2[32], Dr[32]
 constexpr int kDkvV = 2 * kDkvStage;         // V rows of the key block, 4 x 8 KB
 
 // BANDED: 0 < window < S.  A global layer (window 0, or at least S) masks
@@ -656,7 +669,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
   const int nq = q_last / 32 - qt_lo + 1;
   const int ntile = grp * nq;
 
-  // ---- copies: Q' / dO rows 4(2w+j) + L/16 of the tile; lse2 / Dr: lanes
+  // ---- copies: Q' / dO rows 4(2w+j) + L/16 of the tile; nlse2 / Dr: lanes
   // 0..3 of each wave, 16 floats per wave
   const long long qstride = (long long)p.Hq * kD;  // elements between query rows
   int lrow[2];
@@ -676,14 +689,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
     const uint32_t sb = lds_addr(smem + stg * kDkvStage);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      // rows past S read row S-1 (their lse2 is +inf, so P = 0)
+      // rows past S read row S-1 (their nlse2 is -inf, so P = 0)
       const uint32_t off = (uint32_t)((min(q0 + lrow[j], p.S - 1) - q0) * qstride * 2) + chk[j];
       dma16_s(qb, off, sb + (2 * wvu + j) * 1024);
       dma16_s(ob, off, sb + kTileB + (2 * wvu + j) * 1024);
     }
     const long long vrow = ((long long)b * p.Hq + head) * p.Spad + q0;
     if (lane < 4) {
-      const float* src = (wvu < 2 ? p.lse2 : p.dvec) + vrow + 16 * (wvu & 1) + 4 * lane;
+      const float* src = (wvu < 2 ? p.nlse2 : p.dvec) + vrow + 16 * (wvu & 1) + 4 * lane;
       dma16(src, sb + 2 * kTileB + 64 * wvu);
     }
   };
@@ -718,7 +731,6 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) pin(kf[j]);
   const lds_u8* vblk = smem + kDkvV + wvu * kTileB;  // this wave's V rows
-  const float c = p.scale_log2;
   const uint32_t bread = (uint32_t)qcol * kRowB + (((uint32_t)(8 * half) ^ swz(qcol)) << 4);
   const TrOffsets tro = tr_offsets(lane);
 
@@ -748,7 +760,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
     // other workgroup, but still takes part in the copies and barriers.
     const bool active = q0 + 31 >= kw && q0 - (kw + 31) < lim;
     if (active) {
-      f32x16 s = f32x16{}, dp = f32x16{};
+      // the score accumulator starts at -lse2 of its query (register r:
+      // query q0 + 8(r/4) + 4 half + r%4)
+      f32x16 s, dp = f32x16{};
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f32x4 l4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
+            lt + 4 * (8 * m + 4 * half));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[4 * m + e] = l4[e];
+      }
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_read_b128(qt + (bread ^ (uint32_t)(kk << 4))),
@@ -762,14 +783,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
       float pr[16], ds[16];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const f32x4 l4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
-            lt + 4 * (8 * m + 4 * half));
         const f32x4 d4 = *reinterpret_cast<const __attribute__((address_space(3))) f32x4*>(
             lt + 128 + 4 * (8 * m + 4 * half));
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * m + e;
-          float x = fast_exp2(__builtin_fmaf(s[r], c, -l4[e]));
+          float x = fast_exp2(s[r]);
           if constexpr (BANDED) {
             const int dq = q0 + 8 * m + 4 * half + e - kj;
             x = (unsigned)dq < (unsigned)lim ? x : 0.f;
@@ -827,10 +846,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
         *reinterpret_cast<uint2*>(dvd + 32 * bd + 8 * q4) = w;
       }
   }
-  // dk' = tau * dK, then back through RoPE and RMSNorm to dk
+  // dk' = tau * dK = (tau / c) * (Q' c)^T dS, then back through RoPE and
+  // RMSNorm to dk
   static_assert(kEpiBytes <= 2 * kDkvStage + 4 * kTileB, "the epilogue fits the LDS");
   const int r0 = kb0 + 32 * wvu;
-  grad_rows_epilogue(smem, dk, p.scale, p.k + (((long long)b * p.S + r0) * p.Hkv + g) * kD,
+  grad_rows_epilogue(smem, dk, p.scale / p.scale_log2, p.k + (((long long)b * p.S + r0) * p.Hkv + g) * kD,
                      p.dk + (((long long)b * p.S + r0) * p.Hkv + g) * kD, (long long)p.Hkv * kD,
                      min(32, p.S - r0), p.pos_offset + r0, p.k_norm_w, p.rope_half, p.eps, p.tab,
                      p.part_k, bid);
@@ -884,7 +904,7 @@ __global__ __launch_bounds__(kRedRuns * kD) void reduce_final_kernel(const float
 }  // namespace
 
 hipError_t launch_bwd_prep(const uint16_t* dy, const uint16_t* y, const uint16_t* gate,
-                           const float* lse, uint16_t* dO, uint16_t* dgate, float* lse2,
+                           const float* lse, uint16_t* dO, uint16_t* dgate, float* nlse2,
                            float* dvec, int B, int S, int Spad, int Hq, KPrimeJob kp,
                            hipStream_t stream) {
   const long long rows = (long long)B * Hq * Spad;
@@ -893,7 +913,7 @@ hipError_t launch_bwd_prep(const uint16_t* dy, const uint16_t* y, const uint16_t
   if (blocks == 0) return hipSuccess;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, dy, y, gate, lse,
-                     dO, dgate, lse2, dvec, B, S, Spad, Hq, kp);
+                     dO, dgate, nlse2, dvec, B, S, Spad, Hq, kp);
   return hipGetLastError();
 }
 

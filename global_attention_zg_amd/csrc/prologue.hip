@@ -26,8 +26,8 @@ namespace {
 constexpr int kRowsPerBlock = 16;
 constexpr long long kPrologueBlocks = 2048;
 
-// FP8: kout receives the E4M3 codes of K' * k_scale (one byte per element)
-// instead of bf16 K'.
+// kout receives K' * k_scale: as bf16 (the product in fp32, rounded once), or
+// with FP8 as E4M3 codes (one byte per element).
 template <bool FP8>
 __global__ __launch_bounds__(256) void k_prologue_kernel(const uint16_t* __restrict__ k,
                                                          const float* __restrict__ w,
@@ -82,7 +82,7 @@ __global__ __launch_bounds__(256) void k_prologue_kernel(const uint16_t* __restr
       } else {
         u32x4 o;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+        for (int i = 0; i < 4; ++i) o[i] = pack_bf16x2(x[2 * i] * k_scale, x[2 * i + 1] * k_scale);
         st16(static_cast<uint16_t*>(kout) + row * kD + 8 * c16, o);
       }
     }
@@ -188,11 +188,11 @@ static long long prologue_blocks(long long rows) {
 hipError_t launch_k_prologue(const uint16_t* k, const float* w, uint16_t* kout, long long rows,
                              int S, int Hkv, long long pos_offset, int rope_half, float eps,
                              const RopeTable& tab, hipStream_t stream, const int* cu_seqlens,
-                             int nseq) {
+                             int nseq, float out_scale) {
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(k_prologue_kernel<false>, dim3((unsigned)prologue_blocks(rows)), dim3(256), 0,
                      stream, k, w, (void*)kout, rows, S, Hkv, cu_seqlens, nseq, pos_offset,
-                     rope_half, eps, tab, 1.0f);
+                     rope_half, eps, tab, out_scale);
   return hipGetLastError();
 }
 

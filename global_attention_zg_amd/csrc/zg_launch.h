@@ -39,11 +39,12 @@ struct FlashParams {
 // Rows are (token, head) of a token-major [tokens, H, D] tensor.  Token t
 // sits at position pos_offset + (t mod S), or, with cu_seqlens (int32
 // [nseq + 1] on the device), pos_offset + t - cu_seqlens[b] for the sequence
-// b that holds it.
+// b that holds it.  kout receives K' * out_scale in bf16 (rounded once).
 hipError_t launch_k_prologue(const uint16_t* k, const float* w, uint16_t* kout, long long rows,
                              int S, int Hkv, long long pos_offset, int rope_half, float eps,
                              const RopeTable& tab, hipStream_t stream,
-                             const int* cu_seqlens = nullptr, int nseq = 0);
+                             const int* cu_seqlens = nullptr, int nseq = 0,
+                             float out_scale = 1.0f);
 
 // The same with K' written as the E4M3 codes of K' * k_scale (one byte per
 // element: product in fp32, clamped to +-448, rounded to nearest even).
@@ -164,18 +165,20 @@ hipError_t launch_gemm_bf16_tn(GemmParams p, hipStream_t stream);
 hipError_t launch_quantize_fp8(const uint16_t* x, uint8_t* q, long long n, float scale,
                                hipStream_t stream);
 
-// Training backward.  K' is recomputed by launch_k_prologue; so is Q', except
-// where the dq' kernel forms it itself (bwd_dq_fuses_q) and writes it to qp
-// for the dk'/dv kernel.  dO = dY * sigmoid(G) (dY itself on an ungated layer).
+// Training backward.  The prep launch recomputes K' (KPrimeJob).  The score
+// operand Q' * c (c = softmax scale * log2 e, as in the forward) is formed by
+// the dq' kernel where it fuses the query prologue (bwd_dq_fuses_q), else by
+// launch_k_prologue with out_scale c; either way it lands in qp, where the
+// dk'/dv kernel reads it.  dO = dY * sigmoid(G) (dY itself on an ungated layer).
 // The dq' and dk'/dv kernels finish with the RoPE / RMSNorm backward of their
 // rows: they write dq and dk, and one partial sum of the norm-weight gradient
 // per workgroup (part_q, part_k), which launch_reduce_parts adds up.
 struct BwdParams {
-  const uint16_t* qp;   // bf16 [B,S,Hq,D]   Q' (written by the dq' kernel when it fuses Q')
+  const uint16_t* qp;   // bf16 [B,S,Hq,D]   Q' * c, the score operand
   const uint16_t* kp;   // bf16 [B,S,Hkv,D]  K'
   const uint16_t* v;    // bf16 [B,S,Hkv,D]
   const uint16_t* dO;   // bf16 [B,S,Hq,D]
-  const float* lse2;    // fp32 [B,Hq,Spad]  LSE * log2(e); +inf for rows >= S
+  const float* nlse2;   // fp32 [B,Hq,Spad]  -LSE * log2(e); -inf for rows >= S
   const float* dvec;    // fp32 [B,Hq,Spad]  rowsum(dY * Y); 0 for rows >= S
   uint16_t* dq;         // bf16 [B,S,Hq,D]
   uint16_t* dk;         // bf16 [B,S,Hkv,D]
@@ -247,7 +250,7 @@ struct KPrimeJob {
   long long blocks;
 };
 hipError_t launch_bwd_prep(const uint16_t* dy, const uint16_t* y, const uint16_t* gate,
-                           const float* lse, uint16_t* dO, uint16_t* dgate, float* lse2,
+                           const float* lse, uint16_t* dO, uint16_t* dgate, float* nlse2,
                            float* dvec, int B, int S, int Spad, int Hq, KPrimeJob kp,
                            hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdParams& p, hipStream_t stream);

@@ -210,10 +210,11 @@ def test_bwd_global_16k_layer_sampled():
 
 @pytest.mark.parametrize("rope_dim", [42, 30])
 def test_bwd_q_prime_matches_oracle_prologue(rope_dim):
-    """The Q' the backward uses (formed inside the dq' kernel at rope_dim 42,
-    recomputed by the key prologue kernel otherwise) is the oracle's RMSNorm +
-    partial RoPE of q to bf16 rounding.  Q' sits at the start of the
-    workspace (its first segment), rows [B,S,Hq,D]."""
+    """The score operand the backward uses, Q' times c = softmax scale x
+    log2(e) (formed inside the dq' kernel at rope_dim 42, by the key
+    prologue kernel otherwise), is the oracle's RMSNorm + partial RoPE of q,
+    times c, to one bf16 rounding.  It sits at the start of the workspace
+    (its first segment), rows [B,S,Hq,D]."""
     bd = _binding()
     B, S, Hq, Hkv, pos = 2, 150, 8, 2, 33
     c = bwd_case("qprime", B, S, Hq, Hkv, gated=True)
@@ -233,5 +234,6 @@ def test_bwd_q_prime_matches_oracle_prologue(rope_dim):
     qn = orc.rms_norm(zc.f64(c["q"]), c["gq"].astype(np.float64), 1e-6)
     ref = np.stack([orc.apply_partial_rope(qn[b], pos + np.arange(S), rope_dim, 10000.0)
                     for b in range(B)])
+    ref = ref * (np.log2(np.e) / np.sqrt(zc.D))
     d = np.abs(qp - ref)
     assert np.all(d <= 2.0 ** -8 * np.abs(ref) + 1e-5), float(d.max())
