@@ -899,7 +899,10 @@ def varlen_components(torch, bd, iters):
     gq = norm_w(torch, (8, 0, inputs.T_GQ))
     gk = norm_w(torch, (8, 0, inputs.T_GK))
     o = torch.empty_like(q)
-    ws = torch.empty(T * 8 * D * 2, dtype=torch.uint8, device="cuda")
+    # sized for the global layer (K' and the causal kernel's queue counters)
+    ws_p = bd.make_params(len(lens), max(lens), 32, 8, D, 0)
+    ws = torch.empty(bd.zg_attn_fwd_varlen_workspace_size(ws_p, T), dtype=torch.uint8,
+                     device="cuda")
     out = {}
     for kind, window, gate in (("varlen_swa_16x", 128, g), ("varlen_global_16x", 0, None)):
         log(f"component: {kind}")

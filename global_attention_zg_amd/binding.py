@@ -210,6 +210,19 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+# The causal kernel's work-queue counters at the end of a global layer's
+# forward workspace (also needed when K' goes to k_out).
+QUEUE_BYTES = 256
+
+
+def _fwd_workspace(full_bytes, k_out, causal, workspace, device):
+    need = full_bytes if k_out is None else (QUEUE_BYTES if causal else 0)
+    if workspace is None and need:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return workspace, ws_bytes
+
+
 def zg_attn_fwd_workspace_size(p: Params) -> int:
     return int(_lib.zg_attn_fwd_workspace_size(ctypes.byref(p)))
 
@@ -239,15 +252,11 @@ def zg_attn_fwd(q, k, v, gate, q_norm_w, k_norm_w, *, window, rope_dim=42, rope_
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    ws_bytes = 0
-    if k_out is None:
-        ws_bytes = zg_attn_fwd_workspace_size(p)
-        if workspace is None:
-            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
-        ws_bytes = workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _fwd_workspace(zg_attn_fwd_workspace_size(p), k_out, window == 0,
+                                         workspace, q.device)
     st = _lib.zg_attn_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(q_norm_w),
-                          _ptr(k_norm_w), _ptr(out), _ptr(lse), _ptr(k_out),
-                          _ptr(workspace) if k_out is None else None, ws_bytes, _stream(stream))
+                          _ptr(k_norm_w), _ptr(out), _ptr(lse), _ptr(k_out), _ptr(workspace),
+                          ws_bytes, _stream(stream))
     _check(st)
     return out, lse
 
@@ -282,16 +291,11 @@ def zg_attn_fwd_fp8(q, k, v, gate, q_norm_w, k_norm_w, *, k_scale, window=0, rop
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
-    ws_bytes = 0
-    if k_out is None:
-        ws_bytes = zg_attn_fwd_fp8_workspace_size(p)
-        if workspace is None:
-            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
-        ws_bytes = workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _fwd_workspace(zg_attn_fwd_fp8_workspace_size(p), k_out, True,
+                                         workspace, q.device)
     st = _lib.zg_attn_fwd_fp8(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
                               _ptr(q_norm_w), _ptr(k_norm_w), float(k_scale), _ptr(out),
-                              _ptr(lse), _ptr(k_out), _ptr(workspace) if k_out is None else None,
-                              ws_bytes, _stream(stream))
+                              _ptr(lse), _ptr(k_out), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st)
     return out, lse
 
@@ -328,16 +332,11 @@ def zg_attn_fwd_varlen(q, k, v, gate, q_norm_w, k_norm_w, cu_seqlens, max_seqlen
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((Hq, T), dtype=torch.float32, device=q.device)
-    ws_bytes = 0
-    if k_out is None:
-        ws_bytes = zg_attn_fwd_varlen_workspace_size(p, T)
-        if workspace is None:
-            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
-        ws_bytes = workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _fwd_workspace(zg_attn_fwd_varlen_workspace_size(p, T), k_out,
+                                         window == 0, workspace, q.device)
     st = _lib.zg_attn_fwd_varlen(ctypes.byref(p), _ptr(cu_seqlens), T, _ptr(q), _ptr(k), _ptr(v),
                                  _ptr(gate), _ptr(q_norm_w), _ptr(k_norm_w), _ptr(out), _ptr(lse),
-                                 _ptr(k_out), _ptr(workspace) if k_out is None else None,
-                                 ws_bytes, _stream(stream))
+                                 _ptr(k_out), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st)
     return out, lse
 

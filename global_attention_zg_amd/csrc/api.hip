@@ -102,6 +102,10 @@ struct BwdLayout {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The causal kernel's 16 work-queue counters, at the end of the forward
+// workspace.
+constexpr size_t kQueueBytes = 256;
+
 BwdLayout bwd_layout(const zg_attn_params* p) {
   const size_t B = (size_t)p->batch, S = (size_t)p->seqlen, Hq = (size_t)p->n_q_heads,
                Hkv = (size_t)p->n_kv_heads;
@@ -138,11 +142,17 @@ static int fwd_impl(const zg_attn_params* p, const int* cu_seqlens, long long to
       (k_out && !aligned16(k_out)) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return ZG_ERR_INVALID;
   const size_t kp_bytes = (size_t)total * (size_t)p->n_kv_heads * kD * 2;
+  const bool causal = p->window == 0;
   void* kp = k_out;
-  if (!kp) {
-    if (!workspace || workspace_bytes < kp_bytes) return ZG_ERR_WORKSPACE;
+  int* queue = nullptr;
+  if (!kp || causal) {
+    // K' (without k_out), then the causal kernel's queue counters
+    const size_t need = (kp ? 0 : align256(kp_bytes)) + (causal ? kQueueBytes : 0);
+    if (!workspace || workspace_bytes < need) return ZG_ERR_WORKSPACE;
     if (!aligned16(workspace)) return ZG_ERR_INVALID;
-    kp = workspace;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    if (!kp) kp = ws;
+    if (causal) queue = reinterpret_cast<int*>(ws + need - kQueueBytes);
   }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const zg::RopeTable tab = make_rope_table(p);
@@ -150,7 +160,7 @@ static int fwd_impl(const zg_attn_params* p, const int* cu_seqlens, long long to
   hipError_t e = zg::launch_k_prologue(static_cast<const uint16_t*>(k), k_norm_w,
                                        static_cast<uint16_t*>(kp), krows, p->seqlen,
                                        p->n_kv_heads, p->pos_offset, p->rope_dim / 2,
-                                       p->rms_eps, tab, s, cu_seqlens, p->batch);
+                                       p->rms_eps, tab, s, cu_seqlens, p->batch, 1.0f, queue);
   if (e != hipSuccess) return ZG_ERR_HIP;
   zg::FlashParams fp{};
   fp.q = static_cast<const uint16_t*>(q);
@@ -173,6 +183,7 @@ static int fwd_impl(const zg_attn_params* p, const int* cu_seqlens, long long to
   fp.eps = p->rms_eps;
   fp.pos_offset = p->pos_offset;
   fp.tab = tab;
+  fp.queue = queue;
   return hip_status(zg::launch_flash_fwd(fp, s));
 }
 
@@ -190,18 +201,19 @@ static int fwd_fp8_impl(const zg_attn_params* p, const void* q, const void* k, c
       !aligned16(k_norm_w) || !aligned16(out) || (gate && !aligned16(gate)) ||
       (k_out && !aligned16(k_out)) || (lse && (reinterpret_cast<uintptr_t>(lse) & 3u)))
     return ZG_ERR_INVALID;
+  // workspace: the K' codes (without k_out), then the queue counters
   void* kp = k_out;
-  if (!kp) {
-    if (!workspace || workspace_bytes < kprime_bytes(p) / 2) return ZG_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return ZG_ERR_INVALID;
-    kp = workspace;
-  }
+  const size_t need = (kp ? 0 : align256(kprime_bytes(p) / 2)) + kQueueBytes;
+  if (!workspace || workspace_bytes < need) return ZG_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ZG_ERR_INVALID;
+  if (!kp) kp = workspace;
+  int* queue = reinterpret_cast<int*>(static_cast<unsigned char*>(workspace) + need - kQueueBytes);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const zg::RopeTable tab = make_rope_table(p);
   hipError_t e = zg::launch_k_prologue_fp8(
       static_cast<const uint16_t*>(k), k_norm_w, static_cast<uint8_t*>(kp), k_scale,
       (long long)p->batch * p->seqlen * p->n_kv_heads, p->seqlen, p->n_kv_heads, p->pos_offset,
-      p->rope_dim / 2, p->rms_eps, tab, s);
+      p->rope_dim / 2, p->rms_eps, tab, s, nullptr, 0, queue);
   if (e != hipSuccess) return ZG_ERR_HIP;
   zg::FlashParams fp{};
   fp.q = static_cast<const uint16_t*>(q);
@@ -224,6 +236,7 @@ static int fwd_fp8_impl(const zg_attn_params* p, const void* q, const void* k, c
   fp.eps = p->rms_eps;
   fp.pos_offset = p->pos_offset;
   fp.tab = tab;
+  fp.queue = queue;
   return hip_status(zg::launch_flash_causal(fp, s));
 }
 
@@ -389,7 +402,8 @@ const char* zg_attn_strerror(int status) {
 
 size_t zg_attn_fwd_workspace_size(const zg_attn_params* p) {
   if (check_params(p) != ZG_OK) return 0;
-  return kprime_bytes(p);
+  if (kprime_bytes(p) == 0) return 0;  // nothing is launched
+  return align256(kprime_bytes(p)) + (p->window == 0 ? kQueueBytes : 0);
 }
 
 int zg_attn_fwd(const zg_attn_params* p, const void* q, const void* k, const void* v,
@@ -403,7 +417,9 @@ int zg_attn_fwd(const zg_attn_params* p, const void* q, const void* k, const voi
 
 size_t zg_attn_fwd_varlen_workspace_size(const zg_attn_params* p, long long total_tokens) {
   if (check_params(p) != ZG_OK || total_tokens < 0) return 0;
-  return (size_t)total_tokens * (size_t)p->n_kv_heads * kD * 2;
+  if (total_tokens == 0 || p->batch == 0 || p->seqlen == 0) return 0;  // nothing is launched
+  return align256((size_t)total_tokens * (size_t)p->n_kv_heads * kD * 2) +
+         (p->window == 0 ? kQueueBytes : 0);
 }
 
 int zg_attn_fwd_varlen(const zg_attn_params* p, const int* cu_seqlens, long long total_tokens,
@@ -422,7 +438,8 @@ int zg_attn_fwd_varlen(const zg_attn_params* p, const int* cu_seqlens, long long
 
 size_t zg_attn_fwd_fp8_workspace_size(const zg_attn_params* p) {
   if (check_params(p) != ZG_OK) return 0;
-  return kprime_bytes(p) / 2;
+  if (kprime_bytes(p) == 0) return 0;  // nothing is launched
+  return align256(kprime_bytes(p) / 2) + kQueueBytes;
 }
 
 int zg_attn_fwd_fp8(const zg_attn_params* p, const void* q, const void* k, const void* v,

@@ -40,6 +40,8 @@
 // softmax multiplies the code products by c / (query scale * k_scale) in the
 // same FMA that subtracts the row's offset.  P V stays in bf16.
 
+#include <algorithm>
+#include <atomic>
 #include <type_traits>
 
 #include "zg_common.h"
@@ -129,6 +131,32 @@ __device__ __forceinline__ i32x8 join_i32x8(const u32x4& lo, const u32x4& hi) {
                (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
+// Work queues of the persistent grid.  Job j (longest causal rows first,
+// the (batch, kv head, head group) index fastest) sits in queue j % nq at
+// place j / nq; queue[y] counts the places of queue y handed out.  Workgroup
+// b drains queue b % nq first.  Workgroups are dealt to the XCDs in turn, so
+// with nq = 8 an XCD's workgroups share one queue, whose jobs share a KV head
+// when B * Hkv * hgroups is a multiple of 8, and its L2 serves that head's
+// tiles.  An empty queue sends the workgroup to the others in turn, which
+// evens out XCDs that run at different speeds.  Every place is handed out at
+// most once and every job has a place, so each job runs exactly once; -1
+// when all queues are empty.  The counters must be zero at launch.
+__device__ __forceinline__ int pop_job(int* queue, int own, int nq, int n_jobs, bool& own_done) {
+  if (!own_done) {
+    const int j = own + nq * atomicAdd(queue + own, 1);
+    if (j < n_jobs) return j;
+    own_done = true;
+  }
+  for (int d = 1; d < nq; ++d) {
+    const int y = own + d < nq ? own + d : own + d - nq;
+    if (y + nq * __hip_atomic_load(queue + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n_jobs)
+      continue;  // already empty
+    const int j = y + nq * atomicAdd(queue + y, 1);
+    if (j < n_jobs) return j;
+  }
+  return -1;
+}
+
 // RH: rope_dim / 2 when fixed at compile time (21 or 0), else -1.
 // NS: K'/V tile stages in LDS.  FP8: the E4M3 variant.  ILV: the V operand
 // reads are interleaved with the second half's score MFMAs (2-4% faster up
@@ -158,8 +186,17 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
   const int half = lane >> 5;
   const int grp = p.Hq / p.Hkv;
 
-  // ---- workgroup -> (position block, batch, kv head, head group)
-  const int bid = blockIdx.x;
+  __shared__ int job_s[2];  // the next job, one slot per parity of the job loop
+  const int own = blockIdx.x % geo.nq;  // this workgroup's own queue
+  bool own_done = false;
+
+  // One job: query block pb of (batch, kv head, head group) bhg, numbered
+  // longest causal rows first.  Thread 0 claims the workgroup's next job into
+  // `next` once the job's tiles are done, so that the claim's latency hides
+  // under the epilogue, and the workgroups that finish first take the longest
+  // jobs left.
+  auto run_job = [&](const int bid, int& next) __attribute__((always_inline)) {
+  // ---- job -> (position block, batch, kv head, head group)
   const int bhg = bid % geo.n_bhg;
   const int pb = geo.n_pos_blocks - 1 - bid / geo.n_bhg;  // longest causal rows first
   const int hg = bhg % geo.hgroups;
@@ -178,7 +215,10 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
     S = (int)min(c1 - c0, (long long)p.S);
     lse0 = tok0;
     lse_hs = p.total;
-    if (i0w >= S) return;  // whole workgroup: past the end of a short sequence
+    if (i0w >= S) {  // whole workgroup: past the end of a short sequence
+      if (tid == 0) next = pop_job(p.queue, own, geo.nq, geo.n_jobs, own_done);
+      return;
+    }
   }
   // This wave's rows: half h is rows wrow0 + 32 h + (lane % 32).  Rows past
   // the end are padding with row S-1's visibility.
@@ -572,6 +612,7 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
     __builtin_amdgcn_sched_barrier(0);
     sa = sb;
   }
+  if (tid == 0) next = pop_job(p.queue, own, geo.nq, geo.n_jobs, own_done);
   // ---- tail: half 1 of the last tile
   mask(1, nt - 1);
   softmax(1);
@@ -613,9 +654,40 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
       }
     }
   }
+  };
+
+  // ---- persistent loop: one workgroup per CU takes jobs until every queue
+  // is empty.  The barrier at the top of each pass also ends the previous
+  // job's use of the LDS ring.
+  if (tid == 0) job_s[0] = pop_job(p.queue, own, geo.nq, geo.n_jobs, own_done);
+  for (int it = 0;; ++it) {
+    __syncthreads();
+    const int job = __builtin_amdgcn_readfirstlane(job_s[it & 1]);
+    if (job < 0) break;
+    int next = -1;
+    run_job(job, next);
+    if (tid == 0) job_s[(it + 1) & 1] = next;
+  }
 }
 
 constexpr int kCStages = 8;
+
+// Compute units of the current device (looked up once per device).
+int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
+  if (dev >= 0) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
+          hipSuccess || n < 1)
+    n = 256;
+  if (dev >= 0) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
 
 // Sequences up to this length use the interleaved schedule (ILV).
 constexpr int kIlvMaxS = 65536;
@@ -638,8 +710,12 @@ hipError_t launch_flash_causal(const FlashParams& p, hipStream_t stream) {
   geo.n_pos_blocks = (p.S + geo.pos_per_wg - 1) / geo.pos_per_wg;
   geo.n_bhg = p.B * p.Hkv * geo.hgroups;
   const long long blocks = (long long)geo.n_pos_blocks * geo.n_bhg;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  const dim3 grid((unsigned)blocks);
+  if (blocks > 0x3fffffffLL || !p.queue) return hipErrorInvalidValue;
+  // persistent grid: one workgroup per CU (each takes a whole CU's LDS)
+  geo.n_jobs = (int)blocks;
+  const int wgs = (int)std::min<long long>(blocks, device_cu_count());
+  geo.nq = std::min(wgs, 8);
+  const dim3 grid((unsigned)wgs);
   const bool ilv = p.S <= kIlvMaxS;
   if (p.kp8) {  // the E4M3 variant: fixed-length batches
     if (p.cu_seqlens) return hipErrorInvalidValue;

@@ -36,7 +36,9 @@ __global__ __launch_bounds__(256) void k_prologue_kernel(const uint16_t* __restr
                                                          const int* __restrict__ cu_seqlens,
                                                          int nseq, long long pos_offset,
                                                          int rope_half, float eps, RopeTable tab,
-                                                         float k_scale) {
+                                                         float k_scale, int* zero16) {
+  // the causal kernel's work-queue counters, cleared for the launch after
+  if (zero16 && blockIdx.x == 0 && threadIdx.x < 16) zero16[threadIdx.x] = 0;
   __shared__ float xs[kRowsPerBlock][kD];
   __shared__ float cs[kRowsPerBlock][kMaxRopeHalf], sn[kRowsPerBlock][kMaxRopeHalf];
   const int lrow = threadIdx.x / 16;
@@ -188,22 +190,23 @@ static long long prologue_blocks(long long rows) {
 hipError_t launch_k_prologue(const uint16_t* k, const float* w, uint16_t* kout, long long rows,
                              int S, int Hkv, long long pos_offset, int rope_half, float eps,
                              const RopeTable& tab, hipStream_t stream, const int* cu_seqlens,
-                             int nseq, float out_scale) {
+                             int nseq, float out_scale, int* zero16) {
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(k_prologue_kernel<false>, dim3((unsigned)prologue_blocks(rows)), dim3(256), 0,
                      stream, k, w, (void*)kout, rows, S, Hkv, cu_seqlens, nseq, pos_offset,
-                     rope_half, eps, tab, out_scale);
+                     rope_half, eps, tab, out_scale, zero16);
   return hipGetLastError();
 }
 
 hipError_t launch_k_prologue_fp8(const uint16_t* k, const float* w, uint8_t* kout, float k_scale,
                                  long long rows, int S, int Hkv, long long pos_offset,
                                  int rope_half, float eps, const RopeTable& tab,
-                                 hipStream_t stream, const int* cu_seqlens, int nseq) {
+                                 hipStream_t stream, const int* cu_seqlens, int nseq,
+                                 int* zero16) {
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(k_prologue_kernel<true>, dim3((unsigned)prologue_blocks(rows)), dim3(256), 0,
                      stream, k, w, (void*)kout, rows, S, Hkv, cu_seqlens, nseq, pos_offset,
-                     rope_half, eps, tab, k_scale);
+                     rope_half, eps, tab, k_scale, zero16);
   return hipGetLastError();
 }
 

@@ -28,6 +28,9 @@ struct Geo {
   int n_pos_blocks;
   int hgroups;       // workgroups per (b, kv head, position block)
   int n_bhg;         // B * Hkv * hgroups
+  // persistent causal grid: jobs (= position blocks x n_bhg) and work queues
+  int n_jobs;
+  int nq;
 };
 
 struct TileState {

@@ -34,17 +34,23 @@ struct FlashParams {
   // sequences of S tokens.
   const int* cu_seqlens;
   long long total;
+  // Global (causal) layers: 16 int32 work-queue counters in device memory,
+  // zero when the kernel starts (the key prologue clears them) and left
+  // nonzero by it.  Launches that overlap on one set of counters race.
+  int* queue;
 };
 
 // Rows are (token, head) of a token-major [tokens, H, D] tensor.  Token t
 // sits at position pos_offset + (t mod S), or, with cu_seqlens (int32
 // [nseq + 1] on the device), pos_offset + t - cu_seqlens[b] for the sequence
 // b that holds it.  kout receives K' * out_scale in bf16 (rounded once).
+// zero16, if not null, points at 16 int32 that the launch sets to zero (the
+// causal kernel's work-queue counters, FlashParams::queue).
 hipError_t launch_k_prologue(const uint16_t* k, const float* w, uint16_t* kout, long long rows,
                              int S, int Hkv, long long pos_offset, int rope_half, float eps,
                              const RopeTable& tab, hipStream_t stream,
                              const int* cu_seqlens = nullptr, int nseq = 0,
-                             float out_scale = 1.0f);
+                             float out_scale = 1.0f, int* zero16 = nullptr);
 
 // The same with K' written as the E4M3 codes of K' * k_scale (one byte per
 // element: product in fp32, clamped to +-448, rounded to nearest even).
@@ -52,7 +58,7 @@ hipError_t launch_k_prologue_fp8(const uint16_t* k, const float* w, uint8_t* kou
                                  long long rows, int S, int Hkv, long long pos_offset,
                                  int rope_half, float eps, const RopeTable& tab,
                                  hipStream_t stream, const int* cu_seqlens = nullptr,
-                                 int nseq = 0);
+                                 int nseq = 0, int* zero16 = nullptr);
 
 hipError_t launch_flash_fwd(const FlashParams& p, hipStream_t stream);
 // The global (window 0) layer's kernel; launch_flash_fwd routes to it.

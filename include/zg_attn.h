@@ -66,9 +66,14 @@ typedef struct zg_attn_params {
   long long pos_offset; /* position of token 0 (fwd) / added to decode pos.    */
 } zg_attn_params;
 
-/* Bytes of device workspace zg_attn_fwd needs (the normalised and rotated
- * keys K', bf16 [B,S,Hkv,D]); 0 for an invalid p.  When k_out is passed to
- * zg_attn_fwd, K' goes there and the workspace may be NULL. */
+/* Bytes of device workspace zg_attn_fwd needs (16-byte aligned): the
+ * normalised and rotated keys K', bf16 [B,S,Hkv,D], and for a global layer
+ * (window 0) after them, on the next 256-byte boundary, 256 bytes of work-
+ * queue counters that the call clears before its attention kernel uses them;
+ * 0 for an invalid p or an empty batch.  When k_out is passed, K' goes there:
+ * a windowed layer then needs no workspace (NULL is fine), a global layer 256
+ * bytes for the counters.  Calls that run at the same time need workspaces
+ * of their own. */
 size_t zg_attn_fwd_workspace_size(const zg_attn_params* p);
 
 /* Prefill / training forward of one attention layer.
@@ -104,6 +109,7 @@ int zg_attn_fwd(const zg_attn_params* p,
  *   lse           fp32 [Hq,total_tokens] or NULL
  * Token s of every sequence sits at position pos_offset + s.  Each sequence's
  * rows are bit-identical to zg_attn_fwd on that sequence alone. */
+/* Workspace as for zg_attn_fwd, with total_tokens rows of K'. */
 size_t zg_attn_fwd_varlen_workspace_size(const zg_attn_params* p, long long total_tokens);
 int zg_attn_fwd_varlen(const zg_attn_params* p, const int* cu_seqlens, long long total_tokens,
                        const void* q, const void* k, const void* v, const void* gate,
@@ -319,7 +325,9 @@ int zg_attn_decode_paged_fp8(const zg_attn_params* p,
  *
  * Arguments as for zg_attn_fwd, except: k_scale; k_out, when not NULL,
  * receives the uint8 codes [B,S,Hkv,D] (else the workspace holds them, of
- * zg_attn_fwd_fp8_workspace_size bytes).  A window in (0, seqlen) returns
+ * zg_attn_fwd_fp8_workspace_size bytes, the 256 bytes of queue counters
+ * included; with k_out the workspace holds only the counters, 256 bytes).
+ * A window in (0, seqlen) returns
  * ZG_ERR_UNSUPPORTED: windowed layers are bound by HBM bytes, which an E4M3
  * score product does not reduce. */
 size_t zg_attn_fwd_fp8_workspace_size(const zg_attn_params* p);

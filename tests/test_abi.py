@@ -102,6 +102,28 @@ def test_fwd_workspace_rules(bd):
     assert _fwd(bd, p, **dict(base, ws=FAKE + 8, ws_bytes=need)) == bd.ZG_ERR_INVALID
 
 
+def test_fwd_global_workspace_holds_queue_counters(bd):
+    """A global layer (window 0) keeps the causal kernel's 256 bytes of
+    work-queue counters after K' in its workspace, and needs them also when
+    K' goes to k_out."""
+    p = bd.make_params(2, 100, 32, 8, 128, 0)
+    need = bd.zg_attn_fwd_workspace_size(p)
+    assert need == 2 * 100 * 8 * 128 * 2 + bd.QUEUE_BYTES == 409856
+    base = dict(q=FAKE, k=FAKE, v=FAKE, qw=FAKE, kw=FAKE, out=FAKE)
+    assert _fwd(bd, p, **dict(base, ws=FAKE, ws_bytes=need - 1)) == bd.ZG_ERR_WORKSPACE
+    assert _fwd(bd, p, **dict(base, kout=FAKE)) == bd.ZG_ERR_WORKSPACE
+    assert _fwd(bd, p, **dict(base, kout=FAKE, ws=FAKE, ws_bytes=255)) == bd.ZG_ERR_WORKSPACE
+    assert _fwd(bd, p, **dict(base, kout=FAKE, ws=FAKE + 8, ws_bytes=256)) == bd.ZG_ERR_INVALID
+    # K' rows not a multiple of 256 bytes apart: the counters start on the next 256
+    assert bd.zg_attn_fwd_fp8_workspace_size(bd.make_params(1, 3, 4, 1, 128, 0)) == 512 + 256
+    assert bd.zg_attn_fwd_fp8_workspace_size(bd.make_params(1, 2, 4, 1, 128, 0)) == 256 + 256
+    assert bd.zg_attn_fwd_fp8_workspace_size(bd.make_params(1, 4, 4, 1, 128, 0)) == 512 + 256
+    assert bd.zg_attn_fwd_varlen_workspace_size(p, 5000) == 5000 * 8 * 128 * 2 + 256
+    assert bd.zg_attn_fwd_varlen_workspace_size(p, 0) == 0
+    for B, S in ((0, 64), (1, 0)):
+        assert bd.zg_attn_fwd_workspace_size(bd.make_params(B, S, 32, 8, 128, 0)) == 0
+
+
 def test_fwd_empty_launches_nothing(bd):
     for B, S in ((0, 64), (1, 0), (0, 0)):
         p = bd.make_params(B, S, 32, 8, 128, 128)
