@@ -40,7 +40,11 @@ CFLAGS = [
 # Per-source extra flags.  The causal kernel keeps its output accumulators in
 # AGPRs through inline asm and wants every other MFMA result (the scores,
 # which the softmax reads) written straight to VGPRs.
-SOURCE_FLAGS = {"flash_causal.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]}
+# The atomic optimizer is off there too: it would turn the work-queue claim
+# (one lane's atomic add) into a wave-wide form that reads the result at
+# once, where the kernel wants to read it only after the job's epilogue.
+SOURCE_FLAGS = {"flash_causal.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=true",
+                                     "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _run(cmd):

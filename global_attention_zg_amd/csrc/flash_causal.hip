@@ -139,11 +139,20 @@ __device__ __forceinline__ i32x8 join_i32x8(const u32x4& lo, const u32x4& hi) {
 // when B * Hkv * hgroups is a multiple of 8, and its L2 serves that head's
 // tiles.  An empty queue sends the workgroup to the others in turn, which
 // evens out XCDs that run at different speeds.  Every place is handed out at
-// most once and every job has a place, so each job runs exactly once; -1
-// when all queues are empty.  The counters must be zero at launch.
-__device__ __forceinline__ int pop_job(int* queue, int own, int nq, int n_jobs, bool& own_done) {
+// most once and every job has a place, so each job runs exactly once.  The
+// counters must be zero at launch.
+//
+// A claim is split in two, so that its latency can hide under other work:
+// claim_own takes a ticket from the workgroup's own queue (-1 once that is
+// known to be empty) and next_job turns the ticket into a job, taking from
+// the other queues if it is past the end; -1 when all queues are empty.
+__device__ __forceinline__ int claim_own(int* queue, int own, bool own_done) {
+  return own_done ? -1 : atomicAdd(queue + own, 1);
+}
+__device__ __forceinline__ int next_job(int* queue, int own, int nq, int n_jobs, bool& own_done,
+                                        int ticket) {
   if (!own_done) {
-    const int j = own + nq * atomicAdd(queue + own, 1);
+    const int j = own + nq * ticket;
     if (j < n_jobs) return j;
     own_done = true;
   }
@@ -187,14 +196,20 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
   const int grp = p.Hq / p.Hkv;
 
   __shared__ int job_s[2];  // the next job, one slot per parity of the job loop
+  __shared__ __attribute__((aligned(16))) float qw_s[kD];  // query-norm weights
+  if (tid < kD / 4) st16(qw_s + 4 * tid, ld16(p.q_norm_w + 4 * tid));  // (published by the job loop's barrier)
+  // max |w_k| over the 128 key-norm weights (two per lane, then the wave)
+  float wk = fmaxf(fabsf(p.k_norm_w[2 * lane]), fabsf(p.k_norm_w[2 * lane + 1]));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) wk = fmaxf(wk, __shfl_xor(wk, o));
   const int own = blockIdx.x % geo.nq;  // this workgroup's own queue
   bool own_done = false;
 
   // One job: query block pb of (batch, kv head, head group) bhg, numbered
   // longest causal rows first.  Thread 0 claims the workgroup's next job into
-  // `next` once the job's tiles are done, so that the claim's latency hides
-  // under the epilogue, and the workgroups that finish first take the longest
-  // jobs left.
+  // `next`: the ticket is taken once the job's tiles are done and read after
+  // the epilogue, so that the claim's latency hides under it, and the
+  // workgroups that finish first take the longest jobs left.
   auto run_job = [&](const int bid, int& next) __attribute__((always_inline)) {
   // ---- job -> (position block, batch, kv head, head group)
   const int bhg = bid % geo.n_bhg;
@@ -216,7 +231,9 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
     lse0 = tok0;
     lse_hs = p.total;
     if (i0w >= S) {  // whole workgroup: past the end of a short sequence
-      if (tid == 0) next = pop_job(p.queue, own, geo.nq, geo.n_jobs, own_done);
+      if (tid == 0)
+        next = next_job(p.queue, own, geo.nq, geo.n_jobs, own_done,
+                        claim_own(p.queue, own, own_done));
       return;
     }
   }
@@ -321,34 +338,35 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
 #pragma unroll
     for (int jj = 0; jj < NS; ++jj) gload_j(jj, jj);
   };
-  if (RH >= 0) fill_ring();
-  // max |w_k| over the 128 key-norm weights (two per lane, then the wave)
-  float wk = fmaxf(fabsf(p.k_norm_w[2 * lane]), fabsf(p.k_norm_w[2 * lane + 1]));
+  // Both halves' query rows are loaded first and the ring copies issued
+  // after them, so that one round trip brings them all.
+  u32x4 qraw[2][8];
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) wk = fmaxf(wk, __shfl_xor(wk, o));
+  for (int h = 0; h < 2; ++h) {
+    const long long qrow = (tok0 + (qok[h] ? qi[h] : 0)) * p.Hq + head;
+    const uint16_t* src = p.q + qrow * kD + 64 * half;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qraw[h][j] = ld16(src + 8 * j);  // (rows past the end: row 0, zeroed below)
+  }
+  if (RH >= 0) fill_ring();
   QOp qf[2][kKOps];
   float fsc[2] = {1.f, 1.f};  // E4M3: exp2 units per unit of code product, per half
   bool fast_ok = true;
   // (the halves are fenced from each other so that the scheduler does not
-  // overlap their loads: the register peak of the prologue would otherwise
+  // overlap their work: the register peak of the prologue would otherwise
   // push the loop's operands out to scratch)
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     __builtin_amdgcn_sched_barrier(0);
     float x[64];
-    const long long qrow = (tok0 + (qok[h] ? qi[h] : 0)) * p.Hq + head;
-    const uint16_t* src = p.q + qrow * kD + 64 * half;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      u32x4 u = qok[h] ? ld16(src + 8 * j) : u32x4{0, 0, 0, 0};
-      unpack_bf16x8(u, x + 8 * j);
-    }
+    for (int j = 0; j < 8; ++j) unpack_bf16x8(qok[h] ? qraw[h][j] : u32x4{0, 0, 0, 0}, x + 8 * j);
     float* qs = reinterpret_cast<float*>(smem_raw) + (wv * 32 + qcol) * 65;
-    float qq = 0.f, sii = 0.f, u;
+    float qq = 0.f, u;
     if constexpr (FP8) {
       // E4M3 query row: q' with the power-of-two scale 2^(8-e) that puts its
       // amax = m 2^e (m in [0.5, 1), e clamped to >= -100) in [128, 256)
-      q_norm_rope<RH>(x, half, p, p.pos_offset + qi[h], qs);
+      q_norm_rope<RH>(x, half, p, p.pos_offset + qi[h], qs, qw_s);
       float am = 0.f;
 #pragma unroll
       for (int d = 0; d < 64; ++d) am = fmaxf(am, fabsf(x[d]));
@@ -366,6 +384,7 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
       fsc[h] = p.scale_log2 * ldexpf(1.0f / p.k_scale, e - 8);
       // |codes| of the row and its product with the row's own key's codes
       const unsigned char* krow = p.kp8 + ((tok0 + qm[h]) * p.Hkv + g) * kD + 64 * half;
+      float sii = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float qv[8], kv[8];
@@ -386,8 +405,9 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
       // them), with |k'| <= sqrt(D) max|w_k|; 2^-8 covers the fp32 sums.
       const float kc_norm = (p.k_scale * wk * 1.0625f + 0.0009765625f) * sqrtf((float)kD);
       u = fsc[h] * sqrtf(qq) * kc_norm * (1.0f + 0.00390625f);
+      fast_ok = fast_ok && u - sii <= 100.0f;
     } else {
-      q_prologue<RH>(x, half, p, p.pos_offset + qi[h], qs, qf[h]);
+      q_prologue<RH>(x, half, p, p.pos_offset + qi[h], qs, qf[h], qw_s);
     // Softmax offset.  q' is held pre-scaled by c = scale log2(e), so the
     // scores come out in exp2 units.  Every score of this row is at most
     //   U = |c q'| sqrt(D) max|w_k|   (RoPE keeps norms; the key RMSNorm
@@ -396,25 +416,19 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
     // rounding of k' and the fp32 sums.  With P = exp2(s - U) every weight is
     // at most 1.  The row's own key is visible, so its largest weight is at
     // least exp2(s_ii - U); while that stays above 2^-100 the fixed offset
-    // loses nothing to underflow and no running max is needed.
-      const uint16_t* krow = p.kp + ((tok0 + qm[h]) * p.Hkv + g) * kD + 64 * half;
+    // loses nothing to underflow and no running max is needed (s_ii is taken
+    // below, once the ring holds the row's own key).
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        float qv[8], kv[8];
+        float qv[8];
         unpack_bf16x8(__builtin_bit_cast(u32x4, qf[h][j]), qv);
-        unpack_bf16x8(ld16(krow + 8 * j), kv);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          qq = __builtin_fmaf(qv[e], qv[e], qq);
-          sii = __builtin_fmaf(qv[e], kv[e], sii);
-        }
+        for (int e = 0; e < 8; ++e) qq = __builtin_fmaf(qv[e], qv[e], qq);
       }
       qq = pair_sum32(qq);
-      sii = pair_sum32(sii);
       u = sqrtf(qq) * sqrtf((float)kD) * wk * (1.0f + 0.015625f);
     }
     st[h].m_run = u;
-    fast_ok = fast_ok && u - sii <= 100.0f;
     // the query operands stay in accumulation registers for the whole
     // kernel (the matrix cores read their A/B operands from either file),
     // which leaves the vector registers to the loop's working set
@@ -422,12 +436,38 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
     for (int kk = 0; kk < kKOps; ++kk) asm volatile("; q' operand to AGPRs" : "=a"(qf[h][kk]) : "0"(qf[h][kk]));
     __builtin_amdgcn_sched_barrier(0);
   }
+  if (RH < 0) {
+    lds_barrier();  // every wave is done with its rotation rows
+    fill_ring();
+  }
+  sync_tiles<0>();
+  if constexpr (!FP8) {
+    // s_ii from the ring: the row's own key is in the tile of visit
+    // t_hi - qm / 32, which sits in the stage of that number (< NS: a
+    // workgroup covers at most 256 positions), row qm % 32, logical chunk c
+    // at physical chunk c ^ (row % 16)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int tk = qm[h] / kBN;
+      const int r = qm[h] - tk * kBN;
+      const lds_u8* kr = smem + (t_hi - tk) * kKTile + r * kRowBytes;
+      float sii = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float qv[8], kv[8];
+        unpack_bf16x8(__builtin_bit_cast(u32x4, qf[h][j]), qv);
+        unpack_bf16x8(__builtin_bit_cast(u32x4, lds_read_b128(kr + ((uint32_t)((8 * half + j) ^ (r & 15)) << 4))), kv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sii = __builtin_fmaf(qv[e], kv[e], sii);
+      }
+      sii = pair_sum32(sii);
+      fast_ok = fast_ok && st[h].m_run - sii <= 100.0f;
+    }
+  }
   // Workgroup-uniform: if any row's largest weight could underflow, every
   // wave first takes its rows' exact maxima (a pass of the score products
   // alone) and uses those as the offsets instead.
   const bool exact_max = __syncthreads_or(!fast_ok) != 0;
-  if (RH < 0) fill_ring();  // (the barrier above ended the prologue's LDS use)
-  sync_tiles<0>();
 
   // a tile needs masking for half h if it reaches past the half's first row
   auto masked = [&](int j, int h) __attribute__((always_inline)) { return (t_hi - j) * kBN + kBN - 1 > wrow0 + 32 * h; };
@@ -612,12 +652,12 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
     __builtin_amdgcn_sched_barrier(0);
     sa = sb;
   }
-  if (tid == 0) next = pop_job(p.queue, own, geo.nq, geo.n_jobs, own_done);
+  int ticket = -1;
+  if (tid == 0) ticket = claim_own(p.queue, own, own_done);  // read after the epilogue
   // ---- tail: half 1 of the last tile
   mask(1, nt - 1);
   softmax(1);
   pv_agpr(st[1].acc, va, pf[1]);
-  wait_vm<0>();  // the copies of tiles past the end
 
   // ---- epilogue: normalise, gate (if any), store.  Register r of block bd,
   // lane half h -> dim 32 bd + 8 (r/4) + 4 h + r%4: four runs of 4 dims.
@@ -632,6 +672,12 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
     const long long qrow = (tok0 + qi[h]) * p.Hq + head;
     uint16_t* dst = p.out + qrow * kD + 4 * half;
     const uint16_t* gsrc = p.gate ? p.gate + qrow * kD + 4 * half : nullptr;
+    // the gate words of the row first (all sixteen loads in flight at once)
+    uint2 gg[16];
+    if (gsrc) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) gg[i] = *reinterpret_cast<const uint2*>(gsrc + 32 * (i / 4) + 8 * (i % 4));
+    }
 #pragma unroll
     for (int bd = 0; bd < 4; ++bd) {
 #pragma unroll
@@ -641,11 +687,11 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
         for (int e = 0; e < 4; ++e) o[e] = st[h].acc[bd][4 * q4 + e] * inv;
         const int off = 32 * bd + 8 * q4;
         if (gsrc) {
-          const uint2 gg = *reinterpret_cast<const uint2*>(gsrc + off);
-          o[0] *= sigmoidf_(bf_lo(gg.x));
-          o[1] *= sigmoidf_(bf_hi(gg.x));
-          o[2] *= sigmoidf_(bf_lo(gg.y));
-          o[3] *= sigmoidf_(bf_hi(gg.y));
+          const uint2 g2 = gg[4 * bd + q4];
+          o[0] *= sigmoidf_(bf_lo(g2.x));
+          o[1] *= sigmoidf_(bf_hi(g2.x));
+          o[2] *= sigmoidf_(bf_lo(g2.y));
+          o[3] *= sigmoidf_(bf_hi(g2.y));
         }
         uint2 w;
         w.x = pack_bf16x2(o[0], o[1]);
@@ -654,12 +700,21 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
       }
     }
   }
+  wait_vm<0>();  // the ring copies of tiles past the end, the stores and the claim
+  // (read on every lane, so that the compiler's own wait for the claim sits
+  // here on every path, not at the next job's first loads)
+  const int tk = __builtin_amdgcn_readfirstlane(ticket);
+  if (tid == 0) next = next_job(p.queue, own, geo.nq, geo.n_jobs, own_done, tk);
   };
 
   // ---- persistent loop: one workgroup per CU takes jobs until every queue
-  // is empty.  The barrier at the top of each pass also ends the previous
-  // job's use of the LDS ring.
-  if (tid == 0) job_s[0] = pop_job(p.queue, own, geo.nq, geo.n_jobs, own_done);
+  // is empty.  The barrier at the top of each pass publishes the job and
+  // ends the previous job's use of the LDS ring.  Each job ends with its
+  // memory operations complete (its output stores included): letting them
+  // run into the next job was 1% faster at 16K and 64K but 7-10% slower at
+  // 256K, on three boxes.
+  if (tid == 0)
+    job_s[0] = next_job(p.queue, own, geo.nq, geo.n_jobs, own_done, claim_own(p.queue, own, own_done));
   for (int it = 0;; ++it) {
     __syncthreads();
     const int job = __builtin_amdgcn_readfirstlane(job_s[it & 1]);

@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 3) void flash_fwd_kernel(FlashParams p, G
     // wave's own query rows' region, which it has already read, behind the
     // tiles in flight)
     float* qs = reinterpret_cast<float*>(smem_raw + qoff) + qcol * 64;
-    q_prologue<RH>(x, half, p, p.pos_offset + qi, qs, qf);
+    q_prologue<RH>(x, half, p, p.pos_offset + qi, qs, qf, p.q_norm_w);
   }
   // every wave has read its query rows: tile 1 may take its stage
   lds_barrier();

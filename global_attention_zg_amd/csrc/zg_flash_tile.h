@@ -153,16 +153,17 @@ __device__ __forceinline__ void load_vops(bf16x8 (&va)[8], const lds_u8* const (
 // R/2), all inside lane half 0); x then holds those dims of q'.  RH:
 // rope_dim / 2 when fixed at compile time (21 or 0: the rotation stays in
 // registers); -1 for any other even rope_dim <= 64, which rotates through
-// qs, a private LDS row of 64 floats of this lane.
+// qs, a private LDS row of 64 floats of this lane.  qw: the 128 query-norm
+// weights (p.q_norm_w, or a copy of them in LDS).
 template <int RH>
 __device__ __forceinline__ void q_norm_rope(float (&x)[64], int half, const FlashParams& p,
-                                            long long pos, float* qs) {
+                                            long long pos, float* qs, const float* qw) {
   float ss = 0.f;
 #pragma unroll
   for (int d = 0; d < 64; ++d) ss += x[d] * x[d];
   ss = pair_sum32(ss);
   const float r = 1.0f / sqrtf(ss * (1.0f / kD) + p.eps);
-  const float* wsrc = p.q_norm_w + 64 * half;
+  const float* wsrc = qw + 64 * half;
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     u32x4 wv4 = ld16(wsrc + 4 * j);
@@ -204,8 +205,9 @@ __device__ __forceinline__ void q_norm_rope(float (&x)[64], int half, const Flas
 // products then come out in exp2 units).
 template <int RH>
 __device__ __forceinline__ void q_prologue(float (&x)[64], int half, const FlashParams& p,
-                                           long long pos, float* qs, bf16x8 (&qf)[8]) {
-  q_norm_rope<RH>(x, half, p, pos, qs);
+                                           long long pos, float* qs, bf16x8 (&qf)[8],
+                                           const float* qw) {
+  q_norm_rope<RH>(x, half, p, pos, qs, qw);
 #pragma unroll
   for (int d = 0; d < 64; ++d) x[d] *= p.scale_log2;
 #pragma unroll
