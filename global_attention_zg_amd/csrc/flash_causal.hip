@@ -41,7 +41,6 @@
 // same FMA that subtracts the row's offset.  P V stays in bf16.
 
 #include <algorithm>
-#include <atomic>
 #include <type_traits>
 
 #include "zg_common.h"
@@ -49,6 +48,7 @@
 #include "zg_launch.h"
 #include "zg_lds.h"
 #include "zg_flash_tile.h"
+#include "zg_queue.h"
 
 namespace zg {
 
@@ -131,41 +131,6 @@ __device__ __forceinline__ i32x8 join_i32x8(const u32x4& lo, const u32x4& hi) {
                (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
 }
 
-// Work queues of the persistent grid.  Job j (longest causal rows first,
-// the (batch, kv head, head group) index fastest) sits in queue j % nq at
-// place j / nq; queue[y] counts the places of queue y handed out.  Workgroup
-// b drains queue b % nq first.  Workgroups are dealt to the XCDs in turn, so
-// with nq = 8 an XCD's workgroups share one queue, whose jobs share a KV head
-// when B * Hkv * hgroups is a multiple of 8, and its L2 serves that head's
-// tiles.  An empty queue sends the workgroup to the others in turn, which
-// evens out XCDs that run at different speeds.  Every place is handed out at
-// most once and every job has a place, so each job runs exactly once.  The
-// counters must be zero at launch.
-//
-// A claim is split in two, so that its latency can hide under other work:
-// claim_own takes a ticket from the workgroup's own queue (-1 once that is
-// known to be empty) and next_job turns the ticket into a job, taking from
-// the other queues if it is past the end; -1 when all queues are empty.
-__device__ __forceinline__ int claim_own(int* queue, int own, bool own_done) {
-  return own_done ? -1 : atomicAdd(queue + own, 1);
-}
-__device__ __forceinline__ int next_job(int* queue, int own, int nq, int n_jobs, bool& own_done,
-                                        int ticket) {
-  if (!own_done) {
-    const int j = own + nq * ticket;
-    if (j < n_jobs) return j;
-    own_done = true;
-  }
-  for (int d = 1; d < nq; ++d) {
-    const int y = own + d < nq ? own + d : own + d - nq;
-    if (y + nq * __hip_atomic_load(queue + y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= n_jobs)
-      continue;  // already empty
-    const int j = y + nq * atomicAdd(queue + y, 1);
-    if (j < n_jobs) return j;
-  }
-  return -1;
-}
-
 // RH: rope_dim / 2 when fixed at compile time (21 or 0), else -1.
 // NS: K'/V tile stages in LDS.  FP8: the E4M3 variant.  ILV: the V operand
 // reads are interleaved with the second half's score MFMAs (2-4% faster up
@@ -206,7 +171,7 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
   bool own_done = false;
 
   // One job: query block pb of (batch, kv head, head group) bhg, numbered
-  // longest causal rows first.  Thread 0 claims the workgroup's next job into
+  // longest causal rows first.  Wave 0 claims the workgroup's next job into
   // `next`: the ticket is taken once the job's tiles are done and read after
   // the epilogue, so that the claim's latency hides under it, and the
   // workgroups that finish first take the longest jobs left.
@@ -231,9 +196,9 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
     lse0 = tok0;
     lse_hs = p.total;
     if (i0w >= S) {  // whole workgroup: past the end of a short sequence
-      if (tid == 0)
+      if (wv == 0)
         next = next_job(p.queue, own, geo.nq, geo.n_jobs, own_done,
-                        claim_own(p.queue, own, own_done));
+                        __builtin_amdgcn_readfirstlane(claim_own(p.queue, own, own_done)));
       return;
     }
   }
@@ -653,7 +618,7 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
     sa = sb;
   }
   int ticket = -1;
-  if (tid == 0) ticket = claim_own(p.queue, own, own_done);  // read after the epilogue
+  if (wv == 0) ticket = claim_own(p.queue, own, own_done);  // read after the epilogue
   // ---- tail: half 1 of the last tile
   mask(1, nt - 1);
   softmax(1);
@@ -704,7 +669,7 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
   // (read on every lane, so that the compiler's own wait for the claim sits
   // here on every path, not at the next job's first loads)
   const int tk = __builtin_amdgcn_readfirstlane(ticket);
-  if (tid == 0) next = next_job(p.queue, own, geo.nq, geo.n_jobs, own_done, tk);
+  if (wv == 0) next = next_job(p.queue, own, geo.nq, geo.n_jobs, own_done, tk);
   };
 
   // ---- persistent loop: one workgroup per CU takes jobs until every queue
@@ -713,36 +678,20 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
   // memory operations complete (its output stores included): letting them
   // run into the next job was 1% faster at 16K and 64K but 7-10% slower at
   // 256K, on three boxes.
-  if (tid == 0)
-    job_s[0] = next_job(p.queue, own, geo.nq, geo.n_jobs, own_done, claim_own(p.queue, own, own_done));
+  if (wv == 0)
+    job_s[0] = next_job(p.queue, own, geo.nq, geo.n_jobs, own_done,
+                        __builtin_amdgcn_readfirstlane(claim_own(p.queue, own, own_done)));
   for (int it = 0;; ++it) {
     __syncthreads();
     const int job = __builtin_amdgcn_readfirstlane(job_s[it & 1]);
     if (job < 0) break;
     int next = -1;
     run_job(job, next);
-    if (tid == 0) job_s[(it + 1) & 1] = next;
+    if (wv == 0) job_s[(it + 1) & 1] = next;
   }
 }
 
 constexpr int kCStages = 8;
-
-// Compute units of the current device (looked up once per device).
-int device_cu_count() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = -1;
-  if (dev >= 0) {
-    const int c = cached[dev].load(std::memory_order_relaxed);
-    if (c > 0) return c;
-  }
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) !=
-          hipSuccess || n < 1)
-    n = 256;
-  if (dev >= 0) cached[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
 
 // Sequences up to this length use the interleaved schedule (ILV).
 constexpr int kIlvMaxS = 65536;

@@ -386,8 +386,8 @@ int zg_quantize_fp8(long long n, const void* x, float scale, void* q, void* stre
 int zg_linear_fp8(int M, int N, int K, const void* xq, const void* wq, float out_scale,
                   void* y, void* stream);
 
-/* Bytes of device workspace zg_attn_bwd needs (recomputed Q' and K', dO,
- * per-row LSE*log2(e) and rowsum(dY*Y), one partial sum of a weight
+/* Bytes of device workspace zg_attn_bwd needs (recomputed Q' * c and K',
+ * dO, per-row -LSE*log2(e) and rowsum(dY*Y), one partial sum of a weight
  * gradient per workgroup of the two attention-gradient kernels, and 256
  * chunk sums of each); 0 for an invalid p. */
 size_t zg_attn_bwd_workspace_size(const zg_attn_params* p);
