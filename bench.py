@@ -47,7 +47,7 @@ KW = dict(rope_dim=42, rope_theta=10000.0, rms_eps=1e-6)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flash_causal_global_256k_traffic.json")
 # sources the flash kernel is compiled from (the traffic summary is keyed by their hash)
 FLASH_SRCS = [os.path.join(ROOT, "global_attention_zg_amd", "csrc", f)
-              for f in ("flash_causal.hip", "zg_flash_tile.h", "zg_common.h", "zg_lds.h")]
+              for f in ("flash_causal.hip", "zg_flash_tile.h", "zg_common.h", "zg_lds.h", "zg_queue.h")]
 
 
 def inband_pairs(S, W):
