@@ -240,6 +240,36 @@ def test_without_lse_and_with_workspace_reuse():
     zc.compare(o1.float().cpu().numpy(), o, "no lse")
 
 
+def test_global_forward_with_dirty_and_reused_workspace():
+    """The global (causal) forward keeps its work-queue counters in the
+    workspace and clears them itself: a workspace full of 0xFF bytes, the same
+    workspace again right after, and a 256-byte counter-only workspace with
+    k_out all give the bits of a fresh zeroed workspace."""
+    bd = _binding()
+    c = zc.fwd_case(114, 2, 777, 8, 2, gated=False)
+    q, k, v = (zc.to_dev(c[n], torch) for n in ("q", "k", "v"))
+    gq = torch.from_numpy(c["gq"]).cuda()
+    gk = torch.from_numpy(c["gk"]).cuda()
+    p = bd.make_params(2, 777, 8, 2, 128, 0)
+    n = bd.zg_attn_fwd_workspace_size(p)
+    assert n == 2 * 777 * 2 * 128 * 2 + bd.QUEUE_BYTES
+    fresh = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    o_ref, l_ref = bd.zg_attn_fwd(q, k, v, None, gq, gk, window=0, want_lse=True, workspace=fresh)
+    dirty = torch.full((n,), 255, dtype=torch.uint8, device="cuda")
+    for rep in range(2):  # the second call finds the counters the first one left
+        o, l = bd.zg_attn_fwd(q, k, v, None, gq, gk, window=0, want_lse=True, workspace=dirty)
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), rep
+        assert torch.equal(l.view(torch.int32), l_ref.view(torch.int32)), rep
+    ko = torch.empty_like(k)
+    small = torch.full((bd.QUEUE_BYTES,), 255, dtype=torch.uint8, device="cuda")
+    o, _ = bd.zg_attn_fwd(q, k, v, None, gq, gk, window=0, k_out=ko, workspace=small)
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16))
+    ref, _ = run_oracle(c, 0, gated=False)
+    zc.compare(o_ref.float().cpu().numpy(), ref, "global, dirty workspace")
+
+
 def test_too_small_workspace_is_rejected_before_launch():
     bd = _binding()
     c = zc.fwd_case(113, 1, 64, 8, 2, gated=False)

@@ -102,7 +102,11 @@ def test_decode_block_step_replays_equal_eager():
             assert torch.equal(layer.vc.view(torch.int16), caches[i][1].view(torch.int16))
 
 
-def test_forward_replays_equal_eager():
+@pytest.mark.parametrize("window", [128, 0])
+def test_forward_replays_equal_eager(window):
+    """A captured forward replays to the eager bits; at window 0 this runs the
+    persistent causal kernel, whose work-queue counters the captured key
+    prologue clears on every replay."""
     bd = _binding()
     c = zc.fwd_case(510, 1, 700, 16, 4, gated=True)
     q, k, v, g = (zc.to_dev(c[n], torch) for n in ("q", "k", "v", "gate"))
@@ -111,7 +115,7 @@ def test_forward_replays_equal_eager():
     out = torch.empty_like(q)
     lse = torch.empty((1, 16, 700), dtype=torch.float32, device="cuda")
     ko = torch.empty_like(k)
-    run = lambda: bd.zg_attn_fwd(q, k, v, g, gq, gk, window=128, out=out, lse=lse,  # noqa: E731
+    run = lambda: bd.zg_attn_fwd(q, k, v, g, gq, gk, window=window, out=out, lse=lse,  # noqa: E731
                                  k_out=ko, **KW)
     run()
     torch.cuda.synchronize()
