@@ -198,10 +198,15 @@ def flush_buffer(torch):
 
 
 def flash_source_hash():
+    """sha256[:16] of the kernel's sources with their // comments and blank
+    lines removed, so that an edit of the comments alone keeps the counters."""
     h = hashlib.sha256()
     for path in FLASH_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

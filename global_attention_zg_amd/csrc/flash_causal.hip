@@ -21,15 +21,20 @@
 //   B: O1 += V(j)^T P1^T             beside  softmax of half 0 on tile j+1 -> P0
 //   C: S1 = K'(j+1) Q1'^T           beside  the V(j+1) operand reads
 //   D: O0 += V(j+1)^T P0^T           beside  the K'(j+2) operand reads
-// A lazy rescale of an accumulator (the running max grew by more than 2^8 in
-// exp2 units) is applied at the next slot boundary, before that half's next
-// PV product; the row sum is rescaled at once.
+// No running max: each row's softmax offset is a bound on its scores taken
+// from the QK-RMSNorm (see the prologue), so P = exp2(s - U) needs neither a
+// max nor a rescale; a workgroup whose rows could underflow under that bound
+// first takes the exact row maxima in a scores-only pass.
 //
 // K'/V tiles go global -> LDS directly (global_load_lds_dwordx4) through a
 // ring of NS tile stages with the banded kernel's swizzled 256-byte rows;
 // copies fly NS - 2 tiles ahead, and one barrier per tile both publishes the
 // tile two ahead and frees the stage of the tile just read.  Tiles are
-// visited from the diagonal down; query blocks are launched longest-first.
+// visited from the diagonal down.
+//
+// The grid is persistent: one workgroup per CU takes jobs (query blocks,
+// longest causal rows first) from per-XCD work queues (zg_queue.h) until all
+// are empty, so that XCDs running at different speeds finish together.
 //
 // The E4M3 variant (page "ZGCM-1:面向数学与智能体搜索的全开源高效基础模型",
 // section 前置知识 › FP8 混合精度训练与 TWEO: forward matrix multiplies in
