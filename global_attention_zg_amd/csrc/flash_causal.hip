@@ -139,8 +139,8 @@ __device__ __forceinline__ i32x8 join_i32x8(const u32x4& lo, const u32x4& hi) {
 // RH: rope_dim / 2 when fixed at compile time (21 or 0), else -1.
 // NS: K'/V tile stages in LDS.  FP8: the E4M3 variant.  ILV: the V operand
 // reads are interleaved with the second half's score MFMAs (2-4% faster up
-// to 64K keys; at 256K no faster, and the changed pace of the workgroups
-// triples their L2 misses, so long sequences run without it).
+// to 64K keys, and 3% at 256K since the grid is persistent; the E4M3 variant
+// keeps the plain schedule above 64K keys, where it has not been measured).
 template <int RH, bool PACKED, int NS, bool FP8, bool ILV>
 __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams p, Geo geo) {
   constexpr int kKRow = FP8 ? kD : kRowBytes;  // bytes per K' row in LDS
@@ -698,8 +698,9 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
 
 constexpr int kCStages = 8;
 
-// Sequences up to this length use the interleaved schedule (ILV).
-constexpr int kIlvMaxS = 65536;
+// E4M3 sequences up to this length use the interleaved schedule (ILV); bf16
+// ones always do.
+constexpr int kIlvMaxSFp8 = 65536;
 
 template <int RH, bool PACKED, bool FP8 = false, bool ILV = true>
 void launch_causal(dim3 grid, hipStream_t stream, const FlashParams& p, const Geo& geo) {
@@ -725,7 +726,7 @@ hipError_t launch_flash_causal(const FlashParams& p, hipStream_t stream) {
   const int wgs = (int)std::min<long long>(blocks, device_cu_count());
   geo.nq = std::min(wgs, 8);
   const dim3 grid((unsigned)wgs);
-  const bool ilv = p.S <= kIlvMaxS;
+  const bool ilv = p.S <= kIlvMaxSFp8;
   if (p.kp8) {  // the E4M3 variant: fixed-length batches
     if (p.cu_seqlens) return hipErrorInvalidValue;
     if (p.rope_half == 21 && !ilv) launch_causal<21, false, true, false>(grid, stream, p, geo);
@@ -737,8 +738,7 @@ hipError_t launch_flash_causal(const FlashParams& p, hipStream_t stream) {
     else if (p.rope_half == 0) launch_causal<0, true>(grid, stream, p, geo);
     else launch_causal<-1, true>(grid, stream, p, geo);
   } else {
-    if (p.rope_half == 21 && !ilv) launch_causal<21, false, false, false>(grid, stream, p, geo);
-    else if (p.rope_half == 21) launch_causal<21, false>(grid, stream, p, geo);
+    if (p.rope_half == 21) launch_causal<21, false>(grid, stream, p, geo);
     else if (p.rope_half == 0) launch_causal<0, false>(grid, stream, p, geo);
     else launch_causal<-1, false>(grid, stream, p, geo);
   }

@@ -337,10 +337,10 @@ def test_global_exact_max_fallback(Hq, Hkv):
     check_lse(got["lse"], ref_lse, f"exact-max path {Hq}/{Hkv}")
 
 
-def test_global_long_sequence_schedule():
-    """Past 65536 keys the global kernel runs its other instruction schedule
-    (the V reads not interleaved with the score products); S = 70001, 8/2
-    heads, sampled rows against the oracle."""
+def test_global_long_sequence():
+    """A global layer past 65536 keys (where the E4M3 variant changes its
+    schedule; the bf16 kernel keeps the interleaved one at every length):
+    S = 70001, 8/2 heads, sampled rows against the oracle."""
     S = 70001
     c = zc.fwd_case(180, 1, S, 8, 2, gated=False)
     g = run_gpu(c, 0, gated=False)
