@@ -138,10 +138,12 @@ __device__ __forceinline__ i32x8 join_i32x8(const u32x4& lo, const u32x4& hi) {
 
 // RH: rope_dim / 2 when fixed at compile time (21 or 0), else -1.
 // NS: K'/V tile stages in LDS.  FP8: the E4M3 variant.  ILV: the V operand
-// reads are interleaved with the second half's score MFMAs (2-4% faster up
-// to 64K keys, and 3% at 256K since the grid is persistent; the E4M3 variant
-// keeps the plain schedule above 64K keys, where both run alike).
-template <int RH, bool PACKED, int NS, bool FP8, bool ILV>
+// reads are interleaved with the second half's score MFMAs, in groups of
+// ILV MFMAs and 2 * ILV reads (0: not interleaved).  Interleaving is 2-4%
+// faster up to 64K keys and 3% at 256K since the grid is persistent; groups
+// of two are 0.5-0.8% faster again at 256K (0.3% slower at 64K); the E4M3
+// variant keeps the plain schedule above 64K keys, where both run alike.
+template <int RH, bool PACKED, int NS, bool FP8, int ILV>
 __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams p, Geo geo) {
   constexpr int kKRow = FP8 ? kD : kRowBytes;  // bytes per K' row in LDS
   constexpr int kKTile = kBN * kKRow;
@@ -603,11 +605,12 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
     vops(sa);
     // one score MFMA, then its share of the sixteen V reads (so that the
     // reads spread under the products instead of queueing at the barrier)
-    if constexpr (ILV) {
+    if constexpr (ILV > 0) {
+      static_assert(kQkMfma % ILV == 0, "whole groups of score MFMAs");
 #pragma unroll
-      for (int gg = 0; gg < kQkMfma; ++gg) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 16 / kQkMfma, 0);  // LDS reads
+      for (int gg = 0; gg < kQkMfma / ILV; ++gg) {
+        __builtin_amdgcn_sched_group_barrier(0x008, ILV, 0);   // MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 16 * ILV / kQkMfma, 0);  // LDS reads
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -698,11 +701,12 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
 
 constexpr int kCStages = 8;
 
-// E4M3 sequences up to this length use the interleaved schedule (ILV); bf16
-// ones always do.
-constexpr int kIlvMaxSFp8 = 65536;
+// Interleaved schedules by length: bf16 sequences longer than this use
+// groups of two, shorter ones groups of one; E4M3 sequences longer than it
+// are not interleaved.
+constexpr int kIlvLongS = 65536;
 
-template <int RH, bool PACKED, bool FP8 = false, bool ILV = true>
+template <int RH, bool PACKED, bool FP8 = false, int ILV = 1>
 void launch_causal(dim3 grid, hipStream_t stream, const FlashParams& p, const Geo& geo) {
   hipLaunchKernelGGL((flash_causal_kernel<RH, PACKED, kCStages, FP8, ILV>), grid, dim3(kCThreads),
                      0, stream, p, geo);
@@ -726,10 +730,10 @@ hipError_t launch_flash_causal(const FlashParams& p, hipStream_t stream) {
   const int wgs = (int)std::min<long long>(blocks, device_cu_count());
   geo.nq = std::min(wgs, 8);
   const dim3 grid((unsigned)wgs);
-  const bool ilv = p.S <= kIlvMaxSFp8;
+  const bool long_s = p.S > kIlvLongS;
   if (p.kp8) {  // the E4M3 variant: fixed-length batches
     if (p.cu_seqlens) return hipErrorInvalidValue;
-    if (p.rope_half == 21 && !ilv) launch_causal<21, false, true, false>(grid, stream, p, geo);
+    if (p.rope_half == 21 && long_s) launch_causal<21, false, true, 0>(grid, stream, p, geo);
     else if (p.rope_half == 21) launch_causal<21, false, true>(grid, stream, p, geo);
     else if (p.rope_half == 0) launch_causal<0, false, true>(grid, stream, p, geo);
     else launch_causal<-1, false, true>(grid, stream, p, geo);
@@ -738,7 +742,8 @@ hipError_t launch_flash_causal(const FlashParams& p, hipStream_t stream) {
     else if (p.rope_half == 0) launch_causal<0, true>(grid, stream, p, geo);
     else launch_causal<-1, true>(grid, stream, p, geo);
   } else {
-    if (p.rope_half == 21) launch_causal<21, false>(grid, stream, p, geo);
+    if (p.rope_half == 21 && long_s) launch_causal<21, false, false, 2>(grid, stream, p, geo);
+    else if (p.rope_half == 21) launch_causal<21, false>(grid, stream, p, geo);
     else if (p.rope_half == 0) launch_causal<0, false>(grid, stream, p, geo);
     else launch_causal<-1, false>(grid, stream, p, geo);
   }
