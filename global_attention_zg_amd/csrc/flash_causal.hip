@@ -594,6 +594,16 @@ __global__ __launch_bounds__(kCThreads, 1) void flash_causal_kernel(FlashParams 
     __builtin_amdgcn_sched_barrier(0);
     qk(0);
     softmax(1);
+    if constexpr (!FP8) {
+      // each score MFMA followed by six of the softmax's VALU instructions
+      // (left to the scheduler, it clustered them: 1.1-1.3% slower at 16K
+      // and 256K)
+#pragma unroll
+      for (int gg = 0; gg < kQkMfma; ++gg) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);  // VALU
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
     mask(0, j + 1);
     // B
