@@ -596,6 +596,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdParams p, DqGeo geo) 
 #pragma unroll
       for (int bd = 0; bd < 4; ++bd)
         acc[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(kt, tro, bd, 1), dsf1, acc[bd], 0, 0, 0);
+      // each score / dP MFMA after its LDS operand read (left to the
+      // scheduler, the reads went first in a block: 1-2% slower)
+#pragma unroll
+      for (int gg = 0; gg < 16; ++gg) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      }
     }
     // tile j+1 must have landed; tile j+2's four copies may still fly
     if (issue) sync_tiles<4>();
@@ -820,6 +827,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dkv_kernel(BwdParams p) {
       for (int bd = 0; bd < 4; ++bd) {
         dvv[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(ot, tro, bd, 1), pf1, dvv[bd], 0, 0, 0);
         dk[bd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_operand(qt, tro, bd, 1), df1, dk[bd], 0, 0, 0);
+      }
+      // each score MFMA after its operand read and each dP MFMA after its
+      // two (left to the scheduler, the reads went first: 1-2% slower)
+#pragma unroll
+      for (int gg = 0; gg < 8; ++gg) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      }
+#pragma unroll
+      for (int gg = 0; gg < 8; ++gg) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
       }
     }
     // tile i+1 has landed and every wave is done with tile i; then tile i+2
