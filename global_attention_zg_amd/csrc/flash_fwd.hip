@@ -70,6 +70,22 @@ __device__ __forceinline__ int q_stage_off(int w) {
   return w < 2 ? (1 + w) * kTileBytes : kVOff + (w - 1) * kTileBytes;
 }
 
+// The query, gate and output rows are touched once, so they move with the
+// non-temporal hint and leave L2 to the K'/V tiles that the neighbouring
+// query blocks share (B4 S4096 with cold caches: 0.155-0.159 -> 0.137-0.140
+// ms; 256K layer -2%).
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16_nt(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
+// dma16 with the non-temporal hint
+__device__ __forceinline__ void dma16_nt(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "s"(lds)
+               : "memory");
+}
+
 // RH: rope_dim / 2 when known at compile time (0 or 21: the rotation runs in
 // registers), -1 for any other rope_dim (rotation through LDS).
 template <int RH, bool PACKED>
@@ -229,7 +245,7 @@ __global__ __launch_bounds__(kThreads, 3) void flash_fwd_kernel(FlashParams p, G
   for (int n = 0; n < 8; ++n) {
     const int row = 4 * n + (lane >> 4);
     const long long qr = (tok0 + min(wrow0 + row, S - 1)) * p.Hq + head;
-    dma16(p.q + qr * kD + 8 * ((lane & 15) ^ (row & 15)), lds_addr(smem + qoff + n * 1024));
+    dma16_nt(p.q + qr * kD + 8 * ((lane & 15) ^ (row & 15)), lds_addr(smem + qoff + n * 1024));
   }
   gload(t_hi, 0);
   // ---- fused query prologue: RMSNorm (+ weight), partial RoPE, -> bf16 B operand
@@ -265,7 +281,7 @@ __global__ __launch_bounds__(kThreads, 3) void flash_fwd_kernel(FlashParams p, G
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const long long gr = (tok0 + min(wrow0 + 8 * k + (lane >> 3), S - 1)) * p.Hq + head;
-        gco[4 * r + k] = ld16(p.gate + gr * kD + 64 * r + 8 * (lane & 7));
+        gco[4 * r + k] = ld16_nt(p.gate + gr * kD + 64 * r + 8 * (lane & 7));
       }
     }
   }
@@ -317,7 +333,7 @@ __global__ __launch_bounds__(kThreads, 3) void flash_fwd_kernel(FlashParams p, G
         u32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(o[2 * e], o[2 * e + 1]);
-        st16(p.out + orw * kD + 64 * r + 8 * (lane & 7), w);
+        st16_nt(p.out + orw * kD + 64 * r + 8 * (lane & 7), w);
       }
     }
   }
